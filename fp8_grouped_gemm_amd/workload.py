@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs for the FP8 MoE expert forward.
+
+This module only draws inputs.  It holds none of the forward's arithmetic:
+the FP8 quantisation of the inputs uses torch's own float8_e4m3fn cast, and
+both the CPU oracle and the HIP path consume exactly the bytes it returns.
+
+Recipe (one per workload, all synthetic, standing in for the model shapes
+the DeepGEMM MegaMoE pages benchmark: DeepSeek "Flash" 4096/2048/256/top-6,
+"Pro" 7168/3072/384/top-6, and a skewed-routing stress):
+  x        f32 N(0,1) [T,H], quantised per 1x128 block
+  W1[e]    f32 N(0, 1/sqrt(H)) [2I,H] (gate rows, then up rows), per 128x128
+  W2[e]    f32 N(0, 1/sqrt(I)) [H,I], per 128x128
+  block quantisation: sf = max(amax, 1e-10)/448, q = e4m3(clamp(v/sf, +-448))
+  router   logits N(0,1) [T,E]; the skewed workload adds a Zipf(1.2)-ranked
+           bias -1.2*ln(rank_e) with rank_e = 1 + (a seeded permutation)[e];
+           top-K by logit (ties: lower expert id first), topk_w = softmax over
+           the K selected logits.
+Every tensor comes from its own torch.Generator seeded from (seed, tag,
+expert), so any expert's weights can be redrawn alone.
+"""
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    K: int
+    skew: bool = False
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic FLOP if every slot is active: 2*(T*K)*3*H*I."""
+        return 2.0 * self.T * self.K * 3.0 * self.H * self.I
+
+
+CONFIGS = {
+    "tiny": MoEConfig("tiny", 64, 256, 128, 8, 2),
+    "flash_decode": MoEConfig("flash_decode", 128, 4096, 2048, 256, 6),
+    "flash_prefill": MoEConfig("flash_prefill", 2048, 4096, 2048, 256, 6),
+    "pro_prefill": MoEConfig("pro_prefill", 8192, 7168, 3072, 384, 6),
+    "skewed": MoEConfig("skewed", 4096, 4096, 2048, 256, 8, skew=True),
+}
+
+TAG_LOGITS, TAG_X, TAG_W1, TAG_W2, TAG_PERM = 0, 1, 2, 3, 4
+
+
+def default_seed(cfg: MoEConfig) -> int:
+    return 20261202 + list(CONFIGS).index(cfg.name) + 1 if cfg.name in CONFIGS else 20261202
+
+
+def _gen(device, seed: int, tag: int, e: int = 0) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1000003 + tag * 7919 + e * 104729) % (2 ** 63))
+    return g
+
+
+def quantize_blocks(v: torch.Tensor, br: int, bc: int):
+    """Quantise a 2-D f32 tensor in br x bc blocks to e4m3 codes + f32 scales."""
+    R, C = v.shape
+    assert R % br == 0 and C % bc == 0
+    blk = v.reshape(R // br, br, C // bc, bc)
+    amax = blk.abs().amax(dim=(1, 3))
+    sf = torch.clamp(amax, min=1e-10) / 448.0
+    q = torch.clamp(blk / sf[:, None, :, None], -448.0, 448.0)
+    q = q.reshape(R, C).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.contiguous(), sf.to(torch.float32).contiguous()
+
+
+def make_routing(cfg: MoEConfig, seed: int, device="cpu"):
+    g = _gen(device, seed, TAG_LOGITS)
+    logits = torch.randn(cfg.T, cfg.E, generator=g, device=device, dtype=torch.float32)
+    if cfg.skew:
+        gp = _gen(device, seed, TAG_PERM)
+        rank = 1 + torch.randperm(cfg.E, generator=gp, device=device)
+        logits = logits + (-1.2 * torch.log(rank.to(torch.float32)))[None, :]
+    order = torch.sort(logits, dim=1, descending=True, stable=True)
+    idx = order.indices[:, :cfg.K].to(torch.int32).contiguous()
+    sel = order.values[:, :cfg.K]
+    w = torch.softmax(sel, dim=1).to(torch.float32).contiguous()
+    return idx, w
+
+
+def make_x(cfg: MoEConfig, seed: int, device="cpu"):
+    g = _gen(device, seed, TAG_X)
+    x = torch.randn(cfg.T, cfg.H, generator=g, device=device, dtype=torch.float32)
+    return quantize_blocks(x, 1, 128)
+
+
+def make_expert(cfg: MoEConfig, seed: int, e: int, device="cpu"):
+    """(w1 [2I,H] u8, w1_sf [2I/128,H/128], w2 [H,I] u8, w2_sf [H/128,I/128])."""
+    g1 = _gen(device, seed, TAG_W1, e)
+    w1 = torch.randn(2 * cfg.I, cfg.H, generator=g1, device=device,
+                     dtype=torch.float32) * (1.0 / cfg.H ** 0.5)
+    q1, s1 = quantize_blocks(w1, 128, 128)
+    del w1
+    g2 = _gen(device, seed, TAG_W2, e)
+    w2 = torch.randn(cfg.H, cfg.I, generator=g2, device=device,
+                     dtype=torch.float32) * (1.0 / cfg.I ** 0.5)
+    q2, s2 = quantize_blocks(w2, 128, 128)
+    return q1, s1, q2, s2
+
+
+def make_weights(cfg: MoEConfig, seed: int, device="cpu"):
+    """All experts stacked: w1 [E,2I,H] u8, w1_sf, w2 [E,H,I] u8, w2_sf."""
+    E, H, I = cfg.E, cfg.H, cfg.I
+    w1 = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=device)
+    w1_sf = torch.empty(E, 2 * I // 128, H // 128, dtype=torch.float32, device=device)
+    w2 = torch.empty(E, H, I, dtype=torch.uint8, device=device)
+    w2_sf = torch.empty(E, H // 128, I // 128, dtype=torch.float32, device=device)
+    for e in range(E):
+        q1, s1, q2, s2 = make_expert(cfg, seed, e, device)
+        w1[e].copy_(q1)
+        w1_sf[e].copy_(s1)
+        w2[e].copy_(q2)
+        w2_sf[e].copy_(s2)
+    return w1, w1_sf, w2, w2_sf
+
+
+def make_inputs(cfg: MoEConfig, seed: int, device="cpu"):
+    x, x_sf = make_x(cfg, seed, device)
+    idx, w = make_routing(cfg, seed, device)
+    w1, w1_sf, w2, w2_sf = make_weights(cfg, seed, device)
+    return dict(x=x, x_sf=x_sf, topk_idx=idx, topk_w=w, w1=w1, w1_sf=w1_sf,
+                w2=w2, w2_sf=w2_sf)
+
+
+def custom_config(T, H, I, E, K, skew=False, name="custom") -> MoEConfig:
+    return MoEConfig(name, T, H, I, E, K, skew)

@@ -1,0 +1,194 @@
+"""ctypes wrapper of the CPU oracle (oracle/moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: tests/, the smoke entry and the benchmark's
+CPU-baseline leg may import this module; the product package never does,
+and this module imports nothing from the product package.  All arrays are
+numpy arrays on the host.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+ORC_NO_REQUANT = 1
+ORC_NO_BF16 = 2
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        L.orc_e4m3_decode.restype = ctypes.c_float
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_bf16_rne.restype = ctypes.c_uint16
+        L.orc_bf16_rne.argtypes = [ctypes.c_float]
+        L.orc_bf16_to_f32.restype = ctypes.c_float
+        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_route.restype = ctypes.c_int
+        L.orc_route.argtypes = [ctypes.c_int] * 4 + [_i32p, _i32p, _i32p, _i32p,
+                                                     ctypes.c_int, _i32p]
+        L.orc_block_dot_e4m3.restype = ctypes.c_double
+        L.orc_block_dot_e4m3.argtypes = [_u8p, _u8p, ctypes.c_int]
+        L.orc_swiglu.restype = ctypes.c_float
+        L.orc_swiglu.argtypes = [ctypes.c_float] * 3
+        L.orc_requant_block.restype = None
+        L.orc_requant_block.argtypes = [_f32p, ctypes.c_int, _u8p, _f32p]
+        L.orc_moe_forward.restype = ctypes.c_int
+        L.orc_moe_forward.argtypes = (
+            [ctypes.c_int] * 5
+            + [_u8p, _f32p, _i32p, _f32p]
+            + [ctypes.POINTER(ctypes.c_void_p)] * 4
+            + [ctypes.c_int, _i32p, _u16p, _f32p, _f32p, _u8p, _f32p, _u16p,
+               ctypes.c_int, ctypes.c_int])
+        L.orc_max_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a, t):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(t)
+
+
+def e4m3_decode(code: int) -> float:
+    return lib().orc_e4m3_decode(int(code) & 0xFF)
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(float(v))
+
+
+def bf16_rne(v: float) -> int:
+    return lib().orc_bf16_rne(float(v))
+
+
+def bf16_to_f32(b: int) -> float:
+    return lib().orc_bf16_to_f32(int(b) & 0xFFFF)
+
+
+def block_dot(a: np.ndarray, b: np.ndarray) -> float:
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    return lib().orc_block_dot_e4m3(_p(a, _u8p), _p(b, _u8p), a.size)
+
+
+def swiglu(g: float, u: float, w: float) -> float:
+    return lib().orc_swiglu(float(g), float(u), float(w))
+
+
+def requant_block(v: np.ndarray):
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    q = np.zeros(v.size, np.uint8)
+    sf = ctypes.c_float(0)
+    lib().orc_requant_block(_p(v, _f32p), v.size, _p(q, _u8p), ctypes.byref(sf))
+    return q, sf.value
+
+
+def route(topk_idx: np.ndarray, num_experts: int, row_align: int, r_cap: int):
+    """Plan: returns (counts[E], offsets[E+1], row_src[r_cap], src_row[T*K], n_bad)."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, K = idx.shape
+    E = num_experts
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    row_src = np.zeros(max(r_cap, 1), np.int32)
+    src_row = np.zeros(max(T * K, 1), np.int32)
+    bad = lib().orc_route(T, K, E, row_align, _p(idx, _i32p), _p(counts, _i32p),
+                          _p(offsets, _i32p), _p(row_src, _i32p), r_cap,
+                          _p(src_row, _i32p))
+    return counts, offsets, row_src[:r_cap], src_row[:T * K], bad
+
+
+def moe_forward(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
+                flags=0, want=(), nthreads=0):
+    """Oracle forward.
+
+    w1, w1_sf, w2, w2_sf: sequences indexed by expert (arrays or None for
+    experts no listed token uses).  tokens: optional list of token ids.
+    want: subset of {"acc1", "h", "partial", "y_f32"} extra outputs.
+    Returns dict with "y" (uint16 bf16 bits [n,H]) and requested extras,
+    indexed by position in the token list (slot-major: row p*K + j).
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    x_sf = np.ascontiguousarray(x_sf, dtype=np.float32)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    wts = np.ascontiguousarray(topk_w, dtype=np.float32)
+    T, H = x.shape
+    K = idx.shape[1]
+    E = len(w1)
+    I = None
+    keep = []
+
+    def ptrs(seq, dt):
+        arr = (ctypes.c_void_p * E)()
+        for e, a in enumerate(seq):
+            if a is None:
+                arr[e] = None
+            else:
+                a = np.ascontiguousarray(a, dtype=dt)
+                keep.append(a)
+                arr[e] = a.ctypes.data
+        return arr
+
+    for a in w2:
+        if a is not None:
+            I = a.shape[-1]
+            break
+    if I is None:
+        for a in w1:
+            if a is not None:
+                I = a.shape[0] // 2
+                break
+    if I is None:
+        I = 128
+    p1, p1s = ptrs(w1, np.uint8), ptrs(w1_sf, np.float32)
+    p2, p2s = ptrs(w2, np.uint8), ptrs(w2_sf, np.float32)
+    if tokens is None:
+        toks = None
+        n = T
+    else:
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = toks.size
+    y = np.zeros((n, H), np.uint16)
+    y_f32 = np.zeros((n, H), np.float32) if "y_f32" in want else None
+    acc1 = np.zeros((n * K, 2 * I), np.float32) if "acc1" in want else None
+    h = np.zeros((n * K, I), np.uint8) if "h" in want else None
+    h_sf = np.zeros((n * K, I // 128), np.float32) if "h" in want else None
+    partial = np.zeros((n * K, H), np.uint16) if "partial" in want else None
+    rc = lib().orc_moe_forward(
+        T, H, I, E, K, _p(x, _u8p), _p(x_sf, _f32p), _p(idx, _i32p), _p(wts, _f32p),
+        p1, p1s, p2, p2s, n, _p(toks, _i32p), _p(y, _u16p), _p(y_f32, _f32p),
+        _p(acc1, _f32p), _p(h, _u8p), _p(h_sf, _f32p), _p(partial, _u16p),
+        int(flags), int(nthreads))
+    if rc < 0:
+        raise ValueError("oracle: invalid shape or missing expert weights")
+    out = {"y": y, "n_bad": rc}
+    if y_f32 is not None:
+        out["y_f32"] = y_f32
+    if acc1 is not None:
+        out["acc1"] = acc1
+    if h is not None:
+        out["h"] = h
+        out["h_sf"] = h_sf
+    if partial is not None:
+        out["partial"] = partial
+    return out
+
+
+def max_threads() -> int:
+    return lib().orc_max_threads()

@@ -1,0 +1,365 @@
+/*
+ * CPU oracle for the FP8 MoE expert forward.  TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke entry and the benchmark's CPU-baseline leg
+ * may load this library.  It shares no code, header, table or helper with
+ * the HIP path under fp8_grouped_gemm_amd/, and the HIP path never calls it.
+ *
+ * What it computes, step by step, and the passage each step follows
+ * (pages cited by title and section; the reading taken where a page is
+ * silent is stated at the step):
+ *
+ *   route      "07 · MegaMoE" §7 (count tokens per expert, skip masked
+ *              slots) and §4 (per-expert pool segments aligned to the row
+ *              tile, pool offset = prefix sum of aligned segment sizes).
+ *              Reading: rows inside a segment are in ascending flat slot
+ *              index f = t*K + j; §7 says the order inside a segment does
+ *              not affect correctness, so a fixed order is a free choice.
+ *   L1         "MegaMoE SM90 Implementation Design" §5.3: block-scaled FP8
+ *              GEMM, fp32 accumulation, one activation scale per 1x128 and
+ *              one weight scale per 128x128 block (§15.2 scale layout
+ *              [E, N/128, K/128]).  Reading: the sum inside one 128-wide K
+ *              block is taken exactly and rounded once to f32, then
+ *              acc = fmaf(sa*sb, p, acc) over K blocks in ascending order.
+ *   SwiGLU     same doc §10.1 and "07 · MegaMoE" §8: silu(g)*u*w with
+ *              silu(g) = g / (1 + exp(-g)), the router weight applied here
+ *              once.  Gate = rows [0, I) of W1, up = rows [I, 2I).
+ *   requant    DeepGEMM PR #440 "How it works"/"Ring sizing" text on the
+ *              raw scale: sf = max(amax, 1e-10) / 448, q = e4m3(h / sf), one
+ *              scale per 128 consecutive intermediate columns (PR #360 on
+ *              per-128 quantisation of the L1 output).  Division correctly
+ *              rounded; e4m3 is OCP E4M3FN with round-to-nearest-even and
+ *              saturation to +-448.
+ *   L2         design doc §3.3 / §11.1: same block-scaled GEMM over the
+ *              intermediate dimension, fp32 result cast to BF16 (RNE) per
+ *              (token, slot) partial.
+ *   combine    design doc §11.2 and "07 · MegaMoE" §9: per token, fp32 sum
+ *              of its active slots' BF16 partials (slot order ascending,
+ *              starting from 0), cast to BF16.  Slots with an expert id < 0
+ *              (masked) or >= E (out of range) contribute nothing; a token
+ *              with no active slot gets y = 0.
+ *
+ * Pins: every function here is checked by tests/test_oracle_pins.py against
+ * closed forms, library codecs, an fp64 unquantised MoE, a dense SwiGLU FFN
+ * written separately, brute-force routing and exact rational arithmetic.
+ * Parity of the GPU result against this oracle beyond the stated tolerance
+ * (f32 summation order inside the MFMA, expf ulps) is "parity unpinned".
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- codecs */
+
+/* OCP E4M3FN: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, no
+ * infinities, 0x7F / 0xFF are NaN, largest finite magnitude 448. */
+float orc_e4m3_decode(uint8_t code)
+{
+    int sign = code >> 7;
+    int exp = (code >> 3) & 0xF;
+    int man = code & 0x7;
+    float mag;
+    if (exp == 0xF && man == 0x7)
+        return NAN;
+    if (exp == 0)
+        mag = ldexpf((float)man, -9);                 /* man/8 * 2^-6 */
+    else
+        mag = ldexpf(1.0f + (float)man / 8.0f, exp - 7);
+    return sign ? -mag : mag;
+}
+
+/* Nearest finite E4M3FN value; ties go to the even code (even mantissa
+ * LSB); magnitudes at or above 448 saturate to 448; the sign of zero is
+ * kept; NaN maps to 0x7F.  Written as a search over the 127 non-negative
+ * finite codes so that it is the definition, not a bit trick. */
+uint8_t orc_e4m3_encode(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int best = 0;
+    double best_err = a;                               /* distance to code 0 */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double err = fabs((double)orc_e4m3_decode((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* BF16 is the top half of an IEEE binary32; round to nearest even. */
+uint16_t orc_bf16_rne(float v)
+{
+    uint32_t u;
+    memcpy(&u, &v, 4);
+    if (isnan(v))
+        return (uint16_t)((u >> 16) | 0x40);
+    uint32_t lower = u & 0xFFFFu;
+    uint32_t upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1;
+    return (uint16_t)upper;
+}
+
+float orc_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* --------------------------------------------------------------- routing */
+
+/* Plan of the per-expert pool ("07 · MegaMoE" §4, §7).
+ *   counts[e]   number of slots f with idx[f] == e (ids < 0 or >= E skipped)
+ *   offsets[e]  start row of expert e's segment; offsets[E] = pool rows used;
+ *               offsets[e+1] = offsets[e] + ceil(counts[e]/row_align)*row_align
+ *   row_src[r]  flat slot f stored in pool row r, -1 on padding rows,
+ *               for r < r_cap (rows past offsets[E] are -1)
+ *   src_row[f]  pool row of slot f, -1 for skipped slots
+ * Returns the number of slots with an id >= E (flagged, skipped). */
+int orc_route(int T, int K, int E, int row_align, const int32_t* idx,
+              int32_t* counts, int32_t* offsets, int32_t* row_src, int r_cap,
+              int32_t* src_row)
+{
+    int bad = 0;
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int f = 0; f < T * K; ++f) {
+        if (idx[f] >= E)
+            ++bad;
+        else if (idx[f] >= 0)
+            ++counts[idx[f]];
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + (counts[e] + row_align - 1) / row_align * row_align;
+    for (int r = 0; r < r_cap; ++r)
+        row_src[r] = -1;
+    for (int f = 0; f < T * K; ++f)
+        src_row[f] = -1;
+    for (int e = 0; e < E; ++e) {
+        int r = offsets[e];
+        for (int f = 0; f < T * K; ++f) {
+            if (idx[f] == e) {
+                if (r < r_cap)
+                    row_src[r] = f;
+                src_row[f] = r;
+                ++r;
+            }
+        }
+    }
+    return bad;
+}
+
+/* ----------------------------------------------------- block-scaled GEMM */
+
+/* Exact sum over one 128-wide K block of decoded e4m3 products.  Every
+ * e4m3 value is an integer multiple of 2^-9 below 2^9, so each product is
+ * a multiple of 2^-18 below 2^18 and 128 of them sum exactly in binary64. */
+double orc_block_dot_e4m3(const uint8_t* a, const uint8_t* b, int n)
+{
+    double s = 0.0;
+    for (int c = 0; c < n; ++c)
+        s += (double)orc_e4m3_decode(a[c]) * (double)orc_e4m3_decode(b[c]);
+    return s;
+}
+
+/* Same for an f32 activation row against e4m3 weights (test-only path
+ * with the requantisation switched off; not exact, binary64 sum). */
+static double block_dot_f32_e4m3(const float* a, const uint8_t* b, int n)
+{
+    double s = 0.0;
+    for (int c = 0; c < n; ++c)
+        s += (double)a[c] * (double)orc_e4m3_decode(b[c]);
+    return s;
+}
+
+/* One output element of a block-scaled FP8 GEMM (design doc §5.3):
+ *   acc = sum over K blocks kb, ascending, of fmaf(sa[kb]*sb[kb], p_kb, acc)
+ * with p_kb the exact block dot product rounded once to f32. */
+static float scaled_row_dot(const uint8_t* a, const float* sa, const uint8_t* b,
+                            const float* sb, int kblocks)
+{
+    float acc = 0.0f;
+    for (int kb = 0; kb < kblocks; ++kb) {
+        float p = (float)orc_block_dot_e4m3(a + 128 * kb, b + 128 * kb, 128);
+        float s = sa[kb] * sb[kb];
+        acc = fmaf(s, p, acc);
+    }
+    return acc;
+}
+
+/* ------------------------------------------------- SwiGLU and requantise */
+
+float orc_swiglu(float g, float u, float w)
+{
+    float silu = g / (1.0f + expf(-g));
+    return (silu * u) * w;
+}
+
+/* Per-128 requantisation of n values: sf = max(amax, 1e-10)/448 and
+ * q[i] = e4m3(v[i] / sf) with a correctly rounded f32 division. */
+void orc_requant_block(const float* v, int n, uint8_t* q, float* sf_out)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i)
+        amax = fmaxf(amax, fabsf(v[i]));
+    float sf = fmaxf(amax, 1e-10f) / 448.0f;
+    for (int i = 0; i < n; ++i)
+        q[i] = orc_e4m3_encode(v[i] / sf);
+    *sf_out = sf;
+}
+
+/* --------------------------------------------------------------- forward */
+
+enum {
+    ORC_NO_REQUANT = 1, /* test-only: feed f32 SwiGLU output to L2 unquantised */
+    ORC_NO_BF16 = 2     /* test-only: keep partials and y in f32 */
+};
+
+/* Forward for a list of tokens.
+ *   x [T,H] e4m3, x_sf [T,H/128] f32, idx/w [T,K]
+ *   w1[e] -> [2I,H] e4m3 (gate rows then up rows), w1_sf[e] -> [2I/128,H/128]
+ *   w2[e] -> [H,I] e4m3, w2_sf[e] -> [H/128,I/128]
+ *   (per-expert pointers; an expert no listed token uses may be NULL)
+ *   toks [n_tok] token ids to compute (NULL: all T tokens, n_tok = T)
+ * Outputs, indexed by position p in the token list (all optional but y):
+ *   y [n_tok,H] bf16 (or y_f32 [n_tok,H] when ORC_NO_BF16)
+ *   acc1 [n_tok*K, 2I] f32 L1 accumulator before SwiGLU
+ *   h [n_tok*K, I] e4m3, h_sf [n_tok*K, I/128]
+ *   partial [n_tok*K, H] bf16 (skipped slots left untouched)
+ * Returns the number of slots with an id >= E, or -1 when a needed expert
+ * pointer is NULL or a shape is invalid. */
+int orc_moe_forward(int T, int H, int I, int E, int K,
+                    const uint8_t* x, const float* x_sf,
+                    const int32_t* idx, const float* w,
+                    const uint8_t* const* w1, const float* const* w1_sf,
+                    const uint8_t* const* w2, const float* const* w2_sf,
+                    int n_tok, const int32_t* toks,
+                    uint16_t* y, float* y_f32,
+                    float* acc1, uint8_t* h, float* h_sf, uint16_t* partial,
+                    int flags, int nthreads)
+{
+    if (H % 128 || I % 128 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || T < 0)
+        return -1;
+    if (!toks)
+        n_tok = T;
+    const int HB = H / 128, IB = I / 128;
+    int bad = 0, missing = 0;
+    for (int p = 0; p < n_tok; ++p) {
+        int t = toks ? toks[p] : p;
+        if (t < 0 || t >= T)
+            return -1;
+        for (int j = 0; j < K; ++j) {
+            int e = idx[t * K + j];
+            if (e >= E)
+                ++bad;
+            else if (e >= 0 && (!w1[e] || !w1_sf[e] || !w2[e] || !w2_sf[e]))
+                missing = 1;
+        }
+    }
+    if (missing)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+
+    /* L1 -> SwiGLU -> requant -> L2, one (token, slot) per iteration. */
+    float* part_f32 = (float*)calloc((size_t)n_tok * K * H, sizeof(float));
+    if (!part_f32)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ps = 0; ps < n_tok * K; ++ps) {
+        int p = ps / K, j = ps % K;
+        int t = toks ? toks[p] : p;
+        int e = idx[t * K + j];
+        if (e < 0 || e >= E)
+            continue;
+        float* a1 = (float*)malloc(sizeof(float) * 2 * I);
+        float* hv = (float*)malloc(sizeof(float) * I);
+        uint8_t* q = (uint8_t*)malloc(I);
+        float* qs = (float*)malloc(sizeof(float) * IB);
+        const uint8_t* xr = x + (size_t)t * H;
+        const float* xs = x_sf + (size_t)t * HB;
+        for (int n = 0; n < 2 * I; ++n) {
+            const float* ws = w1_sf[e] + (size_t)(n / 128) * HB;
+            a1[n] = scaled_row_dot(xr, xs, w1[e] + (size_t)n * H, ws, HB);
+        }
+        if (acc1)
+            memcpy(acc1 + (size_t)ps * 2 * I, a1, sizeof(float) * 2 * I);
+        for (int i = 0; i < I; ++i)
+            hv[i] = orc_swiglu(a1[i], a1[I + i], w[t * K + j]);
+        if (!(flags & ORC_NO_REQUANT)) {
+            for (int ib = 0; ib < IB; ++ib)
+                orc_requant_block(hv + 128 * ib, 128, q + 128 * ib, qs + ib);
+            if (h)
+                memcpy(h + (size_t)ps * I, q, I);
+            if (h_sf)
+                memcpy(h_sf + (size_t)ps * IB, qs, sizeof(float) * IB);
+        }
+        for (int n = 0; n < H; ++n) {
+            const uint8_t* wr = w2[e] + (size_t)n * I;
+            const float* ws = w2_sf[e] + (size_t)(n / 128) * IB;
+            float acc = 0.0f;
+            if (flags & ORC_NO_REQUANT) {
+                for (int ib = 0; ib < IB; ++ib) {
+                    float pdot = (float)block_dot_f32_e4m3(hv + 128 * ib, wr + 128 * ib, 128);
+                    acc = fmaf(ws[ib], pdot, acc);
+                }
+            } else {
+                acc = scaled_row_dot(q, qs, wr, ws, IB);
+            }
+            float o = (flags & ORC_NO_BF16) ? acc : orc_bf16_to_f32(orc_bf16_rne(acc));
+            part_f32[(size_t)ps * H + n] = o;
+            if (partial)
+                partial[(size_t)ps * H + n] = orc_bf16_rne(acc);
+        }
+        free(a1);
+        free(hv);
+        free(q);
+        free(qs);
+    }
+
+    /* Combine: slot order ascending, f32 sum, one rounding to bf16. */
+#pragma omp parallel for schedule(static)
+    for (int p = 0; p < n_tok; ++p) {
+        int t = toks ? toks[p] : p;
+        for (int n = 0; n < H; ++n) {
+            float a = 0.0f;
+            for (int j = 0; j < K; ++j) {
+                int e = idx[t * K + j];
+                if (e < 0 || e >= E)
+                    continue;
+                a += part_f32[((size_t)p * K + j) * H + n];
+            }
+            if (y)
+                y[(size_t)p * H + n] = orc_bf16_rne(a);
+            if (y_f32)
+                y_f32[(size_t)p * H + n] = a;
+        }
+    }
+    free(part_f32);
+    return bad;
+}
+
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks one oracle function against a closed form, a library
+codec, brute force, exact rational arithmetic, an independently written
+numpy model, or an exact invariant, chosen so that a dropped term, a wrong
+sign or index, or a transposed operand anywhere in the oracle fails one.
+CPU only.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_grouped_gemm_amd import workload as wl
+
+# --------------------------------------------------------------- helpers
+
+
+def e4m3_closed_form(code: int) -> float:
+    """OCP E4M3FN (1-4-3, bias 7, no inf, S.1111.111 = NaN)."""
+    s = -1.0 if code & 0x80 else 1.0
+    E = (code >> 3) & 0xF
+    M = code & 0x7
+    if E == 0xF and M == 0x7:
+        return float("nan")
+    if E == 0:
+        return s * (M / 8.0) * 2.0 ** -6
+    return s * (1.0 + M / 8.0) * 2.0 ** (E - 7)
+
+
+DEC = np.array([e4m3_closed_form(c) for c in range(256)], dtype=np.float64)
+
+
+def dequant_blocks(q, sf, br, bc):
+    """codes [R,C] + scales [R/br, C/bc] -> float64 values."""
+    v = DEC[q.astype(np.int64)]
+    return v * np.repeat(np.repeat(sf.astype(np.float64), br, 0), bc, 1)
+
+
+def small_inputs(T=6, H=384, I=256, E=3, K=2, seed=7, mask=None):
+    cfg = wl.custom_config(T, H, I, E, K)
+    x, x_sf = wl.make_x(cfg, seed)
+    idx, w = wl.make_routing(cfg, seed)
+    ex = [wl.make_expert(cfg, seed, e) for e in range(E)]
+    idx = idx.numpy().copy()
+    if mask is not None:
+        for (t, j), v in mask.items():
+            idx[t, j] = v
+    return dict(x=x.numpy(), x_sf=x_sf.numpy(), idx=idx, w=w.numpy(),
+                w1=[e[0].numpy() for e in ex], w1_sf=[e[1].numpy() for e in ex],
+                w2=[e[2].numpy() for e in ex], w2_sf=[e[3].numpy() for e in ex],
+                H=H, I=I, E=E, K=K, T=T)
+
+
+def run_oracle(d, **kw):
+    return oracle.moe_forward(d["x"], d["x_sf"], d["idx"], d["w"], d["w1"], d["w1_sf"],
+                              d["w2"], d["w2_sf"], **kw)
+
+
+def bf16_bits_to_f64(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# ----------------------------------------------------------------- codecs
+
+
+def test_e4m3_decode_matches_closed_form_all_codes():
+    for c in range(256):
+        got = oracle.e4m3_decode(c)
+        ref = e4m3_closed_form(c)
+        if math.isnan(ref):
+            assert math.isnan(got), c
+        else:
+            assert got == ref and math.copysign(1, got) == math.copysign(1, ref), c
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32)
+    for c in range(256):
+        got, ref = oracle.e4m3_decode(c), float(t[c])
+        assert (math.isnan(got) and math.isnan(ref)) or got == ref, c
+
+
+def test_e4m3_encode_roundtrips_every_finite_code():
+    for c in range(256):
+        if (c & 0x7F) == 0x7F:
+            continue
+        assert oracle.e4m3_encode(oracle.e4m3_decode(c)) == c, hex(c)
+
+
+def test_e4m3_encode_midpoints_go_to_even_code():
+    for c in range(0, 0x7E):
+        lo, hi = DEC[c], DEC[c + 1]
+        mid = (lo + hi) / 2.0  # exact in f32: at most 5 significant bits
+        assert float(np.float32(mid)) == mid
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_encode(mid) == even, hex(c)
+        assert oracle.e4m3_encode(-mid) == 0x80 | even, hex(c)
+        # just off the midpoint goes to the nearer neighbour
+        assert oracle.e4m3_encode(float(np.nextafter(np.float32(mid), np.float32(0)))) == c
+        assert oracle.e4m3_encode(float(np.nextafter(np.float32(mid), np.float32(1e9)))) == c + 1
+
+
+def test_e4m3_encode_saturates_and_special_values():
+    assert oracle.e4m3_encode(448.0) == 0x7E
+    assert oracle.e4m3_encode(463.9) == 0x7E
+    assert oracle.e4m3_encode(1e30) == 0x7E
+    assert oracle.e4m3_encode(float("inf")) == 0x7E
+    assert oracle.e4m3_encode(float("-inf")) == 0xFE
+    assert oracle.e4m3_encode(-500.0) == 0xFE
+    assert oracle.e4m3_encode(float("nan")) == 0x7F
+    assert oracle.e4m3_encode(0.0) == 0x00
+    assert oracle.e4m3_encode(-0.0) == 0x80
+    assert oracle.e4m3_encode(-1e-30) == 0x80  # sign of zero kept
+    assert oracle.e4m3_encode(2.0 ** -10) == 0x00  # half the smallest subnormal: tie to even 0
+    assert oracle.e4m3_encode(3 * 2.0 ** -10) == 0x02  # 1.5 subnormal steps: tie to even 2
+
+
+def test_e4m3_encode_matches_torch_cast_in_range():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 100,
+        rng.standard_normal(20000) * 1e-2,
+        rng.standard_normal(5000) * 1e-3,
+        rng.uniform(-463.9, 463.9, 5000),
+    ]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(float(a)) for a in v], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_rne_matches_torch():
+    rng = np.random.default_rng(2)
+    v = (rng.standard_normal(20000) * 10.0 ** rng.integers(-20, 20, 20000)).astype(np.float32)
+    # exact ties: lower 16 bits = 0x8000, both parities of bit 16
+    ties = rng.integers(0, 2 ** 7, 2000).astype(np.uint32) << 16 | 0x8000
+    ties = (ties | (np.uint32(0x3F) << 24)).view(np.float32)  # finite, both parities
+    v = np.concatenate([v, ties, np.array([0.0, -0.0, 1.0, 65504.0, 3.4e38], np.float32)])
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = np.array([oracle.bf16_rne(float(a)) for a in v], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+    for b in (0x3F80, 0xBF80, 0x0001, 0x7F7F):
+        assert oracle.bf16_rne(oracle.bf16_to_f32(b)) == b
+
+
+# ------------------------------------------------------- block dot product
+
+
+def test_block_dot_is_exact_rational_sum():
+    rng = np.random.default_rng(3)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    for trial in range(20):
+        a = rng.choice(finite, 128)
+        b = rng.choice(finite, 128)
+        if trial == 0:  # largest magnitudes: the sum needs 43 bits
+            a[:] = 0x7E
+            b[:] = 0x7E
+        exact = sum(Fraction(DEC[x]) * Fraction(DEC[y]) for x, y in zip(a, b))
+        assert Fraction(oracle.block_dot(a, b)) == exact
+
+
+# ---------------------------------------------------------- L1 GEMM (acc1)
+
+
+def test_l1_block_scaled_gemm_matches_fp64_model():
+    d = small_inputs(T=5, H=384, I=256, E=3, K=2, seed=11)
+    out = run_oracle(d, want=("acc1",))
+    acc1 = out["acc1"]
+    H, I, K = d["H"], d["I"], d["K"]
+    for t in range(d["T"]):
+        for j in range(K):
+            e = d["idx"][t, j]
+            xq = DEC[d["x"][t].astype(np.int64)]
+            wq = DEC[d["w1"][e].astype(np.int64)]              # [2I, H]
+            ref = np.zeros(2 * I)
+            mag = np.zeros(2 * I)
+            for kb in range(H // 128):
+                blk = wq[:, kb * 128:(kb + 1) * 128] @ xq[kb * 128:(kb + 1) * 128]
+                s = d["x_sf"][t, kb].astype(np.float64) * \
+                    np.repeat(d["w1_sf"][e][:, kb].astype(np.float64), 128)
+                ref += s * blk
+                mag += np.abs(s * blk)
+            got = acc1[t * K + j].astype(np.float64)
+            assert np.all(np.abs(got - ref) <= 4e-7 * mag + 1e-30), (t, j)
+
+
+# ------------------------------------------------- SwiGLU and requantise
+
+
+def test_swiglu_closed_form():
+    for g, u, w in [(0.0, 3.0, 0.5), (1.0, 2.0, 0.25), (-2.0, 1.5, 1.0), (20.0, -1.0, 0.1),
+                    (-30.0, 2.0, 0.7), (0.3, 0.0, 1.0)]:
+        ref = g / (1.0 + math.exp(-g)) * u * w
+        got = oracle.swiglu(g, u, w)
+        assert abs(got - ref) <= 1e-6 * abs(ref) + 1e-30
+    assert oracle.swiglu(0.0, 5.0, 1.0) == 0.0
+    # gate and up are not interchangeable
+    assert oracle.swiglu(2.0, 1.0, 1.0) != oracle.swiglu(1.0, 2.0, 1.0)
+
+
+def test_requant_exact_block_reencodes_exactly():
+    rng = np.random.default_rng(5)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    codes = rng.choice(finite, 128)
+    codes[17] = 0xFE  # -448 sets the amax
+    sf = 2.0 ** -3
+    v = (DEC[codes] * sf).astype(np.float32)
+    q, s = oracle.requant_block(v)
+    assert s == np.float32(448 * sf) / np.float32(448)
+    assert s == sf
+    # -0 and +0 are the same value
+    assert np.array_equal(q & np.where(q == 0x80, 0, 0xFF).astype(np.uint8),
+                          codes & np.where(codes == 0x80, 0, 0xFF).astype(np.uint8))
+
+
+def test_requant_amax_maps_to_448_and_scales_by_powers_of_two():
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal(128).astype(np.float32)
+    q, s = oracle.requant_block(v)
+    i = int(np.argmax(np.abs(v)))
+    assert q[i] in (0x7E, 0xFE)
+    assert s == np.float32(np.float32(np.max(np.abs(v))) / np.float32(448.0))
+    for k in (-5, 3, 11):
+        q2, s2 = oracle.requant_block(v * np.float32(2.0 ** k))
+        assert np.array_equal(q, q2) and s2 == s * 2.0 ** k
+
+
+def test_requant_floor_on_zero_block():
+    q, s = oracle.requant_block(np.zeros(128, np.float32))
+    assert s == np.float32(np.float32(1e-10) / np.float32(448.0))
+    assert not q.any()
+
+
+# ------------------------------------------------------------- whole oracle
+
+
+def numpy_moe(d, requant=True):
+    """Independent fp64 model of the MoE forward (optionally with the per-128
+    requantisation done through torch's e4m3 cast).  Returns y [T,H] float64."""
+    H, I, K, E = d["H"], d["I"], d["K"], d["E"]
+    x = dequant_blocks(d["x"], d["x_sf"], 1, 128)
+    y = np.zeros((d["T"], H))
+    for t in range(d["T"]):
+        for j in range(K):
+            e = d["idx"][t, j]
+            if e < 0 or e >= E:
+                continue
+            w1 = dequant_blocks(d["w1"][e], d["w1_sf"][e], 128, 128)
+            w2 = dequant_blocks(d["w2"][e], d["w2_sf"][e], 128, 128)
+            a = w1 @ x[t]
+            g, u = a[:I], a[I:]
+            hval = g / (1.0 + np.exp(-g)) * u * float(d["w"][t, j])
+            if requant:
+                hb = hval.reshape(-1, 128)
+                sf = np.maximum(np.abs(hb).max(1), 1e-10) / 448.0
+                q = torch.from_numpy((hb / sf[:, None]).astype(np.float32)).to(
+                    torch.float8_e4m3fn).to(torch.float64).numpy()
+                hval = (q * sf[:, None]).reshape(-1)
+            y[t] += w2 @ hval
+    return y
+
+
+def test_unquantised_switches_match_fp64_moe():
+    d = small_inputs(T=6, H=256, I=384, E=4, K=3, seed=21, mask={(1, 2): -1, (4, 0): 9})
+    out = run_oracle(d, flags=oracle.ORC_NO_REQUANT | oracle.ORC_NO_BF16, want=("y_f32",))
+    ref = numpy_moe(d, requant=False)
+    assert out["n_bad"] == 1
+    for t in range(d["T"]):
+        assert rel_l2(out["y_f32"][t].astype(np.float64), ref[t]) <= 1e-5, t
+
+
+def test_full_oracle_within_quantisation_budget_of_fp64_moe():
+    d = small_inputs(T=6, H=256, I=384, E=4, K=3, seed=22, mask={(2, 1): -1})
+    y = bf16_bits_to_f64(run_oracle(d)["y"])
+    ref_q = numpy_moe(d, requant=True)
+    ref_f = numpy_moe(d, requant=False)
+    for t in range(d["T"]):
+        # against the requantising fp64 model: f32 accumulation and bf16 only
+        assert rel_l2(y[t], ref_q[t]) <= 1e-2, t
+        # against the unquantised model: the e4m3 requantisation error
+        r = rel_l2(y[t], ref_f[t])
+        assert 1e-4 <= r <= 0.1, (t, r)
+
+
+def test_dense_ffn_reduction():
+    """E=1, K=1, w=1: the layer is a dense SwiGLU FFN on the same operands."""
+    d = small_inputs(T=4, H=256, I=256, E=1, K=1, seed=23)
+    d["w"] = np.ones_like(d["w"])
+    y = bf16_bits_to_f64(run_oracle(d)["y"])
+    # dense model written without experts, slots or weights
+    x = dequant_blocks(d["x"], d["x_sf"], 1, 128)
+    w1 = dequant_blocks(d["w1"][0], d["w1_sf"][0], 128, 128)
+    w2 = dequant_blocks(d["w2"][0], d["w2_sf"][0], 128, 128)
+    gate = x @ w1[:256].T
+    up = x @ w1[256:].T
+    hid = gate / (1 + np.exp(-gate)) * up
+    blocks = hid.reshape(4, -1, 128)
+    sf = np.maximum(np.abs(blocks).max(-1, keepdims=True), 1e-10) / 448.0
+    q = torch.from_numpy((blocks / sf).astype(np.float32)).to(torch.float8_e4m3fn)
+    hq = (q.to(torch.float64).numpy() * sf).reshape(4, -1)
+    ref = hq @ w2.T
+    for t in range(4):
+        assert rel_l2(y[t], ref[t]) <= 5e-3, t
+
+
+def test_exact_invariants_bitwise():
+    d = small_inputs(T=6, H=256, I=256, E=4, K=2, seed=24)
+    y0 = run_oracle(d)["y"]
+    # (i) router weights x2 -> y x2 (every scaling is by a power of two)
+    d2 = dict(d, w=d["w"] * np.float32(2))
+    assert np.array_equal(bf16_bits_to_f64(run_oracle(d2)["y"]), 2 * bf16_bits_to_f64(y0))
+    # (ii) L2 weight scales x2 -> y x2
+    d3 = dict(d, w2_sf=[s * np.float32(2) for s in d["w2_sf"]])
+    assert np.array_equal(bf16_bits_to_f64(run_oracle(d3)["y"]), 2 * bf16_bits_to_f64(y0))
+    # (iii) permuting tokens permutes y
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    d4 = dict(d, x=d["x"][perm].copy(), x_sf=d["x_sf"][perm].copy(), idx=d["idx"][perm].copy(),
+              w=d["w"][perm].copy())
+    assert np.array_equal(run_oracle(d4)["y"], y0[perm])
+    # (iv) relabelling experts (weights permuted to match) leaves y unchanged
+    rel = np.array([2, 0, 3, 1])  # old expert e becomes rel[e]
+    inv = np.argsort(rel)
+    d5 = dict(d, idx=rel[d["idx"]].astype(np.int32),
+              w1=[d["w1"][inv[e]] for e in range(4)], w1_sf=[d["w1_sf"][inv[e]] for e in range(4)],
+              w2=[d["w2"][inv[e]] for e in range(4)], w2_sf=[d["w2_sf"][inv[e]] for e in range(4)])
+    assert np.array_equal(run_oracle(d5)["y"], y0)
+    # token list subset gives the same rows
+    sub = run_oracle(d, tokens=[4, 1])["y"]
+    assert np.array_equal(sub, y0[[4, 1]])
+
+
+def test_masked_token_gives_zero_and_masked_slot_is_dropped():
+    d = small_inputs(T=4, H=256, I=128, E=3, K=2, seed=25,
+                     mask={(0, 0): -1, (0, 1): -1, (2, 1): -1})
+    out = run_oracle(d, want=("partial",))
+    y = out["y"]
+    assert not y[0].any()
+    # token 2 keeps only slot 0: y = bf16(partial of slot 0)
+    assert np.array_equal(y[2], out["partial"][2 * 2 + 0])
+
+
+# ----------------------------------------------------------------- routing
+
+
+def brute_route(idx, E, ra):
+    T, K = idx.shape
+    flat = idx.reshape(-1)
+    counts = np.array([(flat == e).sum() for e in range(E)], np.int64)
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + -(-counts[e] // ra) * ra)
+    row_src = {}
+    src_row = -np.ones(T * K, np.int64)
+    for e in range(E):
+        fs = sorted(f for f in range(T * K) if flat[f] == e)
+        for i, f in enumerate(fs):
+            row_src[offsets[e] + i] = f
+            src_row[f] = offsets[e] + i
+    return counts, np.array(offsets), row_src, src_row
+
+
+@pytest.mark.parametrize("T,K,E,ra", [(1, 1, 1, 1), (7, 3, 5, 4), (50, 6, 17, 16),
+                                      (33, 2, 8, 128), (200, 8, 64, 32)])
+def test_route_matches_brute_force(T, K, E, ra):
+    rng = np.random.default_rng(T * 31 + E)
+    idx = rng.integers(-1, E + 2, size=(T, K)).astype(np.int32)  # masks, out of range, dups
+    idx[0, :] = 0  # duplicates inside one token
+    r_cap = T * K + E * (ra - 1)
+    counts, offsets, row_src, src_row, bad = oracle.route(idx, E, ra, r_cap)
+    bc, bo, brs, bsr = brute_route(idx, E, ra)
+    assert bad == int((idx >= E).sum())
+    assert np.array_equal(counts, bc) and np.array_equal(offsets, bo)
+    assert np.array_equal(src_row, bsr)
+    for r in range(r_cap):
+        assert row_src[r] == brs.get(r, -1)
+    # invariants
+    assert counts.sum() == int(((idx >= 0) & (idx < E)).sum())
+    assert np.all(offsets % ra == 0) and np.all(np.diff(offsets) >= counts)
+    valid = src_row >= 0
+    assert np.array_equal(row_src[src_row[valid]], np.nonzero(valid)[0])

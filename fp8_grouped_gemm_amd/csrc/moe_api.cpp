@@ -1,0 +1,387 @@
+// Host side of the C ABI declared in include/moe_fp8.h: validation, tile
+// configuration, workspace layout and kernel launches.  Every check runs
+// before the first HIP call, so invalid calls enqueue nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/moe_fp8.h"
+#include "moe_internal.h"
+
+struct moe_plan {
+    moe_shape_t shape;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kVersion = 1;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Config {
+    int tile_m;
+    int kernel;
+};
+
+// Rows per tile from the expected rows per expert T*K/E: the smallest tile
+// that holds an average expert's rows reads each expert's weights once
+// while padding as few MFMA rows as possible (decode: 16).
+Config choose_config(const moe_shape_t& s, int T)
+{
+    if (s.tile_m > 0)
+        return Config{s.tile_m, 0};
+    const double rows = (double)T * s.top_k / s.num_experts;
+    int bm = rows <= 12.0 ? 16 : rows <= 24.0 ? 32 : 64;
+    return Config{bm, 0};
+}
+
+struct Layout {
+    int tile_m, kernel, r_cap, mb_cap, NB;
+    size_t status, counts, offsets, blk, mbe, row_src, src_row, h_sf, h, partial, total;
+};
+
+Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
+{
+    Layout L{};
+    const Config c = choose_config(s, T);
+    L.tile_m = c.tile_m;
+    L.kernel = c.kernel;
+    const int ra = row_align_override > 0 ? row_align_override : c.tile_m;
+    const long long TK = (long long)T * s.top_k;
+    long long r = TK + (long long)s.num_experts * (ra - 1);
+    r = (r + ra - 1) / ra * ra;
+    L.r_cap = (int)std::max<long long>(r, ra);
+    L.mb_cap = L.r_cap / ra;
+    L.NB = (int)std::max<long long>((TK + moe::kRouteThreads - 1) / moe::kRouteThreads, 1);
+    const int E = s.num_experts, H = s.hidden, I = s.intermediate, K = s.top_k;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align_up(o + bytes, kAlign);
+        return at;
+    };
+    L.status = take(4 * sizeof(int32_t));
+    L.counts = take(sizeof(int32_t) * E);
+    L.offsets = take(sizeof(int32_t) * (E + 1));
+    L.blk = take(sizeof(int32_t) * (size_t)L.NB * (E + 1));
+    L.mbe = take(sizeof(int32_t) * (size_t)L.mb_cap);
+    L.row_src = take(sizeof(int32_t) * (size_t)L.r_cap);
+    L.src_row = take(sizeof(int32_t) * (size_t)std::max<long long>(TK, 1));
+    L.h_sf = take(sizeof(float) * (size_t)L.r_cap * (I / 128));
+    L.h = take((size_t)L.r_cap * I);
+    L.partial = take(sizeof(uint16_t) * (size_t)K * T * H);
+    L.total = o;
+    return L;
+}
+
+int validate_shape(const moe_shape_t* s)
+{
+    if (!s)
+        return MOE_ERR_INVALID_ARG;
+    if (s->hidden <= 0 || s->intermediate <= 0 || s->num_experts <= 0 || s->top_k <= 0 ||
+        s->max_tokens < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (s->top_k > s->num_experts)
+        return MOE_ERR_INVALID_ARG;
+    if (s->hidden % 128 || s->intermediate % 128)
+        return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (s->num_experts > moe::kMaxExperts)
+        return MOE_ERR_UNSUPPORTED_SHAPE;
+    if ((long long)s->max_tokens * s->top_k >= (1LL << 24))
+        return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (s->hidden > (1 << 16) || s->intermediate > (1 << 16))
+        return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (s->tile_m != 0 && s->tile_m != 16 && s->tile_m != 32 && s->tile_m != 64)
+        return MOE_ERR_UNSUPPORTED_SHAPE;
+    return MOE_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off)
+{
+    return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+int check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MOE_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return MOE_ERR_NOT_GFX950;
+    return MOE_OK;
+}
+
+// Checked once per process per device ordinal.
+int device_ok()
+{
+    static int cached[64];
+    static bool init[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (dev < 0 || dev >= 64)
+        return check_device();
+    if (!init[dev]) {
+        cached[dev] = check_device();
+        init[dev] = true;
+    }
+    return cached[dev];
+}
+
+moe::RouteArgs route_args(const moe_shape_t& s, int T, const Layout& L, void* ws,
+                          const int32_t* idx, int row_align, int32_t* counts,
+                          int32_t* offsets, int32_t* row_src, int r_cap, int32_t* src_row,
+                          bool with_mblocks)
+{
+    moe::RouteArgs a{};
+    a.idx = idx;
+    a.TK = T * s.top_k;
+    a.E = s.num_experts;
+    a.row_align = row_align;
+    a.NB = L.NB;
+    a.blk = at<int32_t>(ws, L.blk);
+    a.counts = counts;
+    a.offsets = offsets;
+    a.row_src = row_src;
+    a.r_cap = r_cap;
+    a.src_row = src_row;
+    a.mblock_expert = with_mblocks ? at<int32_t>(ws, L.mbe) : nullptr;
+    a.mb_cap = L.mb_cap;
+    a.status = at<int32_t>(ws, L.status);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return kVersion; }
+
+const char* moe_strerror(int code)
+{
+    switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_NOT_GFX950: return "current device is not gfx950";
+    default: return "unknown error";
+    }
+}
+
+int moe_plan_create(const moe_shape_t* shape, moe_plan_t* out)
+{
+    if (!out)
+        return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    const int rc = validate_shape(shape);
+    if (rc != MOE_OK)
+        return rc;
+    moe_plan* p = new (std::nothrow) moe_plan;
+    if (!p)
+        return MOE_ERR_INVALID_ARG;
+    p->shape = *shape;
+    *out = p;
+    return MOE_OK;
+}
+
+int moe_plan_destroy(moe_plan_t plan)
+{
+    delete plan;
+    return MOE_OK;
+}
+
+int moe_plan_info(moe_plan_t plan, int32_t T, moe_tile_info_t* info)
+{
+    if (!plan || !info || T < 0 || T > plan->shape.max_tokens)
+        return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(plan->shape, T);
+    info->tile_m = L.tile_m;
+    info->row_align = L.tile_m;
+    info->pool_rows = L.r_cap;
+    info->l1_tile_n = 256;
+    info->l2_tile_n = 256;
+    info->kernel = L.kernel;
+    return MOE_OK;
+}
+
+int moe_workspace_bytes(moe_plan_t plan, int32_t T, size_t* bytes)
+{
+    if (!plan || !bytes || T < 0 || T > plan->shape.max_tokens)
+        return MOE_ERR_INVALID_ARG;
+    *bytes = make_layout(plan->shape, T).total;
+    return MOE_OK;
+}
+
+int moe_workspace_layout(moe_plan_t plan, int32_t T, moe_ws_layout_t* out)
+{
+    if (!plan || !out || T < 0 || T > plan->shape.max_tokens)
+        return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(plan->shape, T);
+    out->counts = L.counts;
+    out->offsets = L.offsets;
+    out->row_src = L.row_src;
+    out->src_row = L.src_row;
+    out->h = L.h;
+    out->h_sf = L.h_sf;
+    out->partial = L.partial;
+    out->status = L.status;
+    out->total = L.total;
+    return MOE_OK;
+}
+
+int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float* x_sf,
+                      const int32_t* topk_idx, const float* topk_w, const uint8_t* w1,
+                      const float* w1_sf, const uint8_t* w2, const float* w2_sf, uint16_t* y,
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* step_events)
+{
+    if (!plan)
+        return MOE_ERR_INVALID_ARG;
+    const moe_shape_t& s = plan->shape;
+    if (T < 0 || T > s.max_tokens)
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !x_sf || !topk_idx || !topk_w || !w1 || !w1_sf || !w2 || !w2_sf || !y ||
+        !workspace)
+        return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(s, T);
+    if (workspace_bytes < L.total)
+        return MOE_ERR_WORKSPACE_TOO_SMALL;
+    int rc = device_ok();
+    if (rc != MOE_OK)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) {
+        if (step_events && step_events[i])
+            return hipEventRecord(static_cast<hipEvent_t>(step_events[i]), st) == hipSuccess;
+        return true;
+    };
+    if (!mark(0))
+        return MOE_ERR_HIP;
+
+    moe::RouteArgs ra = route_args(s, T, L, workspace, topk_idx, L.tile_m,
+                                   at<int32_t>(workspace, L.counts),
+                                   at<int32_t>(workspace, L.offsets),
+                                   at<int32_t>(workspace, L.row_src), L.r_cap,
+                                   at<int32_t>(workspace, L.src_row), true);
+    if (moe::launch_route(ra, st) != hipSuccess || !mark(1))
+        return MOE_ERR_HIP;
+
+    moe::FwdArgs a{};
+    a.T = T;
+    a.H = s.hidden;
+    a.I = s.intermediate;
+    a.E = s.num_experts;
+    a.K = s.top_k;
+    a.BM = L.tile_m;
+    a.x = x;
+    a.x_sf = x_sf;
+    a.idx = topk_idx;
+    a.topk_w = topk_w;
+    a.w1 = w1;
+    a.w1_sf = w1_sf;
+    a.w2 = w2;
+    a.w2_sf = w2_sf;
+    a.row_src = at<int32_t>(workspace, L.row_src);
+    a.mblock_expert = at<int32_t>(workspace, L.mbe);
+    a.num_mblocks = L.mb_cap;
+    a.h = at<uint8_t>(workspace, L.h);
+    a.h_sf = at<float>(workspace, L.h_sf);
+    a.partial = at<uint16_t>(workspace, L.partial);
+    a.y = y;
+    if (moe::launch_l1(a, L.kernel, st) != hipSuccess || !mark(2))
+        return MOE_ERR_HIP;
+    if (moe::launch_l2(a, L.kernel, st) != hipSuccess || !mark(3))
+        return MOE_ERR_HIP;
+    if (moe::launch_combine(a, st) != hipSuccess || !mark(4))
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_forward(moe_plan_t plan, int32_t T, const uint8_t* x, const float* x_sf,
+                const int32_t* topk_idx, const float* topk_w, const uint8_t* w1,
+                const float* w1_sf, const uint8_t* w2, const float* w2_sf, uint16_t* y,
+                void* workspace, size_t workspace_bytes, void* stream)
+{
+    return moe_forward_timed(plan, T, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
+                             workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_route_workspace_bytes(moe_plan_t plan, int32_t T, size_t* bytes)
+{
+    if (!plan || !bytes || T < 0 || T > plan->shape.max_tokens)
+        return MOE_ERR_INVALID_ARG;
+    // The planner alone uses the status word and the per-chunk table only.
+    const Layout L = make_layout(plan->shape, T);
+    *bytes = L.blk + align_up(sizeof(int32_t) * (size_t)L.NB * (plan->shape.num_experts + 1), kAlign);
+    return MOE_OK;
+}
+
+int moe_route(moe_plan_t plan, int32_t T, const int32_t* topk_idx, int32_t row_align,
+              int32_t* counts, int32_t* offsets, int32_t* row_src, int32_t row_src_len,
+              int32_t* src_row, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!plan)
+        return MOE_ERR_INVALID_ARG;
+    const moe_shape_t& s = plan->shape;
+    if (T < 0 || T > s.max_tokens || row_align < 1 || row_align > 1024)
+        return MOE_ERR_INVALID_ARG;
+    if (!counts || !offsets || !workspace)
+        return MOE_ERR_INVALID_ARG;
+    const long long need_rows = (long long)T * s.top_k + (long long)s.num_experts * (row_align - 1);
+    if (row_src_len < 0 || (long long)row_src_len < need_rows)
+        return MOE_ERR_INVALID_ARG;
+    if (T > 0 && (!topk_idx || !src_row))
+        return MOE_ERR_INVALID_ARG;
+    if (need_rows > 0 && !row_src)
+        return MOE_ERR_INVALID_ARG;
+    size_t need = 0;
+    moe_route_workspace_bytes(plan, T, &need);
+    if (workspace_bytes < need)
+        return MOE_ERR_WORKSPACE_TOO_SMALL;
+    int rc = device_ok();
+    if (rc != MOE_OK)
+        return rc;
+    const Layout L = make_layout(s, T);
+    moe::RouteArgs ra = route_args(s, T, L, workspace, topk_idx, row_align, counts, offsets,
+                                   row_src, row_src_len, src_row, false);
+    if (T == 0) {
+        // Still defines counts = 0, offsets = 0 and every row as padding.
+        ra.NB = 0;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (moe::launch_route(ra, st) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_read_status(moe_plan_t plan, int32_t T, const void* workspace, size_t workspace_bytes,
+                    int32_t* host_status, void* stream)
+{
+    if (!plan || !workspace || !host_status || T < 0 || T > plan->shape.max_tokens)
+        return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(plan->shape, T);
+    if (workspace_bytes < L.status + 4 * sizeof(int32_t))
+        return MOE_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(host_status, static_cast<const char*>(workspace) + L.status,
+                       4 * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Device helpers shared by the gfx950 GEMM, epilogue and combine kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// One gfx950 MFMA: D(16x16, f32) = A(16x128, e4m3) * B(128x16, e4m3) + C.
+// Operand format codes 0/0 select OCP e4m3 for both sides; zero scale
+// operands make the compiler emit the unscaled v_mfma_f32_16x16x128_f8f6f4.
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, 32 K-values
+// each; the K values a lane group (l / 16) supplies are the same set for A
+// and B, so any fixed assignment of K positions to bytes that both operands
+// share yields the full 128-term dot product.  Result: lane l holds column
+// (l % 16), rows 4*(l/16) + i for i = 0..3.
+__device__ __forceinline__ v4f mfma_16x16x128_e4m3(const v8i& a, const v8i& b, const v4f& c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// f32 -> OCP e4m3 (E4M3FN) code, round to nearest even, magnitudes >= 448
+// saturate to 448, sign of zero kept, NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u)
+        return 0x7Fu;
+    if (a >= 0x43E00000u)  // 448.0f
+        return sign | 0x7Eu;
+    if (a >= 0x3C800000u) {  // 2^-6: normal e4m3 range
+        const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;  // RNE to 3 mantissa bits
+        return sign | (r - (120u << 3));
+    }
+    // Subnormal e4m3: multiples of 2^-9; 8 * 2^-9 is the smallest normal.
+    const float s = __uint_as_float(a) * 512.0f;
+    return sign | (uint32_t)__builtin_rintf(s);
+}
+
+// f32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b)
+{
+    return __uint_as_float(b << 16);
+}
+
+// Max over the 16 lanes that share (lane / 16).
+__device__ __forceinline__ float max16(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+
+__device__ __forceinline__ v8i pack_frag(const uint4& lo, const uint4& hi)
+{
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+}  // namespace moe

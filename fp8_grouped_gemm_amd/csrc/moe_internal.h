@@ -1,0 +1,56 @@
+// Internal interface between the host entry points (moe_api.cpp) and the
+// HIP kernels of the FP8 MoE forward.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Routing planner arguments ("07 · MegaMoE" §4 pool layout, §7 counting).
+struct RouteArgs {
+    const int32_t* idx;   // [TK] expert id per flat slot f = t*K + j
+    int32_t TK;           // T*K
+    int32_t E;
+    int32_t row_align;
+    int32_t NB;           // number of 1024-slot chunks
+    int32_t* blk;         // [NB][E+1] per-chunk counts, then per-chunk bases
+    int32_t* counts;      // [E]
+    int32_t* offsets;     // [E+1]
+    int32_t* row_src;     // [r_cap]
+    int32_t r_cap;
+    int32_t* src_row;     // [TK]
+    int32_t* mblock_expert;  // [mb_cap] expert of each row_align block, -1 past the pool (may be null)
+    int32_t mb_cap;
+    int32_t* status;      // [4]
+};
+
+// Everything the GEMM, epilogue and combine kernels read or write.
+struct FwdArgs {
+    int32_t T, H, I, E, K, BM;
+    const uint8_t* x;
+    const float* x_sf;
+    const int32_t* idx;
+    const float* topk_w;
+    const uint8_t* w1;
+    const float* w1_sf;
+    const uint8_t* w2;
+    const float* w2_sf;
+    const int32_t* row_src;
+    const int32_t* mblock_expert;
+    int32_t num_mblocks;
+    uint8_t* h;
+    float* h_sf;
+    uint16_t* partial;
+    uint16_t* y;
+};
+
+constexpr int kRouteThreads = 1024;
+constexpr int kMaxExperts = 1024;
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s);
+hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s);
+hipError_t launch_combine(const FwdArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,158 @@
+// Routing planner: per-expert histogram, aligned prefix sum and a stable
+// slot assignment into per-expert contiguous pool segments.
+//
+// "07 · MegaMoE" §7 counts the tokens of every expert on the device, skips
+// masked slots (id < 0), and §4 lays the pool out expert by expert with
+// every segment aligned to the row tile, the segment start being the prefix
+// sum of the aligned segment sizes; nothing is copied back to the host.
+// The pages fill a segment in atomic-ticket order and say the order inside
+// a segment does not change the result; here the rows of an expert hold its
+// slots in ascending flat index f = t*K + j, which makes the plan
+// deterministic and lets it be compared bit for bit.
+//
+// Three launches, no host synchronisation:
+//   route_count  : one 1024-slot chunk per block, LDS histogram
+//   route_scan   : one block, totals, aligned exclusive scan, per-chunk bases,
+//                  padding rows and the row-block -> expert table
+//   route_assign : one chunk per block, rank of each slot among the earlier
+//                  slots of the same expert in its chunk, scatter
+#include "moe_internal.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(kRouteThreads) void route_count(RouteArgs a)
+{
+    extern __shared__ int32_t hist[];  // [E+1]; hist[E] counts ids >= E
+    for (int e = threadIdx.x; e <= a.E; e += kRouteThreads)
+        hist[e] = 0;
+    __syncthreads();
+    const int f = blockIdx.x * kRouteThreads + threadIdx.x;
+    if (f < a.TK) {
+        const int e = a.idx[f];
+        if (e >= a.E)
+            atomicAdd(&hist[a.E], 1);
+        else if (e >= 0)
+            atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    int32_t* out = a.blk + (size_t)blockIdx.x * (a.E + 1);
+    for (int e = threadIdx.x; e <= a.E; e += kRouteThreads)
+        out[e] = hist[e];
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scan(RouteArgs a)
+{
+    __shared__ int32_t scan[kRouteThreads];
+    __shared__ int32_t bad_sh;
+    const int e = threadIdx.x;  // E <= 1024: one expert per thread
+    int total = 0, seg = 0;
+    if (e < a.E) {
+        for (int b = 0; b < a.NB; ++b)
+            total += a.blk[(size_t)b * (a.E + 1) + e];
+        seg = (total + a.row_align - 1) / a.row_align * a.row_align;
+        a.counts[e] = total;
+    }
+    if (e == 0) {
+        int bad = 0;
+        for (int b = 0; b < a.NB; ++b)
+            bad += a.blk[(size_t)b * (a.E + 1) + a.E];
+        bad_sh = bad;
+    }
+    // Inclusive Hillis-Steele scan of the aligned segment sizes.
+    scan[e] = seg;
+    __syncthreads();
+    for (int d = 1; d < kRouteThreads; d <<= 1) {
+        int v = (e >= d) ? scan[e - d] : 0;
+        __syncthreads();
+        scan[e] += v;
+        __syncthreads();
+    }
+    const int start = scan[e] - seg;
+    const int used = scan[kRouteThreads - 1];
+    if (e < a.E) {
+        a.offsets[e] = start;
+        // Per-chunk base row of this expert's slots.
+        int run = start;
+        for (int b = 0; b < a.NB; ++b) {
+            int32_t* p = a.blk + (size_t)b * (a.E + 1) + e;
+            int c = *p;
+            *p = run;
+            run += c;
+        }
+        // Padding rows at the end of the segment.
+        for (int r = start + total; r < start + seg; ++r)
+            a.row_src[r] = -1;
+        if (a.mblock_expert) {
+            for (int m = start / a.row_align; m < (start + seg) / a.row_align; ++m)
+                a.mblock_expert[m] = e;
+        }
+    }
+    if (e == 0) {
+        a.offsets[a.E] = used;
+        a.status[0] = bad_sh > 0 ? 1 : 0;
+        a.status[1] = bad_sh;
+        a.status[2] = used;
+        a.status[3] = 0;
+    }
+    for (int r = used + e; r < a.r_cap; r += kRouteThreads)
+        a.row_src[r] = -1;
+    if (a.mblock_expert) {
+        for (int m = used / a.row_align + e; m < a.mb_cap; m += kRouteThreads)
+            a.mblock_expert[m] = -1;
+    }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_assign(RouteArgs a)
+{
+    extern __shared__ int32_t wave_cnt[];  // [16][E]: per-wave counts, then per-wave bases
+    constexpr int kWaves = kRouteThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kWaves * a.E; i += kRouteThreads)
+        wave_cnt[i] = 0;
+    __syncthreads();
+    const int f = blockIdx.x * kRouteThreads + threadIdx.x;
+    const int e = (f < a.TK) ? a.idx[f] : -1;
+    const bool valid = e >= 0 && e < a.E;
+    const int key = valid ? e : -1;
+    // Rank among the earlier lanes of this wave with the same expert.
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+        const int other = __shfl(key, j);
+        rank += (j < lane && other == key) ? 1 : 0;
+    }
+    if (valid)
+        atomicAdd(&wave_cnt[wave * a.E + e], 1);
+    __syncthreads();
+    for (int x = threadIdx.x; x < a.E; x += kRouteThreads) {
+        int run = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = wave_cnt[w * a.E + x];
+            wave_cnt[w * a.E + x] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    if (f < a.TK) {
+        if (valid) {
+            const int pos = a.blk[(size_t)blockIdx.x * (a.E + 1) + e] + wave_cnt[wave * a.E + e] + rank;
+            a.row_src[pos] = f;
+            a.src_row[f] = pos;
+        } else {
+            a.src_row[f] = -1;
+        }
+    }
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s)
+{
+    const size_t lds_hist = sizeof(int32_t) * (a.E + 1);
+    const size_t lds_wave = sizeof(int32_t) * 16 * a.E;
+    if (a.NB > 0)
+        hipLaunchKernelGGL(route_count, dim3(a.NB), dim3(kRouteThreads), lds_hist, s, a);
+    hipLaunchKernelGGL(route_scan, dim3(1), dim3(kRouteThreads), 0, s, a);
+    if (a.NB > 0)
+        hipLaunchKernelGGL(route_assign, dim3(a.NB), dim3(kRouteThreads), lds_wave, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,177 @@
+/*
+ * moe_fp8.h — C ABI of the MI355X (gfx950) FP8 MoE expert forward.
+ *
+ * One GPU, all experts resident.  A forward takes FP8 (OCP e4m3) tokens with
+ * 1x128 float scales, a top-k routing, FP8 expert weights with 128x128 float
+ * block scales, and writes the BF16 layer output.  The steps, each a HIP
+ * kernel of this library, follow the fused MoE forward described on the
+ * DeepGEMM "MegaMoE" pages:
+ *   1. routing planner: per-expert count, aligned prefix sum, slot
+ *      assignment into per-expert contiguous pool segments
+ *      ("07 · MegaMoE" §4 token pool, §7 dispatch counting);
+ *   2. L1 grouped FP8 GEMM (gate+up) with per-128-K scale FMAs
+ *      ("MegaMoE SM90 Implementation Design" §5.3);
+ *   3. fused epilogue: silu(gate)*up*topk_w, per-128 e4m3 requantisation
+ *      with sf = max(amax, 1e-10)/448 (design doc §10.1; DeepGEMM PR #440
+ *      "How it works");
+ *   4. L2 grouped FP8 GEMM (down), BF16 partial per (token, slot)
+ *      (design doc §11.1);
+ *   5. combine: per token, f32 sum of its slots' BF16 partials, cast to
+ *      BF16 (design doc §11.2; "07 · MegaMoE" §9).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major,
+ *     densely packed.  The library never allocates or frees device memory;
+ *     all scratch lives in a caller-provided workspace.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; no entry point synchronises the host, except
+ *     moe_read_status, which says so.
+ *   - Every argument is validated on the host BEFORE any HIP call, so an
+ *     invalid call returns an error code and enqueues nothing.
+ *   - Return value: MOE_OK or a negative MOE_ERR_* code (moe_strerror).
+ *   - A plan is immutable after creation and may be shared between threads;
+ *     concurrent forwards need distinct workspaces.
+ *
+ * Shapes: T tokens, H hidden, I intermediate, E experts, K top-k.
+ * Constraints: H % 128 == 0, I % 128 == 0, 1 <= K <= E <= 1024,
+ * 0 <= T <= max_tokens, max_tokens * K < 2^24.
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1)        /* null pointer, T out of range, K > E, ... */
+#define MOE_ERR_UNSUPPORTED_SHAPE (-2)  /* H or I not a multiple of 128, E > 1024, ... */
+#define MOE_ERR_WORKSPACE_TOO_SMALL (-3)
+#define MOE_ERR_HIP (-4)                /* a HIP launch or copy failed */
+#define MOE_ERR_NOT_GFX950 (-5)         /* current device is not gfx950 */
+
+/* Status bits written by the planner into the workspace (moe_read_status). */
+#define MOE_STATUS_EXPERT_OUT_OF_RANGE 1 /* some topk_idx >= E; those slots were skipped */
+
+typedef struct moe_shape {
+    int32_t hidden;       /* H */
+    int32_t intermediate; /* I */
+    int32_t num_experts;  /* E */
+    int32_t top_k;        /* K */
+    int32_t max_tokens;   /* largest T any call on this plan may pass */
+    int32_t tile_m;       /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128 */
+} moe_shape_t;
+
+typedef struct moe_plan* moe_plan_t;
+
+/* Tile configuration a forward with T tokens uses. */
+typedef struct moe_tile_info {
+    int32_t tile_m;      /* rows per GEMM tile = pool segment alignment */
+    int32_t row_align;   /* == tile_m */
+    int32_t pool_rows;   /* capacity R of the pool: T*K + E*(tile_m-1), rounded up to tile_m */
+    int32_t l1_tile_n;   /* L1 output columns per tile (gate + up) */
+    int32_t l2_tile_n;   /* L2 output columns per tile */
+    int32_t kernel;      /* 0 = direct-load tile kernel, 1 = LDS-staged tile kernel */
+} moe_tile_info_t;
+
+/* Byte offsets of the workspace sections used by a forward with T tokens.
+ * Tests read the intermediate tensors through these views.
+ *   counts   int32 [E]            tokens routed to each expert
+ *   offsets  int32 [E+1]          first pool row of each expert's segment
+ *   row_src  int32 [pool_rows]    flat slot f = t*K + j held by a pool row, -1 = padding
+ *   src_row  int32 [T*K]          pool row of slot f, -1 = skipped slot
+ *   h        uint8 [pool_rows, I] e4m3 SwiGLU output (valid rows only)
+ *   h_sf     f32   [pool_rows, I/128]
+ *   partial  uint16 [K, T, H]     bf16 L2 output of slot (t, j) at [j][t]
+ *   status   int32 [4]            status[0] = MOE_STATUS_* bits, status[1] = #ids >= E */
+typedef struct moe_ws_layout {
+    size_t counts, offsets, row_src, src_row, h, h_sf, partial, status;
+    size_t total;
+} moe_ws_layout_t;
+
+/* Validate a shape and create a plan (host only, no HIP call). */
+int moe_plan_create(const moe_shape_t* shape, moe_plan_t* out);
+int moe_plan_destroy(moe_plan_t plan);
+
+/* Tile configuration for a call with num_tokens tokens. */
+int moe_plan_info(moe_plan_t plan, int32_t num_tokens, moe_tile_info_t* info);
+
+/* Workspace bytes a call with num_tokens tokens needs.  The amount is
+ * nondecreasing in num_tokens, so the value for max_tokens serves every
+ * call on the plan.  No zeroing is required: every call rewrites what it
+ * reads. */
+int moe_workspace_bytes(moe_plan_t plan, int32_t num_tokens, size_t* bytes);
+int moe_workspace_layout(moe_plan_t plan, int32_t num_tokens, moe_ws_layout_t* layout);
+
+/*
+ * Full forward (steps 1-5).
+ *   x        uint8  [T, H]        e4m3 tokens
+ *   x_sf     f32    [T, H/128]    per 1x128 block scale
+ *   topk_idx int32  [T, K]        expert ids; < 0 masks the slot; >= E is
+ *                                 skipped and flagged in the status word
+ *   topk_w   f32    [T, K]        router weights, applied in the SwiGLU step
+ *   w1       uint8  [E, 2I, H]    e4m3, rows [0,I) gate, rows [I,2I) up
+ *   w1_sf    f32    [E, 2I/128, H/128]
+ *   w2       uint8  [E, H, I]     e4m3
+ *   w2_sf    f32    [E, H/128, I/128]
+ *   y        uint16 [T, H]        bf16 output, written in full (a token with
+ *                                 no active slot gets zeros)
+ *   workspace / workspace_bytes   at least moe_workspace_bytes(plan, T)
+ * T == 0 is a no-op returning MOE_OK.
+ */
+int moe_forward(moe_plan_t plan, int32_t num_tokens,
+                const uint8_t* x, const float* x_sf,
+                const int32_t* topk_idx, const float* topk_w,
+                const uint8_t* w1, const float* w1_sf,
+                const uint8_t* w2, const float* w2_sf,
+                uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_forward, plus five hipEvent_t recorded on `stream` for measurement:
+ * step_events[0] before the planner, [1] after the planner, [2] after the
+ * L1 GEMM + SwiGLU/requant epilogue, [3] after the L2 GEMM, [4] after the
+ * combine.  Any entry may be NULL (not recorded).  Same validation and
+ * error behaviour as moe_forward; with T == 0 nothing is recorded. */
+int moe_forward_timed(moe_plan_t plan, int32_t num_tokens,
+                      const uint8_t* x, const float* x_sf,
+                      const int32_t* topk_idx, const float* topk_w,
+                      const uint8_t* w1, const float* w1_sf,
+                      const uint8_t* w2, const float* w2_sf,
+                      uint16_t* y, void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* step_events);
+
+/*
+ * Routing planner alone (step 1) with an explicit row alignment in [1, 1024]
+ * ("07 · MegaMoE" §4: segments aligned to the row tile; §7: masked slots
+ * skipped).  Rows of one expert hold its slots in ascending flat index f.
+ *   counts  int32 [E], offsets int32 [E+1]
+ *   row_src int32 [row_src_len]: row_src_len >= T*K + E*(row_align-1);
+ *           rows past offsets[E] are set to -1
+ *   src_row int32 [T*K]
+ * Scratch comes from the workspace (moe_workspace_bytes of a plan covers it
+ * when row_align <= the plan's tile_m; otherwise pass the bytes of
+ * moe_route_workspace_bytes).
+ */
+int moe_route(moe_plan_t plan, int32_t num_tokens, const int32_t* topk_idx,
+              int32_t row_align, int32_t* counts, int32_t* offsets,
+              int32_t* row_src, int32_t row_src_len, int32_t* src_row,
+              void* workspace, size_t workspace_bytes, void* stream);
+int moe_route_workspace_bytes(moe_plan_t plan, int32_t num_tokens, size_t* bytes);
+
+/* Blocking: synchronises `stream`, then copies the 4-int status word of the
+ * last call that used `workspace` into host_status[4]. */
+int moe_read_status(moe_plan_t plan, int32_t num_tokens, const void* workspace,
+                    size_t workspace_bytes, int32_t* host_status, void* stream);
+
+const char* moe_strerror(int code);
+
+/* Library version, for the binding's sanity check. */
+int moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H */

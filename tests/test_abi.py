@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid
+calls on the host before any HIP call (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_grouped_gemm_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp8.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*|size_t)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_symbols() == sorted(moe.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert L.moe_version() >= 1
+
+
+def test_strerror_names_every_code():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert moe.strerror(code) != "unknown error"
+    assert moe.strerror(-99) == "unknown error"
+
+
+@pytest.mark.parametrize("shape,code", [
+    ((250, 128, 8, 2, 64, 0), moe.MOE_ERR_UNSUPPORTED_SHAPE),   # H % 128
+    ((256, 100, 8, 2, 64, 0), moe.MOE_ERR_UNSUPPORTED_SHAPE),   # I % 128
+    ((256, 128, 8, 9, 64, 0), moe.MOE_ERR_INVALID_ARG),         # K > E
+    ((256, 128, 2048, 2, 64, 0), moe.MOE_ERR_UNSUPPORTED_SHAPE),  # E > 1024
+    ((256, 128, 8, 2, -1, 0), moe.MOE_ERR_INVALID_ARG),         # max_tokens < 0
+    ((256, 128, 8, 2, 64, 48), moe.MOE_ERR_UNSUPPORTED_SHAPE),  # tile_m
+    ((0, 128, 8, 2, 64, 0), moe.MOE_ERR_INVALID_ARG),
+    ((256, 128, 8, 8, 1 << 21, 0), moe.MOE_ERR_UNSUPPORTED_SHAPE),  # T*K >= 2^24
+])
+def test_plan_create_rejects(shape, code):
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_plan_create(*shape)
+    assert ei.value.code == code
+
+
+def test_plan_create_null_shape():
+    h = ctypes.c_void_p()
+    assert moe.lib().moe_plan_create(None, ctypes.byref(h)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_plan_info_tile_choice_and_workspace_monotone():
+    p = moe.moe_plan_create(4096, 2048, 256, 6, 8192)
+    try:
+        assert moe.moe_plan_info(p, 128)["tile_m"] == 16      # 3 rows / expert
+        assert moe.moe_plan_info(p, 1024)["tile_m"] == 32     # 24 rows / expert
+        assert moe.moe_plan_info(p, 8192)["tile_m"] >= 64
+        last = 0
+        for T in (0, 1, 17, 128, 500, 1024, 2048, 4096, 8192):
+            b = moe.moe_workspace_bytes(p, T)
+            assert b >= last
+            last = b
+        info = moe.moe_plan_info(p, 128)
+        assert info["pool_rows"] >= 128 * 6 + 256 * 15
+        assert info["pool_rows"] % info["tile_m"] == 0
+        lay = moe.moe_workspace_layout(p, 128)
+        assert lay["total"] == moe.moe_workspace_bytes(p, 128)
+        assert all(lay[k] % 256 == 0 for k in lay if k != "total")
+        with pytest.raises(moe.MoEError):
+            moe.moe_plan_info(p, 8193)
+    finally:
+        moe.moe_plan_destroy(p)
+
+
+class FakeTensor:
+    """Stand-in carrying an address; these calls fail before touching it."""
+
+    def __init__(self, addr=0x1000, nbytes=1 << 20):
+        self.addr, self.nbytes = addr, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def _forward_rc(plan, T, **over):
+    args = dict(x=FakeTensor(), x_sf=FakeTensor(), topk_idx=FakeTensor(), topk_w=FakeTensor(),
+                w1=FakeTensor(), w1_sf=FakeTensor(), w2=FakeTensor(), w2_sf=FakeTensor(),
+                y=FakeTensor(), workspace=FakeTensor())
+    args.update(over)
+    try:
+        moe.moe_forward(plan, T, args["x"], args["x_sf"], args["topk_idx"], args["topk_w"],
+                        args["w1"], args["w1_sf"], args["w2"], args["w2_sf"], args["y"],
+                        args["workspace"], stream=0)
+        return 0
+    except moe.MoEError as e:
+        return e.code
+
+
+def test_forward_host_validation_without_gpu():
+    p = moe.moe_plan_create(256, 128, 8, 2, 64)
+    try:
+        assert _forward_rc(p, 65) == moe.MOE_ERR_INVALID_ARG       # T > max_tokens
+        assert _forward_rc(p, -1) == moe.MOE_ERR_INVALID_ARG
+        assert _forward_rc(p, 0) == moe.MOE_OK                      # no-op, no HIP call
+        for name in ("x", "x_sf", "topk_idx", "topk_w", "w1", "w1_sf", "w2", "w2_sf", "y",
+                     "workspace"):
+            assert _forward_rc(p, 8, **{name: None}) == moe.MOE_ERR_INVALID_ARG, name
+        small = FakeTensor(nbytes=moe.moe_workspace_bytes(p, 8) - 1)
+        assert _forward_rc(p, 8, workspace=small) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+        rc = moe.lib().moe_forward(None, 8, *([ctypes.c_void_p(0x1000)] * 10), 1 << 30, None)
+        assert rc == moe.MOE_ERR_INVALID_ARG
+    finally:
+        moe.moe_plan_destroy(p)
+
+
+def test_route_host_validation_without_gpu():
+    p = moe.moe_plan_create(256, 128, 8, 2, 64)
+    L = moe.lib()
+    a = ctypes.c_void_p(0x1000)
+    big = 1 << 30
+    try:
+        # row_align out of range
+        assert L.moe_route(p, 8, a, 0, a, a, a, 1000, a, a, big, None) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_route(p, 8, a, 2048, a, a, a, 10 ** 6, a, a, big, None) == moe.MOE_ERR_INVALID_ARG
+        # row_src too short for T*K + E*(row_align-1)
+        assert L.moe_route(p, 8, a, 16, a, a, a, 16 + 8 * 15 - 1, a, a, big, None) == \
+            moe.MOE_ERR_INVALID_ARG
+        # workspace too small
+        assert L.moe_route(p, 8, a, 16, a, a, a, 1000, a, a, 8, None) == \
+            moe.MOE_ERR_WORKSPACE_TOO_SMALL
+        # null outputs
+        assert L.moe_route(p, 8, a, 16, None, a, a, 1000, a, a, big, None) == moe.MOE_ERR_INVALID_ARG
+    finally:
+        moe.moe_plan_destroy(p)

@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs.  Routing is compared bit for bit; y within the
+per-token relative L2 bar; intermediate tensors within bounds derived from
+the arithmetic (see the individual tests)."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_grouped_gemm_amd as moe
+import oracle
+from fp8_grouped_gemm_amd import workload as wl
+from parity_util import (check_y, cpu_inputs_to_gpu, gpu_inputs, host_copy_for_oracle,
+                         run_gpu, run_oracle, say, small_case)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ routing
+
+
+def gpu_route(idx_np, E, K, row_align):
+    T = idx_np.shape[0]
+    p = moe.moe_plan_create(128, 128, E, K, max(T, 1))
+    try:
+        idx = torch.from_numpy(np.ascontiguousarray(idx_np, dtype=np.int32)).cuda()
+        r_cap = T * K + E * (row_align - 1)
+        counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+        offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+        row_src = torch.full((max(r_cap, 1),), -7, dtype=torch.int32, device="cuda")
+        src_row = torch.full((max(T * K, 1),), -7, dtype=torch.int32, device="cuda")
+        ws = torch.empty(moe.moe_route_workspace_bytes(p, T), dtype=torch.uint8, device="cuda")
+        moe.moe_route(p, T, idx, row_align, counts, offsets, row_src, src_row, ws)
+        status = moe.moe_read_status(p, T, ws)
+        torch.cuda.synchronize()
+        return (counts.cpu().numpy(), offsets.cpu().numpy(), row_src.cpu().numpy()[:r_cap],
+                src_row.cpu().numpy()[:T * K], status)
+    finally:
+        moe.moe_plan_destroy(p)
+
+
+def assert_route_equal(idx, E, K, ra, what):
+    T = idx.shape[0]
+    r_cap = T * K + E * (ra - 1)
+    say(f"route {what}: T={T} K={K} E={E} row_align={ra}")
+    c, o, rs, sr, status = gpu_route(idx, E, K, ra)
+    rc, ro, rrs, rsr, bad = oracle.route(idx, E, ra, r_cap)
+    assert np.array_equal(c, rc), what
+    assert np.array_equal(o, ro), what
+    assert np.array_equal(rs, rrs), what
+    assert np.array_equal(sr, rsr), what
+    assert status[1] == bad and status[0] == (1 if bad else 0), what
+
+
+@pytest.mark.parametrize("name", ["tiny", "flash_decode", "flash_prefill", "pro_prefill", "skewed"])
+@pytest.mark.parametrize("ra", [16, 64, 128])
+def test_route_bitexact_workloads(name, ra):
+    cfg = wl.CONFIGS[name]
+    for seed in (wl.default_seed(cfg), 0):
+        idx, _ = wl.make_routing(cfg, seed, "cpu")
+        assert_route_equal(idx.numpy(), cfg.E, cfg.K, ra, f"{name} seed {seed}")
+
+
+def test_route_bitexact_adversarial():
+    rng = np.random.default_rng(5)
+    cases = {
+        "all_one_expert": np.full((3000, 6), 7, np.int32),
+        "masks_and_out_of_range": rng.integers(-3, 300, (777, 8)).astype(np.int32),
+        "single_token": np.array([[5, 1, 5]], np.int32),
+        "dups_in_token": np.tile(np.array([[2, 2, 3, 3]], np.int32), (1500, 1)),
+        "ragged_chunks": rng.integers(0, 256, (1023, 3)).astype(np.int32),
+        "all_masked": -np.ones((50, 4), np.int32),
+        "max_experts": rng.integers(0, 1024, (4096, 8)).astype(np.int32),
+    }
+    for what, idx in cases.items():
+        E = 1024 if what == "max_experts" else 256
+        for ra in (1, 16, 128):
+            assert_route_equal(idx, E, idx.shape[1], ra, what)
+
+
+def test_route_zero_tokens():
+    c, o, rs, sr, status = gpu_route(np.zeros((0, 4), np.int32), 32, 4, 16)
+    assert not c.any() and not o.any()
+    assert np.all(rs == -1)
+    assert status[1] == 0
+
+
+# ---------------------------------------------------------------- forward
+
+
+def forward_and_check(host, dev, tile_m, what, check_intermediates=True):
+    say(f"forward {what}: tile_m={tile_m}")
+    y, runner = run_gpu(dev, tile_m=tile_m)
+    T = dev["x"].shape[0]
+    K = dev["topk_idx"].shape[1]
+    ref = run_oracle(host, want=("h", "partial", "acc1"))
+    check_y(y.cpu().numpy(), ref["y"], what=what)
+    if not check_intermediates:
+        return runner
+    # plan: bit-exact against the oracle's routing
+    E = dev["w1"].shape[0]
+    ra = moe.moe_plan_info(runner.plan, T)["tile_m"]
+    R = moe.moe_plan_info(runner.plan, T)["pool_rows"]
+    rc, ro, rrs, rsr, _ = oracle.route(host["idx"], E, ra, R)
+    assert np.array_equal(runner.view("counts", T).cpu().numpy(), rc)
+    assert np.array_equal(runner.view("offsets", T).cpu().numpy(), ro)
+    assert np.array_equal(runner.view("row_src", T).cpu().numpy(), rrs)
+    src_row = runner.view("src_row", T).cpu().numpy()
+    assert np.array_equal(src_row, rsr)
+    # h, h_sf: per slot, dequantised SwiGLU output against the oracle's.  The
+    # gfx950 e4m3 MFMA does not return the exact 128-term block sum the oracle
+    # uses: its result is within ~2e-4 of sum|a*b| (measured), so acc, the
+    # amax and hence h_sf agree to ~1e-3 relative, and an e4m3 code near a
+    # rounding boundary can move by one step.  The bound is therefore on the
+    # dequantised row, with a cap on the share of codes that move.
+    h = runner.view("h", T).cpu().numpy()
+    h_sf = runner.view("h_sf", T).cpu().numpy()
+    dec = np.array([oracle.e4m3_decode(c) for c in range(256)])
+    I = h.shape[1]
+    flips = 0
+    total = 0
+    for f in range(T * K):
+        r = src_row[f]
+        if r < 0:
+            continue
+        g = dec[h[r]].reshape(-1, 128) * h_sf[r][:, None]
+        o = dec[ref["h"][f]].reshape(-1, 128) * ref["h_sf"][f][:, None]
+        den = np.linalg.norm(o)
+        assert np.linalg.norm(g - o) <= 2e-2 * den + 1e-30, (what, f)
+        assert np.allclose(h_sf[r], ref["h_sf"][f], rtol=5e-3, atol=0), (what, f)
+        flips += int((h[r] != ref["h"][f]).sum())
+        total += I
+    say(f"  h codes differing from the oracle: {flips}/{total}")
+    assert flips <= max(8, total // 50), what
+    # partial: bf16 L2 output per valid slot
+    part = runner.view("partial", T).cpu().numpy().astype(np.uint16)
+    for f in range(T * K):
+        if src_row[f] < 0:
+            continue
+        t, j = divmod(f, K)
+        a = (part[j, t].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        b = (ref["partial"][f].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.linalg.norm(a - b) <= 2e-2 * np.linalg.norm(b) + 1e-30, (what, f)
+    return runner
+
+
+@pytest.mark.parametrize("tile_m", [16, 32, 64])
+def test_forward_tiny_all_tiles(tile_m):
+    cfg = wl.CONFIGS["tiny"]
+    host, dev = small_case(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, wl.default_seed(cfg))
+    forward_and_check(host, dev, tile_m, f"tiny tile {tile_m}")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_forward_tiny_seeds_auto_tile(seed):
+    cfg = wl.CONFIGS["tiny"]
+    host, dev = small_case(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, seed)
+    forward_and_check(host, dev, 0, f"tiny seed {seed}")
+
+
+def test_forward_edge_masks_out_of_range_and_empty_tokens():
+    mask = {(0, 0): -1, (0, 1): -1, (0, 2): -1,      # token 0 fully masked -> y = 0
+            (3, 1): 40, (5, 2): 9999,                  # ids >= E: skipped + flagged
+            (7, 0): -5}
+    host, dev = small_case(37, 384, 256, 12, 3, 11, mask=mask)   # H % 256 == 128, I = 2 n-tiles
+    for tile_m in (16, 64):
+        runner = forward_and_check(host, dev, tile_m, f"edge tile {tile_m}")
+        status = moe.moe_read_status(runner.plan, 37, runner.workspace)
+        assert status[0] == moe.MOE_STATUS_EXPERT_OUT_OF_RANGE and status[1] == 2
+
+
+def test_forward_ragged_multi_tile_shapes():
+    # several K blocks, several n tiles, T*K not a multiple of the tile or 1024
+    host, dev = small_case(203, 512, 384, 16, 4, 12)
+    for tile_m in (16, 32, 64):
+        forward_and_check(host, dev, tile_m, f"ragged tile {tile_m}")
+
+
+def test_forward_single_token_and_hot_expert():
+    host, dev = small_case(1, 256, 128, 4, 2, 13)
+    forward_and_check(host, dev, 0, "single token")
+    # every token on expert 2: one long segment, many row tiles
+    T = 150
+    host, dev = small_case(T, 256, 256, 8, 2, 14, mask={(t, 0): 2 for t in range(T)})
+    for tile_m in (16, 64):
+        forward_and_check(host, dev, tile_m, f"hot expert tile {tile_m}")
+
+
+def test_forward_deterministic_and_workspace_reuse():
+    host, dev = small_case(90, 256, 256, 8, 3, 15)
+    y1, runner = run_gpu(dev, tile_m=32, max_tokens=200)
+    # a different, larger call in between leaves stale state in the workspace
+    host2, dev2 = small_case(200, 256, 256, 8, 3, 16)
+    y2, _ = run_gpu(dev2, runner=runner)
+    y3, _ = run_gpu(dev, runner=runner)
+    assert torch.equal(y1, y3)
+    check_y(y2.cpu().numpy(), run_oracle(host2)["y"], what="reuse, larger call")
+
+
+def test_forward_zero_tokens_is_noop():
+    runner = moe.MoEForward(256, 128, 8, 2, 16)
+    y = torch.full((0, 256), 7, dtype=torch.uint16, device="cuda")
+    z = torch.empty(0, dtype=torch.uint8, device="cuda")
+    moe.moe_forward(runner.plan, 0, z, z, z, z, z, z, z, z, y, runner.workspace)
+    torch.cuda.synchronize()
+
+
+# -------------------------------------------------- full-size workloads
+
+
+@pytest.mark.parametrize("name", ["flash_decode", "flash_prefill", "skewed", "pro_prefill"])
+def test_forward_full_size_sampled(name):
+    cfg = wl.CONFIGS[name]
+    seed = wl.default_seed(cfg)
+    say(f"full size {name}: drawing inputs on the GPU")
+    inp = gpu_inputs(cfg, seed)
+    torch.cuda.synchronize()
+    y, runner = run_gpu(inp)
+    info = moe.moe_plan_info(runner.plan, cfg.T)
+    say(f"  tile {info}")
+    yb = y.cpu().numpy()
+    yf = ((yb.astype(np.uint32) << 16).view(np.float32))
+    assert np.all(np.isfinite(yf))
+    # sampled tokens: first, last, and a seeded spread (rows are independent)
+    rng = np.random.default_rng(seed)
+    toks = sorted({0, cfg.T - 1, *rng.choice(cfg.T, 6, replace=False).tolist()})
+    if cfg.skew:  # include a token routed to the hottest expert
+        idx = inp["topk_idx"].cpu().numpy()
+        hot = np.bincount(idx.reshape(-1), minlength=cfg.E).argmax()
+        toks = sorted(set(toks) | {int(np.nonzero((idx == hot).any(1))[0][0])})
+    host = host_copy_for_oracle(inp, toks)
+    ref = run_oracle(host, tokens=toks)
+    # Full-size workloads: every sampled token within 1e-2 (intermediate 2048+,
+    # so one moved e4m3 code in h is far below that).
+    check_y(yb[toks], ref["y"], per_token_tol=1e-2, what=f"{name} sampled tokens {toks}")
+    # plan counts against the oracle's routing (bit-exact, whole workload)
+    ra = info["tile_m"]
+    rc, ro, _, rsr, _ = oracle.route(host["idx"], cfg.E, ra, info["pool_rows"])
+    assert np.array_equal(runner.view("counts", cfg.T).cpu().numpy(), rc)
+    assert np.array_equal(runner.view("src_row", cfg.T).cpu().numpy(), rsr)
+    del inp
+    torch.cuda.empty_cache()

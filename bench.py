@@ -75,7 +75,7 @@ def main():
     ap.add_argument("--workload", default="flash_decode")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=128)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -108,6 +108,11 @@ def main():
     print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # torch creates the HIP event on first record(); do that once so the
+    # library can record the same events between its launches.
+    for step_evs in evs:
+        for e in step_evs:
+            e.record(stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -156,10 +156,13 @@ def moe_forward(plan, num_tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_s
 def moe_forward_timed(plan, num_tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
                       workspace, stream, step_events):
     """moe_forward that also records step_events (5 torch.cuda.Event, or None
-    entries) on `stream` before the planner and after each step."""
+    entries) on `stream` before the planner and after each step.  The events
+    must already exist (torch creates them on their first record())."""
     ws_bytes = workspace.numel() * workspace.element_size()
     ev = (_vp * 5)()
     for i, e in enumerate(step_events):
+        if e is not None and not e.cuda_event:
+            raise ValueError("step event has no HIP event yet: record() it once first")
         ev[i] = None if e is None else e.cuda_event
     rc = lib().moe_forward_timed(plan, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx),
                                  _ptr(topk_w), _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),

@@ -50,17 +50,41 @@ __device__ __forceinline__ Frag2 zero_frag()
     return f;
 }
 
+// Split-K partial store: each of the S K-slices of a tile writes its f32
+// sums, row-major, to part[slice][row][col] for the rows that hold a routed
+// slot; a later kernel adds the slices in slice order.  Lane (lg, lr) holds
+// rows 4*lg + i of column lr of each 16-column subtile.
+template <int MT>
+__device__ __forceinline__ void store_partial(const v4f (&acc)[MT][4], float* part, size_t ld,
+                                              const int32_t* row_src, int row0, const int (&col)[4],
+                                              int lg)
+{
+#pragma unroll
+    for (int ms = 0; ms < MT; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = row0 + 16 * ms + 4 * lg + i;
+            if (row_src[r] < 0)
+                continue;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                part[(size_t)r * ld + col[s]] = acc[ms][s][i];
+        }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------- L1
 
-template <int MT>
+template <int MT, int S>
 __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
 {
     constexpr int BM = 16 * MT;
     const int NT = a.I / 128;
-    const int mb = blockIdx.x / NT;
-    const int nt = blockIdx.x - mb * NT;
+    const int tile = blockIdx.x / S;  // S consecutive workgroups share a tile
+    const int ks = blockIdx.x - tile * S;
+    const int mb = tile / NT;
+    const int nt = tile - mb * NT;
     const int e = a.mblock_expert[mb];
     if (e < 0)
         return;
@@ -68,6 +92,7 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
     const int lr = lane & 15, lg = lane >> 4;
     const int H = a.H, HB = H / 128, I = a.I, K = a.K;
     const int row0 = mb * BM;
+    const int kb0 = ks * HB / S, kb1 = (ks + 1) * HB / S;
 
     // A operand rows: row0 + 16*ms + lr.
     const uint8_t* aptr[MT];
@@ -104,23 +129,36 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
         for (int s = 0; s < 4; ++s)
             acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // Keep the next K block's fragments in flight while multiplying the
+    // current one.
+    constexpr bool PF = true;
     Frag2 fa[MT], fb[4];
+    if (PF && kb0 < kb1) {
 #pragma unroll
-    for (int ms = 0; ms < MT; ++ms)
-        fa[ms] = avalid[ms] ? load_frag(aptr[ms]) : zero_frag();
+        for (int ms = 0; ms < MT; ++ms)
+            fa[ms] = avalid[ms] ? load_frag(aptr[ms] + kb0 * 128) : zero_frag();
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        fb[s] = load_frag(bptr[s]);
+        for (int s = 0; s < 4; ++s)
+            fb[s] = load_frag(bptr[s] + kb0 * 128);
+    }
 
-    for (int kb = 0; kb < HB; ++kb) {
+    for (int kb = kb0; kb < kb1; ++kb) {
         Frag2 na[MT], nb[4];
-        const int kn = kb + 1 < HB ? kb + 1 : kb;
+        const int kn = PF ? (kb + 1 < kb1 ? kb + 1 : kb) : kb;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             nb[s] = load_frag(bptr[s] + kn * 128);
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
             na[ms] = avalid[ms] ? load_frag(aptr[ms] + kn * 128) : zero_frag();
+        if (!PF) {
+#pragma unroll
+            for (int ms = 0; ms < MT; ++ms)
+                fa[ms] = na[ms];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                fb[s] = nb[s];
+        }
         const float sg = sfg[kb], su = sfu[kb];
         float sa[MT][4];
 #pragma unroll
@@ -149,6 +187,16 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
             fb[s] = nb[s];
     }
 
+    if constexpr (S > 1) {
+        // gate and up columns of this lane's four subtiles in the [R, 2I] partials
+        const int col[4] = {nt * 128 + wave * 32 + lr, nt * 128 + wave * 32 + 16 + lr,
+                            I + nt * 128 + wave * 32 + lr, I + nt * 128 + wave * 32 + 16 + lr};
+        store_partial<MT>(acc, a.splitk_part + (size_t)ks * a.splitk_rows * 2 * I, 2 * (size_t)I,
+                          a.row_src, row0, col, lg);
+        return;  // l1_splitk_epilogue finishes the tile
+    }
+    const bool epi = true;
+
     // ---- epilogue: SwiGLU x topk_w, per-row amax over the 128 columns,
     // e4m3 requant, coalesced store through LDS.
     __shared__ float red[4][BM];
@@ -176,23 +224,25 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
                 m = fmaxf(m, fabsf(v));
             }
             m = max16(m);
-            if (lr == 0)
+            if (epi && lr == 0)
                 red[wave][16 * ms + 4 * lg + i] = m;
         }
     }
     __syncthreads();
+    if (epi) {
 #pragma unroll
-    for (int ms = 0; ms < MT; ++ms) {
+        for (int ms = 0; ms < MT; ++ms) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * ms + 4 * lg + i;
-            const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
-            const float sf = fmaxf(amax, 1e-10f) / 448.0f;
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * ms + 4 * lg + i;
+                const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+                const float sf = fmaxf(amax, 1e-10f) / 448.0f;
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                qt[r][wave * 32 + s * 16 + lr] = (uint8_t)f32_to_e4m3(hv[ms][s][i] / sf);
-            if (wave == 0 && lr == 0)
-                a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
+                for (int s = 0; s < 2; ++s)
+                    qt[r][wave * 32 + s * 16 + lr] = (uint8_t)f32_to_e4m3(hv[ms][s][i] / sf);
+                if (wave == 0 && lr == 0)
+                    a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
+            }
         }
     }
     __syncthreads();
@@ -207,20 +257,23 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
 
 // ------------------------------------------------------------------- L2
 
-template <int MT>
+template <int MT, int S>
 __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
 {
     constexpr int BM = 16 * MT;
     const int H = a.H, I = a.I, IB = I / 128, K = a.K, T = a.T;
     const int NT = (H + 255) / 256;  // H % 256 == 128: the last tile has 2 idle waves
-    const int mb = blockIdx.x / NT;
-    const int nt = blockIdx.x - mb * NT;
+    const int tile = blockIdx.x / S;
+    const int ks = blockIdx.x - tile * S;
+    const int mb = tile / NT;
+    const int nt = tile - mb * NT;
     const int e = a.mblock_expert[mb];
     if (e < 0)
         return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int row0 = mb * BM;
+    const int kb0 = ks * IB / S, kb1 = (ks + 1) * IB / S;
 
     const uint8_t* aptr[MT];
     bool avalid[MT];
@@ -252,23 +305,34 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
         for (int s = 0; s < 4; ++s)
             acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    constexpr bool PF = true;  // as in l1_direct
     Frag2 fa[MT], fb[4];
+    if (PF && kb0 < kb1) {
 #pragma unroll
-    for (int ms = 0; ms < MT; ++ms)
-        fa[ms] = avalid[ms] ? load_frag(aptr[ms]) : zero_frag();
+        for (int ms = 0; ms < MT; ++ms)
+            fa[ms] = avalid[ms] ? load_frag(aptr[ms] + kb0 * 128) : zero_frag();
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        fb[s] = load_frag(bptr[s]);
+        for (int s = 0; s < 4; ++s)
+            fb[s] = load_frag(bptr[s] + kb0 * 128);
+    }
 
-    for (int kb = 0; kb < IB; ++kb) {
+    for (int kb = kb0; kb < kb1; ++kb) {
         Frag2 na[MT], nb[4];
-        const int kn = kb + 1 < IB ? kb + 1 : kb;
+        const int kn = PF ? (kb + 1 < kb1 ? kb + 1 : kb) : kb;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             nb[s] = load_frag(bptr[s] + kn * 128);
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
             na[ms] = avalid[ms] ? load_frag(aptr[ms] + kn * 128) : zero_frag();
+        if (!PF) {
+#pragma unroll
+            for (int ms = 0; ms < MT; ++ms)
+                fa[ms] = na[ms];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                fb[s] = nb[s];
+        }
         const float sb = sfb[kb];
         float sa[MT][4];
 #pragma unroll
@@ -296,16 +360,27 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
             fb[s] = nb[s];
     }
 
+    if constexpr (S > 1) {
+        if (nt * 256 + wave * 64 >= H)
+            return;  // idle wave of a half tile
+        const int col[4] = {ncol0 + lr, ncol0 + 16 + lr, ncol0 + 32 + lr, ncol0 + 48 + lr};
+        store_partial<MT>(acc, a.splitk_part + (size_t)ks * a.splitk_rows * H, (size_t)H,
+                          a.row_src, row0, col, lg);
+        return;  // the combine adds the slices
+    }
+
     // ---- epilogue: bf16, stage BM x 256 in LDS, 16-byte stores to the
     // (slot, token) row of the partial buffer.
     __shared__ uint16_t ot[BM][256 + 8];
+    {
 #pragma unroll
-    for (int ms = 0; ms < MT; ++ms)
+        for (int ms = 0; ms < MT; ++ms)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                ot[16 * ms + 4 * lg + i][wave * 64 + s * 16 + lr] = f32_to_bf16(acc[ms][s][i]);
+                for (int i = 0; i < 4; ++i)
+                    ot[16 * ms + 4 * lg + i][wave * 64 + s * 16 + lr] = f32_to_bf16(acc[ms][s][i]);
+    }
     __syncthreads();
     for (int c = threadIdx.x; c < BM * 32; c += 256) {
         const int r = c >> 5, col = (c & 31) * 8;
@@ -320,6 +395,63 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
             *reinterpret_cast<uint4*>(a.partial + ((size_t)j * T + t) * H + nt * 256 + col) = v;
         }
     }
+}
+
+// ------------------------------------------------- L1 split-K epilogue
+
+// Finishes a 16-row L1 tile whose K range ran as S workgroups: adds the S
+// f32 partials in slice order, then the same SwiGLU x topk_w, per-128 amax
+// and e4m3 requant as the l1_direct epilogue.  Thread t: row t/16, gate
+// columns 8*(t%16) .. +8 of the tile's 128-column block and the matching up
+// columns; the 16 threads of a row share one wave quarter.
+__global__ __launch_bounds__(256) void l1_splitk_epilogue(FwdArgs a)
+{
+    const int I = a.I, NT = I / 128, S = a.split_l1;
+    const int mb = blockIdx.x / NT;
+    const int nt = blockIdx.x - mb * NT;
+    if (a.mblock_expert[mb] < 0)
+        return;
+    const int r = mb * 16 + (threadIdx.x >> 4);
+    const int c0 = nt * 128 + (threadIdx.x & 15) * 8;
+    const int f = a.row_src[r];
+    float g[8], u[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        g[q] = u[q] = 0.f;
+    if (f >= 0) {
+        for (int k = 0; k < S; ++k) {
+            const float* row = a.splitk_part + ((size_t)k * a.splitk_rows + r) * 2 * I;
+            const float4 g0 = *reinterpret_cast<const float4*>(row + c0);
+            const float4 g1 = *reinterpret_cast<const float4*>(row + c0 + 4);
+            const float4 u0 = *reinterpret_cast<const float4*>(row + I + c0);
+            const float4 u1 = *reinterpret_cast<const float4*>(row + I + c0 + 4);
+            g[0] += g0.x; g[1] += g0.y; g[2] += g0.z; g[3] += g0.w;
+            g[4] += g1.x; g[5] += g1.y; g[6] += g1.z; g[7] += g1.w;
+            u[0] += u0.x; u[1] += u0.y; u[2] += u0.z; u[3] += u0.w;
+            u[4] += u1.x; u[5] += u1.y; u[6] += u1.z; u[7] += u1.w;
+        }
+    }
+    const float w = f >= 0 ? a.topk_w[f] : 0.f;
+    float hv[8], m = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float silu = g[q] / (1.0f + expf(-g[q]));
+        hv[q] = (silu * u[q]) * w;
+        m = fmaxf(m, fabsf(hv[q]));
+    }
+    m = max16(m);
+    if (f < 0)
+        return;
+    const float sf = fmaxf(m, 1e-10f) / 448.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        lo |= f32_to_e4m3(hv[q] / sf) << (8 * q);
+        hi |= f32_to_e4m3(hv[q + 4] / sf) << (8 * q);
+    }
+    *reinterpret_cast<uint2*>(a.h + (size_t)r * I + c0) = make_uint2(lo, hi);
+    if ((threadIdx.x & 15) == 0)
+        a.h_sf[(size_t)r * NT + nt] = sf;
 }
 
 // -------------------------------------------------------------- combine
@@ -342,7 +474,30 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdArgs a)
         const int e = a.idx[t * a.K + j];
         if (e < 0 || e >= a.E)
             continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(a.partial + ((size_t)j * a.T + t) * a.H + c);
+        uint16_t* prow = a.partial + ((size_t)j * a.T + t) * a.H + c;
+        if (a.split_l2 > 1) {
+            // L2 ran split-K: this slot's bf16 partial is the slice sum, added
+            // in slice order, rounded once; keep it in the partial buffer too.
+            const int r = a.src_row[t * a.K + j];
+            float p[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                p[q] = 0.f;
+            for (int k = 0; k < a.split_l2; ++k) {
+                const float* src = a.splitk_part + ((size_t)k * a.splitk_rows + r) * a.H + c;
+                const float4 v0 = *reinterpret_cast<const float4*>(src);
+                const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+                p[0] += v0.x; p[1] += v0.y; p[2] += v0.z; p[3] += v0.w;
+                p[4] += v1.x; p[5] += v1.y; p[6] += v1.z; p[7] += v1.w;
+            }
+            uint4 o;
+            o.x = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
+            o.y = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
+            o.z = (uint32_t)f32_to_bf16(p[4]) | ((uint32_t)f32_to_bf16(p[5]) << 16);
+            o.w = (uint32_t)f32_to_bf16(p[6]) | ((uint32_t)f32_to_bf16(p[7]) << 16);
+            *reinterpret_cast<uint4*>(prow) = o;
+        }
+        const uint4 v = *reinterpret_cast<const uint4*>(prow);
         s[0] += bf16_to_f32(v.x & 0xFFFFu);
         s[1] += bf16_to_f32(v.x >> 16);
         s[2] += bf16_to_f32(v.y & 0xFFFFu);
@@ -363,11 +518,18 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdArgs a)
 hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s)
 {
     (void)kernel;
-    const dim3 grid(a.num_mblocks * (a.I / 128));
+    const unsigned tiles = a.num_mblocks * (a.I / 128);
     switch (a.BM) {
-    case 16: hipLaunchKernelGGL(l1_direct<1>, grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL(l1_direct<2>, grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(l1_direct<4>, grid, dim3(256), 0, s, a); break;
+    case 16:
+        if (a.split_l1 == 4) {
+            hipLaunchKernelGGL((l1_direct<1, 4>), dim3(tiles * 4), dim3(256), 0, s, a);
+            hipLaunchKernelGGL(l1_splitk_epilogue, dim3(tiles), dim3(256), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((l1_direct<1, 1>), dim3(tiles), dim3(256), 0, s, a);
+        }
+        break;
+    case 32: hipLaunchKernelGGL((l1_direct<2, 1>), dim3(tiles), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((l1_direct<4, 1>), dim3(tiles), dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -376,11 +538,16 @@ hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s)
 hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s)
 {
     (void)kernel;
-    const dim3 grid(a.num_mblocks * ((a.H + 255) / 256));
+    const unsigned tiles = a.num_mblocks * ((a.H + 255) / 256);
     switch (a.BM) {
-    case 16: hipLaunchKernelGGL(l2_direct<1>, grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL(l2_direct<2>, grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(l2_direct<4>, grid, dim3(256), 0, s, a); break;
+    case 16:
+        if (a.split_l2 == 2)
+            hipLaunchKernelGGL((l2_direct<1, 2>), dim3(tiles * 2), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((l2_direct<1, 1>), dim3(tiles), dim3(256), 0, s, a);
+        break;
+    case 32: hipLaunchKernelGGL((l2_direct<2, 1>), dim3(tiles), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((l2_direct<4, 1>), dim3(tiles), dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -42,8 +42,23 @@ Config choose_config(const moe_shape_t& s, int T)
 
 struct Layout {
     int tile_m, kernel, r_cap, mb_cap, NB;
-    size_t status, counts, offsets, blk, mbe, row_src, src_row, h_sf, h, partial, total;
+    int split_l1, split_l2, part_rows;
+    size_t status, counts, offsets, blk, mbe, row_src, src_row, h_sf, h, partial;
+    size_t part, total;
 };
+
+// Split-K across workgroups for the 16-row decode tiles: a tile's weight
+// block is streamed by S workgroups of ~256 KiB each instead of one of ~1
+// MiB, which the HBM stream sustains markedly better on MI355X.
+constexpr int kSplitL1 = 4, kSplitL2 = 2;
+
+// Pool capacity (rows) for T tokens with row alignment ra.
+long long pool_rows(const moe_shape_t& s, long long T, int ra)
+{
+    long long r = T * s.top_k + (long long)s.num_experts * (ra - 1);
+    r = (r + ra - 1) / ra * ra;
+    return std::max<long long>(r, ra);
+}
 
 Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
 {
@@ -53,9 +68,7 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     L.kernel = c.kernel;
     const int ra = row_align_override > 0 ? row_align_override : c.tile_m;
     const long long TK = (long long)T * s.top_k;
-    long long r = TK + (long long)s.num_experts * (ra - 1);
-    r = (r + ra - 1) / ra * ra;
-    L.r_cap = (int)std::max<long long>(r, ra);
+    L.r_cap = (int)pool_rows(s, T, ra);
     L.mb_cap = L.r_cap / ra;
     L.NB = (int)std::max<long long>((TK + moe::kRouteThreads - 1) / moe::kRouteThreads, 1);
     const int E = s.num_experts, H = s.hidden, I = s.intermediate, K = s.top_k;
@@ -75,6 +88,29 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     L.h_sf = take(sizeof(float) * (size_t)L.r_cap * (I / 128));
     L.h = take((size_t)L.r_cap * I);
     L.partial = take(sizeof(uint16_t) * (size_t)K * T * H);
+    // Split-K scratch.  Sized for the largest token count <= T that runs the
+    // 16-row tiles, so the total stays nondecreasing in T.
+    const int NT1 = I / 128, NT2 = (H + 255) / 256;
+    long long t16 = 0;
+    if (s.tile_m == 16)
+        t16 = T;
+    else if (s.tile_m == 0)
+        t16 = std::min<long long>(T, (long long)(12.0 * E / K));
+    while (t16 > 0 && choose_config(s, (int)t16).tile_m != 16)
+        --t16;
+    const int mb16 = t16 > 0 ? (int)(pool_rows(s, t16, 16) / 16) : 0;
+    (void)NT1;
+    (void)NT2;
+    const int s1 = H / 128 >= kSplitL1 ? kSplitL1 : 1;
+    const int s2 = I / 128 >= kSplitL2 ? kSplitL2 : 1;
+    L.split_l1 = c.tile_m == 16 ? s1 : 1;
+    L.split_l2 = c.tile_m == 16 ? s2 : 1;
+    // f32 partials part[slice][row][col]: L1 uses [s1][R][2I], L2 [s2][R][H]
+    // (one after the other, so they share the region).
+    L.part_rows = mb16 * 16;
+    const size_t n1 = s1 > 1 ? (size_t)s1 * L.part_rows * 2 * I : 0;
+    const size_t n2 = s2 > 1 ? (size_t)s2 * L.part_rows * H : 0;
+    L.part = take(sizeof(float) * std::max(n1, n2));
     L.total = o;
     return L;
 }
@@ -301,6 +337,11 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     a.h_sf = at<float>(workspace, L.h_sf);
     a.partial = at<uint16_t>(workspace, L.partial);
     a.y = y;
+    a.src_row = at<int32_t>(workspace, L.src_row);
+    a.split_l1 = L.split_l1;
+    a.split_l2 = L.split_l2;
+    a.splitk_rows = L.part_rows;
+    a.splitk_part = at<float>(workspace, L.part);
     if (moe::launch_l1(a, L.kernel, st) != hipSuccess || !mark(2))
         return MOE_ERR_HIP;
     if (moe::launch_l2(a, L.kernel, st) != hipSuccess || !mark(3))

@@ -43,6 +43,13 @@ struct FwdArgs {
     float* h_sf;
     uint16_t* partial;
     uint16_t* y;
+    const int32_t* src_row;
+    // Split-K across workgroups (tile_m 16): K slices per L1 / L2 tile (1 =
+    // off) and their f32 partial sums, part[slice][row][col] with
+    // splitk_rows rows per slice.
+    int32_t split_l1, split_l2;
+    int32_t splitk_rows;
+    float* splitk_part;
 };
 
 constexpr int kRouteThreads = 1024;

@@ -143,8 +143,98 @@ __global__ __launch_bounds__(kRouteThreads) void route_assign(RouteArgs a)
     }
 }
 
+// All three steps in one block when every slot fits in one chunk
+// (T*K <= 1024, the decode case): one launch instead of three.
+__global__ __launch_bounds__(kRouteThreads) void route_small(RouteArgs a)
+{
+    extern __shared__ int32_t wave_cnt[];  // [16][E]: per-wave counts, then per-wave bases
+    __shared__ int32_t scan[kRouteThreads];
+    __shared__ int32_t bad_sh;
+    constexpr int kWaves = kRouteThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kWaves * a.E; i += kRouteThreads)
+        wave_cnt[i] = 0;
+    if (threadIdx.x == 0)
+        bad_sh = 0;
+    __syncthreads();
+    const int f = threadIdx.x;
+    const int e = (f < a.TK) ? a.idx[f] : -1;
+    const bool valid = e >= 0 && e < a.E;
+    const int key = valid ? e : -1;
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+        const int other = __shfl(key, j);
+        rank += (j < lane && other == key) ? 1 : 0;
+    }
+    if (valid)
+        atomicAdd(&wave_cnt[wave * a.E + e], 1);
+    else if (f < a.TK && e >= a.E)
+        atomicAdd(&bad_sh, 1);
+    __syncthreads();
+    // Thread x owns expert x: total, per-wave bases, aligned segment.
+    const int x = threadIdx.x;
+    int total = 0, seg = 0;
+    if (x < a.E) {
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = wave_cnt[w * a.E + x];
+            wave_cnt[w * a.E + x] = total;
+            total += c;
+        }
+        seg = (total + a.row_align - 1) / a.row_align * a.row_align;
+        a.counts[x] = total;
+    }
+    scan[x] = seg;
+    __syncthreads();
+    for (int d = 1; d < kRouteThreads; d <<= 1) {
+        int v = (x >= d) ? scan[x - d] : 0;
+        __syncthreads();
+        scan[x] += v;
+        __syncthreads();
+    }
+    const int start = scan[x] - seg;
+    const int used = scan[kRouteThreads - 1];
+    if (x < a.E) {
+        a.offsets[x] = start;
+        for (int r = start + total; r < start + seg; ++r)
+            a.row_src[r] = -1;
+        if (a.mblock_expert) {
+            for (int m = start / a.row_align; m < (start + seg) / a.row_align; ++m)
+                a.mblock_expert[m] = x;
+        }
+    }
+    if (x == 0) {
+        a.offsets[a.E] = used;
+        a.status[0] = bad_sh > 0 ? 1 : 0;
+        a.status[1] = bad_sh;
+        a.status[2] = used;
+        a.status[3] = 0;
+    }
+    for (int r = used + x; r < a.r_cap; r += kRouteThreads)
+        a.row_src[r] = -1;
+    if (a.mblock_expert) {
+        for (int m = used / a.row_align + x; m < a.mb_cap; m += kRouteThreads)
+            a.mblock_expert[m] = -1;
+    }
+    __syncthreads();  // scan[] holds inclusive ends: start of expert e = scan[e] - seg(e)
+    if (f < a.TK) {
+        if (valid) {
+            const int seg_e = scan[e] - (e > 0 ? scan[e - 1] : 0);
+            const int pos = scan[e] - seg_e + wave_cnt[wave * a.E + e] + rank;
+            a.row_src[pos] = f;
+            a.src_row[f] = pos;
+        } else {
+            a.src_row[f] = -1;
+        }
+    }
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s)
 {
+    if (a.NB == 1 && a.E <= 512) {
+        hipLaunchKernelGGL(route_small, dim3(1), dim3(kRouteThreads),
+                           sizeof(int32_t) * 16 * a.E, s, a);
+        return hipGetLastError();
+    }
     const size_t lds_hist = sizeof(int32_t) * (a.E + 1);
     const size_t lds_wave = sizeof(int32_t) * 16 * a.E;
     if (a.NB > 0)

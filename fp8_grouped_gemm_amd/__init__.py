@@ -18,11 +18,13 @@ MOE_ERR_WORKSPACE_TOO_SMALL = -3
 MOE_ERR_HIP = -4
 MOE_ERR_NOT_GFX950 = -5
 MOE_STATUS_EXPERT_OUT_OF_RANGE = 1
+MOE_WEIGHTS_ROW_MAJOR = 0
+MOE_WEIGHTS_PACKED = 1
 
 EXPORTED_SYMBOLS = (
     "moe_plan_create", "moe_plan_destroy", "moe_plan_info", "moe_workspace_bytes",
     "moe_workspace_layout", "moe_forward", "moe_forward_timed", "moe_route",
-    "moe_route_workspace_bytes",
+    "moe_route_workspace_bytes", "moe_prepare_weights",
     "moe_read_status", "moe_strerror", "moe_version",
 )
 
@@ -36,7 +38,8 @@ class MoEError(RuntimeError):
 class moe_shape_t(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("max_tokens", ctypes.c_int32), ("tile_m", ctypes.c_int32)]
+                ("max_tokens", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32)]
 
 
 class moe_tile_info_t(ctypes.Structure):
@@ -75,6 +78,7 @@ def lib():
         L.moe_route.argtypes = ([_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp,
                                  ctypes.c_size_t, _vp])
         L.moe_route_workspace_bytes.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_prepare_weights.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_read_status.argtypes = [_vp, _i32, _vp, ctypes.c_size_t,
                                       ctypes.POINTER(ctypes.c_int32), _vp]
         L.moe_strerror.argtypes = [ctypes.c_int]
@@ -114,8 +118,10 @@ def _stream(stream):
 
 # --- the C ABI, one Python function per entry point -----------------------
 
-def moe_plan_create(hidden, intermediate, num_experts, top_k, max_tokens, tile_m=0):
-    shape = moe_shape_t(hidden, intermediate, num_experts, top_k, max_tokens, tile_m)
+def moe_plan_create(hidden, intermediate, num_experts, top_k, max_tokens, tile_m=0,
+                    weight_layout=MOE_WEIGHTS_ROW_MAJOR):
+    shape = moe_shape_t(hidden, intermediate, num_experts, top_k, max_tokens, tile_m,
+                        weight_layout)
     h = ctypes.c_void_p()
     _check(lib().moe_plan_create(ctypes.byref(shape), ctypes.byref(h)), "moe_plan_create")
     return h
@@ -170,6 +176,13 @@ def moe_forward_timed(plan, num_tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2
     _check(rc, "moe_forward_timed")
 
 
+def moe_prepare_weights(plan, w1, w2, w1_packed, w2_packed, stream=None):
+    """Write the packed (MFMA operand order) copies of w1/w2 for a packed plan."""
+    rc = lib().moe_prepare_weights(plan, _ptr(w1), _ptr(w2), _ptr(w1_packed), _ptr(w2_packed),
+                                   _stream(stream))
+    _check(rc, "moe_prepare_weights")
+
+
 def moe_route_workspace_bytes(plan, num_tokens):
     n = ctypes.c_size_t()
     _check(lib().moe_route_workspace_bytes(plan, num_tokens, ctypes.byref(n)),
@@ -200,13 +213,24 @@ class MoEForward:
     """Plan + workspace holder.  forward() writes y for T tokens."""
 
     def __init__(self, hidden, intermediate, num_experts, top_k, max_tokens, tile_m=0,
-                 device="cuda"):
+                 device="cuda", weight_layout=MOE_WEIGHTS_ROW_MAJOR):
         import torch
         self.shape = (hidden, intermediate, num_experts, top_k, max_tokens, tile_m)
+        self.weight_layout = weight_layout
         self.plan = moe_plan_create(hidden, intermediate, num_experts, top_k, max_tokens,
-                                    tile_m)
+                                    tile_m, weight_layout)
         self.ws_bytes = moe_workspace_bytes(self.plan, max_tokens)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    def prepare(self, w1, w2, stream=None):
+        """Packed copies of w1/w2 for this plan (identity for row-major plans)."""
+        import torch
+        if self.weight_layout != MOE_WEIGHTS_PACKED:
+            return w1, w2
+        p1 = torch.empty_like(w1)
+        p2 = torch.empty_like(w2)
+        moe_prepare_weights(self.plan, w1, w2, p1, p2, stream)
+        return p1, p2
 
     def forward(self, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y=None, stream=None):
         import torch

@@ -42,6 +42,27 @@ __device__ __forceinline__ Frag2 load_frag(const uint8_t* p)
     return f;
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// A weight fragment.  Row-major weights: the two 16-byte halves sit 64 bytes
+// apart in the row.  Packed weights (moe_prepare_weights order): each half is
+// one lane's slice of a contiguous 1 KiB run and the other half follows 1 KiB
+// later; the stream is read once, so it is loaded nontemporally.
+template <bool PK>
+__device__ __forceinline__ Frag2 load_wfrag(const uint8_t* p)
+{
+    if constexpr (PK) {
+        const u32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        const u32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 1024));
+        Frag2 f;
+        f.lo = make_uint4(lo.x, lo.y, lo.z, lo.w);
+        f.hi = make_uint4(hi.x, hi.y, hi.z, hi.w);
+        return f;
+    } else {
+        return load_frag(p);
+    }
+}
+
 __device__ __forceinline__ Frag2 zero_frag()
 {
     Frag2 f;
@@ -76,7 +97,7 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[MT][4], float* pa
 
 // ------------------------------------------------------------------- L1
 
-template <int MT, int S>
+template <int MT, int S, bool PK>
 __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
 {
     constexpr int BM = 16 * MT;
@@ -112,12 +133,18 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
             const int f = a.row_src[row0 + 16 * ms + 4 * lg + i];
             asf[ms][i] = a.x_sf + (size_t)(f >= 0 ? f / K : 0) * HB;
         }
-    // B operand: subtile s = 0,1 gate, 2,3 up.
+    // B operand: subtile s = 0,1 gate, 2,3 up.  kstride: bytes between K blocks.
     const uint8_t* bptr[4];
+    constexpr size_t kstride = PK ? 32768 : 128;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const int n = (s >= 2 ? I : 0) + nt * 128 + wave * 32 + (s & 1) * 16 + lr;
-        bptr[s] = a.w1 + ((size_t)e * 2 * I + n) * H + lg * 16;
+        if constexpr (PK) {
+            bptr[s] = a.w1 + (size_t)e * 2 * I * H + (size_t)nt * HB * 32768 + (wave * 4 + s) * 2048 +
+                      lane * 16;
+        } else {
+            const int n = (s >= 2 ? I : 0) + nt * 128 + wave * 32 + (s & 1) * 16 + lr;
+            bptr[s] = a.w1 + ((size_t)e * 2 * I + n) * H + lg * 16;
+        }
     }
     const float* sfg = a.w1_sf + ((size_t)e * (2 * I / 128) + nt) * HB;
     const float* sfu = a.w1_sf + ((size_t)e * (2 * I / 128) + I / 128 + nt) * HB;
@@ -139,7 +166,7 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
             fa[ms] = avalid[ms] ? load_frag(aptr[ms] + kb0 * 128) : zero_frag();
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            fb[s] = load_frag(bptr[s] + kb0 * 128);
+            fb[s] = load_wfrag<PK>(bptr[s] + kb0 * kstride);
     }
 
     for (int kb = kb0; kb < kb1; ++kb) {
@@ -147,7 +174,7 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
         const int kn = PF ? (kb + 1 < kb1 ? kb + 1 : kb) : kb;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            nb[s] = load_frag(bptr[s] + kn * 128);
+            nb[s] = load_wfrag<PK>(bptr[s] + kn * kstride);
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
             na[ms] = avalid[ms] ? load_frag(aptr[ms] + kn * 128) : zero_frag();
@@ -257,7 +284,7 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
 
 // ------------------------------------------------------------------- L2
 
-template <int MT, int S>
+template <int MT, int S, bool PK>
 __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
 {
     constexpr int BM = 16 * MT;
@@ -293,9 +320,15 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
     // wave re-reads column block 0 and stores nothing.
     const int ncol0 = (nt * 256 + wave * 64 < H) ? nt * 256 + wave * 64 : 0;
     const uint8_t* bptr[4];
+    constexpr size_t kstride = PK ? 32768 : 128;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        bptr[s] = a.w2 + ((size_t)e * H + ncol0 + s * 16 + lr) * I + lg * 16;
+    for (int s = 0; s < 4; ++s) {
+        if constexpr (PK)
+            bptr[s] = a.w2 + (size_t)e * H * I + (size_t)nt * IB * 32768 + (wave * 4 + s) * 2048 +
+                      lane * 16;
+        else
+            bptr[s] = a.w2 + ((size_t)e * H + ncol0 + s * 16 + lr) * I + lg * 16;
+    }
     const float* sfb = a.w2_sf + ((size_t)e * (H / 128) + ncol0 / 128) * IB;
 
     v4f acc[MT][4];
@@ -313,7 +346,7 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
             fa[ms] = avalid[ms] ? load_frag(aptr[ms] + kb0 * 128) : zero_frag();
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            fb[s] = load_frag(bptr[s] + kb0 * 128);
+            fb[s] = load_wfrag<PK>(bptr[s] + kb0 * kstride);
     }
 
     for (int kb = kb0; kb < kb1; ++kb) {
@@ -321,7 +354,7 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
         const int kn = PF ? (kb + 1 < kb1 ? kb + 1 : kb) : kb;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            nb[s] = load_frag(bptr[s] + kn * 128);
+            nb[s] = load_wfrag<PK>(bptr[s] + kn * kstride);
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
             na[ms] = avalid[ms] ? load_frag(aptr[ms] + kn * 128) : zero_frag();
@@ -515,42 +548,59 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdArgs a)
     *reinterpret_cast<uint4*>(a.y + (size_t)t * a.H + c) = o;
 }
 
-hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s)
+template <bool PK>
+static hipError_t launch_l1_t(const FwdArgs& a, hipStream_t s)
 {
-    (void)kernel;
     const unsigned tiles = a.num_mblocks * (a.I / 128);
     switch (a.BM) {
     case 16:
-        if (a.split_l1 == 4) {
-            hipLaunchKernelGGL((l1_direct<1, 4>), dim3(tiles * 4), dim3(256), 0, s, a);
+        if (a.split_l1 > 1) {
+            if (a.split_l1 != 4)
+                return hipErrorInvalidValue;
+            hipLaunchKernelGGL((l1_direct<1, 4, PK>), dim3(tiles * 4), dim3(256), 0, s, a);
             hipLaunchKernelGGL(l1_splitk_epilogue, dim3(tiles), dim3(256), 0, s, a);
         } else {
-            hipLaunchKernelGGL((l1_direct<1, 1>), dim3(tiles), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((l1_direct<1, 1, PK>), dim3(tiles), dim3(256), 0, s, a);
         }
         break;
-    case 32: hipLaunchKernelGGL((l1_direct<2, 1>), dim3(tiles), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((l1_direct<4, 1>), dim3(tiles), dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((l1_direct<2, 1, PK>), dim3(tiles), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((l1_direct<4, 1, PK>), dim3(tiles), dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s)
+template <bool PK>
+static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
 {
-    (void)kernel;
     const unsigned tiles = a.num_mblocks * ((a.H + 255) / 256);
     switch (a.BM) {
     case 16:
-        if (a.split_l2 == 2)
-            hipLaunchKernelGGL((l2_direct<1, 2>), dim3(tiles * 2), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((l2_direct<1, 1>), dim3(tiles), dim3(256), 0, s, a);
+        if (a.split_l2 > 1) {
+            if (a.split_l2 != 2)
+                return hipErrorInvalidValue;
+            hipLaunchKernelGGL((l2_direct<1, 2, PK>), dim3(tiles * 2), dim3(256), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((l2_direct<1, 1, PK>), dim3(tiles), dim3(256), 0, s, a);
+        }
         break;
-    case 32: hipLaunchKernelGGL((l2_direct<2, 1>), dim3(tiles), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((l2_direct<4, 1>), dim3(tiles), dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((l2_direct<2, 1, PK>), dim3(tiles), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((l2_direct<4, 1, PK>), dim3(tiles), dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s)
+{
+    (void)kernel;
+    return a.packed ? launch_l1_t<true>(a, s) : launch_l1_t<false>(a, s);
+}
+
+hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s)
+{
+    (void)kernel;
+    return a.packed ? launch_l2_t<true>(a, s) : launch_l2_t<false>(a, s);
 }
 
 hipError_t launch_combine(const FwdArgs& a, hipStream_t s)

@@ -134,6 +134,10 @@ int validate_shape(const moe_shape_t* s)
         return MOE_ERR_UNSUPPORTED_SHAPE;
     if (s->tile_m != 0 && s->tile_m != 16 && s->tile_m != 32 && s->tile_m != 64)
         return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (s->weight_layout != MOE_WEIGHTS_ROW_MAJOR && s->weight_layout != MOE_WEIGHTS_PACKED)
+        return MOE_ERR_INVALID_ARG;
+    if (s->weight_layout == MOE_WEIGHTS_PACKED && s->hidden % 256)
+        return MOE_ERR_UNSUPPORTED_SHAPE;
     return MOE_OK;
 }
 
@@ -322,6 +326,7 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     a.E = s.num_experts;
     a.K = s.top_k;
     a.BM = L.tile_m;
+    a.packed = s.weight_layout == MOE_WEIGHTS_PACKED;
     a.x = x;
     a.x_sf = x_sf;
     a.idx = topk_idx;
@@ -358,6 +363,34 @@ int moe_forward(moe_plan_t plan, int32_t T, const uint8_t* x, const float* x_sf,
 {
     return moe_forward_timed(plan, T, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
                              workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_prepare_weights(moe_plan_t plan, const uint8_t* w1, const uint8_t* w2,
+                        uint8_t* w1_packed, uint8_t* w2_packed, void* stream)
+{
+    if (!plan || !w1 || !w2 || !w1_packed || !w2_packed)
+        return MOE_ERR_INVALID_ARG;
+    const moe_shape_t& s = plan->shape;
+    if (s.weight_layout != MOE_WEIGHTS_PACKED)
+        return MOE_ERR_INVALID_ARG;
+    const size_t b1 = (size_t)s.num_experts * 2 * s.intermediate * s.hidden;
+    const size_t b2 = (size_t)s.num_experts * s.hidden * s.intermediate;
+    auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+        const char* pa = static_cast<const char*>(a);
+        const char* pb = static_cast<const char*>(b);
+        return pa < pb + nb && pb < pa + na;
+    };
+    if (overlap(w1, b1, w1_packed, b1) || overlap(w1, b1, w2_packed, b2) ||
+        overlap(w2, b2, w1_packed, b1) || overlap(w2, b2, w2_packed, b2) ||
+        overlap(w1_packed, b1, w2_packed, b2))
+        return MOE_ERR_INVALID_ARG;
+    int rc = device_ok();
+    if (rc != MOE_OK)
+        return rc;
+    if (moe::launch_pack(w1, w2, w1_packed, w2_packed, s.num_experts, s.hidden, s.intermediate,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
 }
 
 int moe_route_workspace_bytes(moe_plan_t plan, int32_t T, size_t* bytes)

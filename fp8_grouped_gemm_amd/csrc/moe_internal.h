@@ -28,6 +28,7 @@ struct RouteArgs {
 // Everything the GEMM, epilogue and combine kernels read or write.
 struct FwdArgs {
     int32_t T, H, I, E, K, BM;
+    int32_t packed;  // w1/w2 in moe_prepare_weights order
     const uint8_t* x;
     const float* x_sf;
     const int32_t* idx;
@@ -59,5 +60,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s);
 hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s);
 hipError_t launch_combine(const FwdArgs& a, hipStream_t s);
+hipError_t launch_pack(const uint8_t* w1, const uint8_t* w2, uint8_t* w1p, uint8_t* w2p, int E,
+                       int H, int I, hipStream_t s);
 
 }  // namespace moe

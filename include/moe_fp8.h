@@ -56,13 +56,18 @@ extern "C" {
 /* Status bits written by the planner into the workspace (moe_read_status). */
 #define MOE_STATUS_EXPERT_OUT_OF_RANGE 1 /* some topk_idx >= E; those slots were skipped */
 
+/* Weight layouts a plan can expect for w1/w2 (scales are always row-major). */
+#define MOE_WEIGHTS_ROW_MAJOR 0 /* w1 [E,2I,H], w2 [E,H,I] as documented at moe_forward */
+#define MOE_WEIGHTS_PACKED 1    /* written by moe_prepare_weights (needs H % 256 == 0) */
+
 typedef struct moe_shape {
-    int32_t hidden;       /* H */
-    int32_t intermediate; /* I */
-    int32_t num_experts;  /* E */
-    int32_t top_k;        /* K */
-    int32_t max_tokens;   /* largest T any call on this plan may pass */
-    int32_t tile_m;       /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128 */
+    int32_t hidden;        /* H */
+    int32_t intermediate;  /* I */
+    int32_t num_experts;   /* E */
+    int32_t top_k;         /* K */
+    int32_t max_tokens;    /* largest T any call on this plan may pass */
+    int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32 or 64 */
+    int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
 } moe_shape_t;
 
 typedef struct moe_plan* moe_plan_t;
@@ -114,8 +119,9 @@ int moe_workspace_layout(moe_plan_t plan, int32_t num_tokens, moe_ws_layout_t* l
  *                                 skipped and flagged in the status word
  *   topk_w   f32    [T, K]        router weights, applied in the SwiGLU step
  *   w1       uint8  [E, 2I, H]    e4m3, rows [0,I) gate, rows [I,2I) up
+ *                                 (packed plans: the moe_prepare_weights output)
  *   w1_sf    f32    [E, 2I/128, H/128]
- *   w2       uint8  [E, H, I]     e4m3
+ *   w2       uint8  [E, H, I]     e4m3 (packed plans: moe_prepare_weights output)
  *   w2_sf    f32    [E, H/128, I/128]
  *   y        uint16 [T, H]        bf16 output, written in full (a token with
  *                                 no active slot gets zeros)
@@ -141,6 +147,23 @@ int moe_forward_timed(moe_plan_t plan, int32_t num_tokens,
                       const uint8_t* w2, const float* w2_sf,
                       uint16_t* y, void* workspace, size_t workspace_bytes, void* stream,
                       void* const* step_events);
+
+/*
+ * One-time weight re-layout for plans with weight_layout = MOE_WEIGHTS_PACKED
+ * (the pages transform the expert weights once before any forward as well:
+ * "MegaMoE SM90 Implementation Design" §15.1, "07 · MegaMoE" §8).
+ *   w1 [E,2I,H], w2 [E,H,I]: row-major e4m3 input (device, read only)
+ *   w1_packed, w2_packed: device outputs of the same byte sizes; must not
+ *   overlap the inputs.  Scales are not touched and stay row-major.
+ * Packed order: for expert e, column tile n (L1: 128 gate + 128 up rows;
+ * L2: 256 rows), 128-wide K block kb, wave w (0..3), 16-row subtile s (0..3),
+ * half h (bytes [0,64) or [64,128) of the block): 64 lanes x 16 bytes, lane
+ * l = 16*g + r holding bytes [16g, 16g+16) of that half for subtile row r.
+ * One 1 KiB run is exactly one MFMA operand load of one wave.
+ * Returns MOE_ERR_INVALID_ARG if the plan is not a packed plan.
+ */
+int moe_prepare_weights(moe_plan_t plan, const uint8_t* w1, const uint8_t* w2,
+                        uint8_t* w1_packed, uint8_t* w2_packed, void* stream);
 
 /*
  * Routing planner alone (step 1) with an explicit row alignment in [1, 1024]

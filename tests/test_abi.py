@@ -50,6 +50,29 @@ def test_plan_create_rejects(shape, code):
     assert ei.value.code == code
 
 
+def test_packed_layout_validation():
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_plan_create(384, 128, 8, 2, 64, 0, moe.MOE_WEIGHTS_PACKED)  # H % 256
+    assert ei.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_plan_create(256, 128, 8, 2, 64, 0, 7)
+    assert ei.value.code == moe.MOE_ERR_INVALID_ARG
+    L = moe.lib()
+    a, b, c, d = (ctypes.c_void_p(x) for x in (0x10000, 0x20000000, 0x40000000, 0x60000000))
+    row = moe.moe_plan_create(256, 128, 8, 2, 64)
+    pk = moe.moe_plan_create(256, 128, 8, 2, 64, 0, moe.MOE_WEIGHTS_PACKED)
+    try:
+        # a row-major plan has nothing to prepare
+        assert L.moe_prepare_weights(row, a, b, c, d, None) == moe.MOE_ERR_INVALID_ARG
+        # null or overlapping buffers are rejected before any HIP call
+        assert L.moe_prepare_weights(pk, None, b, c, d, None) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_prepare_weights(pk, a, b, ctypes.c_void_p(0x10000 + 4096), d, None) == \
+            moe.MOE_ERR_INVALID_ARG
+    finally:
+        moe.moe_plan_destroy(row)
+        moe.moe_plan_destroy(pk)
+
+
 def test_plan_create_null_shape():
     h = ctypes.c_void_p()
     assert moe.lib().moe_plan_create(None, ctypes.byref(h)) == moe.MOE_ERR_INVALID_ARG

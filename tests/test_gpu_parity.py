@@ -196,6 +196,27 @@ def test_forward_deterministic_and_workspace_reuse():
     check_y(y2.cpu().numpy(), run_oracle(host2)["y"], what="reuse, larger call")
 
 
+@pytest.mark.parametrize("tile_m", [16, 32, 64])
+def test_packed_weights_match_row_major_bitwise(tile_m):
+    # packed weights only change where the kernels read each fragment from:
+    # same arithmetic in the same order, so y is bit-identical
+    host, dev = small_case(203, 512, 384, 16, 4, 17)
+    y_row, _ = run_gpu(dev, tile_m=tile_m)
+    y_pk, runner = run_gpu(dev, tile_m=tile_m, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert torch.equal(y_row, y_pk)
+    check_y(y_pk.cpu().numpy(), run_oracle(host)["y"], what=f"packed tile {tile_m}")
+
+
+def test_packed_weights_full_size_decode_bitwise():
+    cfg = wl.CONFIGS["flash_decode"]
+    inp = gpu_inputs(cfg, wl.default_seed(cfg))
+    y_row, _ = run_gpu(inp)
+    y_pk, _ = run_gpu(inp, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert torch.equal(y_row, y_pk)
+    del inp
+    torch.cuda.empty_cache()
+
+
 def test_forward_zero_tokens_is_noop():
     runner = moe.MoEForward(256, 128, 8, 2, 16)
     y = torch.full((0, 256), 7, dtype=torch.uint16, device="cuda")

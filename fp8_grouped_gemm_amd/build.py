@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_fp8.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["moe_api.cpp", "route.hip", "gemm_direct.hip", "pack.hip"]
+SOURCES = ["moe_api.cpp", "route.hip", "gemm_direct.hip", "gemm_lds.hip", "pack.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 instructions are disabled for every device pass.

@@ -593,13 +593,15 @@ static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
 
 hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s)
 {
-    (void)kernel;
+    if (kernel == 1)
+        return launch_l1_lds(a, s);
     return a.packed ? launch_l1_t<true>(a, s) : launch_l1_t<false>(a, s);
 }
 
 hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s)
 {
-    (void)kernel;
+    if (kernel == 1)
+        return launch_l2_lds(a, s);
     return a.packed ? launch_l2_t<true>(a, s) : launch_l2_t<false>(a, s);
 }
 

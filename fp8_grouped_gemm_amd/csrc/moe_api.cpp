@@ -31,13 +31,21 @@ struct Config {
 // Rows per tile from the expected rows per expert T*K/E: the smallest tile
 // that holds an average expert's rows reads each expert's weights once
 // while padding as few MFMA rows as possible (decode: 16).
+// Beyond ~24 rows per expert the 128 x 256 LDS-staged MFMA tile takes over
+// (it needs H % 256 == 0 for its 256-column L2 tiles; otherwise 64-row
+// direct-load tiles).
 Config choose_config(const moe_shape_t& s, int T)
 {
     if (s.tile_m > 0)
-        return Config{s.tile_m, 0};
+        return Config{s.tile_m, s.tile_m == 128 ? 1 : 0};
     const double rows = (double)T * s.top_k / s.num_experts;
-    int bm = rows <= 12.0 ? 16 : rows <= 24.0 ? 32 : 64;
-    return Config{bm, 0};
+    if (rows <= 12.0)
+        return Config{16, 0};
+    if (rows <= 24.0)
+        return Config{32, 0};
+    if (s.hidden % 256 == 0)
+        return Config{128, 1};
+    return Config{64, 0};
 }
 
 struct Layout {
@@ -132,7 +140,10 @@ int validate_shape(const moe_shape_t* s)
         return MOE_ERR_UNSUPPORTED_SHAPE;
     if (s->hidden > (1 << 16) || s->intermediate > (1 << 16))
         return MOE_ERR_UNSUPPORTED_SHAPE;
-    if (s->tile_m != 0 && s->tile_m != 16 && s->tile_m != 32 && s->tile_m != 64)
+    if (s->tile_m != 0 && s->tile_m != 16 && s->tile_m != 32 && s->tile_m != 64 &&
+        s->tile_m != 128)
+        return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (s->tile_m == 128 && s->hidden % 256)
         return MOE_ERR_UNSUPPORTED_SHAPE;
     if (s->weight_layout != MOE_WEIGHTS_ROW_MAJOR && s->weight_layout != MOE_WEIGHTS_PACKED)
         return MOE_ERR_INVALID_ARG;
@@ -249,7 +260,7 @@ int moe_plan_info(moe_plan_t plan, int32_t T, moe_tile_info_t* info)
     info->tile_m = L.tile_m;
     info->row_align = L.tile_m;
     info->pool_rows = L.r_cap;
-    info->l1_tile_n = 256;
+    info->l1_tile_n = 256;  // 128 gate + 128 up columns
     info->l2_tile_n = 256;
     info->kernel = L.kernel;
     return MOE_OK;

@@ -60,6 +60,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s);
 hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s);
 hipError_t launch_combine(const FwdArgs& a, hipStream_t s);
+hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s);
+hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_pack(const uint8_t* w1, const uint8_t* w2, uint8_t* w1p, uint8_t* w2p, int E,
                        int H, int I, hipStream_t s);
 

@@ -143,7 +143,7 @@ def forward_and_check(host, dev, tile_m, what, check_intermediates=True):
     return runner
 
 
-@pytest.mark.parametrize("tile_m", [16, 32, 64])
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128])
 def test_forward_tiny_all_tiles(tile_m):
     cfg = wl.CONFIGS["tiny"]
     host, dev = small_case(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, wl.default_seed(cfg))
@@ -171,7 +171,7 @@ def test_forward_edge_masks_out_of_range_and_empty_tokens():
 def test_forward_ragged_multi_tile_shapes():
     # several K blocks, several n tiles, T*K not a multiple of the tile or 1024
     host, dev = small_case(203, 512, 384, 16, 4, 12)
-    for tile_m in (16, 32, 64):
+    for tile_m in (16, 32, 64, 128):
         forward_and_check(host, dev, tile_m, f"ragged tile {tile_m}")
 
 
@@ -181,7 +181,7 @@ def test_forward_single_token_and_hot_expert():
     # every token on expert 2: one long segment, many row tiles
     T = 150
     host, dev = small_case(T, 256, 256, 8, 2, 14, mask={(t, 0): 2 for t in range(T)})
-    for tile_m in (16, 64):
+    for tile_m in (16, 64, 128):
         forward_and_check(host, dev, tile_m, f"hot expert tile {tile_m}")
 
 
@@ -196,7 +196,7 @@ def test_forward_deterministic_and_workspace_reuse():
     check_y(y2.cpu().numpy(), run_oracle(host2)["y"], what="reuse, larger call")
 
 
-@pytest.mark.parametrize("tile_m", [16, 32, 64])
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128])
 def test_packed_weights_match_row_major_bitwise(tile_m):
     # packed weights only change where the kernels read each fragment from:
     # same arithmetic in the same order, so y is bit-identical

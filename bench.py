@@ -46,6 +46,24 @@ def algorithmic_bytes(cfg, idx):
     }
 
 
+def measured_traffic(cfg, weights):
+    """HBM bytes per launch of the L1 step from the committed rocprofv3
+    counter summary (FETCH_SIZE / WRITE_SIZE scaled by a plain copy's
+    readings), or None when no summary matches this workload or the kernel
+    sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "flash_decode_l1_traffic.json")
+    if cfg.name != "flash_decode" or weights != "packed" or not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    h = hashlib.sha256()
+    for f in d["source_files"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest()[:16] != d["source_sha256_16"]:
+        return None
+    return d["l1_step_traffic_bytes"]
+
+
 def time_oracle_sample(inp, cfg, n_tokens, seed):
     """CPU oracle on a bounded sample of tokens; returns (us per layer
     extrapolated to T tokens, threads, seconds, sample description)."""
@@ -76,6 +94,9 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=128)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times "
+                         "(the reference kernel for scaling HBM byte counters) and exit")
     ap.add_argument("--weights", choices=("packed", "row_major"), default="packed",
                     help="expert weight layout the plan expects (packed = one-time "
                          "moe_prepare_weights re-layout, done before timing)")
@@ -90,6 +111,16 @@ def main():
 
     import fp8_grouped_gemm_amd as moe
     from fp8_grouped_gemm_amd import workload as wl
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_dispatch": n}), flush=True)
+        return
 
     cfg = wl.CONFIGS[args.workload]
     seed = wl.default_seed(cfg) if args.seed is None else args.seed
@@ -178,13 +209,17 @@ def main():
         "routed_rows": alg["rows"],
         "wall_s_timed": round(wall, 3),
         "roofline": {
-            "kernel": "l1_direct (L1 GEMM + SwiGLU/requant)" if dom == "l1" else "l2_direct (L2 GEMM)",
+            "kernel": ("L1 step: GEMM gate+up, SwiGLU x topk_w, e4m3 requant "
+                       f"({'direct-load tiles' if info['kernel'] == 0 else 'LDS-staged tiles'}, "
+                       f"tile_m {info['tile_m']})") if dom == "l1" else
+                      f"L2 step: GEMM down (tile_m {info['tile_m']})",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg, args.weights) if dom == "l1" else None,
+            "algorithmic_bytes": alg[dom],
         },
         "cpu_baseline": None,
     }

@@ -66,7 +66,7 @@ typedef struct moe_shape {
     int32_t num_experts;   /* E */
     int32_t top_k;         /* K */
     int32_t max_tokens;    /* largest T any call on this plan may pass */
-    int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32 or 64 */
+    int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128 (128: H % 256 == 0) */
     int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
 } moe_shape_t;
 

@@ -93,6 +93,40 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[MT][4], float* pa
         }
 }
 
+// K loop over blocks [kb0, kb1): the fetch of block kb + 1 is issued before
+// block kb is multiplied, into two register sets used in turn (a copy from
+// one set to the other would wait on its loads).  Every fetch inside the
+// steady-state loop is unconditional, so the wait before a multiply leaves
+// exactly the next block's loads outstanding (vector loads retire in
+// order); the last one or two blocks run in a straight-line tail.  (A third
+// set, two blocks ahead, needs over 256 VGPRs and halves the waves per SIMD;
+// it measured slower.)
+template <class B, class F, class M>
+__device__ __forceinline__ void kloop(int kb0, int kb1, F& fetch, M& mul)
+{
+    B b0, b1;
+    int kb = kb0;
+    if (kb >= kb1)
+        return;
+    fetch(b0, kb);
+    for (; kb + 2 < kb1; kb += 2) {
+        fetch(b1, kb + 1);
+        __builtin_amdgcn_sched_barrier(0);  // issue every load before the wait
+        mul(b0);
+        fetch(b0, kb + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mul(b1);
+    }
+    if (kb + 1 < kb1) {
+        fetch(b1, kb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mul(b0);
+        mul(b1);
+    } else {
+        mul(b0);
+    }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------- L1
@@ -115,24 +149,24 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
     const int row0 = mb * BM;
     const int kb0 = ks * HB / S, kb1 = (ks + 1) * HB / S;
 
-    // A operand rows: row0 + 16*ms + lr.
+    // A operand rows: row0 + 16*ms + lr.  Padding rows (row_src < 0) read
+    // token 0 and are masked out of the MFMA.
     const uint8_t* aptr[MT];
     bool avalid[MT];
+    // Output rows of this lane: row0 + 16*ms + 4*lg + i (four consecutive
+    // row_src entries, one 16-byte load).
+    const float* asf[MT][4];
 #pragma unroll
     for (int ms = 0; ms < MT; ++ms) {
         const int f = a.row_src[row0 + 16 * ms + lr];
+        const int4 fo = *reinterpret_cast<const int4*>(a.row_src + row0 + 16 * ms + 4 * lg);
         avalid[ms] = f >= 0;
-        aptr[ms] = a.x + (size_t)(f >= 0 ? f / K : 0) * H + lg * 16;
+        aptr[ms] = a.x + (size_t)(max(f, 0) / K) * H + lg * 16;
+        asf[ms][0] = a.x_sf + (size_t)(max(fo.x, 0) / K) * HB;
+        asf[ms][1] = a.x_sf + (size_t)(max(fo.y, 0) / K) * HB;
+        asf[ms][2] = a.x_sf + (size_t)(max(fo.z, 0) / K) * HB;
+        asf[ms][3] = a.x_sf + (size_t)(max(fo.w, 0) / K) * HB;
     }
-    // Output rows of this lane: row0 + 16*ms + 4*lg + i.
-    const float* asf[MT][4];
-#pragma unroll
-    for (int ms = 0; ms < MT; ++ms)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int f = a.row_src[row0 + 16 * ms + 4 * lg + i];
-            asf[ms][i] = a.x_sf + (size_t)(f >= 0 ? f / K : 0) * HB;
-        }
     // B operand: subtile s = 0,1 gate, 2,3 up.  kstride: bytes between K blocks.
     const uint8_t* bptr[4];
     constexpr size_t kstride = PK ? 32768 : 128;
@@ -156,63 +190,47 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
         for (int s = 0; s < 4; ++s)
             acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Keep the next K block's fragments in flight while multiplying the
-    // current one.
-    constexpr bool PF = true;
-    Frag2 fa[MT], fb[4];
-    if (PF && kb0 < kb1) {
-#pragma unroll
-        for (int ms = 0; ms < MT; ++ms)
-            fa[ms] = avalid[ms] ? load_frag(aptr[ms] + kb0 * 128) : zero_frag();
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            fb[s] = load_wfrag<PK>(bptr[s] + kb0 * kstride);
-    }
-
-    for (int kb = kb0; kb < kb1; ++kb) {
-        Frag2 na[MT], nb[4];
-        const int kn = PF ? (kb + 1 < kb1 ? kb + 1 : kb) : kb;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            nb[s] = load_wfrag<PK>(bptr[s] + kn * kstride);
-#pragma unroll
-        for (int ms = 0; ms < MT; ++ms)
-            na[ms] = avalid[ms] ? load_frag(aptr[ms] + kn * 128) : zero_frag();
-        if (!PF) {
-#pragma unroll
-            for (int ms = 0; ms < MT; ++ms)
-                fa[ms] = na[ms];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                fb[s] = nb[s];
-        }
-        const float sg = sfg[kb], su = sfu[kb];
+    // Everything K block kb needs (fragments and both sides' scales) is
+    // fetched one block ahead, so the wait before a block's MFMAs leaves
+    // the next block's loads in flight (vector loads retire in order).
+    struct Blk {
+        Frag2 fa[MT], fb[4];
         float sa[MT][4];
+        float sg, su;
+    };
+    auto fetch = [&](Blk& b, int kb) {
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                sa[ms][i] = asf[ms][i][kb];
-#pragma unroll
-        for (int ms = 0; ms < MT; ++ms) {
-            const v8i av = pack_frag(fa[ms].lo, fa[ms].hi);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const v4f p = mfma_16x16x128_e4m3(av, pack_frag(fb[s].lo, fb[s].hi),
-                                                  v4f{0.f, 0.f, 0.f, 0.f});
-                const float sb = s >= 2 ? su : sg;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[i], acc[ms][s][i]);
-            }
-        }
+                b.sa[ms][i] = asf[ms][i][kb];
+        b.sg = sfg[kb];
+        b.su = sfu[kb];
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
-            fa[ms] = na[ms];
+            b.fa[ms] = avalid[ms] ? load_frag(aptr[ms] + kb * 128) : zero_frag();
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            fb[s] = nb[s];
-    }
+            b.fb[s] = load_wfrag<PK>(bptr[s] + kb * kstride);
+    };
+    auto mul = [&](const Blk& b) {
+#pragma unroll
+        for (int ms = 0; ms < MT; ++ms) {
+            const v8i av = pack_frag(b.fa[ms].lo, b.fa[ms].hi);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const v4f p = mfma_16x16x128_e4m3(av, pack_frag(b.fb[s].lo, b.fb[s].hi),
+                                                  v4f{0.f, 0.f, 0.f, 0.f});
+                const float sb = s >= 2 ? b.su : b.sg;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[ms][s][i] = fmaf(b.sa[ms][i] * sb, p[i], acc[ms][s][i]);
+            }
+        }
+    };
+    // Two register sets used in turn: no copy between them, so nothing
+    // waits on a load before its block is multiplied.
+    kloop<Blk>(kb0, kb1, fetch, mul);
 
     if constexpr (S > 1) {
         // gate and up columns of this lane's four subtiles in the [R, 2I] partials
@@ -338,60 +356,41 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
         for (int s = 0; s < 4; ++s)
             acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    constexpr bool PF = true;  // as in l1_direct
-    Frag2 fa[MT], fb[4];
-    if (PF && kb0 < kb1) {
-#pragma unroll
-        for (int ms = 0; ms < MT; ++ms)
-            fa[ms] = avalid[ms] ? load_frag(aptr[ms] + kb0 * 128) : zero_frag();
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            fb[s] = load_wfrag<PK>(bptr[s] + kb0 * kstride);
-    }
-
-    for (int kb = kb0; kb < kb1; ++kb) {
-        Frag2 na[MT], nb[4];
-        const int kn = PF ? (kb + 1 < kb1 ? kb + 1 : kb) : kb;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            nb[s] = load_wfrag<PK>(bptr[s] + kn * kstride);
-#pragma unroll
-        for (int ms = 0; ms < MT; ++ms)
-            na[ms] = avalid[ms] ? load_frag(aptr[ms] + kn * 128) : zero_frag();
-        if (!PF) {
-#pragma unroll
-            for (int ms = 0; ms < MT; ++ms)
-                fa[ms] = na[ms];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                fb[s] = nb[s];
-        }
-        const float sb = sfb[kb];
+    // One K block ahead, as in l1_direct.
+    struct Blk {
+        Frag2 fa[MT], fb[4];
         float sa[MT][4];
+        float sb;
+    };
+    auto fetch = [&](Blk& b, int kb) {
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                sa[ms][i] = asf[ms][i][kb];
+                b.sa[ms][i] = asf[ms][i][kb];
+        b.sb = sfb[kb];
+#pragma unroll
+        for (int ms = 0; ms < MT; ++ms)
+            b.fa[ms] = avalid[ms] ? load_frag(aptr[ms] + kb * 128) : zero_frag();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            b.fb[s] = load_wfrag<PK>(bptr[s] + kb * kstride);
+    };
+    auto mul = [&](const Blk& b) {
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms) {
-            const v8i av = pack_frag(fa[ms].lo, fa[ms].hi);
+            const v8i av = pack_frag(b.fa[ms].lo, b.fa[ms].hi);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const v4f p = mfma_16x16x128_e4m3(av, pack_frag(fb[s].lo, fb[s].hi),
+                const v4f p = mfma_16x16x128_e4m3(av, pack_frag(b.fb[s].lo, b.fb[s].hi),
                                                   v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[i], acc[ms][s][i]);
+                    acc[ms][s][i] = fmaf(b.sa[ms][i] * b.sb, p[i], acc[ms][s][i]);
             }
         }
-#pragma unroll
-        for (int ms = 0; ms < MT; ++ms)
-            fa[ms] = na[ms];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            fb[s] = nb[s];
-    }
+    };
+    kloop<Blk>(kb0, kb1, fetch, mul);
 
     if constexpr (S > 1) {
         if (nt * 256 + wave * 64 >= H)

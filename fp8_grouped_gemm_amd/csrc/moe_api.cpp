@@ -307,6 +307,12 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     if (!x || !x_sf || !topk_idx || !topk_w || !w1 || !w1_sf || !w2 || !w2_sf || !y ||
         !workspace)
         return MOE_ERR_INVALID_ARG;
+    // The kernels move 16-byte vectors of x, the weights, y and the
+    // workspace sections (which sit at 256-byte offsets).
+    auto misaligned = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) != 0; };
+    if (misaligned(workspace, 256) || misaligned(x, 16) || misaligned(w1, 16) ||
+        misaligned(w2, 16) || misaligned(y, 16))
+        return MOE_ERR_INVALID_ARG;
     const Layout L = make_layout(s, T);
     if (workspace_bytes < L.total)
         return MOE_ERR_WORKSPACE_TOO_SMALL;

@@ -126,6 +126,8 @@ int moe_workspace_layout(moe_plan_t plan, int32_t num_tokens, moe_ws_layout_t* l
  *   y        uint16 [T, H]        bf16 output, written in full (a token with
  *                                 no active slot gets zeros)
  *   workspace / workspace_bytes   at least moe_workspace_bytes(plan, T)
+ * x, w1, w2 and y must be 16-byte aligned and workspace 256-byte aligned
+ * (MOE_ERR_INVALID_ARG otherwise; torch allocations are).
  * T == 0 is a no-op returning MOE_OK.
  */
 int moe_forward(moe_plan_t plan, int32_t num_tokens,

@@ -140,6 +140,11 @@ def test_forward_host_validation_without_gpu():
         for name in ("x", "x_sf", "topk_idx", "topk_w", "w1", "w1_sf", "w2", "w2_sf", "y",
                      "workspace"):
             assert _forward_rc(p, 8, **{name: None}) == moe.MOE_ERR_INVALID_ARG, name
+        # alignment: 16 bytes for x, w1, w2, y; 256 for the workspace
+        for name in ("x", "w1", "w2", "y"):
+            assert _forward_rc(p, 8, **{name: FakeTensor(addr=0x1008)}) == \
+                moe.MOE_ERR_INVALID_ARG, name
+        assert _forward_rc(p, 8, workspace=FakeTensor(addr=0x1080)) == moe.MOE_ERR_INVALID_ARG
         small = FakeTensor(nbytes=moe.moe_workspace_bytes(p, 8) - 1)
         assert _forward_rc(p, 8, workspace=small) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
         rc = moe.lib().moe_forward(None, 8, *([ctypes.c_void_p(0x1000)] * 10), 1 << 30, None)

@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="flash_decode")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="override the workload's token count (same shapes and routing recipe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=128)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -124,6 +126,9 @@ def main():
 
     cfg = wl.CONFIGS[args.workload]
     seed = wl.default_seed(cfg) if args.seed is None else args.seed
+    if args.tokens is not None:
+        cfg = wl.custom_config(args.tokens, cfg.H, cfg.I, cfg.E, cfg.K, cfg.skew,
+                               name=f"{cfg.name}_T{args.tokens}")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] drawing {cfg} seed {seed} on the GPU", file=sys.stderr, flush=True)

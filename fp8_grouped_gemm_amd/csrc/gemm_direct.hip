@@ -72,9 +72,10 @@ __device__ __forceinline__ Frag2 zero_frag()
 }
 
 // Split-K partial store: each of the S K-slices of a tile writes its f32
-// sums, row-major, to part[slice][row][col] for the rows that hold a routed
-// slot; a later kernel adds the slices in slice order.  Lane (lg, lr) holds
-// rows 4*lg + i of column lr of each 16-column subtile.
+// sums to part[slice][slot][col] for the rows that hold a routed slot
+// (slot = row_src of the row); a later kernel adds the slices in slice
+// order.  Lane (lg, lr) holds rows 4*lg + i of column lr of each 16-column
+// subtile.
 template <int MT>
 __device__ __forceinline__ void store_partial(const v4f (&acc)[MT][4], float* part, size_t ld,
                                               const int32_t* row_src, int row0, const int (&col)[4],
@@ -84,12 +85,12 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[MT][4], float* pa
     for (int ms = 0; ms < MT; ++ms)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = row0 + 16 * ms + 4 * lg + i;
-            if (row_src[r] < 0)
+            const int f = row_src[row0 + 16 * ms + 4 * lg + i];
+            if (f < 0)
                 continue;
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                part[(size_t)r * ld + col[s]] = acc[ms][s][i];
+                part[(size_t)f * ld + col[s]] = acc[ms][s][i];
         }
 }
 
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
         // gate and up columns of this lane's four subtiles in the [R, 2I] partials
         const int col[4] = {nt * 128 + wave * 32 + lr, nt * 128 + wave * 32 + 16 + lr,
                             I + nt * 128 + wave * 32 + lr, I + nt * 128 + wave * 32 + 16 + lr};
-        store_partial<MT>(acc, a.splitk_part + (size_t)ks * a.splitk_rows * 2 * I, 2 * (size_t)I,
+        store_partial<MT>(acc, a.splitk_part + (size_t)ks * a.splitk_slots * 2 * I, 2 * (size_t)I,
                           a.row_src, row0, col, lg);
         return;  // l1_splitk_epilogue finishes the tile
     }
@@ -302,14 +303,13 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
 
 // ------------------------------------------------------------------- L2
 
-template <int MT, int S, bool PK>
+template <int MT, bool PK>
 __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
 {
     constexpr int BM = 16 * MT;
     const int H = a.H, I = a.I, IB = I / 128, K = a.K, T = a.T;
     const int NT = (H + 255) / 256;  // H % 256 == 128: the last tile has 2 idle waves
-    const int tile = blockIdx.x / S;
-    const int ks = blockIdx.x - tile * S;
+    const int tile = blockIdx.x;
     const int mb = tile / NT;
     const int nt = tile - mb * NT;
     const int e = a.mblock_expert[mb];
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int row0 = mb * BM;
-    const int kb0 = ks * IB / S, kb1 = (ks + 1) * IB / S;
+    const int kb0 = 0, kb1 = IB;
 
     const uint8_t* aptr[MT];
     bool avalid[MT];
@@ -392,15 +392,6 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
     };
     kloop<Blk>(kb0, kb1, fetch, mul);
 
-    if constexpr (S > 1) {
-        if (nt * 256 + wave * 64 >= H)
-            return;  // idle wave of a half tile
-        const int col[4] = {ncol0 + lr, ncol0 + 16 + lr, ncol0 + 32 + lr, ncol0 + 48 + lr};
-        store_partial<MT>(acc, a.splitk_part + (size_t)ks * a.splitk_rows * H, (size_t)H,
-                          a.row_src, row0, col, lg);
-        return;  // the combine adds the slices
-    }
-
     // ---- epilogue: bf16, stage BM x 256 in LDS, 16-byte stores to the
     // (slot, token) row of the partial buffer.
     __shared__ uint16_t ot[BM][256 + 8];
@@ -452,7 +443,7 @@ __global__ __launch_bounds__(256) void l1_splitk_epilogue(FwdArgs a)
         g[q] = u[q] = 0.f;
     if (f >= 0) {
         for (int k = 0; k < S; ++k) {
-            const float* row = a.splitk_part + ((size_t)k * a.splitk_rows + r) * 2 * I;
+            const float* row = a.splitk_part + ((size_t)k * a.splitk_slots + f) * 2 * I;
             const float4 g0 = *reinterpret_cast<const float4*>(row + c0);
             const float4 g1 = *reinterpret_cast<const float4*>(row + c0 + 4);
             const float4 u0 = *reinterpret_cast<const float4*>(row + I + c0);
@@ -506,29 +497,7 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdArgs a)
         const int e = a.idx[t * a.K + j];
         if (e < 0 || e >= a.E)
             continue;
-        uint16_t* prow = a.partial + ((size_t)j * a.T + t) * a.H + c;
-        if (a.split_l2 > 1) {
-            // L2 ran split-K: this slot's bf16 partial is the slice sum, added
-            // in slice order, rounded once; keep it in the partial buffer too.
-            const int r = a.src_row[t * a.K + j];
-            float p[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                p[q] = 0.f;
-            for (int k = 0; k < a.split_l2; ++k) {
-                const float* src = a.splitk_part + ((size_t)k * a.splitk_rows + r) * a.H + c;
-                const float4 v0 = *reinterpret_cast<const float4*>(src);
-                const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-                p[0] += v0.x; p[1] += v0.y; p[2] += v0.z; p[3] += v0.w;
-                p[4] += v1.x; p[5] += v1.y; p[6] += v1.z; p[7] += v1.w;
-            }
-            uint4 o;
-            o.x = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
-            o.y = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
-            o.z = (uint32_t)f32_to_bf16(p[4]) | ((uint32_t)f32_to_bf16(p[5]) << 16);
-            o.w = (uint32_t)f32_to_bf16(p[6]) | ((uint32_t)f32_to_bf16(p[7]) << 16);
-            *reinterpret_cast<uint4*>(prow) = o;
-        }
+        const uint16_t* prow = a.partial + ((size_t)j * a.T + t) * a.H + c;
         const uint4 v = *reinterpret_cast<const uint4*>(prow);
         s[0] += bf16_to_f32(v.x & 0xFFFFu);
         s[1] += bf16_to_f32(v.x >> 16);
@@ -554,9 +523,11 @@ static hipError_t launch_l1_t(const FwdArgs& a, hipStream_t s)
     switch (a.BM) {
     case 16:
         if (a.split_l1 > 1) {
-            if (a.split_l1 != 4)
-                return hipErrorInvalidValue;
-            hipLaunchKernelGGL((l1_direct<1, 4, PK>), dim3(tiles * 4), dim3(256), 0, s, a);
+            switch (a.split_l1) {
+            case 2: hipLaunchKernelGGL((l1_direct<1, 2, PK>), dim3(tiles * 2), dim3(256), 0, s, a); break;
+            case 4: hipLaunchKernelGGL((l1_direct<1, 4, PK>), dim3(tiles * 4), dim3(256), 0, s, a); break;
+            default: return hipErrorInvalidValue;
+            }
             hipLaunchKernelGGL(l1_splitk_epilogue, dim3(tiles), dim3(256), 0, s, a);
         } else {
             hipLaunchKernelGGL((l1_direct<1, 1, PK>), dim3(tiles), dim3(256), 0, s, a);
@@ -575,16 +546,10 @@ static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
     const unsigned tiles = a.num_mblocks * ((a.H + 255) / 256);
     switch (a.BM) {
     case 16:
-        if (a.split_l2 > 1) {
-            if (a.split_l2 != 2)
-                return hipErrorInvalidValue;
-            hipLaunchKernelGGL((l2_direct<1, 2, PK>), dim3(tiles * 2), dim3(256), 0, s, a);
-        } else {
-            hipLaunchKernelGGL((l2_direct<1, 1, PK>), dim3(tiles), dim3(256), 0, s, a);
-        }
+        hipLaunchKernelGGL((l2_direct<1, PK>), dim3(tiles), dim3(256), 0, s, a);
         break;
-    case 32: hipLaunchKernelGGL((l2_direct<2, 1, PK>), dim3(tiles), dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((l2_direct<4, 1, PK>), dim3(tiles), dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((l2_direct<2, PK>), dim3(tiles), dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((l2_direct<4, PK>), dim3(tiles), dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

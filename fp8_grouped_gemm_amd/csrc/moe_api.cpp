@@ -50,15 +50,40 @@ Config choose_config(const moe_shape_t& s, int T)
 
 struct Layout {
     int tile_m, kernel, r_cap, mb_cap, NB;
-    int split_l1, split_l2, part_rows;
+    int split_l1;
     size_t status, counts, offsets, blk, mbe, row_src, src_row, h_sf, h, partial;
     size_t part, total;
 };
 
-// Split-K across workgroups for the 16-row decode tiles: a tile's weight
-// block is streamed by S workgroups of ~256 KiB each instead of one of ~1
-// MiB, which the HBM stream sustains markedly better on MI355X.
-constexpr int kSplitL1 = 4, kSplitL2 = 2;
+// Split-K across workgroups for the 16-row L1 tiles.  One workgroup per
+// (row block, column tile) streams that tile's whole weight block (~1 MiB at
+// H = 4096), which sustains the HBM stream best (measured at 1 to 256 tokens
+// of the flash-decode shape) as long as there are at least as many tiles as
+// compute units.  With fewer (a single token: 6 row blocks x 16 tiles) each
+// tile's K range is split over S workgroups, S the smallest power of two
+// (<= 4, <= the K blocks) that reaches kMinItems.  L2 is never split: its
+// slices would have to be added by the combine, which costs more than the
+// split saves (measured).
+constexpr long long kMinItems = 256;  // MI355X compute units
+
+long long mblocks_expected(const moe_shape_t& s, long long T)
+{
+    const long long tk = T * s.top_k;
+    return std::max<long long>((tk + 15) / 16, std::min<long long>(tk, s.num_experts));
+}
+
+// L1 split factor of a call with T tokens and tile configuration c.
+int choose_split(const moe_shape_t& s, int T, const Config& c)
+{
+    if (c.tile_m != 16 || T <= 0)
+        return 1;
+    const long long items = mblocks_expected(s, T) * (s.intermediate / 128);
+    const int kblocks = s.hidden / 128;
+    int S = 1;
+    while (S < 4 && 2 * S <= kblocks && items * S < kMinItems)
+        S *= 2;
+    return S;
+}
 
 // Pool capacity (rows) for T tokens with row alignment ra.
 long long pool_rows(const moe_shape_t& s, long long T, int ra)
@@ -66,6 +91,39 @@ long long pool_rows(const moe_shape_t& s, long long T, int ra)
     long long r = T * s.top_k + (long long)s.num_experts * (ra - 1);
     r = (r + ra - 1) / ra * ra;
     return std::max<long long>(r, ra);
+}
+
+// Floats of split-K scratch a call with T tokens needs, maximised over all
+// token counts <= T so the workspace size never shrinks as T grows (a
+// workspace sized for max_tokens serves every smaller call).  S(t) is a
+// nonincreasing step function of t with values 4, 2, 1, so the maximum of
+// S(t) * t sits at T or at the last t of one of the steps, found by
+// bisection.
+size_t splitk_floats(const moe_shape_t& s, int T)
+{
+    const size_t width = 2 * (size_t)s.intermediate * (size_t)s.top_k;
+    auto S = [&](int t) { return choose_split(s, t, choose_config(s, t)); };
+    auto need = [&](int t) -> size_t {
+        const int v = S(t);
+        return v > 1 ? (size_t)v * (size_t)t * width : 0;
+    };
+    size_t best = need(T);
+    for (int v = 2; v <= 4; v *= 2) {
+        // last t in [1, T] with S(t) >= v (S is nonincreasing in t while the
+        // tiles are 16 rows; once they are not, S is 1)
+        if (T < 1 || S(1) < v)
+            continue;
+        int lo = 1, hi = T;
+        while (lo < hi) {
+            const int mid = lo + (hi - lo + 1) / 2;
+            if (S(mid) >= v)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        best = std::max(best, need(lo));
+    }
+    return best;
 }
 
 Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
@@ -96,29 +154,10 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     L.h_sf = take(sizeof(float) * (size_t)L.r_cap * (I / 128));
     L.h = take((size_t)L.r_cap * I);
     L.partial = take(sizeof(uint16_t) * (size_t)K * T * H);
-    // Split-K scratch.  Sized for the largest token count <= T that runs the
-    // 16-row tiles, so the total stays nondecreasing in T.
-    const int NT1 = I / 128, NT2 = (H + 255) / 256;
-    long long t16 = 0;
-    if (s.tile_m == 16)
-        t16 = T;
-    else if (s.tile_m == 0)
-        t16 = std::min<long long>(T, (long long)(12.0 * E / K));
-    while (t16 > 0 && choose_config(s, (int)t16).tile_m != 16)
-        --t16;
-    const int mb16 = t16 > 0 ? (int)(pool_rows(s, t16, 16) / 16) : 0;
-    (void)NT1;
-    (void)NT2;
-    const int s1 = H / 128 >= kSplitL1 ? kSplitL1 : 1;
-    const int s2 = I / 128 >= kSplitL2 ? kSplitL2 : 1;
-    L.split_l1 = c.tile_m == 16 ? s1 : 1;
-    L.split_l2 = c.tile_m == 16 ? s2 : 1;
-    // f32 partials part[slice][row][col]: L1 uses [s1][R][2I], L2 [s2][R][H]
-    // (one after the other, so they share the region).
-    L.part_rows = mb16 * 16;
-    const size_t n1 = s1 > 1 ? (size_t)s1 * L.part_rows * 2 * I : 0;
-    const size_t n2 = s2 > 1 ? (size_t)s2 * L.part_rows * H : 0;
-    L.part = take(sizeof(float) * std::max(n1, n2));
+    // Split-K scratch: L1's f32 partials part[slice][slot][2I], slot
+    // f = t*K + j.
+    L.split_l1 = choose_split(s, T, c);
+    L.part = take(sizeof(float) * splitk_floats(s, T));
     L.total = o;
     return L;
 }
@@ -263,6 +302,7 @@ int moe_plan_info(moe_plan_t plan, int32_t T, moe_tile_info_t* info)
     info->l1_tile_n = 256;  // 128 gate + 128 up columns
     info->l2_tile_n = 256;
     info->kernel = L.kernel;
+    info->l1_split = L.split_l1;
     return MOE_OK;
 }
 
@@ -361,8 +401,7 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     a.y = y;
     a.src_row = at<int32_t>(workspace, L.src_row);
     a.split_l1 = L.split_l1;
-    a.split_l2 = L.split_l2;
-    a.splitk_rows = L.part_rows;
+    a.splitk_slots = T * s.top_k;
     a.splitk_part = at<float>(workspace, L.part);
     if (moe::launch_l1(a, L.kernel, st) != hipSuccess || !mark(2))
         return MOE_ERR_HIP;

@@ -45,11 +45,11 @@ struct FwdArgs {
     uint16_t* partial;
     uint16_t* y;
     const int32_t* src_row;
-    // Split-K across workgroups (tile_m 16): K slices per L1 / L2 tile (1 =
-    // off) and their f32 partial sums, part[slice][row][col] with
-    // splitk_rows rows per slice.
-    int32_t split_l1, split_l2;
-    int32_t splitk_rows;
+    // Split-K across workgroups (16-row L1 tiles): K slices per tile (1 =
+    // off) and their f32 partial sums, part[slice][slot][2I] for the
+    // splitk_slots = T*K routed slots (slot f = t*K + j).
+    int32_t split_l1;
+    int32_t splitk_slots;
     float* splitk_part;
 };
 

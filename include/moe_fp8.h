@@ -80,6 +80,8 @@ typedef struct moe_tile_info {
     int32_t l1_tile_n;   /* L1 output columns per tile (gate + up) */
     int32_t l2_tile_n;   /* L2 output columns per tile */
     int32_t kernel;      /* 0 = direct-load tile kernel, 1 = LDS-staged tile kernel */
+    int32_t l1_split;    /* workgroups sharing one L1 tile's K range (1 = no split;
+                            16-row tiles with fewer tiles than compute units) */
 } moe_tile_info_t;
 
 /* Byte offsets of the workspace sections used by a forward with T tokens.

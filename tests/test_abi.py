@@ -101,6 +101,35 @@ def test_plan_info_tile_choice_and_workspace_monotone():
         moe.moe_plan_destroy(p)
 
 
+@pytest.mark.parametrize("shape", [(4096, 2048, 256, 6, 0), (256, 128, 8, 2, 16),
+                                   (512, 384, 16, 4, 16), (7168, 3072, 384, 6, 0)])
+def test_split_k_choice_and_workspace_monotone_every_T(shape):
+    # L1 split-K only where the 16-row tiles number fewer than the compute
+    # units (256): S in {1, 2, 4}, nonincreasing in T, at most the K blocks;
+    # the workspace never shrinks as T grows, for every T.
+    H, I, E, K, tile = shape
+    p = moe.moe_plan_create(H, I, E, K, 300, tile_m=tile)
+    try:
+        last_b, last_s = 0, 4
+        for T in range(0, 301):
+            info = moe.moe_plan_info(p, T)
+            S = info["l1_split"]
+            assert S in (1, 2, 4) and S <= max(1, H // 128) and S <= last_s, (T, S)
+            if info["tile_m"] != 16 or T == 0:
+                assert S == 1
+            else:
+                rows = max((T * K + 15) // 16, min(T * K, E))
+                tiles = rows * (I // 128)
+                assert (S == 1) == (tiles >= 256) or S == min(4, H // 128), (T, S, tiles)
+            b = moe.moe_workspace_bytes(p, T)
+            assert b >= last_b, T
+            last_b = b
+            if T > 0:
+                last_s = S
+    finally:
+        moe.moe_plan_destroy(p)
+
+
 class FakeTensor:
     """Stand-in carrying an address; these calls fail before touching it."""
 

@@ -217,6 +217,34 @@ def test_packed_weights_full_size_decode_bitwise():
     torch.cuda.empty_cache()
 
 
+def test_forward_small_token_counts_split_k():
+    # Flash-decode shapes with one or two tokens: fewer (row block, column
+    # tile) pairs than compute units, so each L1 tile's K range is split over
+    # 4 or 2 workgroups (f32 partials per routed slot, added in slice order
+    # by the epilogue kernel); from three tokens on there is no split.  Every
+    # token is checked against the oracle; packed and row-major weights must
+    # agree bit for bit.
+    base = wl.CONFIGS["flash_decode"]
+    full = gpu_inputs(wl.custom_config(8, base.H, base.I, base.E, base.K), wl.default_seed(base))
+    for T, split in {1: 4, 2: 2, 3: 1, 8: 1}.items():
+        inp = dict(full)
+        for k in ("x", "x_sf", "topk_idx", "topk_w"):
+            inp[k] = full[k][:T].contiguous()
+        y_row, runner = run_gpu(inp)
+        info = moe.moe_plan_info(runner.plan, T)
+        say(f"  T={T}: tile {info['tile_m']}, L1 split {info['l1_split']}")
+        assert info["tile_m"] == 16 and info["l1_split"] == split
+        y_pk, _ = run_gpu(inp, weight_layout=moe.MOE_WEIGHTS_PACKED)
+        assert torch.equal(y_row, y_pk), T
+        toks = list(range(T))
+        host = host_copy_for_oracle(inp, toks)
+        ref = run_oracle(host, tokens=toks)
+        check_y(y_pk.cpu().numpy(), ref["y"], per_token_tol=1e-2, what=f"T={T} L1 split {split}")
+        del runner
+    del full, inp
+    torch.cuda.empty_cache()
+
+
 def test_forward_zero_tokens_is_noop():
     runner = moe.MoEForward(256, 128, 8, 2, 16)
     y = torch.full((0, 256), 7, dtype=torch.uint16, device="cuda")

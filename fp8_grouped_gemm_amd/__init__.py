@@ -18,8 +18,12 @@ MOE_ERR_WORKSPACE_TOO_SMALL = -3
 MOE_ERR_HIP = -4
 MOE_ERR_NOT_GFX950 = -5
 MOE_STATUS_EXPERT_OUT_OF_RANGE = 1
+MOE_STATUS_WAIT_TIMEOUT = 2
 MOE_WEIGHTS_ROW_MAJOR = 0
 MOE_WEIGHTS_PACKED = 1
+MOE_FLAG_SINGLE_LAUNCH = 1
+MOE_FLAG_SPLIT_LAUNCH = 2
+MOE_FLAG_TEST_NO_WAIT = 256
 
 EXPORTED_SYMBOLS = (
     "moe_plan_create", "moe_plan_destroy", "moe_plan_info", "moe_workspace_bytes",
@@ -39,14 +43,14 @@ class moe_shape_t(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class moe_tile_info_t(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int32), ("row_align", ctypes.c_int32),
                 ("pool_rows", ctypes.c_int32), ("l1_tile_n", ctypes.c_int32),
                 ("l2_tile_n", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("l1_split", ctypes.c_int32)]
+                ("l1_split", ctypes.c_int32), ("single_launch", ctypes.c_int32)]
 
 
 class moe_ws_layout_t(ctypes.Structure):
@@ -120,9 +124,9 @@ def _stream(stream):
 # --- the C ABI, one Python function per entry point -----------------------
 
 def moe_plan_create(hidden, intermediate, num_experts, top_k, max_tokens, tile_m=0,
-                    weight_layout=MOE_WEIGHTS_ROW_MAJOR):
+                    weight_layout=MOE_WEIGHTS_ROW_MAJOR, flags=0):
     shape = moe_shape_t(hidden, intermediate, num_experts, top_k, max_tokens, tile_m,
-                        weight_layout)
+                        weight_layout, flags)
     h = ctypes.c_void_p()
     _check(lib().moe_plan_create(ctypes.byref(shape), ctypes.byref(h)), "moe_plan_create")
     return h
@@ -214,12 +218,12 @@ class MoEForward:
     """Plan + workspace holder.  forward() writes y for T tokens."""
 
     def __init__(self, hidden, intermediate, num_experts, top_k, max_tokens, tile_m=0,
-                 device="cuda", weight_layout=MOE_WEIGHTS_ROW_MAJOR):
+                 device="cuda", weight_layout=MOE_WEIGHTS_ROW_MAJOR, flags=0):
         import torch
         self.shape = (hidden, intermediate, num_experts, top_k, max_tokens, tile_m)
         self.weight_layout = weight_layout
         self.plan = moe_plan_create(hidden, intermediate, num_experts, top_k, max_tokens,
-                                    tile_m, weight_layout)
+                                    tile_m, weight_layout, flags)
         self.ws_bytes = moe_workspace_bytes(self.plan, max_tokens)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
 

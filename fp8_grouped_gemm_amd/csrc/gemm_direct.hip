@@ -94,6 +94,74 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[MT][4], float* pa
         }
 }
 
+// ---- single-launch hand-off between tiles
+//
+// In the single-launch forward, L2 tiles read the h rows that L1 tiles of
+// the same row block wrote moments earlier, possibly on another XCD (each
+// XCD has its own L2 cache), and the combine reads L2's partials.  A
+// device-scope release fence would write back the producer XCD's whole L2
+// per tile (measured: ruinous), so producers write the hand-off data with
+// agent-scope relaxed atomic stores (sc1: written through to memory) and
+// count a tile as done only after those stores have completed (vmcnt(0))
+// and the workgroup has synchronised.  Consumers touch no hand-off data
+// before the count they wait for is reached.  A cache line of h or of the
+// partials has exactly one producer tile and is read by nobody earlier in
+// the launch (caches start clean of it at kernel start), so ordinary loads
+// see it; a line of h_sf holds scales from several producer tiles, so a
+// copy cached on the reader's XCD could be partly stale, and h_sf is read
+// with agent-scope loads (sc1).
+
+__device__ __forceinline__ void st_co64(void* p, uint64_t v)
+{
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_co32f(const float* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_co32f(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_co128(void* p, uint4 v)
+{
+    st_co64(p, (uint64_t)v.x | ((uint64_t)v.y << 32));
+    st_co64(reinterpret_cast<uint8_t*>(p) + 8, (uint64_t)v.z | ((uint64_t)v.w << 32));
+}
+// Counts one finished tile: every thread's hand-off stores have completed
+// before the workgroup barrier, then one lane bumps the counter.
+__device__ __forceinline__ void count_done(int32_t* ctr)
+{
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this lane's stores are done
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until *ctr >= target.  `hint` is a value of *ctr read earlier (the
+// counts only grow): when it already reaches the target the workgroup goes
+// on at once.  The wait is bounded: past spin_limit polls it gives up, flags
+// MOE_STATUS_WAIT_TIMEOUT in the status word and lets the workgroup go on
+// (the output is then invalid, but every wave exits).
+__device__ __forceinline__ void wait_count(const int32_t* ctr, int target, const FwdArgs& a,
+                                           int hint)
+{
+    if (hint >= target && a.spin_limit >= 0)
+        return;
+    if (threadIdx.x == 0) {
+        int spins = 0;
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (++spins > a.spin_limit) {
+                __hip_atomic_fetch_or(a.status, kStatusWaitTimeout, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+    }
+    __syncthreads();
+}
+
 // K loop over blocks [kb0, kb1): the fetch of block kb + 1 is issued before
 // block kb is multiplied, into two register sets used in turn (a copy from
 // one set to the other would wait on its loads).  Every fetch inside the
@@ -132,13 +200,17 @@ __device__ __forceinline__ void kloop(int kb0, int kb1, F& fetch, M& mul)
 
 // ------------------------------------------------------------------- L1
 
-template <int MT, int S, bool PK>
-__global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
+// L1 tile `item` (with S > 1: K slice item % S of tile item / S).  CO: the
+// single-launch form (h and h_sf handed to L2 through coherent stores and
+// the row block's ready count).
+template <int MT, int S, bool PK, bool CO>
+__device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
 {
+    static_assert(!CO || S == 1, "the single-launch form does not split K");
     constexpr int BM = 16 * MT;
     const int NT = a.I / 128;
-    const int tile = blockIdx.x / S;  // S consecutive workgroups share a tile
-    const int ks = blockIdx.x - tile * S;
+    const int tile = item / S;  // S consecutive items share a tile
+    const int ks = item - tile * S;
     const int mb = tile / NT;
     const int nt = tile - mb * NT;
     const int e = a.mblock_expert[mb];
@@ -286,8 +358,13 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     qt[r][wave * 32 + s * 16 + lr] = (uint8_t)f32_to_e4m3(hv[ms][s][i] / sf);
-                if (wave == 0 && lr == 0)
-                    a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
+                if (wave == 0 && lr == 0) {
+                    float* dst = a.h_sf + (size_t)(row0 + r) * (I / 128) + nt;
+                    if constexpr (CO)
+                        st_co32f(dst, sf);
+                    else
+                        *dst = sf;
+                }
             }
         }
     }
@@ -295,26 +372,43 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
     // BM rows x 128 bytes, 16 bytes per thread.
     for (int c = threadIdx.x; c < BM * 8; c += 256) {
         const int r = c >> 3, col = (c & 7) * 16;
-        if (a.row_src[row0 + r] >= 0)
-            *reinterpret_cast<uint4*>(a.h + (size_t)(row0 + r) * I + nt * 128 + col) =
-                *reinterpret_cast<const uint4*>(&qt[r][col]);
+        if (a.row_src[row0 + r] >= 0) {
+            uint8_t* dst = a.h + (size_t)(row0 + r) * I + nt * 128 + col;
+            const uint4 v = *reinterpret_cast<const uint4*>(&qt[r][col]);
+            if constexpr (CO)
+                st_co128(dst, v);
+            else
+                *reinterpret_cast<uint4*>(dst) = v;
+        }
     }
+    if constexpr (CO)
+        count_done(a.sync + kSyncReady + mb);
+}
+
+template <int MT, int S, bool PK>
+__global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
+{
+    l1_tile<MT, S, PK, false>(a, blockIdx.x);
 }
 
 // ------------------------------------------------------------------- L2
 
-template <int MT, bool PK>
-__global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
+// L2 tile `tile`.  CO: the single-launch form (waits for the row block's
+// L1 tiles, reads h coherently, hands the partials to the combine through
+// coherent stores and the L2 done count).
+template <int MT, bool PK, bool CO>
+__device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hint)
 {
     constexpr int BM = 16 * MT;
     const int H = a.H, I = a.I, IB = I / 128, K = a.K, T = a.T;
     const int NT = (H + 255) / 256;  // H % 256 == 128: the last tile has 2 idle waves
-    const int tile = blockIdx.x;
     const int mb = tile / NT;
     const int nt = tile - mb * NT;
     const int e = a.mblock_expert[mb];
     if (e < 0)
         return;
+    if constexpr (CO)
+        wait_count(a.sync + kSyncReady + mb, a.I / 128, a, hint);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int row0 = mb * BM;
@@ -366,8 +460,12 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                b.sa[ms][i] = asf[ms][i][kb];
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (CO)
+                    b.sa[ms][i] = ld_co32f(asf[ms][i] + kb);
+                else
+                    b.sa[ms][i] = asf[ms][i][kb];
+            }
         b.sb = sfb[kb];
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
@@ -415,9 +513,27 @@ __global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
             v.y = (uint32_t)ot[r][col + 2] | ((uint32_t)ot[r][col + 3] << 16);
             v.z = (uint32_t)ot[r][col + 4] | ((uint32_t)ot[r][col + 5] << 16);
             v.w = (uint32_t)ot[r][col + 6] | ((uint32_t)ot[r][col + 7] << 16);
-            *reinterpret_cast<uint4*>(a.partial + ((size_t)j * T + t) * H + nt * 256 + col) = v;
+            uint16_t* dst = a.partial + ((size_t)j * T + t) * H + nt * 256 + col;
+            if constexpr (CO)
+                st_co128(dst, v);
+            else
+                *reinterpret_cast<uint4*>(dst) = v;
         }
     }
+}
+
+template <int MT, bool PK, bool CO>
+__device__ __forceinline__ void l2_tile(const FwdArgs& a, int tile, int hint = 0)
+{
+    l2_tile_body<MT, PK, CO>(a, tile, hint);
+    if constexpr (CO)
+        count_done(a.sync + kSyncL2Done);  // every L2 item counts, idle ones too
+}
+
+template <int MT, bool PK>
+__global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
+{
+    l2_tile<MT, PK, false>(a, blockIdx.x);
 }
 
 // ------------------------------------------------- L1 split-K epilogue
@@ -481,10 +597,16 @@ __global__ __launch_bounds__(256) void l1_splitk_epilogue(FwdArgs a)
 
 // y[t, n] = bf16( sum over active slots j ascending of f32(partial[j][t][n]) )
 // ("MegaMoE SM90 Implementation Design" §11.2).  8 columns per thread.
-__global__ __launch_bounds__(256) void combine_kernel(FwdArgs a)
+// Combine chunk `blk` (256 threads x 8 columns).  CO: the single-launch
+// form (waits until all n_l2 L2 items are counted, reads the partials
+// coherently).
+template <bool CO>
+__device__ __forceinline__ void combine_chunk(const FwdArgs& a, int blk, int n_l2, int hint = 0)
 {
+    if constexpr (CO)
+        wait_count(a.sync + kSyncL2Done, n_l2, a, hint);
     const int H8 = a.H / 8;
-    const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long g = (long long)blk * 256 + threadIdx.x;
     if (g >= (long long)a.T * H8)
         return;
     const int t = (int)(g / H8);
@@ -514,6 +636,76 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdArgs a)
     o.z = (uint32_t)f32_to_bf16(s[4]) | ((uint32_t)f32_to_bf16(s[5]) << 16);
     o.w = (uint32_t)f32_to_bf16(s[6]) | ((uint32_t)f32_to_bf16(s[7]) << 16);
     *reinterpret_cast<uint4*>(a.y + (size_t)t * a.H + c) = o;
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(FwdArgs a)
+{
+    combine_chunk<false>(a, blockIdx.x, 0);
+}
+
+// ------------------------------------------------- single launch (a6)
+
+// L1 tiles, L2 tiles and combine chunks of one forward in one launch
+// ("07 · MegaMoE" §5-6: L2 tiles of a row block start once all of its L1
+// tiles are in).  Items are numbered L1 tiles first, then L2 tiles, then
+// combine chunks, and workgroups claim them in that order from a counter
+// (two claims ahead, so the claim's latency hides behind the current item).
+// An item only ever waits for items with smaller numbers, which were
+// claimed earlier by running workgroups; a workgroup that holds an
+// unstarted claim is busy with an earlier item, and L1 items never wait, so
+// every wait ends (no co-residency is assumed).  While an item runs, the
+// workgroup also reads the count the next claimed item will wait for, so a
+// row block that is long finished costs no round trip.
+template <int MT, bool PK>
+__global__ __launch_bounds__(256) void fused_direct(FwdArgs a)
+{
+    const int n1 = a.num_mblocks * (a.I / 128);
+    const int NT2 = (a.H + 255) / 256;
+    const int n2 = a.num_mblocks * NT2;
+    const int n3 = (int)(((long long)a.T * (a.H / 8) + 255) / 256);
+    const int total = n1 + n2 + n3;
+    int32_t* queue = a.sync + kSyncQueue;
+    // counter an item waits for (null: none)
+    auto wait_ctr = [&](int it) -> const int32_t* {
+        if (it < n1 || it >= total)
+            return nullptr;
+        if (it < n1 + n2)
+            return a.sync + kSyncReady + (it - n1) / NT2;
+        return a.sync + kSyncL2Done;
+    };
+    __shared__ int s_cur[2], s_nxt[2], s_hint[2];
+    if (threadIdx.x == 0) {
+        s_cur[0] = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_nxt[0] = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_hint[0] = 0;
+    }
+    __syncthreads();
+    int slot = 0;
+    for (;;) {
+        const int cur = s_cur[slot], nxt = s_nxt[slot], hint = s_hint[slot];
+        if (cur >= total)
+            break;
+        int claim = total, nhint = 0;
+        if (threadIdx.x == 0) {
+            if (nxt < total)
+                claim = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (const int32_t* c = wait_ctr(nxt))
+                nhint = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (cur < n1)
+            l1_tile<MT, 1, PK, true>(a, cur);
+        else if (cur < n1 + n2)
+            l2_tile<MT, PK, true>(a, cur - n1, hint);
+        else
+            combine_chunk<true>(a, cur - n1 - n2, n2, hint);
+        slot ^= 1;
+        if (threadIdx.x == 0) {
+            s_cur[slot] = nxt;
+            s_nxt[slot] = claim;
+            s_hint[slot] = nhint;
+        }
+        __syncthreads();
+    }
 }
 
 template <bool PK>
@@ -553,6 +745,40 @@ static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int MT, bool PK>
+static hipError_t launch_fused_t(const FwdArgs& a, hipStream_t s)
+{
+    auto kern = fused_direct<MT, PK>;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess)
+        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess)
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
+    if (err != hipSuccess)
+        return err;
+    if (cus <= 0 || per_cu <= 0)
+        return hipErrorInvalidConfiguration;
+    const long long n = (long long)a.num_mblocks * (a.I / 128 + (a.H + 255) / 256) +
+                        ((long long)a.T * (a.H / 8) + 255) / 256;
+    const long long cap = (long long)cus * per_cu;  // resident workgroups
+    const unsigned grid = (unsigned)(n < cap ? n : cap);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused(const FwdArgs& a, hipStream_t s)
+{
+    if (a.split_l1 != 1 || !a.sync || !a.status)
+        return hipErrorInvalidValue;
+    switch (a.BM) {
+    case 16: return a.packed ? launch_fused_t<1, true>(a, s) : launch_fused_t<1, false>(a, s);
+    case 32: return a.packed ? launch_fused_t<2, true>(a, s) : launch_fused_t<2, false>(a, s);
+    case 64: return a.packed ? launch_fused_t<4, true>(a, s) : launch_fused_t<4, false>(a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s)

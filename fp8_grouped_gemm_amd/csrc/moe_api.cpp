@@ -51,6 +51,9 @@ Config choose_config(const moe_shape_t& s, int T)
 struct Layout {
     int tile_m, kernel, r_cap, mb_cap, NB;
     int split_l1;
+    bool single;  // L1 + L2 + combine in one launch
+    int n_sync;
+    size_t sync;
     size_t status, counts, offsets, blk, mbe, row_src, src_row, h_sf, h, partial;
     size_t part, total;
 };
@@ -65,6 +68,14 @@ struct Layout {
 // slices would have to be added by the combine, which costs more than the
 // split saves (measured).
 constexpr long long kMinItems = 256;  // MI355X compute units
+
+// Direct-tile calls run L1, L2 and the combine as one launch
+// unless the plan asks otherwise.
+constexpr bool kSingleLaunchDefault = false;
+
+// Polls of a single-launch wait before it gives up (~1 s at 8 s_sleep units
+// per poll); a legitimate wait is at most one L1 phase.
+constexpr int kSpinLimit = 1 << 22;
 
 long long mblocks_expected(const moe_shape_t& s, long long T)
 {
@@ -158,6 +169,12 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     // f = t*K + j.
     L.split_l1 = choose_split(s, T, c);
     L.part = take(sizeof(float) * splitk_floats(s, T));
+    // Single-launch counters: L2 done, 3 spare, one ready count per row block.
+    L.single = c.kernel == 0 && L.split_l1 == 1 &&
+               ((s.flags & MOE_FLAG_SINGLE_LAUNCH) ||
+                (kSingleLaunchDefault && !(s.flags & MOE_FLAG_SPLIT_LAUNCH)));
+    L.n_sync = moe::kSyncReady + L.mb_cap;
+    L.sync = take(sizeof(int32_t) * (size_t)L.n_sync);
     L.total = o;
     return L;
 }
@@ -188,6 +205,10 @@ int validate_shape(const moe_shape_t* s)
         return MOE_ERR_INVALID_ARG;
     if (s->weight_layout == MOE_WEIGHTS_PACKED && s->hidden % 256)
         return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (s->flags & ~(MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_SPLIT_LAUNCH | MOE_FLAG_TEST_NO_WAIT))
+        return MOE_ERR_INVALID_ARG;
+    if ((s->flags & MOE_FLAG_SINGLE_LAUNCH) && (s->flags & MOE_FLAG_SPLIT_LAUNCH))
+        return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -247,6 +268,8 @@ moe::RouteArgs route_args(const moe_shape_t& s, int T, const Layout& L, void* ws
     a.mblock_expert = with_mblocks ? at<int32_t>(ws, L.mbe) : nullptr;
     a.mb_cap = L.mb_cap;
     a.status = at<int32_t>(ws, L.status);
+    a.sync = with_mblocks ? at<int32_t>(ws, L.sync) : nullptr;
+    a.n_sync = with_mblocks ? L.n_sync : 0;
     return a;
 }
 
@@ -303,6 +326,7 @@ int moe_plan_info(moe_plan_t plan, int32_t T, moe_tile_info_t* info)
     info->l2_tile_n = 256;
     info->kernel = L.kernel;
     info->l1_split = L.split_l1;
+    info->single_launch = L.single ? 1 : 0;
     return MOE_OK;
 }
 
@@ -403,6 +427,14 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     a.split_l1 = L.split_l1;
     a.splitk_slots = T * s.top_k;
     a.splitk_part = at<float>(workspace, L.part);
+    a.sync = at<int32_t>(workspace, L.sync);
+    a.status = at<int32_t>(workspace, L.status);
+    a.spin_limit = (s.flags & MOE_FLAG_TEST_NO_WAIT) ? -1 : kSpinLimit;
+    if (L.single) {
+        if (moe::launch_fused(a, st) != hipSuccess || !mark(2) || !mark(3) || !mark(4))
+            return MOE_ERR_HIP;
+        return MOE_OK;
+    }
     if (moe::launch_l1(a, L.kernel, st) != hipSuccess || !mark(2))
         return MOE_ERR_HIP;
     if (moe::launch_l2(a, L.kernel, st) != hipSuccess || !mark(3))

@@ -23,6 +23,8 @@ struct RouteArgs {
     int32_t* mblock_expert;  // [mb_cap] expert of each row_align block, -1 past the pool (may be null)
     int32_t mb_cap;
     int32_t* status;      // [4]
+    int32_t* sync;        // [n_sync] single-launch counters, zeroed here (may be null)
+    int32_t n_sync;
 };
 
 // Everything the GEMM, epilogue and combine kernels read or write.
@@ -51,7 +53,19 @@ struct FwdArgs {
     int32_t split_l1;
     int32_t splitk_slots;
     float* splitk_part;
+    // Single launch: counters sync[kSyncL2Done] (L2 items finished),
+    // sync[kSyncQueue] (next item to claim) and sync[kSyncReady + mb] (L1
+    // tiles of row block mb finished), zeroed by the planner; status word for
+    // a wait that gave up; polls before giving up.
+    int32_t* sync;
+    int32_t* status;
+    int32_t spin_limit;
 };
+
+constexpr int kSyncL2Done = 0;
+constexpr int kSyncQueue = 1;  // next unclaimed item
+constexpr int kSyncReady = 4;
+constexpr int32_t kStatusWaitTimeout = 2;  // == MOE_STATUS_WAIT_TIMEOUT
 
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxExperts = 1024;
@@ -59,6 +73,7 @@ constexpr int kMaxExperts = 1024;
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s);
 hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s);
+hipError_t launch_fused(const FwdArgs& a, hipStream_t s);  // L1 + L2 + combine, direct tiles
 hipError_t launch_combine(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s);

@@ -100,6 +100,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan(RouteArgs a)
         for (int m = used / a.row_align + e; m < a.mb_cap; m += kRouteThreads)
             a.mblock_expert[m] = -1;
     }
+    if (a.sync) {
+        for (int i = e; i < a.n_sync; i += kRouteThreads)
+            a.sync[i] = 0;
+    }
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_assign(RouteArgs a)
@@ -214,6 +218,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_small(RouteArgs a)
     if (a.mblock_expert) {
         for (int m = used / a.row_align + x; m < a.mb_cap; m += kRouteThreads)
             a.mblock_expert[m] = -1;
+    }
+    if (a.sync) {
+        for (int i = x; i < a.n_sync; i += kRouteThreads)
+            a.sync[i] = 0;
     }
     __syncthreads();  // scan[] holds inclusive ends: start of expert e = scan[e] - seg(e)
     if (f < a.TK) {

@@ -53,8 +53,19 @@ extern "C" {
 #define MOE_ERR_HIP (-4)                /* a HIP launch or copy failed */
 #define MOE_ERR_NOT_GFX950 (-5)         /* current device is not gfx950 */
 
-/* Status bits written by the planner into the workspace (moe_read_status). */
+/* Status bits written into the workspace by a forward (moe_read_status). */
 #define MOE_STATUS_EXPERT_OUT_OF_RANGE 1 /* some topk_idx >= E; those slots were skipped */
+#define MOE_STATUS_WAIT_TIMEOUT 2        /* single launch: a wait for other tiles gave up
+                                            (bounded spin); y of that call is invalid */
+
+/* Plan flags (moe_shape_t.flags). */
+#define MOE_FLAG_SINGLE_LAUNCH 1  /* L1, L2 and combine of direct-tile calls in one
+                                     launch ("07 · MegaMoE" §5-6) */
+#define MOE_FLAG_SPLIT_LAUNCH 2   /* one launch per step; neither flag: the library's
+                                     choice (see moe_plan_info's single_launch) */
+#define MOE_FLAG_TEST_NO_WAIT 256 /* test-only: the single launch's waits give up at
+                                     once, so MOE_STATUS_WAIT_TIMEOUT is set and y is
+                                     invalid; exercises the timeout path */
 
 /* Weight layouts a plan can expect for w1/w2 (scales are always row-major). */
 #define MOE_WEIGHTS_ROW_MAJOR 0 /* w1 [E,2I,H], w2 [E,H,I] as documented at moe_forward */
@@ -68,6 +79,7 @@ typedef struct moe_shape {
     int32_t max_tokens;    /* largest T any call on this plan may pass */
     int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128 (128: H % 256 == 0) */
     int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
+    int32_t flags;         /* MOE_FLAG_* bits, 0 = defaults */
 } moe_shape_t;
 
 typedef struct moe_plan* moe_plan_t;
@@ -82,6 +94,7 @@ typedef struct moe_tile_info {
     int32_t kernel;      /* 0 = direct-load tile kernel, 1 = LDS-staged tile kernel */
     int32_t l1_split;    /* workgroups sharing one L1 tile's K range (1 = no split;
                             16-row tiles with fewer tiles than compute units) */
+    int32_t single_launch; /* 1: L1, L2 and combine run as one launch */
 } moe_tile_info_t;
 
 /* Byte offsets of the workspace sections used by a forward with T tokens.
@@ -142,8 +155,9 @@ int moe_forward(moe_plan_t plan, int32_t num_tokens,
 /* moe_forward, plus five hipEvent_t recorded on `stream` for measurement:
  * step_events[0] before the planner, [1] after the planner, [2] after the
  * L1 GEMM + SwiGLU/requant epilogue, [3] after the L2 GEMM, [4] after the
- * combine.  Any entry may be NULL (not recorded).  Same validation and
- * error behaviour as moe_forward; with T == 0 nothing is recorded. */
+ * combine.  With a single launch, [2], [3] and [4] are all recorded after
+ * it.  Any entry may be NULL (not recorded).  Same validation and error
+ * behaviour as moe_forward; with T == 0 nothing is recorded. */
 int moe_forward_timed(moe_plan_t plan, int32_t num_tokens,
                       const uint8_t* x, const float* x_sf,
                       const int32_t* topk_idx, const float* topk_w,

@@ -101,6 +101,27 @@ def test_plan_info_tile_choice_and_workspace_monotone():
         moe.moe_plan_destroy(p)
 
 
+def test_plan_flags_and_single_launch_choice():
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_plan_create(256, 128, 8, 2, 64, flags=1 << 5)            # unknown bit
+    assert e.value.code == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoEError):
+        moe.moe_plan_create(256, 128, 8, 2, 64,
+                            flags=moe.MOE_FLAG_SINGLE_LAUNCH | moe.MOE_FLAG_SPLIT_LAUNCH)
+    p = moe.moe_plan_create(4096, 2048, 256, 6, 8192, flags=moe.MOE_FLAG_SINGLE_LAUNCH)
+    q = moe.moe_plan_create(4096, 2048, 256, 6, 8192, flags=moe.MOE_FLAG_SPLIT_LAUNCH)
+    try:
+        assert moe.moe_plan_info(p, 128)["single_launch"] == 1   # 16-row direct tiles
+        assert moe.moe_plan_info(p, 1024)["single_launch"] == 1  # 32-row direct tiles
+        assert moe.moe_plan_info(p, 1)["single_launch"] == 0     # L1 split-K: split launches
+        assert moe.moe_plan_info(p, 8192)["single_launch"] == 0  # LDS tiles: split launches
+        assert all(moe.moe_plan_info(q, T)["single_launch"] == 0 for T in (1, 128, 1024, 8192))
+        assert moe.moe_workspace_bytes(p, 128) == moe.moe_workspace_bytes(q, 128)
+    finally:
+        moe.moe_plan_destroy(p)
+        moe.moe_plan_destroy(q)
+
+
 @pytest.mark.parametrize("shape", [(4096, 2048, 256, 6, 0), (256, 128, 8, 2, 16),
                                    (512, 384, 16, 4, 16), (7168, 3072, 384, 6, 0)])
 def test_split_k_choice_and_workspace_monotone_every_T(shape):

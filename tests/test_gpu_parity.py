@@ -245,6 +245,86 @@ def test_forward_small_token_counts_split_k():
     torch.cuda.empty_cache()
 
 
+# -------------------------------------------- single launch (a6 variant)
+
+
+def _run_flags(inp, flags, tile_m=0, weight_layout=0):
+    T, H = inp["x"].shape
+    E, twoI, _ = inp["w1"].shape
+    K = inp["topk_idx"].shape[1]
+    runner = moe.MoEForward(H, twoI // 2, E, K, T, tile_m=tile_m, weight_layout=weight_layout,
+                            flags=flags)
+    return run_gpu(inp, runner=runner)
+
+
+@pytest.mark.parametrize("case", ["wide16", "wide32", "wide64", "tiny32", "ragged32",
+                                  "ragged64", "edge64", "hot32"])
+def test_single_launch_matches_split_launch_bitwise(case):
+    # Same tiles, same arithmetic in the same order; only the hand-off
+    # between L1, L2 and the combine changes, so y is bit-identical.  (The
+    # single launch runs when L1 does not split K, i.e. 16-row tiles need at
+    # least 256 L1 tiles: hence the wide case.)
+    cfg = wl.CONFIGS["tiny"]
+    tile = int(case[-2:])
+    if case.startswith("wide"):
+        host, dev = small_case(300, 256, 512, 64, 4, 21)
+    elif case.startswith("tiny"):
+        host, dev = small_case(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, wl.default_seed(cfg))
+    elif case.startswith("ragged"):
+        host, dev = small_case(203, 512, 384, 16, 4, 12)
+    elif case.startswith("edge"):
+        host, dev = small_case(37, 384, 256, 12, 3, 11, mask={(0, 0): -1, (0, 1): -1, (0, 2): -1,
+                                                               (3, 1): 40, (7, 0): -5})
+    else:
+        T = 150
+        host, dev = small_case(T, 256, 256, 8, 2, 14, mask={(t, 0): 2 for t in range(T)})
+    y_split, r_split = _run_flags(dev, moe.MOE_FLAG_SPLIT_LAUNCH, tile)
+    y_one, r_one = _run_flags(dev, moe.MOE_FLAG_SINGLE_LAUNCH, tile)
+    T = dev["x"].shape[0]
+    assert moe.moe_plan_info(r_split.plan, T)["single_launch"] == 0
+    assert moe.moe_plan_info(r_one.plan, T)["single_launch"] == 1
+    st = moe.moe_read_status(r_one.plan, T, r_one.workspace)
+    assert not (st[0] & moe.MOE_STATUS_WAIT_TIMEOUT)
+    assert torch.equal(y_split, y_one), case
+    check_y(y_one.cpu().numpy(), run_oracle(host)["y"], what=f"single launch {case}")
+
+
+def test_single_launch_full_size_decode_bitwise_and_repeat():
+    cfg = wl.CONFIGS["flash_decode"]
+    inp = gpu_inputs(cfg, wl.default_seed(cfg))
+    y_split, _ = _run_flags(inp, moe.MOE_FLAG_SPLIT_LAUNCH, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    y_one, runner = _run_flags(inp, moe.MOE_FLAG_SINGLE_LAUNCH,
+                               weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert moe.moe_plan_info(runner.plan, cfg.T)["single_launch"] == 1
+    assert torch.equal(y_split, y_one)
+    # the counters are reset by every call's planner: repeated calls agree
+    w1, w2 = runner.prepare(inp["w1"], inp["w2"])
+    for _ in range(3):
+        y = runner.forward(inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_w"], w1,
+                           inp["w1_sf"], w2, inp["w2_sf"])
+        assert torch.equal(y, y_one)
+    st = moe.moe_read_status(runner.plan, cfg.T, runner.workspace)
+    assert not (st[0] & moe.MOE_STATUS_WAIT_TIMEOUT)
+    del inp, w1, w2
+    torch.cuda.empty_cache()
+
+
+def test_single_launch_wait_timeout_is_reported():
+    # The test flag makes every wait give up at once (no kernel spins): the
+    # call still completes and flags MOE_STATUS_WAIT_TIMEOUT; the next call
+    # on a normal plan with the same inputs is clean and correct.
+    cfg = wl.CONFIGS["tiny"]
+    host, dev = small_case(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, wl.default_seed(cfg))
+    _, bad = _run_flags(dev, moe.MOE_FLAG_SINGLE_LAUNCH | moe.MOE_FLAG_TEST_NO_WAIT, 32)
+    assert moe.moe_plan_info(bad.plan, cfg.T)["single_launch"] == 1
+    st = moe.moe_read_status(bad.plan, cfg.T, bad.workspace)
+    assert st[0] & moe.MOE_STATUS_WAIT_TIMEOUT
+    y, good = _run_flags(dev, moe.MOE_FLAG_SINGLE_LAUNCH, 32)
+    st = moe.moe_read_status(good.plan, cfg.T, good.workspace)
+    assert not (st[0] & moe.MOE_STATUS_WAIT_TIMEOUT)
+    check_y(y.cpu().numpy(), run_oracle(host)["y"], what="single launch after a timeout run")
+
+
 def test_forward_zero_tokens_is_noop():
     runner = moe.MoEForward(256, 128, 8, 2, 16)
     y = torch.full((0, 256), 7, dtype=torch.uint16, device="cuda")

@@ -6,7 +6,8 @@ in HBM.  Prints ONE JSON line.  The default workload is the DeepSeek
 "Flash"-shaped decode layer: T=128 tokens, hidden 4096, intermediate 2048,
 256 experts all resident, top-6, uniform routing.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--tokens T] [--no-cpu-baseline]
+                  [--flush MIB] [--launch auto|single|split] [--weights packed|row_major]
 """
 import argparse
 import json
@@ -99,6 +100,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(the reference kernel for scaling HBM byte counters) and exit")
+    ap.add_argument("--flush", type=int, default=0, metavar="MIB",
+                    help="also time each step alone after writing a MIB MiB scratch buffer "
+                         "(evicts the 256 MB MALL and the L2s); adds a 'cold' object with the "
+                         "median and range of those per-step times")
     ap.add_argument("--launch", choices=("auto", "single", "split"), default="auto",
                     help="single: L1, L2 and combine in one cooperative launch (direct "
                          "tiles); split: one launch per step; auto: the library's choice")
@@ -245,6 +250,23 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.flush:
+        scratch = torch.empty(args.flush << 20, dtype=torch.uint8, device=dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        cold = []
+        for _ in range(args.steps):
+            scratch.fill_(1)
+            e0.record(stream)
+            moe.moe_forward(runner.plan, cfg.T, *fwd_args, stream=stream)
+            e1.record(stream)
+            e1.synchronize()
+            cold.append(e0.elapsed_time(e1) * 1e3)
+        cold.sort()
+        line["cold"] = {"flush_mib": args.flush, "median_us": round(cold[len(cold) // 2], 2),
+                        "min_us": round(cold[0], 2), "max_us": round(cold[-1], 2),
+                        "steps": len(cold)}
+        del scratch
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         us, threads, secs, sample = time_oracle_sample(inp, cfg, args.cpu_sample_tokens, seed)

@@ -24,6 +24,7 @@ MOE_WEIGHTS_PACKED = 1
 MOE_FLAG_SINGLE_LAUNCH = 1
 MOE_FLAG_SPLIT_LAUNCH = 2
 MOE_FLAG_TEST_NO_WAIT = 256
+MOE_FLAG_TEST_SMALL_GRID = 512
 
 EXPORTED_SYMBOLS = (
     "moe_plan_create", "moe_plan_destroy", "moe_plan_info", "moe_workspace_bytes",

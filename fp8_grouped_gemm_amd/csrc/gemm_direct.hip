@@ -336,8 +336,7 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const float g = acc[ms][s][i], u = acc[ms][s + 2][i];
-                const float silu = g / (1.0f + expf(-g));
-                const float v = (silu * u) * wrow[ms][i];
+                const float v = (silu(g) * u) * wrow[ms][i];
                 hv[ms][s][i] = v;
                 m = fmaxf(m, fabsf(v));
             }
@@ -355,9 +354,10 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
                 const int r = 16 * ms + 4 * lg + i;
                 const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
                 const float sf = fmaxf(amax, 1e-10f) / 448.0f;
+                const float rsf = __builtin_amdgcn_rcpf(sf);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    qt[r][wave * 32 + s * 16 + lr] = (uint8_t)f32_to_e4m3(hv[ms][s][i] / sf);
+                    qt[r][wave * 32 + s * 16 + lr] = (uint8_t)requant_e4m3(hv[ms][s][i], sf, rsf);
                 if (wave == 0 && lr == 0) {
                     float* dst = a.h_sf + (size_t)(row0 + r) * (I / 128) + nt;
                     if constexpr (CO)
@@ -574,19 +574,19 @@ __global__ __launch_bounds__(256) void l1_splitk_epilogue(FwdArgs a)
     float hv[8], m = 0.f;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const float silu = g[q] / (1.0f + expf(-g[q]));
-        hv[q] = (silu * u[q]) * w;
+        hv[q] = (silu(g[q]) * u[q]) * w;
         m = fmaxf(m, fabsf(hv[q]));
     }
     m = max16(m);
     if (f < 0)
         return;
     const float sf = fmaxf(m, 1e-10f) / 448.0f;
+    const float rsf = __builtin_amdgcn_rcpf(sf);
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        lo |= f32_to_e4m3(hv[q] / sf) << (8 * q);
-        hi |= f32_to_e4m3(hv[q + 4] / sf) << (8 * q);
+        lo |= requant_e4m3(hv[q], sf, rsf) << (8 * q);
+        hi |= requant_e4m3(hv[q + 4], sf, rsf) << (8 * q);
     }
     *reinterpret_cast<uint2*>(a.h + (size_t)r * I + c0) = make_uint2(lo, hi);
     if ((threadIdx.x & 15) == 0)

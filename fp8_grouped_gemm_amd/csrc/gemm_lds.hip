@@ -1,5 +1,6 @@
 // L1 / L2 grouped FP8 GEMMs for large row tiles (prefill): 128 pool rows x
-// 256 columns per workgroup, operands staged through LDS.
+// 256 columns per tile, operands staged through LDS, one persistent
+// workgroup per compute unit.
 //
 // Same arithmetic as the direct-load kernels ("MegaMoE SM90 Implementation
 // Design" §5.3 promotion per 128-K block, §10.1 / §11.1 epilogues): for every
@@ -15,17 +16,27 @@
 // (pack.hip), so each wave's B operand is 8 KiB in a row of LDS.
 //
 // Each 128-wide K block (A: 128 x 128 B, B: 256 x 128 B, plus the block's
-// 128 activation scales) is copied global -> LDS with gfx950's
+// activation and weight scales) is copied global -> LDS with gfx950's
 // global_load_lds_dwordx4 (each lane's 16 bytes land at base + 16 * lane, so
 // one wave instruction fills 1 KiB in MFMA fragment order: [subtile][half]
-// [lane][16 B], conflict-free ds_read_b128).  Three LDS stages keep two K
-// blocks in flight while the third is multiplied.  The copy is issued as
-// inline assembly and its completion tracked by explicit vmcnt waits: every
-// wave issues exactly kCopiesPerStage copies per stage, so "all but the
-// newest stage landed" is vmcnt <= kCopiesPerStage.  Each step reads all its
-// fragments into registers before issuing the next copy, and the barrier at
-// the top of a step orders the previous step's reads before a stage is
-// overwritten.
+// [lane][16 B], conflict-free ds_read_b128), three stages deep.
+//
+// Persistence.  With 150 KiB of stages only one workgroup fits a compute
+// unit, so a workgroup that ended after each tile left its unit's memory
+// stream idle through the tile's epilogue, its exit and the next
+// workgroup's start (measured: a quarter of the L1 time at the
+// flash-prefill shape).  Instead each workgroup walks tiles t = blockIdx +
+// k * gridDim (tiles of unused row blocks form a suffix) and the copies run
+// as one stream over (tile, K block), two blocks ahead of the multiply and
+// across tile boundaries, so the next tile's first blocks arrive during the
+// current tile's epilogue.  Everything the copies of a tile need from
+// memory -- the tile's row sources, its expert, and (L1) the top-k weight of
+// each row for the epilogue -- also travels by LDS copy, one tile ahead, so
+// the loop holds no other vector memory access and the explicit vmcnt
+// accounting stays exact.  The copy is issued as inline assembly: a batch
+// (one K block's copies, plus on a tile's first block one metadata copy) is
+// the same number of instructions in every wave, so "all but the newest
+// batch landed" is vmcnt <= that batch's size.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -36,28 +47,37 @@ namespace {
 constexpr int BM = 128, BN = 256;
 constexpr int A_BYTES = BM * 128;   // 16 KiB: 8 m-subtiles x 2 halves x 1 KiB
 constexpr int B_BYTES = BN * 128;   // 32 KiB: 16 n-subtiles x 2 halves x 1 KiB
-constexpr int S_BYTES = 8 * 256;    // one 64-scale copy per wave; rows 0..127 are the first 512 B
+constexpr int S_BYTES = 8 * 256;    // one 256-byte scale copy per wave
 constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
 constexpr int NSTAGE = 3;
+// Per-tile metadata slot: row_src of the 128 rows, top-k weight per row
+// (L1), the tile's expert replicated over 64 lanes.
+constexpr int META = 512 + 512 + 256;
+constexpr int NMETA = 4;
+constexpr int META_W = 512, META_E = 1024;
+constexpr int SMEM = NSTAGE * STAGE + NMETA * META;
 constexpr int kThreads = 512;
-constexpr int kCopiesPerStage = 2 + 4 + 1;  // A halves, B halves, scales (per wave)
+constexpr int kCopiesPerBlock = 2 + 4 + 1;  // A halves, B halves, scales (per wave)
+static_assert(SMEM <= 160 * 1024, "LDS");
 
 // s_waitcnt with vmcnt = n (n < 16) and no wait on expcnt / lgkmcnt
 // (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 #define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0xF70 | (n))
-static_assert(kCopiesPerStage < 16, "vmcnt immediate");
 
 // Asynchronous copy global -> LDS of 16 (or 4) bytes per lane to
-// lds_base + 16 * lane (4 * lane).  lds_base must be wave-uniform.
+// lds_base + 16 * lane (4 * lane).  lds_base is wave-uniform (read from the
+// first lane into the scalar register M0 takes).
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory", "m0");
 }
 
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory", "m0");
 }
 
@@ -102,7 +122,8 @@ __device__ __forceinline__ const uint8_t* weight_src(const FwdArgs& a, int e, in
 
 }  // namespace
 
-// L1 (gate + up) when L1 is true, L2 (down) otherwise.
+// L1 (gate + up) when L1 is true, L2 (down) otherwise.  Needs at least two
+// K blocks (H >= 256 and I >= 256; the plan enforces it).
 template <bool L1, bool PK>
 __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 {
@@ -110,68 +131,142 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     const int H = a.H, I = a.I, K = a.K, T = a.T;
     const int NT = L1 ? I / 128 : H / 256;
     const int nkb = L1 ? H / 128 : I / 128;
-    const int mb = blockIdx.x / NT;
-    const int nt = blockIdx.x - mb * NT;
-    const int e = a.mblock_expert[mb];
-    if (e < 0)
-        return;
+    const int n_tiles = a.num_mblocks * NT;
+    const int G = gridDim.x, b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int lr = lane & 15, lg = lane >> 4;
-    const int row0 = mb * BM;
-
-    // ---- copy sources for K block 0 (later blocks add 128 bytes per block
-    // for activations and scales' kb index).
-    // A: wave v copies m-subtile halves q = 2v, 2v+1 (subtile q>>1, half q&1).
-    const uint8_t* a_src[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int q = wave * 2 + j, ms = q >> 1, half = q & 1;
-        const int r = row0 + ms * 16 + lr;
-        if constexpr (L1) {
-            const int f = a.row_src[r];
-            a_src[j] = a.x + (size_t)(f >= 0 ? f / K : 0) * H + half * 64 + 16 * lg;
-        } else {
-            a_src[j] = a.h + (size_t)r * I + half * 64 + 16 * lg;
-        }
-    }
-    // Scales ride in the stage too (one 4-byte-per-lane copy per wave):
-    // waves 0 and 1 copy the activation scales of rows [0, 64) and
-    // [64, 128) into the first 512 bytes of the scale area, wave 2 copies
-    // the block's two weight scales (L1: gate and up block; L2: the two
-    // 128-column blocks of the tile) into lanes 0 and 1 of its slot, and the
-    // other waves copy duplicates, so that every wave issues the same number
-    // of copies and the K loop holds no other vector memory access.
-    const float* s_src;
-    if (wave == 2) {
-        if constexpr (L1)
-            s_src = a.w1_sf + ((size_t)e * (2 * I / 128) + ((lane & 1) ? I / 128 + nt : nt)) * nkb;
-        else
-            s_src = a.w2_sf + ((size_t)e * (H / 128) + 2 * nt + (lane & 1)) * nkb;
-    } else {
-        const int r = row0 + (wave & 1) * 64 + lane;
-        if constexpr (L1) {
-            const int f = a.row_src[r];
-            s_src = a.x_sf + (size_t)(f >= 0 ? f / K : 0) * (H / 128);
-        } else {
-            s_src = a.h_sf + (size_t)r * (I / 128);
-        }
-    }
     const uint32_t smem_base = lds_addr(smem);
+    uint8_t* meta_base = smem + NSTAGE * STAGE;
+    const uint32_t meta_lds = smem_base + NSTAGE * STAGE;
+    auto slot = [&](int k) { return meta_base + (k % NMETA) * META; };
+    auto slot_lds = [&](int k) { return meta_lds + (k % NMETA) * META; };
+    auto tile_of = [&](int k) { return b + k * G; };
 
-    auto issue = [&](int kb, int stage) {
-        const uint32_t st = smem_base + stage * STAGE;
+    if (tile_of(0) >= n_tiles)
+        return;
+
+    // ---- metadata copy for tile k + 1 (and the weights of tile k's rows):
+    // one dma4 per wave.  Waves 0/1 (and duplicates 5/6) copy row_src of
+    // tile k + 1, rows [64 h, 64 h + 64); waves 2/3 gather topk_w of tile k's
+    // rows (L1; L2: duplicates of 0/1); waves 4/7 copy tile k + 1's expert.
+    // A tile past the end reads tile k's (valid) rows instead: its slot is
+    // never used.
+    auto issue_meta = [&](int k) {
+        const int tk = tile_of(k), tn = tile_of(k + 1);
+        const int rown = (tn < n_tiles ? tn / NT : tk / NT) * BM;
+        const int role = (wave == 5) ? 0 : (wave == 6) ? 1 : (wave == 7) ? 4 : wave;
+        if (role <= 1 || (!L1 && role <= 3)) {
+            const int h = role & 1;
+            dma4(a.row_src + rown + 64 * h + lane, slot_lds(k + 1) + 256 * h);
+        } else if (role <= 3) {
+            const int h = role - 2;
+            const int f = reinterpret_cast<const int32_t*>(slot(k))[64 * h + lane];
+            dma4(a.topk_w + (f >= 0 ? f : 0), slot_lds(k) + META_W + 256 * h);
+        } else {
+            dma4(a.mblock_expert + rown / BM, slot_lds(k + 1) + META_E);
+        }
+    };
+
+    // ---- issue side: the next K block of the flattened (tile, kb) stream
+    int i_k = 0, i_kb = 0, i_j = 0;
+    bool i_done = false;
+    int i_e = 0, i_nt = 0;
+    const uint8_t* a_src[2] = {nullptr, nullptr};
+    const float* s_src = nullptr;
+    // Starts issuing tile k: reads its expert and row sources from its
+    // metadata slot (landed and visible: copied with tile k - 1's first
+    // block, at least two batches and one barrier ago).
+    auto begin_tile = [&](int k) {
+        const int t = tile_of(k);
+        if (t >= n_tiles) {
+            i_done = true;
+            return;
+        }
+        const int e = __builtin_amdgcn_readfirstlane(
+            reinterpret_cast<const int32_t*>(slot(k) + META_E)[lane]);
+        if (e < 0) {
+            i_done = true;
+            return;
+        }
+        const int mb = t / NT, nt = t - mb * NT, row0 = mb * BM;
+        i_e = e;
+        i_nt = nt;
+        // A: wave v copies m-subtile v, both halves: rows row0 + 16 v + lr.
+        const int r = row0 + wave * 16 + lr;
+        const int f = reinterpret_cast<const int32_t*>(slot(k))[wave * 16 + lr];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if constexpr (L1)
+                a_src[j] = a.x + (size_t)(f >= 0 ? f / K : 0) * H + j * 64 + 16 * lg;
+            else
+                a_src[j] = a.h + (size_t)r * I + j * 64 + 16 * lg;
+        }
+        // Scales: lanes 16 and 17 the block's two weight scales (L1: gate
+        // and up block of column tile nt; L2: blocks 2 nt, 2 nt + 1), the
+        // other lanes the activation scale of row 16 v + (lane & 15).
+        if (lane == 16 || lane == 17) {
+            const int q = lane - 16;
+            if constexpr (L1)
+                s_src = a.w1_sf + ((size_t)e * (2 * I / 128) + (q ? I / 128 + nt : nt)) * nkb;
+            else
+                s_src = a.w2_sf + ((size_t)e * (H / 128) + 2 * nt + q) * nkb;
+        } else {
+            if constexpr (L1)
+                s_src = a.x_sf + (size_t)(f >= 0 ? f / K : 0) * (H / 128);
+            else
+                s_src = a.h_sf + (size_t)r * (I / 128);
+        }
+    };
+    // Issues the next block; returns the batch size (0 when nothing is left).
+    auto issue_next = [&]() -> int {
+        if (i_done)
+            return 0;
+        if (i_kb == nkb) {
+            ++i_k;
+            i_kb = 0;
+        }
+        if (i_kb == 0) {
+            begin_tile(i_k);
+            if (i_done)
+                return 0;
+        }
+        const uint32_t st = smem_base + (i_j % NSTAGE) * STAGE;
+        const int kb = i_kb;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             dma16(a_src[j] + (size_t)kb * 128, st + (wave * 2 + j) * 1024);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int q = wave * 4 + j, sub = q >> 1, half = q & 1;
-            dma16(weight_src<L1, PK>(a, e, nt, kb, sub, half, lane), st + A_BYTES + q * 1024);
+            dma16(weight_src<L1, PK>(a, i_e, i_nt, kb, sub, half, lane), st + A_BYTES + q * 1024);
         }
         dma4(s_src + kb, st + A_BYTES + B_BYTES + wave * 256);
+        int n = kCopiesPerBlock;
+        if (kb == 0) {
+            issue_meta(i_k);
+            ++n;
+        }
+        ++i_kb;
+        ++i_j;
+        return n;
     };
+
+    // ---- prologue: tile 0's metadata, then blocks 0 and 1 of the stream
+    {
+        const int role = (wave == 5) ? 0 : (wave == 6) ? 1 : (wave == 7) ? 4 : wave;
+        const int row0 = (tile_of(0) / NT) * BM;
+        if (role <= 3)
+            dma4(a.row_src + row0 + 64 * (role & 1) + lane, slot_lds(0) + 256 * (role & 1));
+        else
+            dma4(a.mblock_expert + row0 / BM, slot_lds(0) + META_E);
+        MOE_WAIT_VMCNT(0);
+        __syncthreads();
+    }
+    const int b0 = issue_next();
+    int last = issue_next();  // size of the newest batch
+    (void)b0;
 
     v4f acc[4][4];
 #pragma unroll
@@ -180,29 +275,32 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         for (int s = 0; s < 4; ++s)
             acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    issue(0, 0);
-    if (nkb > 1)
-        issue(1, 1);
-
-    int stage = 0;
-    for (int kb = 0; kb < nkb; ++kb) {
-        // This wave's copies for block kb have landed (block kb + 1's may be
-        // in flight); the barrier makes every wave's copies visible and
-        // orders the previous step's reads before the refill below.
-        if (kb + 1 < nkb)
-            MOE_WAIT_VMCNT(kCopiesPerStage);
-        else
+    // ---- multiply side
+    int m_k = 0, m_kb = 0, j = 0;
+    bool drain = false;  // global stores since the last wait: wait for everything
+    for (;;) {
+        if (i_done && m_k >= i_k)
+            break;  // tiles 0 .. i_k - 1 were valid and are finished
+        // Block j has landed (its batch is not the newest one) and is visible
+        // to all waves; the previous step's fragment reads are done, so the
+        // stage issued below is free.
+        if (drain || last == 0)
             MOE_WAIT_VMCNT(0);
+        else if (last == kCopiesPerBlock)
+            MOE_WAIT_VMCNT(kCopiesPerBlock);
+        else
+            MOE_WAIT_VMCNT(kCopiesPerBlock + 1);
+        drain = false;
         __syncthreads();
 
-        const uint8_t* st = smem + stage * STAGE;
+        const uint8_t* st = smem + (j % NSTAGE) * STAGE;
         v8i af[4], bf[4];
         float sa[4][4];
-        const float* sa_lds = reinterpret_cast<const float*>(st + A_BYTES + B_BYTES);
+        const float* s_lds = reinterpret_cast<const float*>(st + A_BYTES + B_BYTES);
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
             af[ms] = lds_frag(st + ((wm * 4 + ms) * 2) * 1024, lane);
-            const float4 s4 = *reinterpret_cast<const float4*>(sa_lds + wm * 64 + ms * 16 + 4 * lg);
+            const float4 s4 = *reinterpret_cast<const float4*>(s_lds + (wm * 4 + ms) * 64 + 4 * lg);
             sa[ms][0] = s4.x;
             sa[ms][1] = s4.y;
             sa[ms][2] = s4.z;
@@ -211,14 +309,11 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             bf[s] = lds_frag(st + A_BYTES + (wn * 4 + s) * 2048, lane);
-        // weight scales (copied by wave 2): L1 gate / up block; L2 the
-        // wave's 128-column block (256 n + 64 wn) / 128
-        const float* sb_lds = sa_lds + 2 * 64;
-        const float sg = L1 ? sb_lds[0] : sb_lds[wn >> 1];
-        const float su = L1 ? sb_lds[1] : sg;
+        // weight scales: L1 gate / up block; L2 the wave's 128-column block
+        const float sg = L1 ? s_lds[16] : s_lds[16 + (wn >> 1)];
+        const float su = L1 ? s_lds[17] : sg;
 
-        if (kb + 2 < nkb)
-            issue(kb + 2, stage == 0 ? 2 : stage - 1);
+        last = issue_next();
 
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -233,104 +328,139 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                 for (int i = 0; i < 4; ++i)
                     acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[ms][i], acc[ms][s][i]);
         }
-        stage = stage == NSTAGE - 1 ? 0 : stage + 1;
-    }
-    __syncthreads();  // all fragment reads done before the epilogue reuses LDS
+        ++j;
+        if (++m_kb < nkb)
+            continue;
 
-    // ------------------------------------------------------------ epilogues
-    if constexpr (L1) {
-        // acc[ms][s]: rows wm*64 + 16 ms + 4 lg + i; s = 0,1 gate column
-        // 32 wn + 16 s + lr of the block, s = 2,3 the matching up column.
-        float* red = reinterpret_cast<float*>(smem + A_BYTES);  // [4][128]
-        uint8_t* qt = smem;                                     // [128][128]
-        float wrow[4][4];
+        // ---------------------------------------------- epilogue of tile m_k
+        // It works in the stage just multiplied (the next two stages hold
+        // the next tile's first blocks, in flight); the barrier orders every
+        // wave's fragment reads of that stage before it is overwritten, and
+        // the next step's barrier orders the epilogue before the stage is
+        // refilled.
+        const int t = tile_of(m_k);
+        const int mb = t / NT, nt = t - mb * NT, row0 = mb * BM;
+        uint8_t* ep = smem + ((j - 1) % NSTAGE) * STAGE;
+        const int32_t* m_rs = reinterpret_cast<const int32_t*>(slot(m_k));
+        __syncthreads();
+        if constexpr (L1) {
+            // acc[ms][s]: rows wm*64 + 16 ms + 4 lg + i; s = 0,1 gate column
+            // 32 wn + 16 s + lr of the block, s = 2,3 the matching up column.
+            const float* m_w = reinterpret_cast<const float*>(slot(m_k) + META_W);
+            float* red = reinterpret_cast<float*>(ep);  // [4][128]
+            uint8_t* qt = ep + 2048;                    // [128][128]
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
+            for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int f = a.row_src[row0 + wm * 64 + ms * 16 + 4 * lg + i];
-                wrow[ms][i] = f >= 0 ? a.topk_w[f] : 0.f;
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wm * 64 + ms * 16 + 4 * lg + i;
+                    const float w = m_rs[r] >= 0 ? m_w[r] : 0.f;
+                    float m = 0.f;
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float m = 0.f;
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const float g = acc[ms][s][i], u = acc[ms][s + 2][i];
-                    const float silu = g / (1.0f + expf(-g));
-                    const float v = (silu * u) * wrow[ms][i];
-                    acc[ms][s][i] = v;
-                    m = fmaxf(m, fabsf(v));
+                    for (int s = 0; s < 2; ++s) {
+                        const float g = acc[ms][s][i], u = acc[ms][s + 2][i];
+                        const float v = (silu(g) * u) * w;
+                        acc[ms][s][i] = v;
+                        m = fmaxf(m, fabsf(v));
+                    }
+                    m = max16(m);
+                    if (lr == 0)
+                        red[wn * 128 + r] = m;
                 }
-                m = max16(m);
-                if (lr == 0)
-                    red[wn * 128 + wm * 64 + ms * 16 + 4 * lg + i] = m;
-            }
-        __syncthreads();
+            __syncthreads();
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms)
+            for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * 64 + ms * 16 + 4 * lg + i;
-                const float amax =
-                    fmaxf(fmaxf(red[r], red[128 + r]), fmaxf(red[256 + r], red[384 + r]));
-                const float sf = fmaxf(amax, 1e-10f) / 448.0f;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wm * 64 + ms * 16 + 4 * lg + i;
+                    const float amax =
+                        fmaxf(fmaxf(red[r], red[128 + r]), fmaxf(red[256 + r], red[384 + r]));
+                    const float sf = fmaxf(amax, 1e-10f) / 448.0f;
+                    const float rsf = __builtin_amdgcn_rcpf(sf);
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    qt[r * 128 + wn * 32 + s * 16 + lr] = (uint8_t)f32_to_e4m3(acc[ms][s][i] / sf);
-                if (wn == 0 && lr == 0)
-                    a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
-            }
-        __syncthreads();
-        for (int c = threadIdx.x; c < BM * 8; c += kThreads) {
-            const int r = c >> 3, col = (c & 7) * 16;
-            if (a.row_src[row0 + r] >= 0)
+                    for (int s = 0; s < 2; ++s)
+                        qt[r * 128 + wn * 32 + s * 16 + lr] =
+                            (uint8_t)requant_e4m3(acc[ms][s][i], sf, rsf);
+                    if (wn == 0 && lr == 0)
+                        a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
+                }
+            __syncthreads();
+            // BM rows x 128 bytes, 16 bytes per thread, two per thread (rows
+            // without a slot are written too: nothing reads them).
+            for (int c = threadIdx.x; c < BM * 8; c += kThreads) {
+                const int r = c >> 3, col = (c & 7) * 16;
                 *reinterpret_cast<uint4*>(a.h + (size_t)(row0 + r) * I + nt * 128 + col) =
                     *reinterpret_cast<const uint4*>(qt + r * 128 + col);
+            }
+        } else {
+            // acc[ms][s]: rows wm*64 + 16 ms + 4 lg + i, column 64 wn + 16 s
+            // + lr; staged as bf16 one 64-row half at a time (32 KiB).
+            uint16_t* ot = reinterpret_cast<uint16_t*>(ep);  // [64][256]
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                if (wm == hf) {
+#pragma unroll
+                    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                ot[(ms * 16 + 4 * lg + i) * 256 + wn * 64 + s * 16 + lr] =
+                                    f32_to_bf16(acc[ms][s][i]);
+                }
+                __syncthreads();
+                for (int c = threadIdx.x; c < 64 * 32; c += kThreads) {
+                    const int r = c >> 5, col = (c & 31) * 8;
+                    const int f = m_rs[hf * 64 + r];
+                    if (f >= 0) {
+                        const int tt = f / K, jslot = f - tt * K;
+                        *reinterpret_cast<uint4*>(a.partial + ((size_t)jslot * T + tt) * H +
+                                                  nt * 256 + col) =
+                            *reinterpret_cast<const uint4*>(ot + r * 256 + col);
+                    }
+                }
+                __syncthreads();
+            }
         }
-    } else {
-        // acc[ms][s]: rows wm*64 + 16 ms + 4 lg + i, column 64 wn + 16 s + lr.
-        uint16_t* ot = reinterpret_cast<uint16_t*>(smem);  // [128][256] bf16 = 64 KiB
+        drain = true;
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    ot[(wm * 64 + ms * 16 + 4 * lg + i) * 256 + wn * 64 + s * 16 + lr] =
-                        f32_to_bf16(acc[ms][s][i]);
-        __syncthreads();
-        for (int c = threadIdx.x; c < BM * 32; c += kThreads) {
-            const int r = c >> 5, col = (c & 31) * 8;
-            const int f = a.row_src[row0 + r];
-            if (f >= 0) {
-                const int t = f / K, jslot = f - t * K;
-                *reinterpret_cast<uint4*>(a.partial + ((size_t)jslot * T + t) * H + nt * 256 + col) =
-                    *reinterpret_cast<const uint4*>(ot + r * 256 + col);
-            }
-        }
+                acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
+        ++m_k;
+        m_kb = 0;
     }
 }
 
-size_t gemm_lds_smem_bytes() { return (size_t)NSTAGE * STAGE; }
+size_t gemm_lds_smem_bytes() { return (size_t)SMEM; }
 
 template <bool L1>
 static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
 {
-    const unsigned NT = L1 ? a.I / 128 : a.H / 256;
-    const dim3 grid(a.num_mblocks * NT);
+    const int NT = L1 ? a.I / 128 : a.H / 256;
+    const long long n_tiles = (long long)a.num_mblocks * NT;
+    const int nkb = L1 ? a.H / 128 : a.I / 128;
+    if (n_tiles <= 0)
+        return hipSuccess;
+    if (nkb < 2)
+        return hipErrorInvalidValue;
+    int dev = 0, cus = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess)
+        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess)
+        return err;
+    long long g = n_tiles < cus ? n_tiles : cus;
+    if (a.grid_cap > 0 && g > a.grid_cap)
+        g = a.grid_cap;
+    const dim3 grid((unsigned)g);
     const size_t smem = gemm_lds_smem_bytes();
-    if (a.packed) {
-        hipFuncSetAttribute((const void*)gemm_lds<L1, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        hipLaunchKernelGGL((gemm_lds<L1, true>), grid, dim3(kThreads), smem, s, a);
-    } else {
-        hipFuncSetAttribute((const void*)gemm_lds<L1, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        hipLaunchKernelGGL((gemm_lds<L1, false>), grid, dim3(kThreads), smem, s, a);
-    }
+    auto kern = a.packed ? gemm_lds<L1, true> : gemm_lds<L1, false>;
+    err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (err != hipSuccess)
+        return err;
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, s, a);
     return hipGetLastError();
 }
 

@@ -32,8 +32,8 @@ struct Config {
 // that holds an average expert's rows reads each expert's weights once
 // while padding as few MFMA rows as possible (decode: 16).
 // Beyond ~24 rows per expert the 128 x 256 LDS-staged MFMA tile takes over
-// (it needs H % 256 == 0 for its 256-column L2 tiles; otherwise 64-row
-// direct-load tiles).
+// (it needs H % 256 == 0 for its 256-column L2 tiles and I >= 256 for at
+// least two K blocks in L2; otherwise 64-row direct-load tiles).
 Config choose_config(const moe_shape_t& s, int T)
 {
     if (s.tile_m > 0)
@@ -43,7 +43,7 @@ Config choose_config(const moe_shape_t& s, int T)
         return Config{16, 0};
     if (rows <= 24.0)
         return Config{32, 0};
-    if (s.hidden % 256 == 0)
+    if (s.hidden % 256 == 0 && s.intermediate >= 256)
         return Config{128, 1};
     return Config{64, 0};
 }
@@ -199,13 +199,14 @@ int validate_shape(const moe_shape_t* s)
     if (s->tile_m != 0 && s->tile_m != 16 && s->tile_m != 32 && s->tile_m != 64 &&
         s->tile_m != 128)
         return MOE_ERR_UNSUPPORTED_SHAPE;
-    if (s->tile_m == 128 && s->hidden % 256)
+    if (s->tile_m == 128 && (s->hidden % 256 || s->intermediate < 256))
         return MOE_ERR_UNSUPPORTED_SHAPE;
     if (s->weight_layout != MOE_WEIGHTS_ROW_MAJOR && s->weight_layout != MOE_WEIGHTS_PACKED)
         return MOE_ERR_INVALID_ARG;
     if (s->weight_layout == MOE_WEIGHTS_PACKED && s->hidden % 256)
         return MOE_ERR_UNSUPPORTED_SHAPE;
-    if (s->flags & ~(MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_SPLIT_LAUNCH | MOE_FLAG_TEST_NO_WAIT))
+    if (s->flags & ~(MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_SPLIT_LAUNCH | MOE_FLAG_TEST_NO_WAIT |
+                     MOE_FLAG_TEST_SMALL_GRID))
         return MOE_ERR_INVALID_ARG;
     if ((s->flags & MOE_FLAG_SINGLE_LAUNCH) && (s->flags & MOE_FLAG_SPLIT_LAUNCH))
         return MOE_ERR_INVALID_ARG;
@@ -430,6 +431,7 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     a.sync = at<int32_t>(workspace, L.sync);
     a.status = at<int32_t>(workspace, L.status);
     a.spin_limit = (s.flags & MOE_FLAG_TEST_NO_WAIT) ? -1 : kSpinLimit;
+    a.grid_cap = (s.flags & MOE_FLAG_TEST_SMALL_GRID) ? 4 : 0;
     if (L.single) {
         if (moe::launch_fused(a, st) != hipSuccess || !mark(2) || !mark(3) || !mark(4))
             return MOE_ERR_HIP;

@@ -42,6 +42,41 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v)
     return sign | (uint32_t)__builtin_rintf(s);
 }
 
+// The same code from the gfx950 converter: v_cvt_pk_fp8_f32 rounds to
+// nearest even; clamping to +-448 first gives the saturation, and NaN is
+// mapped explicitly.  Equal to f32_to_e4m3 for every one of the 2^32 f32
+// bit patterns (checked exhaustively on the GPU).
+__device__ __forceinline__ uint32_t f32_to_e4m3_hw(float v)
+{
+    if (v != v)
+        return 0x7Fu;
+    const float c = __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+// e4m3 code of the correctly rounded quotient v / sf, given rsf = 1 / sf
+// from the hardware reciprocal (<= 1 ulp): y = v * rsf lies within 2^-22
+// (relative) of the rounded quotient, so the quotient lies between
+// y (1 - 2^-20) and y (1 + 2^-20); the encoder is monotone, so when both ends
+// give the same code, so does the quotient.  Only otherwise (y within ~2^-20
+// of a rounding boundary of the e4m3 grid) is the division done.
+__device__ __forceinline__ uint32_t requant_e4m3(float v, float sf, float rsf)
+{
+    const float y = v * rsf;
+    const uint32_t lo = f32_to_e4m3_hw(y * (1.0f - 0x1p-20f));
+    const uint32_t hi = f32_to_e4m3_hw(y * (1.0f + 0x1p-20f));
+    if (lo == hi)
+        return lo;
+    return f32_to_e4m3_hw(v / sf);
+}
+
+// SiLU with the hardware exp2 and reciprocal (a few ulp from
+// g / (1 + expf(-g)); g -> -inf gives -0, g -> +inf gives g).
+__device__ __forceinline__ float silu(float g)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
+}
+
 // f32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float v)
 {

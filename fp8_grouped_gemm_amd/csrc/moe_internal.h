@@ -60,6 +60,7 @@ struct FwdArgs {
     int32_t* sync;
     int32_t* status;
     int32_t spin_limit;
+    int32_t grid_cap;  // > 0: at most this many workgroups for the persistent kernels
 };
 
 constexpr int kSyncL2Done = 0;

@@ -66,6 +66,9 @@ extern "C" {
 #define MOE_FLAG_TEST_NO_WAIT 256 /* test-only: the single launch's waits give up at
                                      once, so MOE_STATUS_WAIT_TIMEOUT is set and y is
                                      invalid; exercises the timeout path */
+#define MOE_FLAG_TEST_SMALL_GRID 512 /* test-only: the persistent 128-row-tile kernels
+                                        launch at most 4 workgroups, so each walks many
+                                        tiles (same results as the full grid) */
 
 /* Weight layouts a plan can expect for w1/w2 (scales are always row-major). */
 #define MOE_WEIGHTS_ROW_MAJOR 0 /* w1 [E,2I,H], w2 [E,H,I] as documented at moe_forward */
@@ -77,7 +80,8 @@ typedef struct moe_shape {
     int32_t num_experts;   /* E */
     int32_t top_k;         /* K */
     int32_t max_tokens;    /* largest T any call on this plan may pass */
-    int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128 (128: H % 256 == 0) */
+    int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128
+                              (128: H % 256 == 0 and I >= 256) */
     int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
     int32_t flags;         /* MOE_FLAG_* bits, 0 = defaults */
 } moe_shape_t;

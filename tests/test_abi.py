@@ -101,6 +101,21 @@ def test_plan_info_tile_choice_and_workspace_monotone():
         moe.moe_plan_destroy(p)
 
 
+def test_tile128_needs_two_k_blocks_per_layer():
+    # the persistent 128-row-tile kernels need H % 256 == 0 and I >= 256
+    for shape in ((256, 128, 8, 2), (384, 256, 8, 2)):
+        with pytest.raises(moe.MoEError) as e:
+            moe.moe_plan_create(*shape, 64, tile_m=128)
+        assert e.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE
+    p = moe.moe_plan_create(256, 128, 8, 2, 4096)   # auto choice never picks them there
+    try:
+        assert moe.moe_plan_info(p, 4096)["tile_m"] == 64
+        assert moe.moe_plan_info(p, 4096)["kernel"] == 0
+    finally:
+        moe.moe_plan_destroy(p)
+    moe.moe_plan_destroy(moe.moe_plan_create(256, 256, 8, 2, 64, tile_m=128))
+
+
 def test_plan_flags_and_single_launch_choice():
     with pytest.raises(moe.MoEError) as e:
         moe.moe_plan_create(256, 128, 8, 2, 64, flags=1 << 5)            # unknown bit

@@ -143,7 +143,7 @@ def forward_and_check(host, dev, tile_m, what, check_intermediates=True):
     return runner
 
 
-@pytest.mark.parametrize("tile_m", [16, 32, 64, 128])
+@pytest.mark.parametrize("tile_m", [16, 32, 64])
 def test_forward_tiny_all_tiles(tile_m):
     cfg = wl.CONFIGS["tiny"]
     host, dev = small_case(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, wl.default_seed(cfg))
@@ -242,6 +242,46 @@ def test_forward_small_token_counts_split_k():
         check_y(y_pk.cpu().numpy(), ref["y"], per_token_tol=1e-2, what=f"T={T} L1 split {split}")
         del runner
     del full, inp
+    torch.cuda.empty_cache()
+
+
+# ------------------------------- 128-row tiles: persistent LDS kernels
+
+
+@pytest.mark.parametrize("case", ["ragged", "hot", "many_blocks", "tiny_rows"])
+def test_tile128_persistent_small_grid_matches_full_grid(case):
+    # With the test flag the persistent kernels run on 4 workgroups, so each
+    # walks many tiles (copies of the next tile overlap the current tile's
+    # epilogue, metadata slots rotate); the arithmetic per tile is the same,
+    # so y is bit-identical to the full grid, and both match the oracle.
+    if case == "ragged":
+        host, dev = small_case(203, 512, 384, 16, 4, 12)
+    elif case == "hot":
+        T = 150
+        host, dev = small_case(T, 256, 256, 8, 2, 14, mask={(t, 0): 2 for t in range(T)})
+    elif case == "many_blocks":
+        host, dev = small_case(600, 512, 512, 16, 4, 22)
+    else:  # one K block more than the minimum, masked slots, a token with no slot
+        host, dev = small_case(45, 256, 256, 6, 3, 23, mask={(0, 0): -1, (0, 1): -1, (0, 2): -1,
+                                                             (5, 1): -3})
+    y_full, r_full = _run_flags(dev, 0, 128)
+    y_small, r_small = _run_flags(dev, moe.MOE_FLAG_TEST_SMALL_GRID, 128)
+    T = dev["x"].shape[0]
+    assert moe.moe_plan_info(r_small.plan, T)["kernel"] == 1
+    assert torch.equal(y_full, y_small), case
+    check_y(y_small.cpu().numpy(), run_oracle(host)["y"], what=f"tile 128 small grid {case}")
+
+
+def test_tile128_full_size_packed_small_grid():
+    # The flash-prefill workload on 4 workgroups (every workgroup walks
+    # ~1400 L1 tiles) against the full grid, packed weights.
+    cfg = wl.CONFIGS["flash_prefill"]
+    inp = gpu_inputs(cfg, wl.default_seed(cfg))
+    y_full, r = _run_flags(inp, 0, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert moe.moe_plan_info(r.plan, cfg.T)["kernel"] == 1
+    y_small, _ = _run_flags(inp, moe.MOE_FLAG_TEST_SMALL_GRID, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert torch.equal(y_full, y_small)
+    del inp
     torch.cuda.empty_cache()
 
 

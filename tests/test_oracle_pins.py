@@ -385,3 +385,113 @@ def test_route_matches_brute_force(T, K, E, ra):
     assert np.all(offsets % ra == 0) and np.all(np.diff(offsets) >= counts)
     valid = src_row >= 0
     assert np.array_equal(row_src[src_row[valid]], np.nonzero(valid)[0])
+
+
+# ------------------------------------------- whole layer in exact arithmetic
+
+
+def _round_binary(q: Fraction, mant: int, emin: int) -> Fraction:
+    """Nearest binary floating-point value with `mant` fraction bits and
+    minimum normal exponent `emin` (subnormals below), ties to even."""
+    if q == 0:
+        return Fraction(0)
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, emin) - mant)
+    m = a / ulp
+    n = m.numerator // m.denominator
+    r = m - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return (n * ulp) if q > 0 else -(n * ulp)
+
+
+def _f32(q):
+    return _round_binary(q, 23, -126)
+
+
+def _bf16_bits(q):
+    v = np.float32(float(_round_binary(q, 7, -126)))  # exactly representable
+    return int(np.array([v]).view(np.uint32)[0] >> 16)
+
+
+_E4M3_CODE = {Fraction(float(DEC[c])): c for c in range(0x7F)}
+
+
+def _e4m3(q):
+    """OCP e4m3 code of an exact value: RNE to 3 fraction bits, subnormals
+    below 2^-6, saturating at 448 (zero's sign is not represented here)."""
+    r = _round_binary(q, 3, -6)
+    r = max(min(r, Fraction(448)), Fraction(-448))
+    code = _E4M3_CODE[abs(r)]
+    return code | (0x80 if r < 0 else 0)
+
+
+def test_whole_layer_in_exact_arithmetic_tiny():
+    # Every rounding point of the layer written out with exact rationals:
+    # block sums as integers (e4m3 values are multiples of 2^-9), each f32
+    # product, fma, division and sum rounded once to nearest even, the requant
+    # quotient encoded to e4m3, bf16 partials and output.  SiLU comes from the
+    # oracle's own routine (pinned above against its closed form): expf has
+    # no exact rational value.  Two K blocks on both layers exercise the
+    # accumulation, gate/up block indexing and the slot-ascending combine.
+    T, H, I, E, K = 3, 256, 256, 2, 2
+    d = small_inputs(T=T, H=H, I=I, E=E, K=K, seed=31, mask={(2, 1): -1})
+    out = run_oracle(d, want=("acc1", "h", "partial"))
+    xi = (DEC[d["x"].astype(np.int64)] * 512).astype(np.int64)
+    F = lambda v: Fraction(float(v))
+    one_e10 = F(np.float32(1e-10))
+    y_exact = np.zeros((T, H), np.uint16)
+    for t in range(T):
+        a_sum = [Fraction(0)] * H
+        for j in range(K):
+            e = int(d["idx"][t, j])
+            if e < 0:
+                continue
+            f = t * K + j
+            w1i = (DEC[d["w1"][e].astype(np.int64)] * 512).astype(np.int64)
+            # L1
+            acc = []
+            for n in range(2 * I):
+                a = Fraction(0)
+                for kb in range(H // 128):
+                    p = Fraction(int(w1i[n, kb * 128:(kb + 1) * 128] @ xi[t, kb * 128:(kb + 1) * 128]),
+                                 2 ** 18)
+                    s = _f32(F(d["x_sf"][t, kb]) * F(d["w1_sf"][e][n // 128, kb]))
+                    a = _f32(s * _f32(p) + a)
+                acc.append(a)
+                assert a == F(out["acc1"][f, n]), (t, j, n)
+            # SwiGLU (oracle routine), per-128 requant
+            hv = [Fraction(float(oracle.swiglu(float(acc[i]), float(acc[I + i]), float(d["w"][t, j]))))
+                  for i in range(I)]
+            q, sfs = [], []
+            for ib in range(I // 128):
+                blk = hv[ib * 128:(ib + 1) * 128]
+                sf = _f32(max(max(abs(v) for v in blk), one_e10) / 448)
+                sfs.append(sf)
+                q += [_e4m3(_f32(v / sf)) for v in blk]
+                assert sf == F(out["h_sf"][f, ib]), (t, j, ib)
+            got = out["h"][f].astype(np.int64)
+            want = np.array(q, np.int64)
+            zero = (got & 0x7F) == 0
+            assert np.array_equal(np.where(zero, 0, got), np.where((want & 0x7F) == 0, 0, want)), (t, j)
+            # L2 from the exact codes
+            hi = (DEC[np.array(q, np.int64)] * 512).astype(np.int64)
+            w2i = (DEC[d["w2"][e].astype(np.int64)] * 512).astype(np.int64)
+            for n in range(H):
+                a = Fraction(0)
+                for ib in range(I // 128):
+                    p = Fraction(int(w2i[n, ib * 128:(ib + 1) * 128] @ hi[ib * 128:(ib + 1) * 128]), 2 ** 18)
+                    s = _f32(sfs[ib] * F(d["w2_sf"][e][n // 128, ib]))
+                    a = _f32(s * _f32(p) + a)
+                bits = _bf16_bits(a)
+                assert bits == int(out["partial"][f, n]), (t, j, n)
+                pv = Fraction(float(bf16_bits_to_f64(np.array([bits]))[0]))
+                a_sum[n] = _f32(a_sum[n] + pv)
+        for n in range(H):
+            y_exact[t, n] = _bf16_bits(a_sum[n])
+    assert np.array_equal(out["y"], y_exact)

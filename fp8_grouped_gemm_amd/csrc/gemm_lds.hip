@@ -142,7 +142,17 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     const uint32_t meta_lds = smem_base + NSTAGE * STAGE;
     auto slot = [&](int k) { return meta_base + (k % NMETA) * META; };
     auto slot_lds = [&](int k) { return meta_lds + (k % NMETA) * META; };
-    auto tile_of = [&](int k) { return b + k * G; };
+    // Position of this workgroup within each round of G tiles.  Workgroups
+    // go to the 8 XCDs round-robin (b % 8); giving XCD x the contiguous
+    // positions [x W, x W + W) of every round keeps the tiles that share a
+    // row block's activations, and neighbouring row blocks of one expert
+    // (same weights), under one L2.  A workgroup's positions still grow with
+    // k, so tiles of unused row blocks stay a suffix of its sequence.
+    // (Measured on the pro-prefill shape: L1 fabric reads 32.1 -> 25.8 GB,
+    // L2 14.7 -> 12.5 GB against plain b + k G.)
+    const int W = G / 8;
+    const int pos = (G % 8 == 0) ? (b % 8) * W + b / 8 : b;
+    auto tile_of = [&](int k) { return pos + k * G; };
 
     if (tile_of(0) >= n_tiles)
         return;

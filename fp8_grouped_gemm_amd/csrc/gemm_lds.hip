@@ -131,7 +131,6 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     const int H = a.H, I = a.I, K = a.K, T = a.T;
     const int NT = L1 ? I / 128 : H / 256;
     const int nkb = L1 ? H / 128 : I / 128;
-    const int n_tiles = a.num_mblocks * NT;
     const int G = gridDim.x, b = blockIdx.x;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -142,19 +141,26 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     const uint32_t meta_lds = smem_base + NSTAGE * STAGE;
     auto slot = [&](int k) { return meta_base + (k % NMETA) * META; };
     auto slot_lds = [&](int k) { return meta_lds + (k % NMETA) * META; };
-    // Position of this workgroup within each round of G tiles.  Workgroups
-    // go to the 8 XCDs round-robin (b % 8); giving XCD x the contiguous
-    // positions [x W, x W + W) of every round keeps the tiles that share a
-    // row block's activations, and neighbouring row blocks of one expert
-    // (same weights), under one L2.  A workgroup's positions still grow with
-    // k, so tiles of unused row blocks stay a suffix of its sequence.
-    // (Measured on the pro-prefill shape: L1 fabric reads 32.1 -> 25.8 GB,
-    // L2 14.7 -> 12.5 GB against plain b + k G.)
+    // Tiles are numbered by position p = mb * NT + nt over the row blocks
+    // that hold routed slots (the planner's used-row count; unused row
+    // blocks are never visited).  Workgroups go to the 8 XCDs round-robin
+    // (b % 8); XCD x takes the contiguous positions [x W, x W + W) of every
+    // round of G, so the column tiles of a row block (shared activations)
+    // and neighbouring row blocks of one expert (shared weights) meet in one
+    // L2.  (Pro-prefill shape: L1 fabric reads 32.1 -> 25.8 GB, L2 14.7 ->
+    // 12.5 GB against plain b + k G; grouping row blocks column tile by
+    // column tile measured no better.)
+    const int used_mb = min(a.num_mblocks, a.status[2] / BM);
+    const int n_pos = used_mb * NT;
     const int W = G / 8;
     const int pos = (G % 8 == 0) ? (b % 8) * W + b / 8 : b;
-    auto tile_of = [&](int k) { return pos + k * G; };
+    auto tile_of = [&](int k) { return pos + k * G; };  // position of tile k
+    auto tile_at = [&](int p, int& mb, int& nt) {
+        mb = p / NT;
+        nt = p - mb * NT;
+    };
 
-    if (tile_of(0) >= n_tiles)
+    if (tile_of(0) >= n_pos)
         return;
 
     // ---- metadata copy for tile k + 1 (and the weights of tile k's rows):
@@ -164,8 +170,13 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     // A tile past the end reads tile k's (valid) rows instead: its slot is
     // never used.
     auto issue_meta = [&](int k) {
-        const int tk = tile_of(k), tn = tile_of(k + 1);
-        const int rown = (tn < n_tiles ? tn / NT : tk / NT) * BM;
+        int mbk, ntk, mbn, ntn;
+        tile_at(tile_of(k), mbk, ntk);
+        if (tile_of(k + 1) < n_pos)
+            tile_at(tile_of(k + 1), mbn, ntn);
+        else
+            mbn = mbk;
+        const int rown = mbn * BM;
         const int role = (wave == 5) ? 0 : (wave == 6) ? 1 : (wave == 7) ? 4 : wave;
         if (role <= 1 || (!L1 && role <= 3)) {
             const int h = role & 1;
@@ -189,8 +200,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     // metadata slot (landed and visible: copied with tile k - 1's first
     // block, at least two batches and one barrier ago).
     auto begin_tile = [&](int k) {
-        const int t = tile_of(k);
-        if (t >= n_tiles) {
+        if (tile_of(k) >= n_pos) {
             i_done = true;
             return;
         }
@@ -200,7 +210,9 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             i_done = true;
             return;
         }
-        const int mb = t / NT, nt = t - mb * NT, row0 = mb * BM;
+        int mb, nt;
+        tile_at(tile_of(k), mb, nt);
+        const int row0 = mb * BM;
         i_e = e;
         i_nt = nt;
         // A: wave v copies m-subtile v, both halves: rows row0 + 16 v + lr.
@@ -266,7 +278,9 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     // ---- prologue: tile 0's metadata, then blocks 0 and 1 of the stream
     {
         const int role = (wave == 5) ? 0 : (wave == 6) ? 1 : (wave == 7) ? 4 : wave;
-        const int row0 = (tile_of(0) / NT) * BM;
+        int mb0, nt0;
+        tile_at(tile_of(0), mb0, nt0);
+        const int row0 = mb0 * BM;
         if (role <= 3)
             dma4(a.row_src + row0 + 64 * (role & 1) + lane, slot_lds(0) + 256 * (role & 1));
         else
@@ -348,8 +362,9 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         // wave's fragment reads of that stage before it is overwritten, and
         // the next step's barrier orders the epilogue before the stage is
         // refilled.
-        const int t = tile_of(m_k);
-        const int mb = t / NT, nt = t - mb * NT, row0 = mb * BM;
+        int mb, nt;
+        tile_at(tile_of(m_k), mb, nt);
+        const int row0 = mb * BM;
         uint8_t* ep = smem + ((j - 1) % NSTAGE) * STAGE;
         const int32_t* m_rs = reinterpret_cast<const int32_t*>(slot(m_k));
         __syncthreads();

@@ -46,18 +46,27 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan(RouteArgs a)
     __shared__ int32_t bad_sh;
     const int e = threadIdx.x;  // E <= 1024: one expert per thread
     int total = 0, seg = 0;
+    // Column sums of the per-chunk counts, 16 loads in flight at a time.
+    auto column_sum = [&](int col) {
+        int sum = 0;
+        for (int b0 = 0; b0 < a.NB; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                c[i] = (b0 + i < a.NB) ? a.blk[(size_t)(b0 + i) * (a.E + 1) + col] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                sum += c[i];
+        }
+        return sum;
+    };
     if (e < a.E) {
-        for (int b = 0; b < a.NB; ++b)
-            total += a.blk[(size_t)b * (a.E + 1) + e];
+        total = column_sum(e);
         seg = (total + a.row_align - 1) / a.row_align * a.row_align;
         a.counts[e] = total;
     }
-    if (e == 0) {
-        int bad = 0;
-        for (int b = 0; b < a.NB; ++b)
-            bad += a.blk[(size_t)b * (a.E + 1) + a.E];
-        bad_sh = bad;
-    }
+    if (e == 0)
+        bad_sh = column_sum(a.E);
     // Inclusive Hillis-Steele scan of the aligned segment sizes.
     scan[e] = seg;
     __syncthreads();
@@ -71,13 +80,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan(RouteArgs a)
     const int used = scan[kRouteThreads - 1];
     if (e < a.E) {
         a.offsets[e] = start;
-        // Per-chunk base row of this expert's slots.
+        // Per-chunk base row of this expert's slots (the chunk counts are
+        // loaded 16 at a time, so their latencies overlap).
         int run = start;
-        for (int b = 0; b < a.NB; ++b) {
-            int32_t* p = a.blk + (size_t)b * (a.E + 1) + e;
-            int c = *p;
-            *p = run;
-            run += c;
+        int32_t* col = a.blk + e;
+        const size_t ld = (size_t)a.E + 1;
+        for (int b0 = 0; b0 < a.NB; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                c[i] = (b0 + i < a.NB) ? col[(size_t)(b0 + i) * ld] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (b0 + i < a.NB) {
+                    col[(size_t)(b0 + i) * ld] = run;
+                    run += c[i];
+                }
+            }
         }
         // Padding rows at the end of the segment.
         for (int r = start + total; r < start + seg; ++r)

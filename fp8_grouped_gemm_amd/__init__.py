@@ -51,7 +51,8 @@ class moe_tile_info_t(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int32), ("row_align", ctypes.c_int32),
                 ("pool_rows", ctypes.c_int32), ("l1_tile_n", ctypes.c_int32),
                 ("l2_tile_n", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("l1_split", ctypes.c_int32), ("single_launch", ctypes.c_int32)]
+                ("l1_split", ctypes.c_int32), ("single_launch", ctypes.c_int32),
+                ("l2_group_tiles", ctypes.c_int32)]
 
 
 class moe_ws_layout_t(ctypes.Structure):

@@ -396,14 +396,19 @@ __global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
 // L2 tile `tile`.  CO: the single-launch form (waits for the row block's
 // L1 tiles, reads h coherently, hands the partials to the combine through
 // coherent stores and the L2 done count).
-template <int MT, bool PK, bool CO>
+// WV waves per workgroup: the workgroup covers WV / 4 consecutive 256-column
+// tiles (a wave with no columns left re-reads column block 0 of the
+// expert and stores nothing).
+template <int MT, bool PK, bool CO, int WV = 4>
 __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hint)
 {
     constexpr int BM = 16 * MT;
+    constexpr int NTG = WV / 4;
     const int H = a.H, I = a.I, IB = I / 128, K = a.K, T = a.T;
     const int NT = (H + 255) / 256;  // H % 256 == 128: the last tile has 2 idle waves
-    const int mb = tile / NT;
-    const int nt = tile - mb * NT;
+    const int NG = (NT + NTG - 1) / NTG;
+    const int mb = tile / NG;
+    const int g = tile - mb * NG;
     const int e = a.mblock_expert[mb];
     if (e < 0)
         return;
@@ -413,6 +418,10 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
     const int lr = lane & 15, lg = lane >> 4;
     const int row0 = mb * BM;
     const int kb0 = 0, kb1 = IB;
+    const int nt_w = g * NTG + (wave >> 2);               // this wave's 256-column tile
+    const bool busy = nt_w < NT && nt_w * 256 + (wave & 3) * 64 < H;
+    const int nt = busy ? nt_w : 0;                       // idle waves read tile 0
+    const int w4 = wave & 3;
 
     const uint8_t* aptr[MT];
     bool avalid[MT];
@@ -430,14 +439,14 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
             asf[ms][i] = a.h_sf + (size_t)(row0 + 16 * ms + 4 * lg + i) * IB;
     // A wave's 64 columns are either all inside H or all past it; an idle
     // wave re-reads column block 0 and stores nothing.
-    const int ncol0 = (nt * 256 + wave * 64 < H) ? nt * 256 + wave * 64 : 0;
+    const int ncol0 = busy ? nt * 256 + w4 * 64 : 0;
     const uint8_t* bptr[4];
     constexpr size_t kstride = PK ? 32768 : 128;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         if constexpr (PK)
-            bptr[s] = a.w2 + (size_t)e * H * I + (size_t)nt * IB * 32768 + (wave * 4 + s) * 2048 +
-                      lane * 16;
+            bptr[s] = a.w2 + (size_t)e * H * I + (size_t)nt * IB * 32768 +
+                      ((busy ? w4 : 0) * 4 + s) * 2048 + lane * 16;
         else
             bptr[s] = a.w2 + ((size_t)e * H + ncol0 + s * 16 + lr) * I + lg * 16;
     }
@@ -492,7 +501,7 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
 
     // ---- epilogue: bf16, stage BM x 256 in LDS, 16-byte stores to the
     // (slot, token) row of the partial buffer.
-    __shared__ uint16_t ot[BM][256 + 8];
+    __shared__ uint16_t ot[BM][WV * 64 + 8];
     {
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms)
@@ -503,17 +512,18 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
                     ot[16 * ms + 4 * lg + i][wave * 64 + s * 16 + lr] = f32_to_bf16(acc[ms][s][i]);
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < BM * 32; c += 256) {
-        const int r = c >> 5, col = (c & 31) * 8;
+    const int gcol0 = g * NTG * 256;  // first column of the workgroup
+    for (int c = threadIdx.x; c < BM * WV * 8; c += WV * 64) {
+        const int r = c / (WV * 8), col = (c - r * WV * 8) * 8;
         const int f = a.row_src[row0 + r];
-        if (f >= 0 && nt * 256 + col < H) {
+        if (f >= 0 && gcol0 + col < H) {
             const int t = f / K, j = f - t * K;
             uint4 v;
             v.x = (uint32_t)ot[r][col + 0] | ((uint32_t)ot[r][col + 1] << 16);
             v.y = (uint32_t)ot[r][col + 2] | ((uint32_t)ot[r][col + 3] << 16);
             v.z = (uint32_t)ot[r][col + 4] | ((uint32_t)ot[r][col + 5] << 16);
             v.w = (uint32_t)ot[r][col + 6] | ((uint32_t)ot[r][col + 7] << 16);
-            uint16_t* dst = a.partial + ((size_t)j * T + t) * H + nt * 256 + col;
+            uint16_t* dst = a.partial + ((size_t)j * T + t) * H + gcol0 + col;
             if constexpr (CO)
                 st_co128(dst, v);
             else
@@ -530,10 +540,10 @@ __device__ __forceinline__ void l2_tile(const FwdArgs& a, int tile, int hint = 0
         count_done(a.sync + kSyncL2Done);  // every L2 item counts, idle ones too
 }
 
-template <int MT, bool PK>
-__global__ __launch_bounds__(256) void l2_direct(FwdArgs a)
+template <int MT, bool PK, int WV = 4>
+__global__ __launch_bounds__(WV * 64) void l2_direct(FwdArgs a)
 {
-    l2_tile<MT, PK, false>(a, blockIdx.x);
+    l2_tile_body<MT, PK, false, WV>(a, blockIdx.x, 0);
 }
 
 // ------------------------------------------------- L1 split-K epilogue
@@ -738,7 +748,12 @@ static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
     const unsigned tiles = a.num_mblocks * ((a.H + 255) / 256);
     switch (a.BM) {
     case 16:
-        hipLaunchKernelGGL((l2_direct<1, PK>), dim3(tiles), dim3(256), 0, s, a);
+        if (a.l2_wide) {  // two 256-column tiles per workgroup, 8 waves
+            const unsigned groups = a.num_mblocks * (((a.H + 255) / 256 + 1) / 2);
+            hipLaunchKernelGGL((l2_direct<1, PK, 8>), dim3(groups), dim3(512), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((l2_direct<1, PK, 4>), dim3(tiles), dim3(256), 0, s, a);
+        }
         break;
     case 32: hipLaunchKernelGGL((l2_direct<2, PK>), dim3(tiles), dim3(256), 0, s, a); break;
     case 64: hipLaunchKernelGGL((l2_direct<4, PK>), dim3(tiles), dim3(256), 0, s, a); break;

@@ -51,6 +51,7 @@ Config choose_config(const moe_shape_t& s, int T)
 struct Layout {
     int tile_m, kernel, r_cap, mb_cap, NB;
     int split_l1;
+    bool l2_wide;
     bool single;  // L1 + L2 + combine in one launch
     int n_sync;
     size_t sync;
@@ -81,6 +82,19 @@ long long mblocks_expected(const moe_shape_t& s, long long T)
 {
     const long long tk = T * s.top_k;
     return std::max<long long>((tk + 15) / 16, std::min<long long>(tk, s.num_experts));
+}
+
+// 16-row L2 tiles: one 8-wave workgroup per two 256-column tiles (1 MiB of
+// weights at the flash shape, like an L1 tile) streams better than one
+// 4-wave workgroup per tile when there are enough of them; with few routed
+// rows it halves an already small workgroup count (measured at the flash
+// shape: T = 128 and 32 gain ~1.7 % in L2, T = 8 loses 7 %).
+bool choose_l2_wide(const moe_shape_t& s, int T, const Config& c)
+{
+    if (c.tile_m != 16 || T <= 0)
+        return false;
+    const long long groups = mblocks_expected(s, T) * (((s.hidden + 255) / 256 + 1) / 2);
+    return groups >= 4 * kMinItems;
 }
 
 // L1 split factor of a call with T tokens and tile configuration c.
@@ -168,6 +182,7 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     // Split-K scratch: L1's f32 partials part[slice][slot][2I], slot
     // f = t*K + j.
     L.split_l1 = choose_split(s, T, c);
+    L.l2_wide = choose_l2_wide(s, T, c);
     L.part = take(sizeof(float) * splitk_floats(s, T));
     // Single-launch counters: L2 done, 3 spare, one ready count per row block.
     L.single = c.kernel == 0 && L.split_l1 == 1 &&
@@ -328,6 +343,7 @@ int moe_plan_info(moe_plan_t plan, int32_t T, moe_tile_info_t* info)
     info->kernel = L.kernel;
     info->l1_split = L.split_l1;
     info->single_launch = L.single ? 1 : 0;
+    info->l2_group_tiles = L.l2_wide ? 2 : 1;
     return MOE_OK;
 }
 
@@ -426,6 +442,7 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     a.y = y;
     a.src_row = at<int32_t>(workspace, L.src_row);
     a.split_l1 = L.split_l1;
+    a.l2_wide = L.l2_wide ? 1 : 0;
     a.splitk_slots = T * s.top_k;
     a.splitk_part = at<float>(workspace, L.part);
     a.sync = at<int32_t>(workspace, L.sync);

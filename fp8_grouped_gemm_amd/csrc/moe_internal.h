@@ -51,6 +51,7 @@ struct FwdArgs {
     // off) and their f32 partial sums, part[slice][slot][2I] for the
     // splitk_slots = T*K routed slots (slot f = t*K + j).
     int32_t split_l1;
+    int32_t l2_wide;  // 16-row L2 tiles: 1 = 8-wave workgroups over two 256-column tiles
     int32_t splitk_slots;
     float* splitk_part;
     // Single launch: counters sync[kSyncL2Done] (L2 items finished),

@@ -99,6 +99,8 @@ typedef struct moe_tile_info {
     int32_t l1_split;    /* workgroups sharing one L1 tile's K range (1 = no split;
                             16-row tiles with fewer tiles than compute units) */
     int32_t single_launch; /* 1: L1, L2 and combine run as one launch */
+    int32_t l2_group_tiles; /* L2 tiles (of l2_tile_n columns) per workgroup: 2 for
+                               16-row tiles when at least 1024 workgroups remain, else 1 */
 } moe_tile_info_t;
 
 /* Byte offsets of the workspace sections used by a forward with T tokens.

@@ -157,6 +157,14 @@ def test_split_k_choice_and_workspace_monotone_every_T(shape):
                 rows = max((T * K + 15) // 16, min(T * K, E))
                 tiles = rows * (I // 128)
                 assert (S == 1) == (tiles >= 256) or S == min(4, H // 128), (T, S, tiles)
+            # 16-row L2 tiles pair up in 8-wave workgroups once at least
+            # 1024 such workgroups are expected
+            g = info["l2_group_tiles"]
+            if info["tile_m"] == 16 and T > 0:
+                rows = max((T * K + 15) // 16, min(T * K, E))
+                assert (g == 2) == (rows * ((H // 256 + 1) // 2) >= 1024), (T, g)
+            else:
+                assert g == 1
             b = moe.moe_workspace_bytes(p, T)
             assert b >= last_b, T
             last_b = b

@@ -221,19 +221,22 @@ def test_forward_small_token_counts_split_k():
     # Flash-decode shapes with one or two tokens: fewer (row block, column
     # tile) pairs than compute units, so each L1 tile's K range is split over
     # 4 or 2 workgroups (f32 partials per routed slot, added in slice order
-    # by the epilogue kernel); from three tokens on there is no split.  Every
-    # token is checked against the oracle; packed and row-major weights must
-    # agree bit for bit.
+    # by the epilogue kernel); from three tokens on there is no split.  At
+    # 32 tokens the L2 workgroups each take two column tiles.  Every token is
+    # checked against the oracle; packed and row-major weights must agree bit
+    # for bit.
     base = wl.CONFIGS["flash_decode"]
-    full = gpu_inputs(wl.custom_config(8, base.H, base.I, base.E, base.K), wl.default_seed(base))
-    for T, split in {1: 4, 2: 2, 3: 1, 8: 1}.items():
+    full = gpu_inputs(wl.custom_config(32, base.H, base.I, base.E, base.K), wl.default_seed(base))
+    for T, (split, l2g) in {1: (4, 1), 2: (2, 1), 3: (1, 1), 8: (1, 1), 32: (1, 2)}.items():
         inp = dict(full)
         for k in ("x", "x_sf", "topk_idx", "topk_w"):
             inp[k] = full[k][:T].contiguous()
         y_row, runner = run_gpu(inp)
         info = moe.moe_plan_info(runner.plan, T)
-        say(f"  T={T}: tile {info['tile_m']}, L1 split {info['l1_split']}")
+        say(f"  T={T}: tile {info['tile_m']}, L1 split {info['l1_split']}, "
+            f"L2 tiles/workgroup {info['l2_group_tiles']}")
         assert info["tile_m"] == 16 and info["l1_split"] == split
+        assert info["l2_group_tiles"] == l2g
         y_pk, _ = run_gpu(inp, weight_layout=moe.MOE_WEIGHTS_PACKED)
         assert torch.equal(y_row, y_pk), T
         toks = list(range(T))

@@ -7,7 +7,15 @@ in HBM.  Prints ONE JSON line.  The default workload is the DeepSeek
 256 experts all resident, top-6, uniform routing.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--tokens T] [--no-cpu-baseline]
-                  [--flush MIB] [--launch auto|single|split] [--weights packed|row_major]
+                  [--flush MIB] [--no-peaks] [--launch auto|single|split]
+                  [--weights packed|row_major]
+
+Beside the timed steps it measures, unless told not to, (a) the same call
+with caches flushed before each call (3 observations of K calls; median of
+the per-observation medians and the range), and (b) the ceilings this GPU
+sustains: a streaming HBM read and a dense FP8 MFMA loop (libmoe_peaks.so),
+best of a small sweep of launch shapes; the roofline is then stated against
+both the published and the measured peak.
 """
 import argparse
 import json
@@ -86,6 +94,59 @@ def time_oracle_sample(inp, cfg, n_tokens, seed):
     return per_layer_us, threads, dt, f"{len(toks)} of {cfg.T} tokens ({len(toks) * cfg.K} slots), extrapolated linearly in tokens"
 
 
+def measure_peaks(torch, dev, stream, read_gib=4, reps=3):
+    """Best streaming-read GB/s and FP8 MFMA TFLOP/s over a small sweep."""
+    from fp8_grouped_gemm_amd import peaks
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def best_ms(launch):
+        launch()
+        ts = []
+        for _ in range(reps):
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    nbytes = read_gib << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(4 * 16 * cus, dtype=torch.int32, device=dev)
+    read = {"gbs": 0.0}
+    for mode in (peaks.MOE_PEAK_READ_PLAIN, peaks.MOE_PEAK_READ_NONTEMPORAL):
+        for unroll in (4, 8):
+            for per_cu in (2, 4, 8, 16):
+                ms = best_ms(lambda: peaks.stream_read(buf, per_cu * cus, out, unroll=unroll,
+                                                       mode=mode, stream=stream))
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                if gbs > read["gbs"]:
+                    read = {"gbs": gbs, "workgroups_per_cu": per_cu, "unroll": unroll,
+                            "nontemporal": bool(mode)}
+    del buf, out
+    mf = {"tflops": 0.0}
+    iters = 2048
+    fout = torch.empty(256 * 8 * cus, dtype=torch.float32, device=dev)
+    for per_cu in (1, 2, 4, 8):
+        blocks = per_cu * cus
+        ms = best_ms(lambda: peaks.mfma_fp8(blocks, iters, fout, stream=stream))
+        tf = peaks.mfma_flop(blocks, iters) / (ms * 1e-3) / 1e12
+        if tf > mf["tflops"]:
+            mf = {"tflops": tf, "workgroups_per_cu": per_cu}
+    del fout
+    return {
+        "hbm_read_gbs": round(read["gbs"], 1),
+        "hbm_read_launch": {k: v for k, v in read.items() if k != "gbs"},
+        "hbm_read_bytes": nbytes,
+        "mfma_fp8_tflops": round(mf["tflops"], 1),
+        "mfma_launch": {"workgroups_per_cu": mf["workgroups_per_cu"], "rounds": iters,
+                        "instruction": "v_mfma_f32_16x16x128_f8f6f4, 8 independent per wave"},
+        "method": f"best of {reps} timed launches per shape after one untimed; HIP events",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,10 +161,16 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(the reference kernel for scaling HBM byte counters) and exit")
-    ap.add_argument("--flush", type=int, default=0, metavar="MIB",
+    ap.add_argument("--flush", type=int, default=1024, metavar="MIB",
                     help="also time each step alone after writing a MIB MiB scratch buffer "
-                         "(evicts the 256 MB MALL and the L2s); adds a 'cold' object with the "
-                         "median and range of those per-step times")
+                         "(evicts the 256 MB MALL and the L2s), in 3 observations of K "
+                         "steps; adds a 'cold' object with the median of the observation "
+                         "medians and the range (0 = skip)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the streaming-read and FP8 MFMA ceilings")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="only measure the streaming-read and FP8 MFMA ceilings, print them "
+                         "as one JSON line and exit")
     ap.add_argument("--launch", choices=("auto", "single", "split"), default="auto",
                     help="single: L1, L2 and combine in one cooperative launch (direct "
                          "tiles); split: one launch per step; auto: the library's choice")
@@ -130,6 +197,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_dispatch": n}), flush=True)
+        return
+
+    if args.peaks_only:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        print(json.dumps({"achievable": measure_peaks(torch, dev, torch.cuda.current_stream())}),
+              flush=True)
         return
 
     cfg = wl.CONFIGS[args.workload]
@@ -251,22 +325,40 @@ def main():
         "cpu_baseline": None,
     }
     if args.flush:
+        print("[bench] cold-cache observations", file=sys.stderr, flush=True)
         scratch = torch.empty(args.flush << 20, dtype=torch.uint8, device=dev)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        cold = []
-        for _ in range(args.steps):
-            scratch.fill_(1)
-            e0.record(stream)
-            moe.moe_forward(runner.plan, cfg.T, *fwd_args, stream=stream)
-            e1.record(stream)
-            e1.synchronize()
-            cold.append(e0.elapsed_time(e1) * 1e3)
-        cold.sort()
-        line["cold"] = {"flush_mib": args.flush, "median_us": round(cold[len(cold) // 2], 2),
-                        "min_us": round(cold[0], 2), "max_us": round(cold[-1], 2),
-                        "steps": len(cold)}
+        medians, every = [], []
+        for _ in range(3):
+            obs = []
+            for _ in range(args.steps):
+                scratch.fill_(1)
+                e0.record(stream)
+                moe.moe_forward(runner.plan, cfg.T, *fwd_args, stream=stream)
+                e1.record(stream)
+                e1.synchronize()
+                obs.append(e0.elapsed_time(e1) * 1e3)
+            obs.sort()
+            medians.append(obs[len(obs) // 2])
+            every += obs
+        medians.sort()
+        line["cold"] = {"flush_mib": args.flush, "median_us": round(medians[1], 2),
+                        "observation_medians_us": [round(m, 2) for m in medians],
+                        "min_us": round(min(every), 2), "max_us": round(max(every), 2),
+                        "steps_per_observation": args.steps}
         del scratch
+    if not args.no_peaks:
+        print("[bench] measuring the read and MFMA ceilings", file=sys.stderr, flush=True)
+        pk = measure_peaks(torch, dev, stream)
+        line["achievable"] = pk
+        rl = line["roofline"]
+        rl["achievable_peak"] = pk["hbm_read_gbs"]
+        rl["frac_of_achievable"] = round(rl["achieved"] / pk["hbm_read_gbs"], 4)
+        t_hbm_meas = bytes_total / (pk["hbm_read_gbs"] * 1e9) * 1e6
+        t_mfma_meas = flops / (pk["mfma_fp8_tflops"] * 1e12) * 1e6
+        line["pct_hbm_achievable"] = round(100 * t_hbm_meas / us_per_layer, 2)
+        line["pct_mfma_achievable"] = round(100 * t_mfma_meas / us_per_layer, 2)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         us, threads, secs, sample = time_oracle_sample(inp, cfg, args.cpu_sample_tokens, seed)

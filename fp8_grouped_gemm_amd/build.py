@@ -1,4 +1,5 @@
-"""Build the HIP library libmoe_fp8.so in-tree for gfx950 with hipcc."""
+"""Build the HIP libraries in-tree for gfx950 with hipcc: libmoe_fp8.so (the
+MoE forward) and libmoe_peaks.so (the ceiling-measurement kernels)."""
 import os
 import shutil
 import subprocess
@@ -9,6 +10,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_fp8.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["moe_api.cpp", "route.hip", "gemm_direct.hip", "gemm_lds.hip", "pack.hip"]
+PEAKS_LIB = os.path.join(HERE, "libmoe_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 instructions are disabled for every device pass.
@@ -17,10 +20,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I" + os.path.join(HERE, "..", "include"), "-Wall"]
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def _compile(sources, verbose):
     objs, procs = [], []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
@@ -28,8 +30,25 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
                                             stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)
+    return objs, procs
+
+
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (all in parallel) and link both libraries."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs, procs = _compile(SOURCES, verbose)
+    peak_objs, peak_procs = _compile(PEAKS_SOURCES, verbose)
     failed = False
-    for src, p in procs:
+    for src, p in procs + peak_procs:
         out, _ = p.communicate()
         if out.strip() and (verbose or p.returncode):
             sys.stdout.write(out)
@@ -38,12 +57,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             sys.stdout.write(f"hipcc failed on {src}\n")
     if failed:
         raise RuntimeError("HIP build failed")
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    _link(objs, LIB, verbose)
+    _link(peak_objs, PEAKS_LIB, verbose)
     return LIB
 
 

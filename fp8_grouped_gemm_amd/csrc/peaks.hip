@@ -1,0 +1,136 @@
+// Ceiling measurements for MI355X (gfx950): a streaming HBM read and a dense
+// FP8 MFMA loop.  The MoE kernels are bound by one or the other, so their
+// rates are reported against these measured ceilings beside the published
+// ones.  C ABI in include/moe_peaks.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <cstring>
+
+#include "moe_peaks.h"
+#include "moe_device.h"
+
+namespace {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Each lane keeps U 16-byte loads in flight: one round of a workgroup covers
+// U * 256 consecutive 16-byte words, lane l taking words l, l + 256, ...;
+// workgroups take rounds b, b + G, ....  Full rounds load unconditionally;
+// the one partial round at the end checks each word.
+template <int U, bool NT>
+__global__ void __launch_bounds__(256) stream_read(const v4u* __restrict__ p, size_t n,
+                                                   uint32_t* __restrict__ out)
+{
+    const size_t round = (size_t)256 * U;
+    const size_t stride = (size_t)gridDim.x * round;
+    const size_t full = n / round * round;  // words covered by full rounds
+    uint32_t acc = 0;
+    size_t base = (size_t)blockIdx.x * round;
+    for (; base < full; base += stride) {
+        v4u v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const v4u* q = p + base + (size_t)u * 256 + threadIdx.x;
+            v[u] = NT ? __builtin_nontemporal_load(q) : *q;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (base < n) {  // the partial round, if any, falls to exactly one workgroup
+        for (int u = 0; u < U; ++u) {
+            const size_t j = base + (size_t)u * 256 + threadIdx.x;
+            if (j < n) {
+                const v4u v = p[j];
+                acc ^= v.x ^ v.y ^ v.z ^ v.w;
+            }
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1)
+        acc ^= __shfl_xor(acc, o);
+    if ((threadIdx.x & 63) == 0)
+        out[blockIdx.x * 4 + threadIdx.x / 64] = acc;
+}
+
+// 8 independent accumulators per wave, so consecutive MFMAs never wait on
+// each other's results.
+__global__ void __launch_bounds__(256) mfma_fp8_loop(int iters, float* __restrict__ out)
+{
+    using moe::v4f;
+    using moe::v8i;
+    const int ones = 0x38383838;    // e4m3 1.0 in every byte
+    const int halves = 0x30303030;  // e4m3 0.5
+    // The operands come from a lane-dependent expression so the compiler
+    // cannot treat the loop as constant.
+    const int lane_zero = (int)(threadIdx.x >> 8);  // 0 for every lane of a 256-lane block
+    const v8i a = {ones + lane_zero, ones, ones, ones, ones, ones, ones, ones};
+    const v8i b = {halves + lane_zero, halves, halves, halves, halves, halves, halves, halves};
+    // eight named accumulators: an array here made the register allocator
+    // shuffle accumulator registers inside the loop
+    v4f c0{}, c1{}, c2{}, c3{}, c4{}, c5{}, c6{}, c7{};
+    for (int i = 0; i < iters; ++i) {
+        c0 = moe::mfma_16x16x128_e4m3(a, b, c0);
+        c1 = moe::mfma_16x16x128_e4m3(a, b, c1);
+        c2 = moe::mfma_16x16x128_e4m3(a, b, c2);
+        c3 = moe::mfma_16x16x128_e4m3(a, b, c3);
+        c4 = moe::mfma_16x16x128_e4m3(a, b, c4);
+        c5 = moe::mfma_16x16x128_e4m3(a, b, c5);
+        c6 = moe::mfma_16x16x128_e4m3(a, b, c6);
+        c7 = moe::mfma_16x16x128_e4m3(a, b, c7);
+    }
+    const v4f t = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+    out[blockIdx.x * 256 + threadIdx.x] = (t.x + t.y) + (t.z + t.w);
+}
+
+int device_is_gfx950()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MOE_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return MOE_ERR_HIP;
+    return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? MOE_OK : MOE_ERR_NOT_GFX950;
+}
+
+}  // namespace
+
+extern "C" int moe_peak_stream_read(const void* buf, size_t bytes, int32_t blocks, int32_t unroll,
+                                    int32_t mode, uint32_t* out, void* stream)
+{
+    if (!buf || !out || (reinterpret_cast<uintptr_t>(buf) & 15) || bytes == 0 || (bytes & 15) ||
+        blocks < 1 || blocks > 65536 || (unroll != 4 && unroll != 8) ||
+        (mode != MOE_PEAK_READ_PLAIN && mode != MOE_PEAK_READ_NONTEMPORAL))
+        return MOE_ERR_INVALID_ARG;
+    const int dev = device_is_gfx950();
+    if (dev != MOE_OK)
+        return dev;
+    const v4u* p = static_cast<const v4u*>(buf);
+    const size_t n = bytes / 16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool nt = mode == MOE_PEAK_READ_NONTEMPORAL;
+    if (unroll == 4) {
+        if (nt)
+            hipLaunchKernelGGL((stream_read<4, true>), dim3(blocks), dim3(256), 0, s, p, n, out);
+        else
+            hipLaunchKernelGGL((stream_read<4, false>), dim3(blocks), dim3(256), 0, s, p, n, out);
+    } else {
+        if (nt)
+            hipLaunchKernelGGL((stream_read<8, true>), dim3(blocks), dim3(256), 0, s, p, n, out);
+        else
+            hipLaunchKernelGGL((stream_read<8, false>), dim3(blocks), dim3(256), 0, s, p, n, out);
+    }
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" int moe_peak_mfma_fp8(int32_t blocks, int32_t iters, float* out, void* stream)
+{
+    if (!out || blocks < 1 || blocks > 65536 || iters < 1 || iters > 2048)
+        return MOE_ERR_INVALID_ARG;
+    const int dev = device_is_gfx950();
+    if (dev != MOE_OK)
+        return dev;
+    hipLaunchKernelGGL(mfma_fp8_loop, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       iters, out);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}

@@ -10,10 +10,11 @@ import fp8_grouped_gemm_amd as moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_fp8.h")
+PEAKS_HEADER = os.path.join(ROOT, "include", "moe_peaks.h")
 
 
-def declared_symbols():
-    text = open(HEADER).read()
+def declared_symbols(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^(?:int|const char\*|size_t)\s+(moe_\w+)\s*\(", text, re.M)))
 
 
@@ -26,6 +27,35 @@ def test_library_exports_every_declared_symbol():
     for name in declared_symbols():
         assert hasattr(L, name), name
     assert L.moe_version() >= 1
+
+
+def test_peaks_library_exports_every_declared_symbol():
+    from fp8_grouped_gemm_amd import peaks
+    assert declared_symbols(PEAKS_HEADER) == sorted(peaks.EXPORTED_SYMBOLS)
+    L = peaks.lib()
+    for name in peaks.EXPORTED_SYMBOLS:
+        assert hasattr(L, name), name
+
+
+def test_peaks_reject_invalid_arguments_on_host():
+    # every case fails the host checks, before the device is queried
+    from fp8_grouped_gemm_amd import peaks
+    L = peaks.lib()
+    buf, out = ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20)
+    bad_reads = [
+        (None, 1 << 20, 256, 8, 1, out),                   # null buffer
+        (buf, 1 << 20, 256, 8, 1, None),                   # null out
+        (ctypes.c_void_p((1 << 20) + 8), 1 << 20, 256, 8, 1, out),  # misaligned
+        (buf, 0, 256, 8, 1, out), (buf, 1000, 256, 8, 1, out),      # size
+        (buf, 1 << 20, 0, 8, 1, out), (buf, 1 << 20, 65537, 8, 1, out),  # blocks
+        (buf, 1 << 20, 256, 2, 1, out), (buf, 1 << 20, 256, 16, 1, out),  # unroll
+        (buf, 1 << 20, 256, 8, 2, out), (buf, 1 << 20, 256, 8, -1, out),  # mode
+    ]
+    for a in bad_reads:
+        assert L.moe_peak_stream_read(*a, None) == moe.MOE_ERR_INVALID_ARG, a
+    for blocks, iters, o in [(0, 16, out), (65537, 16, out), (256, 0, out), (256, 2049, out),
+                             (256, 16, None)]:
+        assert L.moe_peak_mfma_fp8(blocks, iters, o, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_strerror_names_every_code():

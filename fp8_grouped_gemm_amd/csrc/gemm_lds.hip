@@ -216,8 +216,12 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         i_e = e;
         i_nt = nt;
         // A: wave v copies m-subtile v, both halves: rows row0 + 16 v + lr.
-        const int r = row0 + wave * 16 + lr;
+        // Padding rows (f < 0) copy a valid row instead (L1: token 0; L2:
+        // the block's first row, which always holds a routed slot), so their
+        // lanes share cache lines with others; their products land only in
+        // padding rows of the accumulator, which are never stored.
         const int f = reinterpret_cast<const int32_t*>(slot(k))[wave * 16 + lr];
+        const int r = f >= 0 ? row0 + wave * 16 + lr : row0;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             if constexpr (L1)

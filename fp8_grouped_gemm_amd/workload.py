@@ -17,6 +17,12 @@ the DeepGEMM MegaMoE pages benchmark: DeepSeek "Flash" 4096/2048/256/top-6,
            the K selected logits.
 Every tensor comes from its own torch.Generator seeded from (seed, tag,
 expert), so any expert's weights can be redrawn alone.
+
+The FP8 x MXFP4 inputs (make_inputs_mx) quantise the same f32 draws with
+one power-of-two (UE8M0) scale per 1x32 block: x to e4m3 with
+sf = 2^ceil(log2(max(amax, 1e-10)/448)), weights to e2m1 (round to nearest,
+ties to the even code) with sf = 2^ceil(log2(max(amax, 1e-10)/6)), packed
+two per byte with the even element in the low nibble.
 """
 from dataclasses import dataclass
 
@@ -70,6 +76,42 @@ def quantize_blocks(v: torch.Tensor, br: int, bc: int):
     q = torch.clamp(blk / sf[:, None, :, None], -448.0, 448.0)
     q = q.reshape(R, C).to(torch.float8_e4m3fn).view(torch.uint8)
     return q.contiguous(), sf.to(torch.float32).contiguous()
+
+
+_E2M1_MID = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)  # midpoints of 0,.5,1,1.5,2,3,4,6
+
+
+def _pow2_ceil_code(s: torch.Tensor) -> torch.Tensor:
+    """UE8M0 code (int32) of the smallest power of two >= s, for s > 0."""
+    m, e = torch.frexp(s)  # s = m * 2^e, 0.5 <= m < 1
+    return torch.where(m == 0.5, e - 1, e).to(torch.int32) + 127
+
+
+def quantize_mx_e4m3(v: torch.Tensor):
+    """[R,C] f32 -> e4m3 codes [R,C] u8 + UE8M0 scale codes [R,C/32] u8."""
+    R, C = v.shape
+    blk = v.reshape(R, C // 32, 32)
+    code = _pow2_ceil_code(torch.clamp(blk.abs().amax(-1), min=1e-10) / 448.0)
+    sf = torch.ldexp(torch.ones_like(blk[..., 0]), code - 127)
+    q = torch.clamp(blk / sf[..., None], -448.0, 448.0).reshape(R, C)
+    return (q.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(),
+            code.to(torch.uint8).contiguous())
+
+
+def quantize_mx_e2m1(v: torch.Tensor):
+    """[R,C] f32 -> packed e2m1 [R,C/2] u8 + UE8M0 scale codes [R,C/32] u8."""
+    R, C = v.shape
+    blk = v.reshape(R, C // 32, 32)
+    code = _pow2_ceil_code(torch.clamp(blk.abs().amax(-1), min=1e-10) / 6.0)
+    sf = torch.ldexp(torch.ones_like(blk[..., 0]), code - 127)
+    a = (blk / sf[..., None]).reshape(R, C)
+    mag = a.abs().clamp(max=6.0)
+    mid = torch.tensor(_E2M1_MID, dtype=a.dtype, device=a.device)
+    lo = torch.bucketize(mag, mid)  # number of midpoints below mag
+    tie = (lo < 7) & (mag == mid[lo.clamp(max=6)]) & (lo % 2 == 1)
+    c4 = (lo + tie.to(lo.dtype)) | ((a < 0).to(lo.dtype) << 3)
+    packed = (c4[:, 0::2] | (c4[:, 1::2] << 4)).to(torch.uint8)
+    return packed.contiguous(), code.to(torch.uint8).contiguous()
 
 
 def make_routing(cfg: MoEConfig, seed: int, device="cpu"):
@@ -126,6 +168,50 @@ def make_inputs(cfg: MoEConfig, seed: int, device="cpu"):
     x, x_sf = make_x(cfg, seed, device)
     idx, w = make_routing(cfg, seed, device)
     w1, w1_sf, w2, w2_sf = make_weights(cfg, seed, device)
+    return dict(x=x, x_sf=x_sf, topk_idx=idx, topk_w=w, w1=w1, w1_sf=w1_sf,
+                w2=w2, w2_sf=w2_sf)
+
+
+def make_x_mx(cfg: MoEConfig, seed: int, device="cpu"):
+    g = _gen(device, seed, TAG_X)
+    x = torch.randn(cfg.T, cfg.H, generator=g, device=device, dtype=torch.float32)
+    return quantize_mx_e4m3(x)
+
+
+def make_expert_mx(cfg: MoEConfig, seed: int, e: int, device="cpu"):
+    """(w1 [2I,H/2] u8, w1_sf [2I,H/32] u8, w2 [H,I/2] u8, w2_sf [H,I/32] u8)."""
+    g1 = _gen(device, seed, TAG_W1, e)
+    w1 = torch.randn(2 * cfg.I, cfg.H, generator=g1, device=device,
+                     dtype=torch.float32) * (1.0 / cfg.H ** 0.5)
+    q1, s1 = quantize_mx_e2m1(w1)
+    del w1
+    g2 = _gen(device, seed, TAG_W2, e)
+    w2 = torch.randn(cfg.H, cfg.I, generator=g2, device=device,
+                     dtype=torch.float32) * (1.0 / cfg.I ** 0.5)
+    q2, s2 = quantize_mx_e2m1(w2)
+    return q1, s1, q2, s2
+
+
+def make_weights_mx(cfg: MoEConfig, seed: int, device="cpu"):
+    """All experts stacked: w1 [E,2I,H/2], w1_sf [E,2I,H/32], w2 [E,H,I/2], w2_sf [E,H,I/32]."""
+    E, H, I = cfg.E, cfg.H, cfg.I
+    w1 = torch.empty(E, 2 * I, H // 2, dtype=torch.uint8, device=device)
+    w1_sf = torch.empty(E, 2 * I, H // 32, dtype=torch.uint8, device=device)
+    w2 = torch.empty(E, H, I // 2, dtype=torch.uint8, device=device)
+    w2_sf = torch.empty(E, H, I // 32, dtype=torch.uint8, device=device)
+    for e in range(E):
+        q1, s1, q2, s2 = make_expert_mx(cfg, seed, e, device)
+        w1[e].copy_(q1)
+        w1_sf[e].copy_(s1)
+        w2[e].copy_(q2)
+        w2_sf[e].copy_(s2)
+    return w1, w1_sf, w2, w2_sf
+
+
+def make_inputs_mx(cfg: MoEConfig, seed: int, device="cpu"):
+    x, x_sf = make_x_mx(cfg, seed, device)
+    idx, w = make_routing(cfg, seed, device)
+    w1, w1_sf, w2, w2_sf = make_weights_mx(cfg, seed, device)
     return dict(x=x, x_sf=x_sf, topk_idx=idx, topk_w=w, w1=w1, w1_sf=w1_sf,
                 w2=w2, w2_sf=w2_sf)
 

@@ -54,6 +54,23 @@ def lib():
             + [ctypes.c_int, _i32p, _u16p, _f32p, _f32p, _u8p, _f32p, _u16p,
                ctypes.c_int, ctypes.c_int])
         L.orc_max_threads.restype = ctypes.c_int
+        L.orc_e2m1_decode.restype = ctypes.c_float
+        L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_decode.restype = ctypes.c_double
+        L.orc_e8m0_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_ceil.restype = ctypes.c_uint8
+        L.orc_e8m0_ceil.argtypes = [ctypes.c_float]
+        L.orc_mx_dot.restype = ctypes.c_double
+        L.orc_mx_dot.argtypes = [_u8p, _u8p, _u8p, _u8p, ctypes.c_int]
+        L.orc_requant_block_mx.restype = None
+        L.orc_requant_block_mx.argtypes = [_f32p, ctypes.c_int, _u8p, _u8p]
+        L.orc_moe_forward_mx.restype = ctypes.c_int
+        L.orc_moe_forward_mx.argtypes = (
+            [ctypes.c_int] * 5
+            + [_u8p, _u8p, _i32p, _f32p]
+            + [ctypes.POINTER(ctypes.c_void_p)] * 4
+            + [ctypes.c_int, _i32p, _u16p, _f32p, _f32p, _u8p, _u8p, _u16p,
+               ctypes.c_int, ctypes.c_int])
         _lib = L
     return _lib
 
@@ -96,6 +113,34 @@ def requant_block(v: np.ndarray):
     q = np.zeros(v.size, np.uint8)
     sf = ctypes.c_float(0)
     lib().orc_requant_block(_p(v, _f32p), v.size, _p(q, _u8p), ctypes.byref(sf))
+    return q, sf.value
+
+
+def e2m1_decode(code: int) -> float:
+    return lib().orc_e2m1_decode(int(code) & 0xF)
+
+
+def e8m0_decode(code: int) -> float:
+    return lib().orc_e8m0_decode(int(code) & 0xFF)
+
+
+def e8m0_ceil(s: float) -> int:
+    return lib().orc_e8m0_ceil(float(s))
+
+
+def mx_dot(a, sa, b_packed, sb) -> float:
+    """MX GEMM element: e4m3 a [n], UE8M0 sa [n/32], packed e2m1 b [n/2], sb [n/32]."""
+    a, sa, b, sb = (np.ascontiguousarray(v, dtype=np.uint8) for v in (a, sa, b_packed, sb))
+    assert a.size % 32 == 0 and b.size * 2 == a.size and sa.size == sb.size == a.size // 32
+    return lib().orc_mx_dot(_p(a, _u8p), _p(sa, _u8p), _p(b, _u8p), _p(sb, _u8p), a.size)
+
+
+def requant_block_mx(v: np.ndarray):
+    """Power-of-two-scaled e4m3 requantisation: (codes, UE8M0 scale code)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    q = np.zeros(v.size, np.uint8)
+    sf = ctypes.c_uint8(0)
+    lib().orc_requant_block_mx(_p(v, _f32p), v.size, _p(q, _u8p), ctypes.byref(sf))
     return q, sf.value
 
 
@@ -187,6 +232,64 @@ def moe_forward(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
         out["h_sf"] = h_sf
     if partial is not None:
         out["partial"] = partial
+    return out
+
+
+def moe_forward_mx(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
+                   flags=0, want=(), nthreads=0):
+    """Oracle forward of the FP8 x MXFP4 recipe (see moe_oracle.c).
+
+    x [T,H] e4m3, x_sf [T,H/32] UE8M0; per expert w1 [2I,H/2] packed e2m1,
+    w1_sf [2I,H/32], w2 [H,I/2], w2_sf [H,I/32] (None for unused experts).
+    Same outputs as moe_forward; "h" comes with "h_sf" [n*K, I/32] UE8M0.
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    x_sf = np.ascontiguousarray(x_sf, dtype=np.uint8)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    wts = np.ascontiguousarray(topk_w, dtype=np.float32)
+    T, H = x.shape
+    K = idx.shape[1]
+    E = len(w1)
+    keep = []
+
+    def ptrs(seq):
+        arr = (ctypes.c_void_p * E)()
+        for e, a in enumerate(seq):
+            if a is None:
+                arr[e] = None
+            else:
+                a = np.ascontiguousarray(a, dtype=np.uint8)
+                keep.append(a)
+                arr[e] = a.ctypes.data
+        return arr
+
+    I = next((a.shape[-1] * 2 for a in w2 if a is not None), None)
+    if I is None:
+        I = next((a.shape[0] // 2 for a in w1 if a is not None), 128)
+    p1, p1s, p2, p2s = ptrs(w1), ptrs(w1_sf), ptrs(w2), ptrs(w2_sf)
+    if tokens is None:
+        toks, n = None, T
+    else:
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = toks.size
+    y = np.zeros((n, H), np.uint16)
+    y_f32 = np.zeros((n, H), np.float32) if "y_f32" in want else None
+    acc1 = np.zeros((n * K, 2 * I), np.float32) if "acc1" in want else None
+    h = np.zeros((n * K, I), np.uint8) if "h" in want else None
+    h_sf = np.zeros((n * K, I // 32), np.uint8) if "h" in want else None
+    partial = np.zeros((n * K, H), np.uint16) if "partial" in want else None
+    rc = lib().orc_moe_forward_mx(
+        T, H, I, E, K, _p(x, _u8p), _p(x_sf, _u8p), _p(idx, _i32p), _p(wts, _f32p),
+        p1, p1s, p2, p2s, n, _p(toks, _i32p), _p(y, _u16p), _p(y_f32, _f32p),
+        _p(acc1, _f32p), _p(h, _u8p), _p(h_sf, _u8p), _p(partial, _u16p),
+        int(flags), int(nthreads))
+    if rc < 0:
+        raise ValueError("oracle: invalid shape or missing expert weights")
+    out = {"y": y, "n_bad": rc}
+    for k, v in (("y_f32", y_f32), ("acc1", acc1), ("h", h), ("h_sf", h_sf),
+                 ("partial", partial)):
+        if v is not None:
+            out[k] = v
     return out
 
 

@@ -39,6 +39,24 @@
  *              (masked) or >= E (out of range) contribute nothing; a token
  *              with no active slot gets y = 0.
  *
+ * Second recipe, FP8 activations x MXFP4 weights ("07 · MegaMoE" §0 and the
+ * "MegaMoE SM90 Implementation Design" §2.1/§15.2 contrast of the SM100
+ * kernel: e4m3 activations, e2m1 weights, one UE8M0 scale per 32 K values,
+ * recipe (1,1,32), and the L1 epilogue's per-block UE8M0 scale for the
+ * requantised intermediate).  Readings where the pages are silent:
+ *   - scales apply per element inside the sum (they are the MX block
+ *     scales of both operands); the GEMM value is the sum over all of K,
+ *     each 32-block's sum exact, the blocks added in ascending order in
+ *     binary64, rounded once to f32 -- the exact sum whenever a row's block
+ *     sums span fewer than 53 bits, as for every input drawn here (checked
+ *     against exact rationals);
+ *   - the intermediate uses the same 1x32 blocks as the activations, with
+ *     sf = the smallest power of two >= max(amax, 1e-10)/448 (PR #440 "How
+ *     it works" names rounding the scale up to a power of two as #383's
+ *     choice; a power of two is what a UE8M0 code can hold), q = e4m3(h/sf);
+ *   - e2m1 pairs are packed two per byte, element k in byte k/2, the even
+ *     element in the low nibble; UE8M0 code c means 2^(c-127), 0xFF is NaN.
+ *
  * Pins: every function here is checked by tests/test_oracle_pins.py against
  * closed forms, library codecs, an fp64 unquantised MoE, a dense SwiGLU FFN
  * written separately, brute-force routing and exact rational arithmetic.
@@ -222,7 +240,144 @@ void orc_requant_block(const float* v, int n, uint8_t* q, float* sf_out)
     *sf_out = sf;
 }
 
+/* ------------------------------------------ MX codecs and block scaling */
+
+/* OCP E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0, no
+ * infinities or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Only the low
+ * nibble of `code` is read. */
+float orc_e2m1_decode(uint8_t code)
+{
+    int sign = (code >> 3) & 1;
+    int exp = (code >> 1) & 3;
+    int man = code & 1;
+    float mag = exp == 0 ? 0.5f * (float)man : ldexpf(1.0f + 0.5f * (float)man, exp - 1);
+    return sign ? -mag : mag;
+}
+
+/* Element k of a row of packed e2m1 pairs. */
+static float e2m1_at(const uint8_t* row, int k)
+{
+    uint8_t b = row[k >> 1];
+    return orc_e2m1_decode((k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0xF));
+}
+
+/* UE8M0: value 2^(code - 127); code 0xFF is NaN. */
+double orc_e8m0_decode(uint8_t code)
+{
+    if (code == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+/* The smallest power of two >= s (s > 0), as a UE8M0 code; found by search
+ * over the codes so that it is the definition. */
+uint8_t orc_e8m0_ceil(float s)
+{
+    for (int c = 0; c < 0xFF; ++c)
+        if (orc_e8m0_decode((uint8_t)c) >= (double)s)
+            return (uint8_t)c;
+    return 0xFE;
+}
+
+/* One output element of an MX GEMM:
+ *   sum over k of (e4m3(a[k]) * 2^(sa[k/32]-127)) * (e2m1(b[k]) * 2^(sb[k/32]-127))
+ * Each 32-term block sum is exact in binary64 (products are multiples of
+ * 2^-10 of magnitude below 2688), scaling it by a power of two is exact,
+ * and the blocks are added in ascending order in binary64.  NaN if a scale
+ * code is 0xFF. */
+double orc_mx_dot(const uint8_t* a, const uint8_t* sa, const uint8_t* b_packed,
+                  const uint8_t* sb, int n)
+{
+    double s = 0.0;
+    for (int blk = 0; blk < n / 32; ++blk) {
+        if (sa[blk] == 0xFF || sb[blk] == 0xFF)
+            return NAN;
+        double p = 0.0;
+        for (int c = 32 * blk; c < 32 * blk + 32; ++c)
+            p += (double)orc_e4m3_decode(a[c]) * (double)e2m1_at(b_packed, c);
+        s += ldexp(p, (int)sa[blk] + (int)sb[blk] - 254);
+    }
+    return s;
+}
+
+/* Test-only: the same sum for an f32 activation row (requantisation off). */
+static double mx_dot_f32(const float* a, const uint8_t* b_packed, const uint8_t* sb, int n)
+{
+    double s = 0.0;
+    for (int blk = 0; blk < n / 32; ++blk) {
+        double p = 0.0;
+        for (int c = 32 * blk; c < 32 * blk + 32; ++c)
+            p += (double)a[c] * (double)e2m1_at(b_packed, c);
+        s += ldexp(p, (int)sb[blk] - 127);
+    }
+    return s;
+}
+
+/* Requantisation of n values to e4m3 with one power-of-two scale:
+ * s = max(amax, 1e-10)/448 (f32 division), sf = the smallest power of two
+ * >= s, q[i] = e4m3(v[i] / sf) (an exact scaling, then the e4m3 rounding). */
+void orc_requant_block_mx(const float* v, int n, uint8_t* q, uint8_t* sf_code)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i)
+        amax = fmaxf(amax, fabsf(v[i]));
+    float s = fmaxf(amax, 1e-10f) / 448.0f;
+    uint8_t c = orc_e8m0_ceil(s);
+    float sf = (float)orc_e8m0_decode(c);
+    for (int i = 0; i < n; ++i)
+        q[i] = orc_e4m3_encode(v[i] / sf);
+    *sf_code = c;
+}
+
 /* --------------------------------------------------------------- forward */
+
+/* Combine (design doc §11.2; "07 · MegaMoE" §9): per token, slot order
+ * ascending, f32 sum of the active slots' (bf16-rounded) partials, one
+ * rounding to bf16. */
+static void combine(int T, int H, int E, int K, const int32_t* idx, int n_tok,
+                    const int32_t* toks, const float* part_f32, uint16_t* y, float* y_f32)
+{
+    (void)T;
+#pragma omp parallel for schedule(static)
+    for (int p = 0; p < n_tok; ++p) {
+        int t = toks ? toks[p] : p;
+        for (int n = 0; n < H; ++n) {
+            float a = 0.0f;
+            for (int j = 0; j < K; ++j) {
+                int e = idx[t * K + j];
+                if (e < 0 || e >= E)
+                    continue;
+                a += part_f32[((size_t)p * K + j) * H + n];
+            }
+            if (y)
+                y[(size_t)p * H + n] = orc_bf16_rne(a);
+            if (y_f32)
+                y_f32[(size_t)p * H + n] = a;
+        }
+    }
+}
+
+/* Token-list validation shared by both recipes: -1 on a bad token id or a
+ * missing expert array, else the number of slots with an id >= E. */
+static int check_tokens(int T, int E, int K, const int32_t* idx, int n_tok, const int32_t* toks,
+                        const void* const* w1, const void* const* w1_sf,
+                        const void* const* w2, const void* const* w2_sf)
+{
+    int bad = 0;
+    for (int p = 0; p < n_tok; ++p) {
+        int t = toks ? toks[p] : p;
+        if (t < 0 || t >= T)
+            return -1;
+        for (int j = 0; j < K; ++j) {
+            int e = idx[t * K + j];
+            if (e >= E)
+                ++bad;
+            else if (e >= 0 && (!w1[e] || !w1_sf[e] || !w2[e] || !w2_sf[e]))
+                return -1;
+        }
+    }
+    return bad;
+}
 
 enum {
     ORC_NO_REQUANT = 1, /* test-only: feed f32 SwiGLU output to L2 unquantised */
@@ -257,20 +412,10 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
     if (!toks)
         n_tok = T;
     const int HB = H / 128, IB = I / 128;
-    int bad = 0, missing = 0;
-    for (int p = 0; p < n_tok; ++p) {
-        int t = toks ? toks[p] : p;
-        if (t < 0 || t >= T)
-            return -1;
-        for (int j = 0; j < K; ++j) {
-            int e = idx[t * K + j];
-            if (e >= E)
-                ++bad;
-            else if (e >= 0 && (!w1[e] || !w1_sf[e] || !w2[e] || !w2_sf[e]))
-                missing = 1;
-        }
-    }
-    if (missing)
+    int bad = check_tokens(T, E, K, idx, n_tok, toks, (const void* const*)w1,
+                           (const void* const*)w1_sf, (const void* const*)w2,
+                           (const void* const*)w2_sf);
+    if (bad < 0)
         return -1;
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -333,24 +478,7 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
         free(qs);
     }
 
-    /* Combine: slot order ascending, f32 sum, one rounding to bf16. */
-#pragma omp parallel for schedule(static)
-    for (int p = 0; p < n_tok; ++p) {
-        int t = toks ? toks[p] : p;
-        for (int n = 0; n < H; ++n) {
-            float a = 0.0f;
-            for (int j = 0; j < K; ++j) {
-                int e = idx[t * K + j];
-                if (e < 0 || e >= E)
-                    continue;
-                a += part_f32[((size_t)p * K + j) * H + n];
-            }
-            if (y)
-                y[(size_t)p * H + n] = orc_bf16_rne(a);
-            if (y_f32)
-                y_f32[(size_t)p * H + n] = a;
-        }
-    }
+    combine(T, H, E, K, idx, n_tok, toks, part_f32, y, y_f32);
     free(part_f32);
     return bad;
 }
@@ -362,4 +490,87 @@ int orc_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* Forward of the FP8 x MXFP4 recipe, same structure and outputs as
+ * orc_moe_forward:
+ *   x [T,H] e4m3, x_sf [T,H/32] UE8M0, idx/w [T,K]
+ *   w1[e] -> [2I,H/2] packed e2m1 (gate rows then up rows), w1_sf[e] -> [2I,H/32]
+ *   w2[e] -> [H,I/2] packed e2m1, w2_sf[e] -> [H,I/32]
+ *   acc1 [n*K,2I] f32, h [n*K,I] e4m3, h_sf [n*K,I/32] UE8M0, partial [n*K,H]
+ * ORC_NO_REQUANT feeds the f32 SwiGLU output to L2 unquantised; ORC_NO_BF16
+ * keeps partials and y in f32. */
+int orc_moe_forward_mx(int T, int H, int I, int E, int K,
+                       const uint8_t* x, const uint8_t* x_sf,
+                       const int32_t* idx, const float* w,
+                       const uint8_t* const* w1, const uint8_t* const* w1_sf,
+                       const uint8_t* const* w2, const uint8_t* const* w2_sf,
+                       int n_tok, const int32_t* toks,
+                       uint16_t* y, float* y_f32,
+                       float* acc1, uint8_t* h, uint8_t* h_sf, uint16_t* partial,
+                       int flags, int nthreads)
+{
+    if (H % 32 || I % 32 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || T < 0)
+        return -1;
+    if (!toks)
+        n_tok = T;
+    const int HS = H / 32, IS = I / 32;
+    int bad = check_tokens(T, E, K, idx, n_tok, toks, (const void* const*)w1,
+                           (const void* const*)w1_sf, (const void* const*)w2,
+                           (const void* const*)w2_sf);
+    if (bad < 0)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+    float* part_f32 = (float*)calloc((size_t)n_tok * K * H, sizeof(float));
+    if (!part_f32)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ps = 0; ps < n_tok * K; ++ps) {
+        int p = ps / K, j = ps % K;
+        int t = toks ? toks[p] : p;
+        int e = idx[t * K + j];
+        if (e < 0 || e >= E)
+            continue;
+        float* a1 = (float*)malloc(sizeof(float) * 2 * I);
+        float* hv = (float*)malloc(sizeof(float) * I);
+        uint8_t* q = (uint8_t*)malloc(I);
+        uint8_t* qs = (uint8_t*)malloc(IS);
+        const uint8_t* xr = x + (size_t)t * H;
+        const uint8_t* xs = x_sf + (size_t)t * HS;
+        for (int n = 0; n < 2 * I; ++n)
+            a1[n] = (float)orc_mx_dot(xr, xs, w1[e] + (size_t)n * (H / 2),
+                                      w1_sf[e] + (size_t)n * HS, H);
+        if (acc1)
+            memcpy(acc1 + (size_t)ps * 2 * I, a1, sizeof(float) * 2 * I);
+        for (int i = 0; i < I; ++i)
+            hv[i] = orc_swiglu(a1[i], a1[I + i], w[t * K + j]);
+        if (!(flags & ORC_NO_REQUANT)) {
+            for (int ib = 0; ib < IS; ++ib)
+                orc_requant_block_mx(hv + 32 * ib, 32, q + 32 * ib, qs + ib);
+            if (h)
+                memcpy(h + (size_t)ps * I, q, I);
+            if (h_sf)
+                memcpy(h_sf + (size_t)ps * IS, qs, IS);
+        }
+        for (int n = 0; n < H; ++n) {
+            const uint8_t* wr = w2[e] + (size_t)n * (I / 2);
+            const uint8_t* ws = w2_sf[e] + (size_t)n * IS;
+            float acc = (flags & ORC_NO_REQUANT) ? (float)mx_dot_f32(hv, wr, ws, I)
+                                                 : (float)orc_mx_dot(q, qs, wr, ws, I);
+            float o = (flags & ORC_NO_BF16) ? acc : orc_bf16_to_f32(orc_bf16_rne(acc));
+            part_f32[(size_t)ps * H + n] = o;
+            if (partial)
+                partial[(size_t)ps * H + n] = orc_bf16_rne(acc);
+        }
+        free(a1);
+        free(hv);
+        free(q);
+        free(qs);
+    }
+    combine(T, H, E, K, idx, n_tok, toks, part_f32, y, y_f32);
+    free(part_f32);
+    return bad;
 }

@@ -25,10 +25,13 @@ MOE_FLAG_SINGLE_LAUNCH = 1
 MOE_FLAG_SPLIT_LAUNCH = 2
 MOE_FLAG_TEST_NO_WAIT = 256
 MOE_FLAG_TEST_SMALL_GRID = 512
+MOE_RECIPE_FP8_BLOCK128 = 0
+MOE_RECIPE_MXFP4 = 1
 
 EXPORTED_SYMBOLS = (
     "moe_plan_create", "moe_plan_destroy", "moe_plan_info", "moe_workspace_bytes",
-    "moe_workspace_layout", "moe_forward", "moe_forward_timed", "moe_route",
+    "moe_workspace_layout", "moe_forward", "moe_forward_timed", "moe_forward_mx",
+    "moe_forward_mx_timed", "moe_route",
     "moe_route_workspace_bytes", "moe_prepare_weights",
     "moe_read_status", "moe_strerror", "moe_version",
 )
@@ -44,7 +47,8 @@ class moe_shape_t(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("recipe", ctypes.c_int32)]
 
 
 class moe_tile_info_t(ctypes.Structure):
@@ -82,6 +86,8 @@ def lib():
         L.moe_forward.argtypes = [_vp, _i32] + [_vp] * 10 + [ctypes.c_size_t, _vp]
         L.moe_forward_timed.argtypes = [_vp, _i32] + [_vp] * 10 + [ctypes.c_size_t, _vp,
                                                                    ctypes.POINTER(_vp)]
+        L.moe_forward_mx.argtypes = L.moe_forward.argtypes
+        L.moe_forward_mx_timed.argtypes = L.moe_forward_timed.argtypes
         L.moe_route.argtypes = ([_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp,
                                  ctypes.c_size_t, _vp])
         L.moe_route_workspace_bytes.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_size_t)]
@@ -126,9 +132,10 @@ def _stream(stream):
 # --- the C ABI, one Python function per entry point -----------------------
 
 def moe_plan_create(hidden, intermediate, num_experts, top_k, max_tokens, tile_m=0,
-                    weight_layout=MOE_WEIGHTS_ROW_MAJOR, flags=0):
+                    weight_layout=MOE_WEIGHTS_ROW_MAJOR, flags=0,
+                    recipe=MOE_RECIPE_FP8_BLOCK128):
     shape = moe_shape_t(hidden, intermediate, num_experts, top_k, max_tokens, tile_m,
-                        weight_layout, flags)
+                        weight_layout, flags, recipe)
     h = ctypes.c_void_p()
     _check(lib().moe_plan_create(ctypes.byref(shape), ctypes.byref(h)), "moe_plan_create")
     return h
@@ -183,6 +190,30 @@ def moe_forward_timed(plan, num_tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2
     _check(rc, "moe_forward_timed")
 
 
+def moe_forward_mx(plan, num_tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
+                   workspace, stream=None):
+    """FP8 x MXFP4 forward: UE8M0 scale codes (uint8) and packed e2m1 weights."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().moe_forward_mx(plan, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx),
+                              _ptr(topk_w), _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
+                              _ptr(y), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(rc, "moe_forward_mx")
+
+
+def moe_forward_mx_timed(plan, num_tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
+                         workspace, stream, step_events):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    ev = (_vp * 5)()
+    for i, e in enumerate(step_events):
+        if e is not None and not e.cuda_event:
+            raise ValueError("step event has no HIP event yet: record() it once first")
+        ev[i] = None if e is None else e.cuda_event
+    rc = lib().moe_forward_mx_timed(plan, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx),
+                                    _ptr(topk_w), _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
+                                    _ptr(y), _ptr(workspace), ws_bytes, _stream(stream), ev)
+    _check(rc, "moe_forward_mx_timed")
+
+
 def moe_prepare_weights(plan, w1, w2, w1_packed, w2_packed, stream=None):
     """Write the packed (MFMA operand order) copies of w1/w2 for a packed plan."""
     rc = lib().moe_prepare_weights(plan, _ptr(w1), _ptr(w2), _ptr(w1_packed), _ptr(w2_packed),
@@ -220,12 +251,14 @@ class MoEForward:
     """Plan + workspace holder.  forward() writes y for T tokens."""
 
     def __init__(self, hidden, intermediate, num_experts, top_k, max_tokens, tile_m=0,
-                 device="cuda", weight_layout=MOE_WEIGHTS_ROW_MAJOR, flags=0):
+                 device="cuda", weight_layout=MOE_WEIGHTS_ROW_MAJOR, flags=0,
+                 recipe=MOE_RECIPE_FP8_BLOCK128):
         import torch
         self.shape = (hidden, intermediate, num_experts, top_k, max_tokens, tile_m)
         self.weight_layout = weight_layout
+        self.recipe = recipe
         self.plan = moe_plan_create(hidden, intermediate, num_experts, top_k, max_tokens,
-                                    tile_m, weight_layout, flags)
+                                    tile_m, weight_layout, flags, recipe)
         self.ws_bytes = moe_workspace_bytes(self.plan, max_tokens)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
 
@@ -244,8 +277,9 @@ class MoEForward:
         T = x.shape[0]
         if y is None:
             y = torch.empty(T, self.shape[0], dtype=torch.uint16, device=x.device)
-        moe_forward(self.plan, T, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
-                    self.workspace, stream)
+        fwd = moe_forward_mx if self.recipe == MOE_RECIPE_MXFP4 else moe_forward
+        fwd(self.plan, T, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
+            self.workspace, stream)
         return y
 
     def view(self, name, num_tokens):
@@ -261,7 +295,8 @@ class MoEForward:
             "row_src": (torch.int32, (R,)),
             "src_row": (torch.int32, (num_tokens * K,)),
             "h": (torch.uint8, (R, I)),
-            "h_sf": (torch.float32, (R, I // 128)),
+            "h_sf": ((torch.uint8, (R, I // 32)) if self.recipe == MOE_RECIPE_MXFP4
+                     else (torch.float32, (R, I // 128))),
             "partial": (torch.int16, (K, num_tokens, H)),
             "status": (torch.int32, (4,)),
         }[name]

@@ -34,6 +34,7 @@ struct Config {
 // Beyond ~24 rows per expert the 128 x 256 LDS-staged MFMA tile takes over
 // (it needs H % 256 == 0 for its 256-column L2 tiles and I >= 256 for at
 // least two K blocks in L2; otherwise 64-row direct-load tiles).
+// The FP8 x MXFP4 recipe has direct-load tiles only (16, 32, 64 rows).
 Config choose_config(const moe_shape_t& s, int T)
 {
     if (s.tile_m > 0)
@@ -43,7 +44,7 @@ Config choose_config(const moe_shape_t& s, int T)
         return Config{16, 0};
     if (rows <= 24.0)
         return Config{32, 0};
-    if (s.hidden % 256 == 0 && s.intermediate >= 256)
+    if (s.recipe == MOE_RECIPE_FP8_BLOCK128 && s.hidden % 256 == 0 && s.intermediate >= 256)
         return Config{128, 1};
     return Config{64, 0};
 }
@@ -91,7 +92,7 @@ long long mblocks_expected(const moe_shape_t& s, long long T)
 // shape: T = 128 and 32 gain ~1.7 % in L2, T = 8 loses 7 %).
 bool choose_l2_wide(const moe_shape_t& s, int T, const Config& c)
 {
-    if (c.tile_m != 16 || T <= 0)
+    if (c.tile_m != 16 || T <= 0 || s.recipe != MOE_RECIPE_FP8_BLOCK128)
         return false;
     const long long groups = mblocks_expected(s, T) * (((s.hidden + 255) / 256 + 1) / 2);
     return groups >= 4 * kMinItems;
@@ -100,7 +101,7 @@ bool choose_l2_wide(const moe_shape_t& s, int T, const Config& c)
 // L1 split factor of a call with T tokens and tile configuration c.
 int choose_split(const moe_shape_t& s, int T, const Config& c)
 {
-    if (c.tile_m != 16 || T <= 0)
+    if (c.tile_m != 16 || T <= 0 || s.recipe != MOE_RECIPE_FP8_BLOCK128)
         return 1;
     const long long items = mblocks_expected(s, T) * (s.intermediate / 128);
     const int kblocks = s.hidden / 128;
@@ -176,6 +177,7 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     L.mbe = take(sizeof(int32_t) * (size_t)L.mb_cap);
     L.row_src = take(sizeof(int32_t) * (size_t)L.r_cap);
     L.src_row = take(sizeof(int32_t) * (size_t)std::max<long long>(TK, 1));
+    // f32 [R, I/128] (FP8 recipe) or UE8M0 bytes [R, I/32] (MXFP4): same size
     L.h_sf = take(sizeof(float) * (size_t)L.r_cap * (I / 128));
     L.h = take((size_t)L.r_cap * I);
     L.partial = take(sizeof(uint16_t) * (size_t)K * T * H);
@@ -223,6 +225,14 @@ int validate_shape(const moe_shape_t* s)
     if (s->flags & ~(MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_SPLIT_LAUNCH | MOE_FLAG_TEST_NO_WAIT |
                      MOE_FLAG_TEST_SMALL_GRID))
         return MOE_ERR_INVALID_ARG;
+    if (s->recipe != MOE_RECIPE_FP8_BLOCK128 && s->recipe != MOE_RECIPE_MXFP4)
+        return MOE_ERR_INVALID_ARG;
+    if (s->recipe == MOE_RECIPE_MXFP4) {
+        if (s->tile_m == 128)
+            return MOE_ERR_UNSUPPORTED_SHAPE;
+        if (s->weight_layout != MOE_WEIGHTS_ROW_MAJOR || (s->flags & MOE_FLAG_SINGLE_LAUNCH))
+            return MOE_ERR_INVALID_ARG;
+    }
     if ((s->flags & MOE_FLAG_SINGLE_LAUNCH) && (s->flags & MOE_FLAG_SPLIT_LAUNCH))
         return MOE_ERR_INVALID_ARG;
     return MOE_OK;
@@ -372,27 +382,44 @@ int moe_workspace_layout(moe_plan_t plan, int32_t T, moe_ws_layout_t* out)
     return MOE_OK;
 }
 
-int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float* x_sf,
-                      const int32_t* topk_idx, const float* topk_w, const uint8_t* w1,
-                      const float* w1_sf, const uint8_t* w2, const float* w2_sf, uint16_t* y,
-                      void* workspace, size_t workspace_bytes, void* stream,
-                      void* const* step_events)
+}  // extern "C"
+
+namespace {
+
+// Operands of one forward; the scale pointers are f32 (FP8 recipe) or
+// UE8M0 bytes (MXFP4), as the plan's recipe says.
+struct FwdOperands {
+    const uint8_t* x;
+    const void* x_sf;
+    const int32_t* topk_idx;
+    const float* topk_w;
+    const uint8_t* w1;
+    const void* w1_sf;
+    const uint8_t* w2;
+    const void* w2_sf;
+    uint16_t* y;
+};
+
+int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, void* workspace,
+                 size_t workspace_bytes, void* stream, void* const* step_events)
 {
     if (!plan)
         return MOE_ERR_INVALID_ARG;
     const moe_shape_t& s = plan->shape;
+    if (s.recipe != recipe)
+        return MOE_ERR_INVALID_ARG;
     if (T < 0 || T > s.max_tokens)
         return MOE_ERR_INVALID_ARG;
     if (T == 0)
         return MOE_OK;
-    if (!x || !x_sf || !topk_idx || !topk_w || !w1 || !w1_sf || !w2 || !w2_sf || !y ||
-        !workspace)
+    if (!op.x || !op.x_sf || !op.topk_idx || !op.topk_w || !op.w1 || !op.w1_sf || !op.w2 ||
+        !op.w2_sf || !op.y || !workspace)
         return MOE_ERR_INVALID_ARG;
     // The kernels move 16-byte vectors of x, the weights, y and the
     // workspace sections (which sit at 256-byte offsets).
     auto misaligned = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) != 0; };
-    if (misaligned(workspace, 256) || misaligned(x, 16) || misaligned(w1, 16) ||
-        misaligned(w2, 16) || misaligned(y, 16))
+    if (misaligned(workspace, 256) || misaligned(op.x, 16) || misaligned(op.w1, 16) ||
+        misaligned(op.w2, 16) || misaligned(op.y, 16))
         return MOE_ERR_INVALID_ARG;
     const Layout L = make_layout(s, T);
     if (workspace_bytes < L.total)
@@ -409,7 +436,7 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     if (!mark(0))
         return MOE_ERR_HIP;
 
-    moe::RouteArgs ra = route_args(s, T, L, workspace, topk_idx, L.tile_m,
+    moe::RouteArgs ra = route_args(s, T, L, workspace, op.topk_idx, L.tile_m,
                                    at<int32_t>(workspace, L.counts),
                                    at<int32_t>(workspace, L.offsets),
                                    at<int32_t>(workspace, L.row_src), L.r_cap,
@@ -417,6 +444,7 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     if (moe::launch_route(ra, st) != hipSuccess || !mark(1))
         return MOE_ERR_HIP;
 
+    const bool mx = recipe == MOE_RECIPE_MXFP4;
     moe::FwdArgs a{};
     a.T = T;
     a.H = s.hidden;
@@ -425,21 +453,29 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
     a.K = s.top_k;
     a.BM = L.tile_m;
     a.packed = s.weight_layout == MOE_WEIGHTS_PACKED;
-    a.x = x;
-    a.x_sf = x_sf;
-    a.idx = topk_idx;
-    a.topk_w = topk_w;
-    a.w1 = w1;
-    a.w1_sf = w1_sf;
-    a.w2 = w2;
-    a.w2_sf = w2_sf;
+    a.x = op.x;
+    a.idx = op.topk_idx;
+    a.topk_w = op.topk_w;
+    a.w1 = op.w1;
+    a.w2 = op.w2;
+    a.mx = mx ? 1 : 0;
+    if (mx) {
+        a.x_sfq = static_cast<const uint8_t*>(op.x_sf);
+        a.w1_sfq = static_cast<const uint8_t*>(op.w1_sf);
+        a.w2_sfq = static_cast<const uint8_t*>(op.w2_sf);
+        a.h_sfq = at<uint8_t>(workspace, L.h_sf);
+    } else {
+        a.x_sf = static_cast<const float*>(op.x_sf);
+        a.w1_sf = static_cast<const float*>(op.w1_sf);
+        a.w2_sf = static_cast<const float*>(op.w2_sf);
+        a.h_sf = at<float>(workspace, L.h_sf);
+    }
     a.row_src = at<int32_t>(workspace, L.row_src);
     a.mblock_expert = at<int32_t>(workspace, L.mbe);
     a.num_mblocks = L.mb_cap;
     a.h = at<uint8_t>(workspace, L.h);
-    a.h_sf = at<float>(workspace, L.h_sf);
     a.partial = at<uint16_t>(workspace, L.partial);
-    a.y = y;
+    a.y = op.y;
     a.src_row = at<int32_t>(workspace, L.src_row);
     a.split_l1 = L.split_l1;
     a.l2_wide = L.l2_wide ? 1 : 0;
@@ -454,13 +490,35 @@ int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float*
             return MOE_ERR_HIP;
         return MOE_OK;
     }
-    if (moe::launch_l1(a, L.kernel, st) != hipSuccess || !mark(2))
-        return MOE_ERR_HIP;
-    if (moe::launch_l2(a, L.kernel, st) != hipSuccess || !mark(3))
-        return MOE_ERR_HIP;
+    if (mx) {
+        if (moe::launch_l1_mx(a, st) != hipSuccess || !mark(2))
+            return MOE_ERR_HIP;
+        if (moe::launch_l2_mx(a, st) != hipSuccess || !mark(3))
+            return MOE_ERR_HIP;
+    } else {
+        if (moe::launch_l1(a, L.kernel, st) != hipSuccess || !mark(2))
+            return MOE_ERR_HIP;
+        if (moe::launch_l2(a, L.kernel, st) != hipSuccess || !mark(3))
+            return MOE_ERR_HIP;
+    }
     if (moe::launch_combine(a, st) != hipSuccess || !mark(4))
         return MOE_ERR_HIP;
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const float* x_sf,
+                      const int32_t* topk_idx, const float* topk_w, const uint8_t* w1,
+                      const float* w1_sf, const uint8_t* w2, const float* w2_sf, uint16_t* y,
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* step_events)
+{
+    const FwdOperands op{x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y};
+    return forward_impl(plan, MOE_RECIPE_FP8_BLOCK128, T, op, workspace, workspace_bytes, stream,
+                        step_events);
 }
 
 int moe_forward(moe_plan_t plan, int32_t T, const uint8_t* x, const float* x_sf,
@@ -470,6 +528,26 @@ int moe_forward(moe_plan_t plan, int32_t T, const uint8_t* x, const float* x_sf,
 {
     return moe_forward_timed(plan, T, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
                              workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_forward_mx_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const uint8_t* x_sf,
+                         const int32_t* topk_idx, const float* topk_w, const uint8_t* w1,
+                         const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf,
+                         uint16_t* y, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* step_events)
+{
+    const FwdOperands op{x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y};
+    return forward_impl(plan, MOE_RECIPE_MXFP4, T, op, workspace, workspace_bytes, stream,
+                        step_events);
+}
+
+int moe_forward_mx(moe_plan_t plan, int32_t T, const uint8_t* x, const uint8_t* x_sf,
+                   const int32_t* topk_idx, const float* topk_w, const uint8_t* w1,
+                   const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf, uint16_t* y,
+                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    return moe_forward_mx_timed(plan, T, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
+                                workspace, workspace_bytes, stream, nullptr);
 }
 
 int moe_prepare_weights(moe_plan_t plan, const uint8_t* w1, const uint8_t* w2,

@@ -22,6 +22,37 @@ __device__ __forceinline__ v4f mfma_16x16x128_e4m3(const v8i& a, const v8i& b, c
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// One gfx950 block-scaled MFMA: D(16x16, f32) = A(16x128, e4m3) * B(128x16,
+// e2m1) + C, each operand with one UE8M0 scale per 32 K values applied in
+// the instruction (A format 0 = e4m3, B format 4 = e2m1).  Operand layout
+// (checked on the GPU against exact arithmetic), g = lane / 16:
+//   A lane l: row l % 16; bytes 0..15 hold K 16g .. 16g+15 and bytes 16..31
+//     hold K 64+16g .. 64+16g+15 (the same bytes mfma_16x16x128_e4m3 uses);
+//   B lane l: column l % 16; the low 16 bytes hold K 32g .. 32g+31, two per
+//     byte, the even K in the low nibble (the upper 16 bytes are unused);
+//   scale operands: the low byte of lane l's value is the UE8M0 exponent
+//     of K block g (K 32g .. 32g+31) of row (A) / column (B) l % 16.
+__device__ __forceinline__ v4f mfma_16x16x128_e4m3_e2m1(const v8i& a, const v8i& b,
+                                                        const v4f& c, int sa, int sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
+}
+
+// UE8M0 code of the smallest power of two >= s, for a positive normal f32 s
+// (the f32 exponent field has the same bias, 127, as UE8M0).
+__device__ __forceinline__ uint32_t e8m0_ceil_code(float s)
+{
+    const uint32_t u = __float_as_uint(s);
+    return (u >> 23) + ((u & 0x7FFFFFu) != 0u);
+}
+
+// 2^(127 - code) as an f32, for 1 <= code <= 253: the reciprocal of the
+// scale a UE8M0 code stands for, exact.
+__device__ __forceinline__ float e8m0_inverse(uint32_t code)
+{
+    return __uint_as_float((254u - code) << 23);
+}
+
 // f32 -> OCP e4m3 (E4M3FN) code, round to nearest even, magnitudes >= 448
 // saturate to 448, sign of zero kept, NaN -> 0x7F.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v)

@@ -62,6 +62,14 @@ struct FwdArgs {
     int32_t* status;
     int32_t spin_limit;
     int32_t grid_cap;  // > 0: at most this many workgroups for the persistent kernels
+    // FP8 x MXFP4 recipe (mx = 1): UE8M0 scale codes, one per 32 K values,
+    // x_sfq [T,H/32], w1_sfq [E,2I,H/32], w2_sfq [E,H,I/32], h_sfq [R,I/32];
+    // w1/w2 hold packed e2m1 pairs.  The f32 scale pointers are unused.
+    int32_t mx;
+    const uint8_t* x_sfq;
+    const uint8_t* w1_sfq;
+    const uint8_t* w2_sfq;
+    uint8_t* h_sfq;
 };
 
 constexpr int kSyncL2Done = 0;
@@ -77,6 +85,8 @@ hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s);
 hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s);
 hipError_t launch_fused(const FwdArgs& a, hipStream_t s);  // L1 + L2 + combine, direct tiles
 hipError_t launch_combine(const FwdArgs& a, hipStream_t s);
+hipError_t launch_l1_mx(const FwdArgs& a, hipStream_t s);  // direct tiles, tile_m 16/32/64
+hipError_t launch_l2_mx(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_pack(const uint8_t* w1, const uint8_t* w2, uint8_t* w1p, uint8_t* w2p, int E,

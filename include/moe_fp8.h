@@ -70,6 +70,14 @@ extern "C" {
                                         launch at most 4 workgroups, so each walks many
                                         tiles (same results as the full grid) */
 
+/* Quantisation recipes (moe_shape_t.recipe). */
+#define MOE_RECIPE_FP8_BLOCK128 0 /* e4m3 x e4m3, f32 scales: x per 1x128, weights per
+                                     128x128, intermediate per 1x128 (moe_forward) */
+#define MOE_RECIPE_MXFP4 1        /* e4m3 activations x e2m1 weights, UE8M0 scales per
+                                     1x32 on x, weights and the intermediate
+                                     (moe_forward_mx; the SM100 recipe (1,1,32) of
+                                     "07 · MegaMoE" §0) */
+
 /* Weight layouts a plan can expect for w1/w2 (scales are always row-major). */
 #define MOE_WEIGHTS_ROW_MAJOR 0 /* w1 [E,2I,H], w2 [E,H,I] as documented at moe_forward */
 #define MOE_WEIGHTS_PACKED 1    /* written by moe_prepare_weights (needs H % 256 == 0) */
@@ -84,6 +92,8 @@ typedef struct moe_shape {
                               (128: H % 256 == 0 and I >= 256) */
     int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
     int32_t flags;         /* MOE_FLAG_* bits, 0 = defaults */
+    int32_t recipe;        /* MOE_RECIPE_*; MXFP4 plans: tile_m 0, 16, 32 or 64, row-major
+                              weights, no single launch */
 } moe_shape_t;
 
 typedef struct moe_plan* moe_plan_t;
@@ -110,7 +120,7 @@ typedef struct moe_tile_info {
  *   row_src  int32 [pool_rows]    flat slot f = t*K + j held by a pool row, -1 = padding
  *   src_row  int32 [T*K]          pool row of slot f, -1 = skipped slot
  *   h        uint8 [pool_rows, I] e4m3 SwiGLU output (valid rows only)
- *   h_sf     f32   [pool_rows, I/128]
+ *   h_sf     f32   [pool_rows, I/128]  (MXFP4 plans: uint8 UE8M0 [pool_rows, I/32])
  *   partial  uint16 [K, T, H]     bf16 L2 output of slot (t, j) at [j][t]
  *   status   int32 [4]            status[0] = MOE_STATUS_* bits, status[1] = #ids >= E */
 typedef struct moe_ws_layout {
@@ -171,6 +181,41 @@ int moe_forward_timed(moe_plan_t plan, int32_t num_tokens,
                       const uint8_t* w2, const float* w2_sf,
                       uint16_t* y, void* workspace, size_t workspace_bytes, void* stream,
                       void* const* step_events);
+
+/*
+ * Full forward of the FP8 x MXFP4 recipe (plans with recipe =
+ * MOE_RECIPE_MXFP4; MOE_ERR_INVALID_ARG for other plans, and moe_forward
+ * rejects MXFP4 plans the same way).  Same steps, routing, workspace and
+ * output as moe_forward; what differs is the operand encoding:
+ *   x      uint8 [T, H]          e4m3 tokens
+ *   x_sf   uint8 [T, H/32]       UE8M0 scale codes (2^(c-127)), one per 1x32 block
+ *   w1     uint8 [E, 2I, H/2]    e2m1 pairs, element k of a row in byte k/2,
+ *                                even k in the low nibble; rows [0,I) gate, [I,2I) up
+ *   w1_sf  uint8 [E, 2I, H/32]   UE8M0 per row and 32 K values
+ *   w2     uint8 [E, H, I/2]     e2m1 pairs
+ *   w2_sf  uint8 [E, H, I/32]
+ * L1 and L2 are block-scaled GEMMs with both operands' scales applied per 32
+ * K values and f32 accumulation; the SwiGLU output is requantised per 1x32
+ * with sf = the smallest power of two >= max(amax, 1e-10)/448 (a UE8M0
+ * code), q = e4m3(h / sf) ("07 · MegaMoE" §8 per-block UE8M0 scale).
+ * Scale codes of 0xFF (NaN) give NaN in the rows they touch.
+ * x, w1, w2 and y must be 16-byte aligned, workspace 256-byte aligned.
+ */
+int moe_forward_mx(moe_plan_t plan, int32_t num_tokens,
+                   const uint8_t* x, const uint8_t* x_sf,
+                   const int32_t* topk_idx, const float* topk_w,
+                   const uint8_t* w1, const uint8_t* w1_sf,
+                   const uint8_t* w2, const uint8_t* w2_sf,
+                   uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_forward_mx with the five step events of moe_forward_timed. */
+int moe_forward_mx_timed(moe_plan_t plan, int32_t num_tokens,
+                         const uint8_t* x, const uint8_t* x_sf,
+                         const int32_t* topk_idx, const float* topk_w,
+                         const uint8_t* w1, const uint8_t* w1_sf,
+                         const uint8_t* w2, const uint8_t* w2_sf,
+                         uint16_t* y, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* step_events);
 
 /*
  * One-time weight re-layout for plans with weight_layout = MOE_WEIGHTS_PACKED

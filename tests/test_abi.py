@@ -275,3 +275,43 @@ def test_route_host_validation_without_gpu():
         assert L.moe_route(p, 8, a, 16, None, a, a, 1000, a, a, big, None) == moe.MOE_ERR_INVALID_ARG
     finally:
         moe.moe_plan_destroy(p)
+
+
+def test_mx_recipe_validation_and_choices():
+    # recipe values, and what an MXFP4 plan accepts
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_plan_create(256, 256, 4, 2, 8, recipe=2)
+    assert ei.value.code == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_plan_create(256, 256, 4, 2, 8, tile_m=128, recipe=moe.MOE_RECIPE_MXFP4)
+    assert ei.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE
+    for kw in (dict(weight_layout=moe.MOE_WEIGHTS_PACKED), dict(flags=moe.MOE_FLAG_SINGLE_LAUNCH)):
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_plan_create(256, 256, 4, 2, 8, recipe=moe.MOE_RECIPE_MXFP4, **kw)
+        assert ei.value.code == moe.MOE_ERR_INVALID_ARG
+    p = moe.moe_plan_create(4096, 2048, 256, 6, 8192, recipe=moe.MOE_RECIPE_MXFP4)
+    q = moe.moe_plan_create(4096, 2048, 256, 6, 8192)
+    try:
+        for T in (1, 2, 8, 128, 1024, 8192):
+            info = moe.moe_plan_info(p, T)
+            # direct-load tiles only, no split-K, one L2 tile per workgroup
+            assert info["tile_m"] in (16, 32, 64) and info["kernel"] == 0, T
+            assert info["l1_split"] == 1 and info["l2_group_tiles"] == 1 and \
+                info["single_launch"] == 0, T
+            # same workspace as the FP8 plan (h_sf: I/32 bytes = I/128 floats per row)
+            assert moe.moe_workspace_bytes(p, T) <= moe.moe_workspace_bytes(q, T) or \
+                moe.moe_plan_info(q, T)["tile_m"] != info["tile_m"]
+        # each forward entry point rejects the other recipe's plan before any
+        # HIP call (fake pointers are never touched)
+        fake = [ctypes.c_void_p(4096 * (i + 1)) for i in range(10)]
+        L = moe.lib()
+        args = [fake[0], fake[1], fake[2], fake[3], fake[4], fake[5], fake[6], fake[7], fake[8],
+                fake[9], 1 << 30, None]
+        assert L.moe_forward(p, 4, *args) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_forward_mx(q, 4, *args) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_forward_mx(p, -1, *args) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_forward_mx(p, 4, None, *args[1:]) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_forward_mx(p, 0, *args) == moe.MOE_OK  # T == 0: no-op
+    finally:
+        moe.moe_plan_destroy(p)
+        moe.moe_plan_destroy(q)

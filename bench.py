@@ -30,19 +30,27 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA, published
 
 
-def algorithmic_bytes(cfg, idx):
+def algorithmic_bytes(cfg, idx, mx=False):
     """Bytes each kernel must move at least once (weights of active experts
-    read once, activations read/written once).  Returns dict per kernel."""
+    read once, activations read/written once).  Returns dict per kernel.
+    mx: the FP8 x MXFP4 recipe (e2m1 weights, one UE8M0 byte per 32 values
+    of x, the weights and h)."""
     import torch
     E, H, I, K, T = cfg.E, cfg.H, cfg.I, cfg.K, cfg.T
     valid = (idx >= 0) & (idx < E)
     rows = int(valid.sum())
     active = int(torch.unique(idx[valid]).numel())
-    w1 = active * (2 * I * H + 4 * (2 * I // 128) * (H // 128))
-    w2 = active * (H * I + 4 * (H // 128) * (I // 128))
-    x = T * H + 4 * T * (H // 128)
+    if mx:
+        w1 = active * (2 * I * H // 2 + 2 * I * H // 32)
+        w2 = active * (H * I // 2 + H * I // 32)
+        x = T * H + T * H // 32
+        h = rows * I + rows * I // 32
+    else:
+        w1 = active * (2 * I * H + 4 * (2 * I // 128) * (H // 128))
+        w2 = active * (H * I + 4 * (H // 128) * (I // 128))
+        x = T * H + 4 * T * (H // 128)
+        h = rows * I + 4 * rows * (I // 128)
     topk = 8 * T * K
-    h = rows * I + 4 * rows * (I // 128)
     part = 2 * rows * H
     y = 2 * T * H
     return {
@@ -73,7 +81,7 @@ def measured_traffic(cfg, weights):
     return d["l1_step_traffic_bytes"]
 
 
-def time_oracle_sample(inp, cfg, n_tokens, seed):
+def time_oracle_sample(inp, cfg, n_tokens, seed, mx=False):
     """CPU oracle on a bounded sample of tokens; returns (us per layer
     extrapolated to T tokens, threads, seconds, sample description)."""
     import numpy as np
@@ -88,7 +96,7 @@ def time_oracle_sample(inp, cfg, n_tokens, seed):
             sel(inp["w1"]), sel(inp["w1_sf"]), sel(inp["w2"]), sel(inp["w2_sf"]))
     threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    oracle.moe_forward(*args, tokens=toks, nthreads=threads)
+    (oracle.moe_forward_mx if mx else oracle.moe_forward)(*args, tokens=toks, nthreads=threads)
     dt = time.perf_counter() - t0
     per_layer_us = dt * 1e6 * cfg.T / len(toks)
     return per_layer_us, threads, dt, f"{len(toks)} of {cfg.T} tokens ({len(toks) * cfg.K} slots), extrapolated linearly in tokens"
@@ -174,6 +182,10 @@ def main():
     ap.add_argument("--launch", choices=("auto", "single", "split"), default="auto",
                     help="single: L1, L2 and combine in one cooperative launch (direct "
                          "tiles); split: one launch per step; auto: the library's choice")
+    ap.add_argument("--recipe", choices=("fp8", "mxfp4"), default="fp8",
+                    help="fp8: e4m3 x e4m3 with f32 block scales (1x128, 128x128); mxfp4: "
+                         "e4m3 activations x e2m1 weights with UE8M0 scales per 32 "
+                         "(row-major weights)")
     ap.add_argument("--weights", choices=("packed", "row_major"), default="packed",
                     help="expert weight layout the plan expects (packed = one-time "
                          "moe_prepare_weights re-layout, done before timing)")
@@ -214,26 +226,37 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] drawing {cfg} seed {seed} on the GPU", file=sys.stderr, flush=True)
-    inp = wl.make_inputs(cfg, seed, dev)
+    mx = args.recipe == "mxfp4"
+    if cfg.H % 256:
+        args.weights = "row_major"  # the packed layouts need whole 256-row L2 tiles
+    inp = (wl.make_inputs_mx if mx else wl.make_inputs)(cfg, seed, dev)
     torch.cuda.synchronize()
     layout = moe.MOE_WEIGHTS_PACKED if args.weights == "packed" else moe.MOE_WEIGHTS_ROW_MAJOR
     flags = {"auto": 0, "single": moe.MOE_FLAG_SINGLE_LAUNCH,
              "split": moe.MOE_FLAG_SPLIT_LAUNCH}[args.launch]
     runner = moe.MoEForward(cfg.H, cfg.I, cfg.E, cfg.K, cfg.T, device=dev, weight_layout=layout,
+                            recipe=moe.MOE_RECIPE_MXFP4 if mx else moe.MOE_RECIPE_FP8_BLOCK128,
                             flags=flags)
     info = moe.moe_plan_info(runner.plan, cfg.T)
     y = torch.empty(cfg.T, cfg.H, dtype=torch.uint16, device=dev)
     stream = torch.cuda.current_stream()
     prep0 = time.perf_counter()
-    w1, w2 = runner.prepare(inp["w1"], inp["w2"], stream)
+    if mx:
+        w1, w1_sf, w2, w2_sf = runner.prepare_mx(inp["w1"], inp["w1_sf"], inp["w2"],
+                                                 inp["w2_sf"], stream)
+    else:
+        w1, w2 = runner.prepare(inp["w1"], inp["w2"], stream)
+        w1_sf, w2_sf = inp["w1_sf"], inp["w2_sf"]
     torch.cuda.synchronize()
     prepare_ms = (time.perf_counter() - prep0) * 1e3
     # (the row-major copies stay for the CPU-oracle baseline, which reads them)
-    fwd_args = (inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_w"], w1, inp["w1_sf"],
-                w2, inp["w2_sf"], y, runner.workspace)
+    forward = moe.moe_forward_mx if mx else moe.moe_forward
+    forward_timed = moe.moe_forward_mx_timed if mx else moe.moe_forward_timed
+    fwd_args = (inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_w"], w1, w1_sf,
+                w2, w2_sf, y, runner.workspace)
 
     for _ in range(args.warmup):
-        moe.moe_forward(runner.plan, cfg.T, *fwd_args, stream=stream)
+        forward(runner.plan, cfg.T, *fwd_args, stream=stream)
     torch.cuda.synchronize()
     print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
 
@@ -249,7 +272,7 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for k in range(args.steps):
-        moe.moe_forward_timed(runner.plan, cfg.T, *fwd_args, stream, evs[k])
+        forward_timed(runner.plan, cfg.T, *fwd_args, stream, evs[k])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -262,7 +285,7 @@ def main():
     avg = {n: sum(v) / len(v) for n, v in per.items()}
     us_per_layer = total_ms * 1e3 / args.steps
 
-    alg = algorithmic_bytes(cfg, inp["topk_idx"])
+    alg = algorithmic_bytes(cfg, inp["topk_idx"], mx)
     flops = 2.0 * alg["rows"] * 3 * cfg.H * cfg.I
     bytes_total = alg["route"] + alg["l1"] + alg["l2"] + alg["combine"]
     single = bool(info["single_launch"])
@@ -276,10 +299,10 @@ def main():
     else:
         dom = max(("l1", "l2"), key=lambda n: avg[n])
         dom_bytes = alg[dom]
-        kernel_name = (("L1 step: GEMM gate+up, SwiGLU x topk_w, e4m3 requant "
+        kernel_name = (("MXFP4 " if mx else "") + ("L1 step: GEMM gate+up, SwiGLU x topk_w, e4m3 requant "
                         f"({'direct-load tiles' if info['kernel'] == 0 else 'LDS-staged tiles'}, "
                         f"tile_m {info['tile_m']})") if dom == "l1" else
-                       f"L2 step: GEMM down (tile_m {info['tile_m']})")
+                       ("MXFP4 " if mx else "") + f"L2 step: GEMM down (tile_m {info['tile_m']})")
     achieved = dom_bytes / (avg[dom] * 1e-6) / 1e9
     t_hbm = bytes_total / (HBM_PEAK_GBS * 1e9) * 1e6
     t_mfma = flops / (FP8_PEAK_TFLOPS * 1e12) * 1e6
@@ -295,12 +318,15 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 x e4m3 -> f32 accumulate, bf16 out",
-        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights, e4m3 block-quantised)",
+        "dtype": ("e4m3 x e2m1 (UE8M0 per 32) -> f32 accumulate, bf16 out" if mx else
+                  "e4m3 x e4m3 -> f32 accumulate, bf16 out"),
+        "data": ("synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights, "
+                 + ("MX-quantised: e4m3 / e2m1 with UE8M0 scales per 32)" if mx else
+                    "e4m3 block-quantised)")),
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H,
                    "intermediate": cfg.I, "experts": cfg.E, "top_k": cfg.K,
                    "routing": "zipf-skewed" if cfg.skew else "uniform", "seed": seed,
-                   "weights": args.weights, "tile": info},
+                   "recipe": args.recipe, "weights": args.weights, "tile": info},
         "prepare_weights_ms_once": round(prepare_ms, 2) if layout else 0.0,
         "tflops": round(flops / (us_per_layer * 1e-6) / 1e12, 2),
         "hbm_gbs_algorithmic": round(bytes_total / (us_per_layer * 1e-6) / 1e9, 1),
@@ -319,7 +345,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(cfg, args.weights) if dom == "l1" and not single else None,
+            "traffic": (measured_traffic(cfg, args.weights)
+                        if dom == "l1" and not single and not mx else None),
             "algorithmic_bytes": dom_bytes,
         },
         "cpu_baseline": None,
@@ -335,7 +362,7 @@ def main():
             for _ in range(args.steps):
                 scratch.fill_(1)
                 e0.record(stream)
-                moe.moe_forward(runner.plan, cfg.T, *fwd_args, stream=stream)
+                forward(runner.plan, cfg.T, *fwd_args, stream=stream)
                 e1.record(stream)
                 e1.synchronize()
                 obs.append(e0.elapsed_time(e1) * 1e3)
@@ -361,7 +388,7 @@ def main():
         line["pct_mfma_achievable"] = round(100 * t_mfma_meas / us_per_layer, 2)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
-        us, threads, secs, sample = time_oracle_sample(inp, cfg, args.cpu_sample_tokens, seed)
+        us, threads, secs, sample = time_oracle_sample(inp, cfg, args.cpu_sample_tokens, seed, mx)
         line["cpu_baseline"] = {"value": round(us, 1), "unit": "us", "cores": threads,
                                 "kind": "oracle", "sample": sample,
                                 "seconds": round(secs, 2)}

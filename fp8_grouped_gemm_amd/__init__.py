@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "moe_plan_create", "moe_plan_destroy", "moe_plan_info", "moe_workspace_bytes",
     "moe_workspace_layout", "moe_forward", "moe_forward_timed", "moe_forward_mx",
     "moe_forward_mx_timed", "moe_route",
-    "moe_route_workspace_bytes", "moe_prepare_weights",
+    "moe_route_workspace_bytes", "moe_prepare_weights", "moe_prepare_weights_mx",
     "moe_read_status", "moe_strerror", "moe_version",
 )
 
@@ -92,6 +92,7 @@ def lib():
                                  ctypes.c_size_t, _vp])
         L.moe_route_workspace_bytes.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_prepare_weights.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_prepare_weights_mx.argtypes = [_vp] * 10
         L.moe_read_status.argtypes = [_vp, _i32, _vp, ctypes.c_size_t,
                                       ctypes.POINTER(ctypes.c_int32), _vp]
         L.moe_strerror.argtypes = [ctypes.c_int]
@@ -221,6 +222,15 @@ def moe_prepare_weights(plan, w1, w2, w1_packed, w2_packed, stream=None):
     _check(rc, "moe_prepare_weights")
 
 
+def moe_prepare_weights_mx(plan, w1, w1_sf, w2, w2_sf, w1_packed, w1_sf_packed, w2_packed,
+                           w2_sf_packed, stream=None):
+    """Packed copies of MXFP4 weights and their scale codes for a packed MXFP4 plan."""
+    rc = lib().moe_prepare_weights_mx(plan, _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
+                                      _ptr(w1_packed), _ptr(w1_sf_packed), _ptr(w2_packed),
+                                      _ptr(w2_sf_packed), _stream(stream))
+    _check(rc, "moe_prepare_weights_mx")
+
+
 def moe_route_workspace_bytes(plan, num_tokens):
     n = ctypes.c_size_t()
     _check(lib().moe_route_workspace_bytes(plan, num_tokens, ctypes.byref(n)),
@@ -271,6 +281,15 @@ class MoEForward:
         p2 = torch.empty_like(w2)
         moe_prepare_weights(self.plan, w1, w2, p1, p2, stream)
         return p1, p2
+
+    def prepare_mx(self, w1, w1_sf, w2, w2_sf, stream=None):
+        """Packed copies of MXFP4 weights and scales (identity for row-major plans)."""
+        import torch
+        if self.weight_layout != MOE_WEIGHTS_PACKED:
+            return w1, w1_sf, w2, w2_sf
+        out = [torch.empty_like(t) for t in (w1, w1_sf, w2, w2_sf)]
+        moe_prepare_weights_mx(self.plan, w1, w1_sf, w2, w2_sf, *out, stream=stream)
+        return tuple(out)
 
     def forward(self, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y=None, stream=None):
         import torch

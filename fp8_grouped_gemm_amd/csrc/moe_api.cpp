@@ -228,9 +228,10 @@ int validate_shape(const moe_shape_t* s)
     if (s->recipe != MOE_RECIPE_FP8_BLOCK128 && s->recipe != MOE_RECIPE_MXFP4)
         return MOE_ERR_INVALID_ARG;
     if (s->recipe == MOE_RECIPE_MXFP4) {
-        if (s->tile_m == 128)
+        // the MXFP4 kernels address x with 32-bit buffer offsets
+        if (s->tile_m == 128 || (long long)s->max_tokens * s->hidden > 0x7FFFFFFFLL)
             return MOE_ERR_UNSUPPORTED_SHAPE;
-        if (s->weight_layout != MOE_WEIGHTS_ROW_MAJOR || (s->flags & MOE_FLAG_SINGLE_LAUNCH))
+        if (s->flags & MOE_FLAG_SINGLE_LAUNCH)
             return MOE_ERR_INVALID_ARG;
     }
     if ((s->flags & MOE_FLAG_SINGLE_LAUNCH) && (s->flags & MOE_FLAG_SPLIT_LAUNCH))
@@ -556,7 +557,7 @@ int moe_prepare_weights(moe_plan_t plan, const uint8_t* w1, const uint8_t* w2,
     if (!plan || !w1 || !w2 || !w1_packed || !w2_packed)
         return MOE_ERR_INVALID_ARG;
     const moe_shape_t& s = plan->shape;
-    if (s.weight_layout != MOE_WEIGHTS_PACKED)
+    if (s.weight_layout != MOE_WEIGHTS_PACKED || s.recipe != MOE_RECIPE_FP8_BLOCK128)
         return MOE_ERR_INVALID_ARG;
     const size_t b1 = (size_t)s.num_experts * 2 * s.intermediate * s.hidden;
     const size_t b2 = (size_t)s.num_experts * s.hidden * s.intermediate;
@@ -574,6 +575,44 @@ int moe_prepare_weights(moe_plan_t plan, const uint8_t* w1, const uint8_t* w2,
         return rc;
     if (moe::launch_pack(w1, w2, w1_packed, w2_packed, s.num_experts, s.hidden, s.intermediate,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_prepare_weights_mx(moe_plan_t plan, const uint8_t* w1, const uint8_t* w1_sf,
+                           const uint8_t* w2, const uint8_t* w2_sf, uint8_t* w1_packed,
+                           uint8_t* w1_sf_packed, uint8_t* w2_packed, uint8_t* w2_sf_packed,
+                           void* stream)
+{
+    if (!plan || !w1 || !w1_sf || !w2 || !w2_sf || !w1_packed || !w1_sf_packed || !w2_packed ||
+        !w2_sf_packed)
+        return MOE_ERR_INVALID_ARG;
+    const moe_shape_t& s = plan->shape;
+    if (s.weight_layout != MOE_WEIGHTS_PACKED || s.recipe != MOE_RECIPE_MXFP4)
+        return MOE_ERR_INVALID_ARG;
+    const size_t E = s.num_experts, H = s.hidden, I = s.intermediate;
+    const void* in[4] = {w1, w1_sf, w2, w2_sf};
+    const void* out[4] = {w1_packed, w1_sf_packed, w2_packed, w2_sf_packed};
+    const size_t nb[4] = {E * 2 * I * H / 2, E * 2 * I * H / 32, E * H * I / 2, E * H * I / 32};
+    auto overlap = [](const void* a, size_t na, const void* b, size_t nb2) {
+        const char* pa = static_cast<const char*>(a);
+        const char* pb = static_cast<const char*>(b);
+        return pa < pb + nb2 && pb < pa + na;
+    };
+    // the weights move 16 bytes at a time; the scales byte by byte
+    for (int i = 0; i < 4; i += 2)
+        if (reinterpret_cast<uintptr_t>(in[i]) % 16 || reinterpret_cast<uintptr_t>(out[i]) % 16)
+            return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j)
+            if (overlap(out[i], nb[i], in[j], nb[j]) || (j != i && overlap(out[i], nb[i], out[j], nb[j])))
+                return MOE_ERR_INVALID_ARG;
+    int rc = device_ok();
+    if (rc != MOE_OK)
+        return rc;
+    if (moe::launch_pack_mx(w1, w1_sf, w2, w2_sf, w1_packed, w1_sf_packed, w2_packed, w2_sf_packed,
+                            s.num_experts, s.hidden, s.intermediate,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
 }

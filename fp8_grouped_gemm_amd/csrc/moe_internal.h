@@ -91,5 +91,8 @@ hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_pack(const uint8_t* w1, const uint8_t* w2, uint8_t* w1p, uint8_t* w2p, int E,
                        int H, int I, hipStream_t s);
+hipError_t launch_pack_mx(const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2,
+                          const uint8_t* w2_sf, uint8_t* w1p, uint8_t* w1_sfp, uint8_t* w2p,
+                          uint8_t* w2_sfp, int E, int H, int I, hipStream_t s);
 
 }  // namespace moe

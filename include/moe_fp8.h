@@ -92,8 +92,8 @@ typedef struct moe_shape {
                               (128: H % 256 == 0 and I >= 256) */
     int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
     int32_t flags;         /* MOE_FLAG_* bits, 0 = defaults */
-    int32_t recipe;        /* MOE_RECIPE_*; MXFP4 plans: tile_m 0, 16, 32 or 64, row-major
-                              weights, no single launch */
+    int32_t recipe;        /* MOE_RECIPE_*; MXFP4 plans: tile_m 0, 16, 32 or 64, no single
+                              launch, max_tokens * H < 2^31 */
 } moe_shape_t;
 
 typedef struct moe_plan* moe_plan_t;
@@ -233,6 +233,28 @@ int moe_forward_mx_timed(moe_plan_t plan, int32_t num_tokens,
  */
 int moe_prepare_weights(moe_plan_t plan, const uint8_t* w1, const uint8_t* w2,
                         uint8_t* w1_packed, uint8_t* w2_packed, void* stream);
+
+/*
+ * One-time re-layout of FP8 x MXFP4 weights for plans with recipe =
+ * MOE_RECIPE_MXFP4 and weight_layout = MOE_WEIGHTS_PACKED (needs H % 256 ==
+ * 0); moe_forward_mx then takes the four packed arrays in place of w1,
+ * w1_sf, w2, w2_sf.
+ *   w1 [E,2I,H/2], w1_sf [E,2I,H/32], w2 [E,H,I/2], w2_sf [E,H,I/32]: the
+ *   row-major inputs (device, read only); the outputs have the same byte
+ *   sizes and must not overlap any input or each other; w1, w2 and their
+ *   packed copies 16-byte aligned.
+ * Packed order: for expert e, column tile n (L1: 128 gate + 128 up rows;
+ * L2: 256 rows), 128-wide K block kb, wave w (0..3), 16-row subtile s
+ * (0..3): 64 lanes x 16 bytes, lane l = 16*g + r holding bytes
+ * [64*kb + 16*g, 64*kb + 16*g + 16) of subtile row r (K values 128*kb + 32*g
+ * .. + 31), i.e. one wave's e2m1 MFMA operand; the scales in the same order,
+ * one byte per lane (code 4*kb + g of row r).
+ * Returns MOE_ERR_INVALID_ARG for any other plan.
+ */
+int moe_prepare_weights_mx(moe_plan_t plan, const uint8_t* w1, const uint8_t* w1_sf,
+                           const uint8_t* w2, const uint8_t* w2_sf, uint8_t* w1_packed,
+                           uint8_t* w1_sf_packed, uint8_t* w2_packed, uint8_t* w2_sf_packed,
+                           void* stream);
 
 /*
  * Routing planner alone (step 1) with an explicit row alignment in [1, 1024]

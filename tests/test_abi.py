@@ -285,10 +285,41 @@ def test_mx_recipe_validation_and_choices():
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_plan_create(256, 256, 4, 2, 8, tile_m=128, recipe=moe.MOE_RECIPE_MXFP4)
     assert ei.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE
-    for kw in (dict(weight_layout=moe.MOE_WEIGHTS_PACKED), dict(flags=moe.MOE_FLAG_SINGLE_LAUNCH)):
-        with pytest.raises(moe.MoEError) as ei:
-            moe.moe_plan_create(256, 256, 4, 2, 8, recipe=moe.MOE_RECIPE_MXFP4, **kw)
-        assert ei.value.code == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoEError) as ei:  # x must be addressable with 32-bit offsets
+        moe.moe_plan_create(65536, 256, 4, 2, 32768, recipe=moe.MOE_RECIPE_MXFP4)
+    assert ei.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_plan_create(256, 256, 4, 2, 8, recipe=moe.MOE_RECIPE_MXFP4,
+                            flags=moe.MOE_FLAG_SINGLE_LAUNCH)
+    assert ei.value.code == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoEError) as ei:  # packed needs whole 256-row L2 tiles
+        moe.moe_plan_create(384, 256, 4, 2, 8, recipe=moe.MOE_RECIPE_MXFP4,
+                            weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert ei.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE
+    # moe_prepare_weights_mx: only packed MXFP4 plans, no overlaps, aligned
+    # weights; moe_prepare_weights refuses MXFP4 plans (no HIP call is made)
+    L = moe.lib()
+    pk = moe.moe_plan_create(256, 256, 4, 2, 8, recipe=moe.MOE_RECIPE_MXFP4,
+                             weight_layout=moe.MOE_WEIGHTS_PACKED)
+    rm = moe.moe_plan_create(256, 256, 4, 2, 8, recipe=moe.MOE_RECIPE_MXFP4)
+    fp = moe.moe_plan_create(256, 256, 4, 2, 8, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    try:
+        M = 1 << 24
+        bufs = [ctypes.c_void_p(M * (i + 1)) for i in range(8)]
+        for plan in (rm, fp):
+            assert L.moe_prepare_weights_mx(plan, *bufs, None) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_prepare_weights(pk, bufs[0], bufs[2], bufs[4], bufs[6], None) == \
+            moe.MOE_ERR_INVALID_ARG
+        same = list(bufs)
+        same[4] = bufs[0]  # packed w1 over the input w1
+        assert L.moe_prepare_weights_mx(pk, *same, None) == moe.MOE_ERR_INVALID_ARG
+        mis = list(bufs)
+        mis[6] = ctypes.c_void_p(M * 7 + 8)  # packed w2 not 16-byte aligned
+        assert L.moe_prepare_weights_mx(pk, *mis, None) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_prepare_weights_mx(pk, None, *bufs[1:], None) == moe.MOE_ERR_INVALID_ARG
+    finally:
+        for plan in (pk, rm, fp):
+            moe.moe_plan_destroy(plan)
     p = moe.moe_plan_create(4096, 2048, 256, 6, 8192, recipe=moe.MOE_RECIPE_MXFP4)
     q = moe.moe_plan_create(4096, 2048, 256, 6, 8192)
     try:

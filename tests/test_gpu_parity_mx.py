@@ -34,15 +34,16 @@ def mx_case(T, H, I, E, K, seed, mask=None, skew=False):
     return host, {k: v.cuda() for k, v in inp.items()}
 
 
-def run_gpu_mx(dev, tile_m=0, max_tokens=None, runner=None):
+def run_gpu_mx(dev, tile_m=0, max_tokens=None, runner=None, weight_layout=0):
     T, H = dev["x"].shape
     E, twoI, _ = dev["w1"].shape
     K = dev["topk_idx"].shape[1]
     if runner is None:
         runner = moe.MoEForward(H, twoI // 2, E, K, max_tokens or T, tile_m=tile_m,
-                                recipe=moe.MOE_RECIPE_MXFP4)
-    y = runner.forward(dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_w"], dev["w1"],
-                       dev["w1_sf"], dev["w2"], dev["w2_sf"])
+                                recipe=moe.MOE_RECIPE_MXFP4, weight_layout=weight_layout)
+    w1, w1_sf, w2, w2_sf = runner.prepare_mx(dev["w1"], dev["w1_sf"], dev["w2"], dev["w2_sf"])
+    y = runner.forward(dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_w"], w1, w1_sf, w2,
+                       w2_sf)
     torch.cuda.synchronize()
     return y, runner
 
@@ -130,6 +131,17 @@ def test_mx_forward_deterministic_and_auto_tile():
     check_y(y1.cpu().numpy(), run_oracle_mx(host)["y"], what="auto tile")
 
 
+@pytest.mark.parametrize("tile_m", [16, 32, 64])
+def test_mx_packed_weights_match_row_major_bitwise(tile_m):
+    # the packed layout only changes where each operand byte is read from:
+    # same MFMAs in the same order, so y is bit-identical
+    host, dev = mx_case(37, 512, 384, 16, 4, 211, mask={(5, 1): -1, (20, 3): 40})
+    y_row, _ = run_gpu_mx(dev, tile_m=tile_m)
+    y_pk, _ = run_gpu_mx(dev, tile_m=tile_m, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert torch.equal(y_row, y_pk)
+    check_y(y_pk.cpu().numpy(), run_oracle_mx(host)["y"], what=f"packed tile {tile_m}")
+
+
 @pytest.mark.parametrize("T", [1, 3, 128])
 def test_mx_flash_decode_shape_sampled(T):
     # full flash-decode shape (256 experts, H 4096, I 2048) drawn on the GPU;
@@ -138,6 +150,8 @@ def test_mx_flash_decode_shape_sampled(T):
     cfg = wl.custom_config(T, base.H, base.I, base.E, base.K)
     dev = wl.make_inputs_mx(cfg, wl.default_seed(base), "cuda")
     y, runner = run_gpu_mx(dev)
+    y_pk, _ = run_gpu_mx(dev, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert torch.equal(y, y_pk)
     toks = list(range(T)) if T <= 8 else [0, 1, 37, 64, 99, T - 1]
     E = base.E
     idx = dev["topk_idx"].cpu().numpy()

@@ -35,8 +35,18 @@
 // the loop holds no other vector memory access and the explicit vmcnt
 // accounting stays exact.  The copy is issued as inline assembly: a batch
 // (one K block's copies, plus on a tile's first block one metadata copy) is
-// the same number of instructions in every wave, so "all but the newest
-// batch landed" is vmcnt <= that batch's size.
+// the same number of instructions in every wave, so "block j landed" is
+// vmcnt <= the sizes of the batches issued after it.
+//
+// FP8 x MXFP4 recipe (MX = true; the SM100 recipe of the "07 · MegaMoE"
+// page §0): e2m1 weights halve B to 16 KiB per K block (subtile = 16 rows x
+// 32 K-values per lane group, 1 KiB, the packed MXFP4 order of pack.hip),
+// and each stage carries the block's UE8M0 codes -- 4 per activation row
+// and 64 per weight subtile -- which the block-scaled MFMA
+// (mfma_16x16x128_e4m3_e2m1) applies itself, accumulating in f32.  With
+// 34 KiB stages, four fit and three blocks stay in flight.  L1's epilogue
+// requantises per 32 columns: one wave's gate columns, so no cross-wave
+// amax; sf = the smallest power of two >= max(amax, 1e-10)/448.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -46,23 +56,54 @@ namespace {
 
 constexpr int BM = 128, BN = 256;
 constexpr int A_BYTES = BM * 128;   // 16 KiB: 8 m-subtiles x 2 halves x 1 KiB
-constexpr int B_BYTES = BN * 128;   // 32 KiB: 16 n-subtiles x 2 halves x 1 KiB
 constexpr int S_BYTES = 8 * 256;    // one 256-byte scale copy per wave
-constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-constexpr int NSTAGE = 3;
 // Per-tile metadata slot: row_src of the 128 rows, top-k weight per row
 // (L1), the tile's expert replicated over 64 lanes.
 constexpr int META = 512 + 512 + 256;
 constexpr int NMETA = 4;
 constexpr int META_W = 512, META_E = 1024;
-constexpr int SMEM = NSTAGE * STAGE + NMETA * META;
 constexpr int kThreads = 512;
-constexpr int kCopiesPerBlock = 2 + 4 + 1;  // A halves, B halves, scales (per wave)
-static_assert(SMEM <= 160 * 1024, "LDS");
+
+// Stage geometry per recipe.  FP8: B = 16 n-subtiles x 2 halves x 1 KiB,
+// copies per wave and block = 2 A + 4 B + 1 scale.  MXFP4: B = 16 subtiles
+// x 1 KiB of e2m1, 2 A + 2 B + 1 scale.
+template <bool MX>
+struct LdsCfg {
+    static constexpr int B_BYTES = MX ? BN * 64 : BN * 128;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int NSTAGE = MX ? 4 : 3;
+    static constexpr int COPIES = MX ? 2 + 2 + 1 : 2 + 4 + 1;
+    static constexpr int SMEM = NSTAGE * STAGE + NMETA * META;
+};
+static_assert(LdsCfg<false>::SMEM <= 160 * 1024 && LdsCfg<true>::SMEM <= 160 * 1024, "LDS");
 
 // s_waitcnt with vmcnt = n (n < 16) and no wait on expcnt / lgkmcnt
 // (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 #define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0xF70 | (n))
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15] (the immediate must
+// be a constant).
+__device__ __forceinline__ void wait_vmcnt(int n)
+{
+    switch (n) {
+    case 0: MOE_WAIT_VMCNT(0); break;
+    case 1: MOE_WAIT_VMCNT(1); break;
+    case 2: MOE_WAIT_VMCNT(2); break;
+    case 3: MOE_WAIT_VMCNT(3); break;
+    case 4: MOE_WAIT_VMCNT(4); break;
+    case 5: MOE_WAIT_VMCNT(5); break;
+    case 6: MOE_WAIT_VMCNT(6); break;
+    case 7: MOE_WAIT_VMCNT(7); break;
+    case 8: MOE_WAIT_VMCNT(8); break;
+    case 9: MOE_WAIT_VMCNT(9); break;
+    case 10: MOE_WAIT_VMCNT(10); break;
+    case 11: MOE_WAIT_VMCNT(11); break;
+    case 12: MOE_WAIT_VMCNT(12); break;
+    case 13: MOE_WAIT_VMCNT(13); break;
+    case 14: MOE_WAIT_VMCNT(14); break;
+    default: MOE_WAIT_VMCNT(0); break;  // (never larger here; waiting for all is safe)
+    }
+}
 
 // Asynchronous copy global -> LDS of 16 (or 4) bytes per lane to
 // lds_base + 16 * lane (4 * lane).  lds_base is wave-uniform (read from the
@@ -120,13 +161,37 @@ __device__ __forceinline__ const uint8_t* weight_src(const FwdArgs& a, int e, in
     }
 }
 
+// MXFP4: address of the 16 bytes lane `lane` copies for weight subtile
+// q = 4 w + s of K block kb (packed: moe_prepare_weights_mx order).
+template <bool L1, bool PK>
+__device__ __forceinline__ const uint8_t* weight_src_mx(const FwdArgs& a, int e, int nt, int kb,
+                                                        int q, int lane)
+{
+    const int H = a.H, I = a.I;
+    const int K = L1 ? H : I;
+    if constexpr (PK) {
+        const int NT = L1 ? I / 128 : H / 256;
+        const uint8_t* base = L1 ? a.w1 : a.w2;
+        return base + (((size_t)e * NT + nt) * (K / 128) + kb) * 16384 + q * 1024 + lane * 16;
+    } else {
+        const int w4 = q >> 2, s = q & 3, lr = lane & 15, lg = lane >> 4;
+        const int row = L1 ? (s >= 2 ? I : 0) + nt * 128 + w4 * 32 + (s & 1) * 16 + lr
+                           : nt * 256 + w4 * 64 + s * 16 + lr;
+        const size_t n = (size_t)e * (L1 ? 2 * I : H) + row;
+        return (L1 ? a.w1 : a.w2) + n * (K / 2) + kb * 64 + lg * 16;
+    }
+}
+
 }  // namespace
 
 // L1 (gate + up) when L1 is true, L2 (down) otherwise.  Needs at least two
 // K blocks (H >= 256 and I >= 256; the plan enforces it).
-template <bool L1, bool PK>
+template <bool L1, bool PK, bool MX>
 __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 {
+    using C = LdsCfg<MX>;
+    constexpr int B_BYTES = C::B_BYTES, STAGE = C::STAGE, NSTAGE = C::NSTAGE;
+    constexpr int kCopiesPerBlock = C::COPIES;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const int H = a.H, I = a.I, K = a.K, T = a.T;
     const int NT = L1 ? I / 128 : H / 256;
@@ -196,6 +261,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     int i_e = 0, i_nt = 0;
     const uint8_t* a_src[2] = {nullptr, nullptr};
     const float* s_src = nullptr;
+    const uint8_t* s_src_mx = nullptr;  // MXFP4: this wave's 4 scale bytes per lane
+    uint32_t s_stride = 0;              // bytes between K blocks of s_src_mx
     // Starts issuing tile k: reads its expert and row sources from its
     // metadata slot (landed and visible: copied with tile k - 1's first
     // block, at least two batches and one barrier ago).
@@ -229,20 +296,54 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             else
                 a_src[j] = a.h + (size_t)r * I + j * 64 + 16 * lg;
         }
-        // Scales: lanes 16 and 17 the block's two weight scales (L1: gate
-        // and up block of column tile nt; L2: blocks 2 nt, 2 nt + 1), the
-        // other lanes the activation scale of row 16 v + (lane & 15).
-        if (lane == 16 || lane == 17) {
-            const int q = lane - 16;
-            if constexpr (L1)
-                s_src = a.w1_sf + ((size_t)e * (2 * I / 128) + (q ? I / 128 + nt : nt)) * nkb;
-            else
-                s_src = a.w2_sf + ((size_t)e * (H / 128) + 2 * nt + q) * nkb;
+        if constexpr (MX) {
+            // UE8M0 codes of K block kb, 4 bytes per lane: waves 0-1 the
+            // activation rows 64 wave + lane (a padding row: token 0 resp.
+            // the block's first row), waves 2-5 the weight subtile rows
+            // 64 (wave - 2) + lane (packed: that part of the block's 1 KiB),
+            // waves 6-7 a spare copy of row 0's codes (every wave issues the
+            // same copies).
+            const int HS = H / 32, IS = I / 32;
+            const int rr = wave < 2 ? wave * 64 + lane : lane;
+            const int fr = reinterpret_cast<const int32_t*>(slot(k))[rr];
+            if (wave < 2 || wave >= 6) {
+                const bool spare = wave >= 6;
+                if constexpr (L1)
+                    s_src_mx = a.x_sfq + (size_t)(fr >= 0 && !spare ? fr / K : 0) * HS;
+                else
+                    s_src_mx = a.h_sfq + (size_t)(row0 + (fr >= 0 && !spare ? rr : 0)) * IS;
+                s_stride = 4;
+            } else {
+                const int i = (wave - 2) * 64 + lane;
+                const uint8_t* wsf = L1 ? a.w1_sfq : a.w2_sfq;
+                if constexpr (PK) {
+                    const int NT2 = L1 ? I / 128 : H / 256;
+                    s_src_mx = wsf + ((size_t)e * NT2 + nt) * nkb * 1024 + i * 4;
+                    s_stride = 1024;
+                } else {
+                    const int w4 = i >> 6, sq = (i >> 4) & 3, r2 = i & 15;
+                    const int row = L1 ? (sq >= 2 ? I : 0) + nt * 128 + w4 * 32 + (sq & 1) * 16 + r2
+                                       : nt * 256 + w4 * 64 + sq * 16 + r2;
+                    s_src_mx = wsf + ((size_t)e * (L1 ? 2 * I : H) + row) * (L1 ? HS : IS);
+                    s_stride = 4;
+                }
+            }
         } else {
-            if constexpr (L1)
-                s_src = a.x_sf + (size_t)(f >= 0 ? f / K : 0) * (H / 128);
-            else
-                s_src = a.h_sf + (size_t)r * (I / 128);
+            // Scales: lanes 16 and 17 the block's two weight scales (L1:
+            // gate and up block of column tile nt; L2: blocks 2 nt, 2 nt + 1),
+            // the other lanes the activation scale of row 16 v + (lane & 15).
+            if (lane == 16 || lane == 17) {
+                const int q = lane - 16;
+                if constexpr (L1)
+                    s_src = a.w1_sf + ((size_t)e * (2 * I / 128) + (q ? I / 128 + nt : nt)) * nkb;
+                else
+                    s_src = a.w2_sf + ((size_t)e * (H / 128) + 2 * nt + q) * nkb;
+            } else {
+                if constexpr (L1)
+                    s_src = a.x_sf + (size_t)(f >= 0 ? f / K : 0) * (H / 128);
+                else
+                    s_src = a.h_sf + (size_t)r * (I / 128);
+            }
         }
     };
     // Issues the next block; returns the batch size (0 when nothing is left).
@@ -263,12 +364,21 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             dma16(a_src[j] + (size_t)kb * 128, st + (wave * 2 + j) * 1024);
+        if constexpr (MX) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int q = wave * 4 + j, sub = q >> 1, half = q & 1;
-            dma16(weight_src<L1, PK>(a, i_e, i_nt, kb, sub, half, lane), st + A_BYTES + q * 1024);
+            for (int j = 0; j < 2; ++j) {
+                const int q = wave * 2 + j;
+                dma16(weight_src_mx<L1, PK>(a, i_e, i_nt, kb, q, lane), st + A_BYTES + q * 1024);
+            }
+            dma4(s_src_mx + (size_t)kb * s_stride, st + A_BYTES + B_BYTES + wave * 256);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q = wave * 4 + j, sub = q >> 1, half = q & 1;
+                dma16(weight_src<L1, PK>(a, i_e, i_nt, kb, sub, half, lane), st + A_BYTES + q * 1024);
+            }
+            dma4(s_src + kb, st + A_BYTES + B_BYTES + wave * 256);
         }
-        dma4(s_src + kb, st + A_BYTES + B_BYTES + wave * 256);
         int n = kCopiesPerBlock;
         if (kb == 0) {
             issue_meta(i_k);
@@ -292,9 +402,13 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         MOE_WAIT_VMCNT(0);
         __syncthreads();
     }
-    const int b0 = issue_next();
-    int last = issue_next();  // size of the newest batch
-    (void)b0;
+    // Blocks 0 .. NSTAGE - 2 in flight; pend[] = the sizes of the batches
+    // issued after the block the next step multiplies, oldest first.
+    (void)issue_next();
+    int pend[NSTAGE - 2];
+#pragma unroll
+    for (int q = 0; q < NSTAGE - 2; ++q)
+        pend[q] = issue_next();
 
     v4f acc[4][4];
 #pragma unroll
@@ -312,49 +426,92 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         // Block j has landed (its batch is not the newest one) and is visible
         // to all waves; the previous step's fragment reads are done, so the
         // stage issued below is free.
-        if (drain || last == 0)
-            MOE_WAIT_VMCNT(0);
-        else if (last == kCopiesPerBlock)
-            MOE_WAIT_VMCNT(kCopiesPerBlock);
-        else
-            MOE_WAIT_VMCNT(kCopiesPerBlock + 1);
+        if constexpr (NSTAGE == 3) {  // one newer batch: its size is one of three
+            if (drain || pend[0] == 0)
+                MOE_WAIT_VMCNT(0);
+            else if (pend[0] == kCopiesPerBlock)
+                MOE_WAIT_VMCNT(kCopiesPerBlock);
+            else
+                MOE_WAIT_VMCNT(kCopiesPerBlock + 1);
+        } else {
+            int newer = 0;
+#pragma unroll
+            for (int q = 0; q < NSTAGE - 2; ++q)
+                newer += pend[q];
+            wait_vmcnt(drain ? 0 : newer);
+        }
         drain = false;
         __syncthreads();
 
         const uint8_t* st = smem + (j % NSTAGE) * STAGE;
-        v8i af[4], bf[4];
-        float sa[4][4];
-        const float* s_lds = reinterpret_cast<const float*>(st + A_BYTES + B_BYTES);
+        // the copy of the block NSTAGE - 1 ahead, into the stage read last step
+        auto issue_shift = [&]() {
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-            af[ms] = lds_frag(st + ((wm * 4 + ms) * 2) * 1024, lane);
-            const float4 s4 = *reinterpret_cast<const float4*>(s_lds + (wm * 4 + ms) * 64 + 4 * lg);
-            sa[ms][0] = s4.x;
-            sa[ms][1] = s4.y;
-            sa[ms][2] = s4.z;
-            sa[ms][3] = s4.w;
-        }
+            for (int q = 0; q + 1 < NSTAGE - 2; ++q)
+                pend[q] = pend[q + 1];
+            pend[NSTAGE - 3] = issue_next();
+        };
+        if constexpr (MX) {
+            // A as for FP8; B: subtile wn*4 + s, 16 bytes of e2m1 per lane;
+            // codes: activation row r at byte 4 r + lg, weight subtile bytes
+            // after them (packed: per lane; row-major: 4 per subtile row).
+            const uint8_t* s_lds = st + A_BYTES + B_BYTES;
+            v8i af[4];
+            uint4 bf[4];
+            int sa[4], sb[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            bf[s] = lds_frag(st + A_BYTES + (wn * 4 + s) * 2048, lane);
-        // weight scales: L1 gate / up block; L2 the wave's 128-column block
-        const float sg = L1 ? s_lds[16] : s_lds[16 + (wn >> 1)];
-        const float su = L1 ? s_lds[17] : sg;
+            for (int ms = 0; ms < 4; ++ms) {
+                af[ms] = lds_frag(st + ((wm * 4 + ms) * 2) * 1024, lane);
+                sa[ms] = s_lds[(wm * 64 + ms * 16 + lr) * 4 + lg];
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf[s] = *reinterpret_cast<const uint4*>(st + A_BYTES + (wn * 4 + s) * 1024 + lane * 16);
+                sb[s] = PK ? s_lds[512 + (wn * 4 + s) * 64 + lane]
+                           : s_lds[512 + ((wn * 4 + s) * 16 + lr) * 4 + lg];
+            }
+            issue_shift();
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int ms = 0; ms < 4; ++ms)
+                    acc[ms][s] = mfma_16x16x128_e4m3_e2m1(af[ms], e2m1_operand(bf[s]), acc[ms][s],
+                                                          sa[ms], sb[s]);
+        } else {
+            v8i af[4], bf[4];
+            float sa[4][4];
+            const float* s_lds = reinterpret_cast<const float*>(st + A_BYTES + B_BYTES);
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                af[ms] = lds_frag(st + ((wm * 4 + ms) * 2) * 1024, lane);
+                const float4 s4 = *reinterpret_cast<const float4*>(s_lds + (wm * 4 + ms) * 64 + 4 * lg);
+                sa[ms][0] = s4.x;
+                sa[ms][1] = s4.y;
+                sa[ms][2] = s4.z;
+                sa[ms][3] = s4.w;
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                bf[s] = lds_frag(st + A_BYTES + (wn * 4 + s) * 2048, lane);
+            // weight scales: L1 gate / up block; L2 the wave's 128-column block
+            const float sg = L1 ? s_lds[16] : s_lds[16 + (wn >> 1)];
+            const float su = L1 ? s_lds[17] : sg;
 
-        last = issue_next();
+            issue_shift();
 
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const float sb = (L1 && s >= 2) ? su : sg;
-            v4f p[4];
+            for (int s = 0; s < 4; ++s) {
+                const float sb = (L1 && s >= 2) ? su : sg;
+                v4f p[4];
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
-                p[ms] = mfma_16x16x128_e4m3(af[ms], bf[s], v4f{0.f, 0.f, 0.f, 0.f});
+                for (int ms = 0; ms < 4; ++ms)
+                    p[ms] = mfma_16x16x128_e4m3(af[ms], bf[s], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
+                for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[ms][i], acc[ms][s][i]);
+                    for (int i = 0; i < 4; ++i)
+                        acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[ms][i], acc[ms][s][i]);
+            }
         }
         ++j;
         if (++m_kb < nkb)
@@ -372,7 +529,37 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         uint8_t* ep = smem + ((j - 1) % NSTAGE) * STAGE;
         const int32_t* m_rs = reinterpret_cast<const int32_t*>(slot(m_k));
         __syncthreads();
-        if constexpr (L1) {
+        if constexpr (L1 && MX) {
+            // acc[ms][s] as below; wave wn's 32 gate columns are one 32-wide
+            // requantisation block of each of its rows: amax over them, the
+            // power-of-two scale as a UE8M0 code, codes staged in LDS.
+            const float* m_w = reinterpret_cast<const float*>(slot(m_k) + META_W);
+            uint8_t* qt = ep;  // [128][128]
+            const int IS = I / 32;
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wm * 64 + ms * 16 + 4 * lg + i;
+                    const bool valid = m_rs[r] >= 0;
+                    const float w = valid ? m_w[r] : 0.f;
+                    const float v0 = (silu(acc[ms][0][i]) * acc[ms][2][i]) * w;
+                    const float v1 = (silu(acc[ms][1][i]) * acc[ms][3][i]) * w;
+                    const float amax = max16(fmaxf(fabsf(v0), fabsf(v1)));
+                    const uint32_t code = min(e8m0_ceil_code(fmaxf(amax, 1e-10f) / 448.0f), 253u);
+                    const float inv = e8m0_inverse(code);
+                    qt[r * 128 + wn * 32 + lr] = (uint8_t)f32_to_e4m3_hw(v0 * inv);
+                    qt[r * 128 + wn * 32 + 16 + lr] = (uint8_t)f32_to_e4m3_hw(v1 * inv);
+                    if (lr == 0 && valid)
+                        a.h_sfq[(size_t)(row0 + r) * IS + nt * 4 + wn] = (uint8_t)code;
+                }
+            __syncthreads();
+            for (int c = threadIdx.x; c < BM * 8; c += kThreads) {
+                const int r = c >> 3, col = (c & 7) * 16;
+                *reinterpret_cast<uint4*>(a.h + (size_t)(row0 + r) * I + nt * 128 + col) =
+                    *reinterpret_cast<const uint4*>(qt + r * 128 + col);
+            }
+        } else if constexpr (L1) {
             // acc[ms][s]: rows wm*64 + 16 ms + 4 lg + i; s = 0,1 gate column
             // 32 wn + 16 s + lr of the block, s = 2,3 the matching up column.
             const float* m_w = reinterpret_cast<const float*>(slot(m_k) + META_W);
@@ -462,9 +649,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     }
 }
 
-size_t gemm_lds_smem_bytes() { return (size_t)SMEM; }
-
-template <bool L1>
+template <bool L1, bool MX>
 static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
 {
     const int NT = L1 ? a.I / 128 : a.H / 256;
@@ -472,7 +657,9 @@ static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
     const int nkb = L1 ? a.H / 128 : a.I / 128;
     if (n_tiles <= 0)
         return hipSuccess;
-    if (nkb < 2)
+    // a tile's metadata copy must land before that tile's first block is
+    // issued, NSTAGE - 1 blocks ahead of the multiply
+    if (nkb < LdsCfg<MX>::NSTAGE - 1)
         return hipErrorInvalidValue;
     int dev = 0, cus = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -484,8 +671,8 @@ static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
     if (a.grid_cap > 0 && g > a.grid_cap)
         g = a.grid_cap;
     const dim3 grid((unsigned)g);
-    const size_t smem = gemm_lds_smem_bytes();
-    auto kern = a.packed ? gemm_lds<L1, true> : gemm_lds<L1, false>;
+    const size_t smem = (size_t)LdsCfg<MX>::SMEM;
+    auto kern = a.packed ? gemm_lds<L1, true, MX> : gemm_lds<L1, false, MX>;
     err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (err != hipSuccess)
         return err;
@@ -493,7 +680,13 @@ static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s) { return launch_lds<true>(a, s); }
-hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s) { return launch_lds<false>(a, s); }
+hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s)
+{
+    return a.mx ? launch_lds<true, true>(a, s) : launch_lds<true, false>(a, s);
+}
+hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s)
+{
+    return a.mx ? launch_lds<false, true>(a, s) : launch_lds<false, false>(a, s);
+}
 
 }  // namespace moe

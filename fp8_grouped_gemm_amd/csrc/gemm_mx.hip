@@ -39,14 +39,6 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ v8i e2m1_operand(const uint4& v)
-{
-    v8i r;
-    r[0] = (int)v.x; r[1] = (int)v.y; r[2] = (int)v.z; r[3] = (int)v.w;
-    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
-    return r;
-}
-
 // Operands of two consecutive 128-K blocks (a final half step repeats the
 // first block's loads and multiplies it once).
 template <int MT>

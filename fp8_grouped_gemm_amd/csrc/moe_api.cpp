@@ -34,7 +34,14 @@ struct Config {
 // Beyond ~24 rows per expert the 128 x 256 LDS-staged MFMA tile takes over
 // (it needs H % 256 == 0 for its 256-column L2 tiles and I >= 256 for at
 // least two K blocks in L2; otherwise 64-row direct-load tiles).
-// The FP8 x MXFP4 recipe has direct-load tiles only (16, 32, 64 rows).
+// The LDS tile keeps NSTAGE - 1 K blocks in flight and needs that many per
+// layer: 2 for the FP8 recipe, 3 for FP8 x MXFP4.
+bool lds_tile_fits(const moe_shape_t& s)
+{
+    const int min_kb = s.recipe == MOE_RECIPE_MXFP4 ? 3 : 2;
+    return s.hidden % 256 == 0 && s.hidden / 128 >= min_kb && s.intermediate / 128 >= min_kb;
+}
+
 Config choose_config(const moe_shape_t& s, int T)
 {
     if (s.tile_m > 0)
@@ -44,7 +51,7 @@ Config choose_config(const moe_shape_t& s, int T)
         return Config{16, 0};
     if (rows <= 24.0)
         return Config{32, 0};
-    if (s.recipe == MOE_RECIPE_FP8_BLOCK128 && s.hidden % 256 == 0 && s.intermediate >= 256)
+    if (lds_tile_fits(s))
         return Config{128, 1};
     return Config{64, 0};
 }
@@ -216,7 +223,9 @@ int validate_shape(const moe_shape_t* s)
     if (s->tile_m != 0 && s->tile_m != 16 && s->tile_m != 32 && s->tile_m != 64 &&
         s->tile_m != 128)
         return MOE_ERR_UNSUPPORTED_SHAPE;
-    if (s->tile_m == 128 && (s->hidden % 256 || s->intermediate < 256))
+    if (s->recipe != MOE_RECIPE_FP8_BLOCK128 && s->recipe != MOE_RECIPE_MXFP4)
+        return MOE_ERR_INVALID_ARG;
+    if (s->tile_m == 128 && !lds_tile_fits(*s))
         return MOE_ERR_UNSUPPORTED_SHAPE;
     if (s->weight_layout != MOE_WEIGHTS_ROW_MAJOR && s->weight_layout != MOE_WEIGHTS_PACKED)
         return MOE_ERR_INVALID_ARG;
@@ -225,11 +234,9 @@ int validate_shape(const moe_shape_t* s)
     if (s->flags & ~(MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_SPLIT_LAUNCH | MOE_FLAG_TEST_NO_WAIT |
                      MOE_FLAG_TEST_SMALL_GRID))
         return MOE_ERR_INVALID_ARG;
-    if (s->recipe != MOE_RECIPE_FP8_BLOCK128 && s->recipe != MOE_RECIPE_MXFP4)
-        return MOE_ERR_INVALID_ARG;
     if (s->recipe == MOE_RECIPE_MXFP4) {
         // the MXFP4 kernels address x with 32-bit buffer offsets
-        if (s->tile_m == 128 || (long long)s->max_tokens * s->hidden > 0x7FFFFFFFLL)
+        if ((long long)s->max_tokens * s->hidden > 0x7FFFFFFFLL)
             return MOE_ERR_UNSUPPORTED_SHAPE;
         if (s->flags & MOE_FLAG_SINGLE_LAUNCH)
             return MOE_ERR_INVALID_ARG;
@@ -422,6 +429,10 @@ int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, 
     if (misaligned(workspace, 256) || misaligned(op.x, 16) || misaligned(op.w1, 16) ||
         misaligned(op.w2, 16) || misaligned(op.y, 16))
         return MOE_ERR_INVALID_ARG;
+    // MXFP4 scale codes are copied 4 bytes at a time by the LDS tiles (f32
+    // scales are naturally aligned)
+    if (misaligned(op.x_sf, 4) || misaligned(op.w1_sf, 4) || misaligned(op.w2_sf, 4))
+        return MOE_ERR_INVALID_ARG;
     const Layout L = make_layout(s, T);
     if (workspace_bytes < L.total)
         return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -491,12 +502,12 @@ int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, 
             return MOE_ERR_HIP;
         return MOE_OK;
     }
-    if (mx) {
+    if (mx && L.kernel == 0) {
         if (moe::launch_l1_mx(a, st) != hipSuccess || !mark(2))
             return MOE_ERR_HIP;
         if (moe::launch_l2_mx(a, st) != hipSuccess || !mark(3))
             return MOE_ERR_HIP;
-    } else {
+    } else {  // the LDS tiles serve both recipes
         if (moe::launch_l1(a, L.kernel, st) != hipSuccess || !mark(2))
             return MOE_ERR_HIP;
         if (moe::launch_l2(a, L.kernel, st) != hipSuccess || !mark(3))

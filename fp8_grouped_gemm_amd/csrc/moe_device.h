@@ -38,6 +38,16 @@ __device__ __forceinline__ v4f mfma_16x16x128_e4m3_e2m1(const v8i& a, const v8i&
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
 }
 
+// The e2m1 operand of mfma_16x16x128_e4m3_e2m1: a lane's 16 bytes in the
+// low half (the upper half is not read).
+__device__ __forceinline__ v8i e2m1_operand(const uint4& v)
+{
+    v8i r;
+    r[0] = (int)v.x; r[1] = (int)v.y; r[2] = (int)v.z; r[3] = (int)v.w;
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+}
+
 // UE8M0 code of the smallest power of two >= s, for a positive normal f32 s
 // (the f32 exponent field has the same bias, 127, as UE8M0).
 __device__ __forceinline__ uint32_t e8m0_ceil_code(float s)

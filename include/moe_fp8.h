@@ -89,11 +89,11 @@ typedef struct moe_shape {
     int32_t top_k;         /* K */
     int32_t max_tokens;    /* largest T any call on this plan may pass */
     int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128
-                              (128: H % 256 == 0 and I >= 256) */
+                              (128: H % 256 == 0 and I >= 256; MXFP4: I >= 384) */
     int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
     int32_t flags;         /* MOE_FLAG_* bits, 0 = defaults */
-    int32_t recipe;        /* MOE_RECIPE_*; MXFP4 plans: tile_m 0, 16, 32 or 64, no single
-                              launch, max_tokens * H < 2^31 */
+    int32_t recipe;        /* MOE_RECIPE_*; MXFP4 plans: no single launch,
+                              max_tokens * H < 2^31, tile_m 128 needs H, I >= 384 */
 } moe_shape_t;
 
 typedef struct moe_plan* moe_plan_t;
@@ -199,7 +199,8 @@ int moe_forward_timed(moe_plan_t plan, int32_t num_tokens,
  * with sf = the smallest power of two >= max(amax, 1e-10)/448 (a UE8M0
  * code), q = e4m3(h / sf) ("07 · MegaMoE" §8 per-block UE8M0 scale).
  * Scale codes of 0xFF (NaN) give NaN in the rows they touch.
- * x, w1, w2 and y must be 16-byte aligned, workspace 256-byte aligned.
+ * x, w1, w2 and y must be 16-byte aligned, x_sf, w1_sf and w2_sf 4-byte
+ * aligned, workspace 256-byte aligned.
  */
 int moe_forward_mx(moe_plan_t plan, int32_t num_tokens,
                    const uint8_t* x, const uint8_t* x_sf,

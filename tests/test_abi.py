@@ -282,9 +282,13 @@ def test_mx_recipe_validation_and_choices():
     with pytest.raises(moe.MoEError) as ei:
         moe.moe_plan_create(256, 256, 4, 2, 8, recipe=2)
     assert ei.value.code == moe.MOE_ERR_INVALID_ARG
-    with pytest.raises(moe.MoEError) as ei:
-        moe.moe_plan_create(256, 256, 4, 2, 8, tile_m=128, recipe=moe.MOE_RECIPE_MXFP4)
-    assert ei.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE
+    # the MXFP4 LDS tile keeps three K blocks in flight: H, I >= 384
+    for H, I in ((256, 256), (512, 256)):
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_plan_create(H, I, 4, 2, 8, tile_m=128, recipe=moe.MOE_RECIPE_MXFP4)
+        assert ei.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE
+    moe.moe_plan_destroy(moe.moe_plan_create(512, 384, 4, 2, 8, tile_m=128,
+                                             recipe=moe.MOE_RECIPE_MXFP4))
     with pytest.raises(moe.MoEError) as ei:  # x must be addressable with 32-bit offsets
         moe.moe_plan_create(65536, 256, 4, 2, 32768, recipe=moe.MOE_RECIPE_MXFP4)
     assert ei.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE
@@ -325,8 +329,9 @@ def test_mx_recipe_validation_and_choices():
     try:
         for T in (1, 2, 8, 128, 1024, 8192):
             info = moe.moe_plan_info(p, T)
-            # direct-load tiles only, no split-K, one L2 tile per workgroup
-            assert info["tile_m"] in (16, 32, 64) and info["kernel"] == 0, T
+            # the same tile choice as FP8 (LDS tiles from ~24 rows per
+            # expert), no split-K, one L2 tile per workgroup
+            assert info["tile_m"] == moe.moe_plan_info(q, T)["tile_m"], T
             assert info["l1_split"] == 1 and info["l2_group_tiles"] == 1 and \
                 info["single_launch"] == 0, T
             # same workspace as the FP8 plan (h_sf: I/32 bytes = I/128 floats per row)

@@ -142,6 +142,47 @@ def test_mx_packed_weights_match_row_major_bitwise(tile_m):
     check_y(y_pk.cpu().numpy(), run_oracle_mx(host)["y"], what=f"packed tile {tile_m}")
 
 
+@pytest.mark.parametrize("case", ["hot", "ragged"])
+def test_mx_lds_tile_128(case):
+    # LDS-staged persistent 128-row tiles: intermediates against the oracle,
+    # packed weights bit-identical to row-major, and a 4-workgroup grid (each
+    # workgroup walking many tiles across tile boundaries) bit-identical to
+    # the full grid
+    if case == "hot":
+        host, dev = mx_case(300, 512, 384, 4, 3, 411, skew=True)
+    else:
+        host, dev = mx_case(157, 768, 512, 6, 2, 412, mask={(3, 0): -1, (40, 1): 77})
+    y, runner = check_case(host, dev, 128, f"LDS tile 128 {case}")
+    assert moe.moe_plan_info(runner.plan, dev["x"].shape[0])["kernel"] == 1
+    y_pk, _ = run_gpu_mx(dev, tile_m=128, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert torch.equal(y, y_pk)
+    T, H = dev["x"].shape
+    E, twoI, _ = dev["w1"].shape
+    small = moe.MoEForward(H, twoI // 2, E, dev["topk_idx"].shape[1], T, tile_m=128,
+                           recipe=moe.MOE_RECIPE_MXFP4, flags=moe.MOE_FLAG_TEST_SMALL_GRID)
+    y_small, _ = run_gpu_mx(dev, runner=small)
+    assert torch.equal(y, y_small)
+
+
+def test_mx_flash_prefill_full_size_sampled():
+    cfg = wl.CONFIGS["flash_prefill"]
+    dev = wl.make_inputs_mx(cfg, wl.default_seed(cfg), "cuda")
+    y, runner = run_gpu_mx(dev, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert moe.moe_plan_info(runner.plan, cfg.T)["tile_m"] == 128
+    toks = [0, 1, 517, 1024, 1999, cfg.T - 1]
+    E = cfg.E
+    idx = dev["topk_idx"].cpu().numpy()
+    need = sorted({int(e) for e in idx[toks].reshape(-1) if 0 <= e < E})
+    sel = lambda t: [t[e].cpu().numpy() if e in need else None for e in range(E)]
+    host = dict(x=dev["x"].cpu().numpy(), x_sf=dev["x_sf"].cpu().numpy(), idx=idx,
+                w=dev["topk_w"].cpu().numpy(), w1=sel(dev["w1"]), w1_sf=sel(dev["w1_sf"]),
+                w2=sel(dev["w2"]), w2_sf=sel(dev["w2_sf"]))
+    ref = run_oracle_mx(host, tokens=toks)
+    check_y(y.cpu().numpy()[toks], ref["y"], per_token_tol=1e-2, what="flash prefill MX")
+    del dev
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("T", [1, 3, 128])
 def test_mx_flash_decode_shape_sampled(T):
     # full flash-decode shape (256 experts, H 4096, I 2048) drawn on the GPU;

@@ -182,6 +182,8 @@ def main():
     ap.add_argument("--launch", choices=("auto", "single", "split"), default="auto",
                     help="single: L1, L2 and combine in one cooperative launch (direct "
                          "tiles); split: one launch per step; auto: the library's choice")
+    ap.add_argument("--tile-m", type=int, default=0, choices=(0, 16, 32, 64, 128),
+                    help="rows per GEMM tile (0 = the library's choice per call)")
     ap.add_argument("--recipe", choices=("fp8", "mxfp4"), default="fp8",
                     help="fp8: e4m3 x e4m3 with f32 block scales (1x128, 128x128); mxfp4: "
                          "e4m3 activations x e2m1 weights with UE8M0 scales per 32 "
@@ -234,7 +236,8 @@ def main():
     layout = moe.MOE_WEIGHTS_PACKED if args.weights == "packed" else moe.MOE_WEIGHTS_ROW_MAJOR
     flags = {"auto": 0, "single": moe.MOE_FLAG_SINGLE_LAUNCH,
              "split": moe.MOE_FLAG_SPLIT_LAUNCH}[args.launch]
-    runner = moe.MoEForward(cfg.H, cfg.I, cfg.E, cfg.K, cfg.T, device=dev, weight_layout=layout,
+    runner = moe.MoEForward(cfg.H, cfg.I, cfg.E, cfg.K, cfg.T, tile_m=args.tile_m, device=dev,
+                            weight_layout=layout,
                             recipe=moe.MOE_RECIPE_MXFP4 if mx else moe.MOE_RECIPE_FP8_BLOCK128,
                             flags=flags)
     info = moe.moe_plan_info(runner.plan, cfg.T)

@@ -311,8 +311,10 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
         count_done(a.sync + kSyncReady + mb);
 }
 
+// 32-row tiles: bounded to two waves per SIMD (<= 256 VGPRs, no spills; 260
+// unbounded, i.e. one wave per SIMD).
 template <int MT, int S, bool PK>
-__global__ __launch_bounds__(256) void l1_direct(FwdArgs a)
+__global__ __launch_bounds__(256, MT == 2 ? 2 : 1) void l1_direct(FwdArgs a)
 {
     l1_tile<MT, S, PK, false>(a, blockIdx.x);
 }
@@ -467,7 +469,7 @@ __device__ __forceinline__ void l2_tile(const FwdArgs& a, int tile, int hint = 0
 }
 
 template <int MT, bool PK, int WV = 4>
-__global__ __launch_bounds__(WV * 64) void l2_direct(FwdArgs a)
+__global__ __launch_bounds__(WV * 64, MT == 2 && PK ? 2 : 1) void l2_direct(FwdArgs a)
 {
     l2_tile_body<MT, PK, false, WV>(a, blockIdx.x, 0);
 }

@@ -6,7 +6,8 @@ both the CPU oracle and the HIP path consume exactly the bytes it returns.
 
 Recipe (one per workload, all synthetic, standing in for the model shapes
 the DeepGEMM MegaMoE pages benchmark: DeepSeek "Flash" 4096/2048/256/top-6,
-"Pro" 7168/3072/384/top-6, and a skewed-routing stress):
+"Pro" 7168/3072/384/top-6, a skewed-routing stress, and one GPU's expert
+share of the flash layer under 8-way expert parallelism):
   x        f32 N(0,1) [T,H], quantised per 1x128 block
   W1[e]    f32 N(0, 1/sqrt(H)) [2I,H] (gate rows, then up rows), per 128x128
   W2[e]    f32 N(0, 1/sqrt(I)) [H,I], per 128x128
@@ -51,6 +52,10 @@ CONFIGS = {
     "flash_prefill": MoEConfig("flash_prefill", 2048, 4096, 2048, 256, 6),
     "pro_prefill": MoEConfig("pro_prefill", 8192, 7168, 3072, 384, 6),
     "skewed": MoEConfig("skewed", 4096, 4096, 2048, 256, 8, skew=True),
+    # one GPU's share of the flash layer under 8-way expert parallelism at
+    # 128 tokens per rank: 32 resident experts receiving 768 routed rows
+    # (~24 per expert, 805 MB of FP8 weights)
+    "flash_decode_ep8": MoEConfig("flash_decode_ep8", 128, 4096, 2048, 32, 6),
 }
 
 TAG_LOGITS, TAG_X, TAG_W1, TAG_W2, TAG_PERM = 0, 1, 2, 3, 4

@@ -51,7 +51,8 @@ def assert_route_equal(idx, E, K, ra, what):
     assert status[1] == bad and status[0] == (1 if bad else 0), what
 
 
-@pytest.mark.parametrize("name", ["tiny", "flash_decode", "flash_prefill", "pro_prefill", "skewed"])
+@pytest.mark.parametrize("name", ["tiny", "flash_decode", "flash_prefill", "pro_prefill", "skewed",
+                                  "flash_decode_ep8"])
 @pytest.mark.parametrize("ra", [16, 64, 128])
 def test_route_bitexact_workloads(name, ra):
     cfg = wl.CONFIGS[name]
@@ -379,7 +380,8 @@ def test_forward_zero_tokens_is_noop():
 # -------------------------------------------------- full-size workloads
 
 
-@pytest.mark.parametrize("name", ["flash_decode", "flash_prefill", "skewed", "pro_prefill"])
+@pytest.mark.parametrize("name", ["flash_decode", "flash_prefill", "skewed", "pro_prefill",
+                                  "flash_decode_ep8"])
 def test_forward_full_size_sampled(name):
     cfg = wl.CONFIGS[name]
     seed = wl.default_seed(cfg)

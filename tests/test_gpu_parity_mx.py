@@ -183,6 +183,24 @@ def test_mx_flash_prefill_full_size_sampled():
     torch.cuda.empty_cache()
 
 
+def test_mx_flash_decode_ep8_share_sampled():
+    # one GPU's expert share under 8-way expert parallelism: 32 experts,
+    # ~24 rows each (32-row direct tiles)
+    cfg = wl.CONFIGS["flash_decode_ep8"]
+    dev = wl.make_inputs_mx(cfg, wl.default_seed(cfg), "cuda")
+    y, runner = run_gpu_mx(dev, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert moe.moe_plan_info(runner.plan, cfg.T)["tile_m"] == 32
+    toks = [0, 5, 63, 100, cfg.T - 1]
+    idx = dev["topk_idx"].cpu().numpy()
+    need = sorted({int(e) for e in idx[toks].reshape(-1) if 0 <= e < cfg.E})
+    sel = lambda t: [t[e].cpu().numpy() if e in need else None for e in range(cfg.E)]
+    host = dict(x=dev["x"].cpu().numpy(), x_sf=dev["x_sf"].cpu().numpy(), idx=idx,
+                w=dev["topk_w"].cpu().numpy(), w1=sel(dev["w1"]), w1_sf=sel(dev["w1_sf"]),
+                w2=sel(dev["w2"]), w2_sf=sel(dev["w2_sf"]))
+    check_y(y.cpu().numpy()[toks], run_oracle_mx(host, tokens=toks)["y"], per_token_tol=1e-2,
+            what="flash decode EP8 share MX")
+
+
 @pytest.mark.parametrize("T", [1, 3, 128])
 def test_mx_flash_decode_shape_sampled(T):
     # full flash-decode shape (256 experts, H 4096, I 2048) drawn on the GPU;

@@ -16,6 +16,8 @@ _lib = None
 
 ORC_NO_REQUANT = 1
 ORC_NO_BF16 = 2
+ORC_POW2_SCALE = 4
+ORC_SF_GRAN64 = 8
 
 _u8p = ctypes.POINTER(ctypes.c_uint8)
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -52,8 +54,12 @@ def lib():
             + [_u8p, _f32p, _i32p, _f32p]
             + [ctypes.POINTER(ctypes.c_void_p)] * 4
             + [ctypes.c_int, _i32p, _u16p, _f32p, _f32p, _u8p, _f32p, _u16p,
-               ctypes.c_int, ctypes.c_int])
+               ctypes.c_int, ctypes.c_float, ctypes.c_int])
         L.orc_max_threads.restype = ctypes.c_int
+        L.orc_requant_block_pow2.restype = None
+        L.orc_requant_block_pow2.argtypes = [_f32p, ctypes.c_int, _u8p, _f32p]
+        L.orc_quantize_rows.restype = None
+        L.orc_quantize_rows.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, _u8p, _f32p]
         L.orc_e2m1_decode.restype = ctypes.c_float
         L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
         L.orc_e8m0_decode.restype = ctypes.c_double
@@ -70,7 +76,7 @@ def lib():
             + [_u8p, _u8p, _i32p, _f32p]
             + [ctypes.POINTER(ctypes.c_void_p)] * 4
             + [ctypes.c_int, _i32p, _u16p, _f32p, _f32p, _u8p, _u8p, _u16p,
-               ctypes.c_int, ctypes.c_int])
+               ctypes.c_int, ctypes.c_float, ctypes.c_int])
         _lib = L
     return _lib
 
@@ -108,12 +114,23 @@ def swiglu(g: float, u: float, w: float) -> float:
     return lib().orc_swiglu(float(g), float(u), float(w))
 
 
-def requant_block(v: np.ndarray):
+def requant_block(v: np.ndarray, pow2=False):
     v = np.ascontiguousarray(v, dtype=np.float32)
     q = np.zeros(v.size, np.uint8)
     sf = ctypes.c_float(0)
-    lib().orc_requant_block(_p(v, _f32p), v.size, _p(q, _u8p), ctypes.byref(sf))
+    fn = lib().orc_requant_block_pow2 if pow2 else lib().orc_requant_block
+    fn(_p(v, _f32p), v.size, _p(q, _u8p), ctypes.byref(sf))
     return q, sf.value
+
+
+def quantize_rows(x: np.ndarray):
+    """Per-1x128 e4m3 quantisation of [T,H] activations: (codes, f32 scales)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    T, H = x.shape
+    q = np.zeros((T, H), np.uint8)
+    sf = np.zeros((T, H // 128), np.float32)
+    lib().orc_quantize_rows(_p(x, _f32p), T, H, _p(q, _u8p), _p(sf, _f32p))
+    return q, sf
 
 
 def e2m1_decode(code: int) -> float:
@@ -160,7 +177,7 @@ def route(topk_idx: np.ndarray, num_experts: int, row_align: int, r_cap: int):
 
 
 def moe_forward(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
-                flags=0, want=(), nthreads=0):
+                flags=0, want=(), nthreads=0, clamp=0.0):
     """Oracle forward.
 
     w1, w1_sf, w2, w2_sf: sequences indexed by expert (arrays or None for
@@ -213,13 +230,14 @@ def moe_forward(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
     y_f32 = np.zeros((n, H), np.float32) if "y_f32" in want else None
     acc1 = np.zeros((n * K, 2 * I), np.float32) if "acc1" in want else None
     h = np.zeros((n * K, I), np.uint8) if "h" in want else None
-    h_sf = np.zeros((n * K, I // 128), np.float32) if "h" in want else None
+    G = 64 if flags & ORC_SF_GRAN64 else 128
+    h_sf = np.zeros((n * K, I // G), np.float32) if "h" in want else None
     partial = np.zeros((n * K, H), np.uint16) if "partial" in want else None
     rc = lib().orc_moe_forward(
         T, H, I, E, K, _p(x, _u8p), _p(x_sf, _f32p), _p(idx, _i32p), _p(wts, _f32p),
         p1, p1s, p2, p2s, n, _p(toks, _i32p), _p(y, _u16p), _p(y_f32, _f32p),
         _p(acc1, _f32p), _p(h, _u8p), _p(h_sf, _f32p), _p(partial, _u16p),
-        int(flags), int(nthreads))
+        int(flags), float(clamp), int(nthreads))
     if rc < 0:
         raise ValueError("oracle: invalid shape or missing expert weights")
     out = {"y": y, "n_bad": rc}
@@ -236,7 +254,7 @@ def moe_forward(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
 
 
 def moe_forward_mx(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
-                   flags=0, want=(), nthreads=0):
+                   flags=0, want=(), nthreads=0, clamp=0.0):
     """Oracle forward of the FP8 x MXFP4 recipe (see moe_oracle.c).
 
     x [T,H] e4m3, x_sf [T,H/32] UE8M0; per expert w1 [2I,H/2] packed e2m1,
@@ -282,7 +300,7 @@ def moe_forward_mx(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=No
         T, H, I, E, K, _p(x, _u8p), _p(x_sf, _u8p), _p(idx, _i32p), _p(wts, _f32p),
         p1, p1s, p2, p2s, n, _p(toks, _i32p), _p(y, _u16p), _p(y_f32, _f32p),
         _p(acc1, _f32p), _p(h, _u8p), _p(h_sf, _u8p), _p(partial, _u16p),
-        int(flags), int(nthreads))
+        int(flags), float(clamp), int(nthreads))
     if rc < 0:
         raise ValueError("oracle: invalid shape or missing expert weights")
     out = {"y": y, "n_bad": rc}

@@ -57,6 +57,20 @@
  *   - e2m1 pairs are packed two per byte, element k in byte k/2, the even
  *     element in the low nibble; UE8M0 code c means 2^(c-127), 0xFF is NaN.
  *
+ * Recipe options (both recipes unless noted):
+ *   clamp      "MegaMoE SM90 Implementation Design" §10.1: with an activation
+ *              clamp c, gate = clamp(gate, -c, c) and up = clamp(up, -c, c)
+ *              before the SwiGLU (c <= 0 here means no clamp, the default).
+ *   pow2 scale (FP8 recipe) DeepGEMM PR #440 "How it works": #383 rounds the
+ *              requant scale up to the next power of two; sf = the smallest
+ *              power of two >= max(amax, 1e-10)/448, q = e4m3(h / sf).
+ *   per-64     (FP8 recipe) design doc §5.4: one scale per 64 intermediate
+ *              columns, and L2 splits each 128-K block into two 64-K halves,
+ *              each scaled by its own activation scale and the block's weight
+ *              scale.  Reading: within block kb, acc = fmaf(sa[2kb] sb, p_lo,
+ *              acc) then acc = fmaf(sa[2kb+1] sb, p_hi, acc), p_lo / p_hi the
+ *              exact 64-term sums rounded once to f32.
+ *
  * Pins: every function here is checked by tests/test_oracle_pins.py against
  * closed forms, library codecs, an fp64 unquantised MoE, a dense SwiGLU FFN
  * written separately, brute-force routing and exact rational arithmetic.
@@ -227,7 +241,7 @@ float orc_swiglu(float g, float u, float w)
     return (silu * u) * w;
 }
 
-/* Per-128 requantisation of n values: sf = max(amax, 1e-10)/448 and
+/* Per-block requantisation of n values: sf = max(amax, 1e-10)/448 and
  * q[i] = e4m3(v[i] / sf) with a correctly rounded f32 division. */
 void orc_requant_block(const float* v, int n, uint8_t* q, float* sf_out)
 {
@@ -238,6 +252,41 @@ void orc_requant_block(const float* v, int n, uint8_t* q, float* sf_out)
     for (int i = 0; i < n; ++i)
         q[i] = orc_e4m3_encode(v[i] / sf);
     *sf_out = sf;
+}
+
+/* Forward declaration (defined with the MX codecs below). */
+uint8_t orc_e8m0_ceil(float s);
+double orc_e8m0_decode(uint8_t code);
+
+/* The same with the scale rounded up to a power of two (PR #383's choice):
+ * sf = the smallest power of two >= max(amax, 1e-10)/448. */
+void orc_requant_block_pow2(const float* v, int n, uint8_t* q, float* sf_out)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i)
+        amax = fmaxf(amax, fabsf(v[i]));
+    float sf = (float)orc_e8m0_decode(orc_e8m0_ceil(fmaxf(amax, 1e-10f) / 448.0f));
+    for (int i = 0; i < n; ++i)
+        q[i] = orc_e4m3_encode(v[i] / sf);
+    *sf_out = sf;
+}
+
+/* Activation clamp before the SwiGLU (design doc §10.1); c <= 0: none. */
+static float clamp_act(float v, float c)
+{
+    return c > 0.0f ? fminf(fmaxf(v, -c), c) : v;
+}
+
+/* Per-1x128 quantisation of an activation matrix, the step the pages leave
+ * to the caller before each call ("07 · MegaMoE" §3 copies FP8 x and its
+ * scales into the buffer): x [T,H] f32 (bf16 inputs are exact in f32) ->
+ * q [T,H] e4m3, sf [T,H/128] with the requant rule above. */
+void orc_quantize_rows(const float* x, int T, int H, uint8_t* q, float* sf)
+{
+    for (int t = 0; t < T; ++t)
+        for (int kb = 0; kb < H / 128; ++kb)
+            orc_requant_block(x + (size_t)t * H + 128 * kb, 128, q + (size_t)t * H + 128 * kb,
+                              sf + (size_t)t * (H / 128) + kb);
 }
 
 /* ------------------------------------------ MX codecs and block scaling */
@@ -381,7 +430,9 @@ static int check_tokens(int T, int E, int K, const int32_t* idx, int n_tok, cons
 
 enum {
     ORC_NO_REQUANT = 1, /* test-only: feed f32 SwiGLU output to L2 unquantised */
-    ORC_NO_BF16 = 2     /* test-only: keep partials and y in f32 */
+    ORC_NO_BF16 = 2,    /* test-only: keep partials and y in f32 */
+    ORC_POW2_SCALE = 4, /* FP8 recipe: power-of-two requant scales */
+    ORC_SF_GRAN64 = 8   /* FP8 recipe: per-64 intermediate scales, dual-half L2 */
 };
 
 /* Forward for a list of tokens.
@@ -405,13 +456,15 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
                     int n_tok, const int32_t* toks,
                     uint16_t* y, float* y_f32,
                     float* acc1, uint8_t* h, float* h_sf, uint16_t* partial,
-                    int flags, int nthreads)
+                    int flags, float clamp, int nthreads)
 {
     if (H % 128 || I % 128 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || T < 0)
         return -1;
     if (!toks)
         n_tok = T;
     const int HB = H / 128, IB = I / 128;
+    const int G = (flags & ORC_SF_GRAN64) ? 64 : 128;  /* intermediate scale block */
+    const int NG = I / G;
     int bad = check_tokens(T, E, K, idx, n_tok, toks, (const void* const*)w1,
                            (const void* const*)w1_sf, (const void* const*)w2,
                            (const void* const*)w2_sf);
@@ -436,7 +489,7 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
         float* a1 = (float*)malloc(sizeof(float) * 2 * I);
         float* hv = (float*)malloc(sizeof(float) * I);
         uint8_t* q = (uint8_t*)malloc(I);
-        float* qs = (float*)malloc(sizeof(float) * IB);
+        float* qs = (float*)malloc(sizeof(float) * NG);
         const uint8_t* xr = x + (size_t)t * H;
         const float* xs = x_sf + (size_t)t * HB;
         for (int n = 0; n < 2 * I; ++n) {
@@ -446,14 +499,18 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
         if (acc1)
             memcpy(acc1 + (size_t)ps * 2 * I, a1, sizeof(float) * 2 * I);
         for (int i = 0; i < I; ++i)
-            hv[i] = orc_swiglu(a1[i], a1[I + i], w[t * K + j]);
+            hv[i] = orc_swiglu(clamp_act(a1[i], clamp), clamp_act(a1[I + i], clamp), w[t * K + j]);
         if (!(flags & ORC_NO_REQUANT)) {
-            for (int ib = 0; ib < IB; ++ib)
-                orc_requant_block(hv + 128 * ib, 128, q + 128 * ib, qs + ib);
+            for (int ib = 0; ib < NG; ++ib) {
+                if (flags & ORC_POW2_SCALE)
+                    orc_requant_block_pow2(hv + G * ib, G, q + G * ib, qs + ib);
+                else
+                    orc_requant_block(hv + G * ib, G, q + G * ib, qs + ib);
+            }
             if (h)
                 memcpy(h + (size_t)ps * I, q, I);
             if (h_sf)
-                memcpy(h_sf + (size_t)ps * IB, qs, sizeof(float) * IB);
+                memcpy(h_sf + (size_t)ps * NG, qs, sizeof(float) * NG);
         }
         for (int n = 0; n < H; ++n) {
             const uint8_t* wr = w2[e] + (size_t)n * I;
@@ -463,6 +520,14 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
                 for (int ib = 0; ib < IB; ++ib) {
                     float pdot = (float)block_dot_f32_e4m3(hv + 128 * ib, wr + 128 * ib, 128);
                     acc = fmaf(ws[ib], pdot, acc);
+                }
+            } else if (G == 64) {
+                /* design doc §5.4: each 128-K block as two 64-K halves */
+                for (int kb = 0; kb < IB; ++kb) {
+                    float p_lo = (float)orc_block_dot_e4m3(q + 128 * kb, wr + 128 * kb, 64);
+                    float p_hi = (float)orc_block_dot_e4m3(q + 128 * kb + 64, wr + 128 * kb + 64, 64);
+                    acc = fmaf(qs[2 * kb] * ws[kb], p_lo, acc);
+                    acc = fmaf(qs[2 * kb + 1] * ws[kb], p_hi, acc);
                 }
             } else {
                 acc = scaled_row_dot(q, qs, wr, ws, IB);
@@ -508,7 +573,7 @@ int orc_moe_forward_mx(int T, int H, int I, int E, int K,
                        int n_tok, const int32_t* toks,
                        uint16_t* y, float* y_f32,
                        float* acc1, uint8_t* h, uint8_t* h_sf, uint16_t* partial,
-                       int flags, int nthreads)
+                       int flags, float clamp, int nthreads)
 {
     if (H % 32 || I % 32 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || T < 0)
         return -1;
@@ -546,7 +611,7 @@ int orc_moe_forward_mx(int T, int H, int I, int E, int K,
         if (acc1)
             memcpy(acc1 + (size_t)ps * 2 * I, a1, sizeof(float) * 2 * I);
         for (int i = 0; i < I; ++i)
-            hv[i] = orc_swiglu(a1[i], a1[I + i], w[t * K + j]);
+            hv[i] = orc_swiglu(clamp_act(a1[i], clamp), clamp_act(a1[I + i], clamp), w[t * K + j]);
         if (!(flags & ORC_NO_REQUANT)) {
             for (int ib = 0; ib < IS; ++ib)
                 orc_requant_block_mx(hv + 32 * ib, 32, q + 32 * ib, qs + ib);

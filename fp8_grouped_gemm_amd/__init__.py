@@ -23,6 +23,7 @@ MOE_WEIGHTS_ROW_MAJOR = 0
 MOE_WEIGHTS_PACKED = 1
 MOE_FLAG_SINGLE_LAUNCH = 1
 MOE_FLAG_SPLIT_LAUNCH = 2
+MOE_FLAG_POW2_SCALE = 4
 MOE_FLAG_TEST_NO_WAIT = 256
 MOE_FLAG_TEST_SMALL_GRID = 512
 MOE_RECIPE_FP8_BLOCK128 = 0
@@ -33,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "moe_workspace_layout", "moe_forward", "moe_forward_timed", "moe_forward_mx",
     "moe_forward_mx_timed", "moe_route",
     "moe_route_workspace_bytes", "moe_prepare_weights", "moe_prepare_weights_mx",
+    "moe_quantize_act",
     "moe_read_status", "moe_strerror", "moe_version",
 )
 
@@ -48,7 +50,8 @@ class moe_shape_t(ctypes.Structure):
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("weight_layout", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("recipe", ctypes.c_int32)]
+                ("recipe", ctypes.c_int32), ("act_sf_gran", ctypes.c_int32),
+                ("activation_clamp", ctypes.c_float)]
 
 
 class moe_tile_info_t(ctypes.Structure):
@@ -56,7 +59,7 @@ class moe_tile_info_t(ctypes.Structure):
                 ("pool_rows", ctypes.c_int32), ("l1_tile_n", ctypes.c_int32),
                 ("l2_tile_n", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("l1_split", ctypes.c_int32), ("single_launch", ctypes.c_int32),
-                ("l2_group_tiles", ctypes.c_int32)]
+                ("l2_group_tiles", ctypes.c_int32), ("act_sf_gran", ctypes.c_int32)]
 
 
 class moe_ws_layout_t(ctypes.Structure):
@@ -93,6 +96,7 @@ def lib():
         L.moe_route_workspace_bytes.argtypes = [_vp, _i32, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_prepare_weights.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_prepare_weights_mx.argtypes = [_vp] * 10
+        L.moe_quantize_act.argtypes = [_vp, _i32, _vp, _vp, _vp, _vp]
         L.moe_read_status.argtypes = [_vp, _i32, _vp, ctypes.c_size_t,
                                       ctypes.POINTER(ctypes.c_int32), _vp]
         L.moe_strerror.argtypes = [ctypes.c_int]
@@ -134,9 +138,9 @@ def _stream(stream):
 
 def moe_plan_create(hidden, intermediate, num_experts, top_k, max_tokens, tile_m=0,
                     weight_layout=MOE_WEIGHTS_ROW_MAJOR, flags=0,
-                    recipe=MOE_RECIPE_FP8_BLOCK128):
+                    recipe=MOE_RECIPE_FP8_BLOCK128, act_sf_gran=0, activation_clamp=0.0):
     shape = moe_shape_t(hidden, intermediate, num_experts, top_k, max_tokens, tile_m,
-                        weight_layout, flags, recipe)
+                        weight_layout, flags, recipe, act_sf_gran, activation_clamp)
     h = ctypes.c_void_p()
     _check(lib().moe_plan_create(ctypes.byref(shape), ctypes.byref(h)), "moe_plan_create")
     return h
@@ -231,6 +235,13 @@ def moe_prepare_weights_mx(plan, w1, w1_sf, w2, w2_sf, w1_packed, w1_sf_packed, 
     _check(rc, "moe_prepare_weights_mx")
 
 
+def moe_quantize_act(plan, num_tokens, x_bf16, x, x_sf, stream=None):
+    """bf16 activations -> e4m3 codes + scales for the plan's recipe."""
+    rc = lib().moe_quantize_act(plan, num_tokens, _ptr(x_bf16), _ptr(x), _ptr(x_sf),
+                                _stream(stream))
+    _check(rc, "moe_quantize_act")
+
+
 def moe_route_workspace_bytes(plan, num_tokens):
     n = ctypes.c_size_t()
     _check(lib().moe_route_workspace_bytes(plan, num_tokens, ctypes.byref(n)),
@@ -262,13 +273,14 @@ class MoEForward:
 
     def __init__(self, hidden, intermediate, num_experts, top_k, max_tokens, tile_m=0,
                  device="cuda", weight_layout=MOE_WEIGHTS_ROW_MAJOR, flags=0,
-                 recipe=MOE_RECIPE_FP8_BLOCK128):
+                 recipe=MOE_RECIPE_FP8_BLOCK128, act_sf_gran=0, activation_clamp=0.0):
         import torch
         self.shape = (hidden, intermediate, num_experts, top_k, max_tokens, tile_m)
         self.weight_layout = weight_layout
         self.recipe = recipe
         self.plan = moe_plan_create(hidden, intermediate, num_experts, top_k, max_tokens,
-                                    tile_m, weight_layout, flags, recipe)
+                                    tile_m, weight_layout, flags, recipe, act_sf_gran,
+                                    activation_clamp)
         self.ws_bytes = moe_workspace_bytes(self.plan, max_tokens)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
 
@@ -315,7 +327,7 @@ class MoEForward:
             "src_row": (torch.int32, (num_tokens * K,)),
             "h": (torch.uint8, (R, I)),
             "h_sf": ((torch.uint8, (R, I // 32)) if self.recipe == MOE_RECIPE_MXFP4
-                     else (torch.float32, (R, I // 128))),
+                     else (torch.float32, (R, I // info["act_sf_gran"]))),
             "partial": (torch.int16, (K, num_tokens, H)),
             "status": (torch.int32, (4,)),
         }[name]

@@ -261,7 +261,8 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
             float m = 0.f;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const float g = acc[ms][s][i], u = acc[ms][s + 2][i];
+                const float g = clamp_act(acc[ms][s][i], a.clamp);
+                const float u = clamp_act(acc[ms][s + 2][i], a.clamp);
                 const float v = (silu(g) * u) * wrow[ms][i];
                 hv[ms][s][i] = v;
                 m = fmaxf(m, fabsf(v));
@@ -278,14 +279,19 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * ms + 4 * lg + i;
-                const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
-                const float sf = fmaxf(amax, 1e-10f) / 448.0f;
-                const float rsf = __builtin_amdgcn_rcpf(sf);
+                // per-64 scales: waves 2b, 2b+1 share block b of the tile
+                const float amax = a.sf_gran64 ? fmaxf(red[wave & 2][r], red[(wave & 2) + 1][r])
+                                               : fmaxf(fmaxf(red[0][r], red[1][r]),
+                                                       fmaxf(red[2][r], red[3][r]));
+                float rsf;
+                const float sf = requant_sf(amax, a.pow2_scale, rsf);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    qt[r][wave * 32 + s * 16 + lr] = (uint8_t)requant_e4m3(hv[ms][s][i], sf, rsf);
-                if (wave == 0 && lr == 0) {
-                    float* dst = a.h_sf + (size_t)(row0 + r) * (I / 128) + nt;
+                    qt[r][wave * 32 + s * 16 + lr] =
+                        (uint8_t)requant_q(hv[ms][s][i], sf, rsf, a.pow2_scale);
+                if ((a.sf_gran64 ? (wave & 1) == 0 : wave == 0) && lr == 0) {
+                    float* dst = a.sf_gran64 ? a.h_sf + (size_t)(row0 + r) * (I / 64) + nt * 2 + (wave >> 1)
+                                             : a.h_sf + (size_t)(row0 + r) * (I / 128) + nt;
                     if constexpr (CO)
                         st_co32f(dst, sf);
                     else
@@ -327,7 +333,12 @@ __global__ __launch_bounds__(256, MT == 2 ? 2 : 1) void l1_direct(FwdArgs a)
 // WV waves per workgroup: the workgroup covers WV / 4 consecutive 256-column
 // tiles (a wave with no columns left re-reads column block 0 of the
 // expert and stores nothing).
-template <int MT, bool PK, bool CO, int WV = 4>
+// G64: per-64 intermediate scales ("MegaMoE SM90 Implementation Design"
+// §5.4): each 128-K block is multiplied as its two 64-K halves -- the A
+// fragment's bytes 0..15 are K 0..63 of every lane group, bytes 16..31 are
+// K 64..127, so zeroing one half leaves the other -- and each half is
+// promoted with its own activation scale.
+template <int MT, bool PK, bool CO, int WV = 4, bool G64 = false>
 __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hint)
 {
     constexpr int BM = 16 * MT;
@@ -364,7 +375,7 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
     for (int ms = 0; ms < MT; ++ms)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            asf[ms][i] = a.h_sf + (size_t)(row0 + 16 * ms + 4 * lg + i) * IB;
+            asf[ms][i] = a.h_sf + (size_t)(row0 + 16 * ms + 4 * lg + i) * (G64 ? 2 * IB : IB);
     // A wave's 64 columns are either all inside H or all past it; an idle
     // wave re-reads column block 0 and stores nothing.
     const int ncol0 = busy ? nt * 256 + w4 * 64 : 0;
@@ -391,6 +402,7 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
     struct Blk {
         Frag2 fa[MT], fb[4];
         float sa[MT][4];
+        float sa2[G64 ? MT : 1][4];  // G64: the second half's scales
         float sb;
     };
     auto fetch = [&](Blk& b, int kb) {
@@ -398,10 +410,14 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
         for (int ms = 0; ms < MT; ++ms)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if constexpr (CO)
+                if constexpr (G64) {
+                    b.sa[ms][i] = asf[ms][i][2 * kb];
+                    b.sa2[ms][i] = asf[ms][i][2 * kb + 1];
+                } else if constexpr (CO) {
                     b.sa[ms][i] = ld_co32f(asf[ms][i] + kb);
-                else
+                } else {
                     b.sa[ms][i] = asf[ms][i][kb];
+                }
             }
         b.sb = sfb[kb];
 #pragma unroll
@@ -414,14 +430,30 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
     auto mul = [&](const Blk& b) {
 #pragma unroll
         for (int ms = 0; ms < MT; ++ms) {
-            const v8i av = pack_frag(b.fa[ms].lo, b.fa[ms].hi);
+            if constexpr (G64) {
+                const uint4 z = make_uint4(0, 0, 0, 0);
+                const v8i alo = pack_frag(b.fa[ms].lo, z), ahi = pack_frag(z, b.fa[ms].hi);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const v4f p = mfma_16x16x128_e4m3(av, pack_frag(b.fb[s].lo, b.fb[s].hi),
-                                                  v4f{0.f, 0.f, 0.f, 0.f});
+                for (int s = 0; s < 4; ++s) {
+                    const v8i bv = pack_frag(b.fb[s].lo, b.fb[s].hi);
+                    const v4f plo = mfma_16x16x128_e4m3(alo, bv, v4f{0.f, 0.f, 0.f, 0.f});
+                    const v4f phi = mfma_16x16x128_e4m3(ahi, bv, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[ms][s][i] = fmaf(b.sa[ms][i] * b.sb, p[i], acc[ms][s][i]);
+                    for (int i = 0; i < 4; ++i) {
+                        acc[ms][s][i] = fmaf(b.sa[ms][i] * b.sb, plo[i], acc[ms][s][i]);
+                        acc[ms][s][i] = fmaf(b.sa2[ms][i] * b.sb, phi[i], acc[ms][s][i]);
+                    }
+                }
+            } else {
+                const v8i av = pack_frag(b.fa[ms].lo, b.fa[ms].hi);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const v4f p = mfma_16x16x128_e4m3(av, pack_frag(b.fb[s].lo, b.fb[s].hi),
+                                                      v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[ms][s][i] = fmaf(b.sa[ms][i] * b.sb, p[i], acc[ms][s][i]);
+                }
             }
         }
     };
@@ -468,10 +500,10 @@ __device__ __forceinline__ void l2_tile(const FwdArgs& a, int tile, int hint = 0
         count_done(a.sync + kSyncL2Done);  // every L2 item counts, idle ones too
 }
 
-template <int MT, bool PK, int WV = 4>
-__global__ __launch_bounds__(WV * 64, MT == 2 && PK ? 2 : 1) void l2_direct(FwdArgs a)
+template <int MT, bool PK, int WV = 4, bool G64 = false>
+__global__ __launch_bounds__(WV * 64, MT == 2 && PK && !G64 ? 2 : 1) void l2_direct(FwdArgs a)
 {
-    l2_tile_body<MT, PK, false, WV>(a, blockIdx.x, 0);
+    l2_tile_body<MT, PK, false, WV, G64>(a, blockIdx.x, 0);
 }
 
 // ------------------------------------------------- L1 split-K epilogue
@@ -512,23 +544,32 @@ __global__ __launch_bounds__(256) void l1_splitk_epilogue(FwdArgs a)
     float hv[8], m = 0.f;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        hv[q] = (silu(g[q]) * u[q]) * w;
+        hv[q] = (silu(clamp_act(g[q], a.clamp)) * clamp_act(u[q], a.clamp)) * w;
         m = fmaxf(m, fabsf(hv[q]));
     }
-    m = max16(m);
+    // the row's 16 threads cover 128 columns; per-64 scales: 8 threads each
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    if (!a.sf_gran64)
+        m = fmaxf(m, __shfl_xor(m, 8));
     if (f < 0)
         return;
-    const float sf = fmaxf(m, 1e-10f) / 448.0f;
-    const float rsf = __builtin_amdgcn_rcpf(sf);
+    float rsf;
+    const float sf = requant_sf(m, a.pow2_scale, rsf);
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        lo |= requant_e4m3(hv[q], sf, rsf) << (8 * q);
-        hi |= requant_e4m3(hv[q + 4], sf, rsf) << (8 * q);
+        lo |= requant_q(hv[q], sf, rsf, a.pow2_scale) << (8 * q);
+        hi |= requant_q(hv[q + 4], sf, rsf, a.pow2_scale) << (8 * q);
     }
     *reinterpret_cast<uint2*>(a.h + (size_t)r * I + c0) = make_uint2(lo, hi);
-    if ((threadIdx.x & 15) == 0)
+    if (a.sf_gran64) {
+        if ((threadIdx.x & 7) == 0)
+            a.h_sf[(size_t)r * (I / 64) + nt * 2 + ((threadIdx.x >> 3) & 1)] = sf;
+    } else if ((threadIdx.x & 15) == 0) {
         a.h_sf[(size_t)r * NT + nt] = sf;
+    }
 }
 
 // -------------------------------------------------------------- combine
@@ -674,6 +715,15 @@ template <bool PK>
 static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
 {
     const unsigned tiles = a.num_mblocks * ((a.H + 255) / 256);
+    if (a.sf_gran64) {  // per-64 intermediate scales: dual-half L2, 4-wave tiles
+        switch (a.BM) {
+        case 16: hipLaunchKernelGGL((l2_direct<1, PK, 4, true>), dim3(tiles), dim3(256), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((l2_direct<2, PK, 4, true>), dim3(tiles), dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((l2_direct<4, PK, 4, true>), dim3(tiles), dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (a.BM) {
     case 16:
         if (a.l2_wide) {  // two 256-column tiles per workgroup, 8 waves

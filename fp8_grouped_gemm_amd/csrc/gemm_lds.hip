@@ -543,8 +543,10 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                     const int r = wm * 64 + ms * 16 + 4 * lg + i;
                     const bool valid = m_rs[r] >= 0;
                     const float w = valid ? m_w[r] : 0.f;
-                    const float v0 = (silu(acc[ms][0][i]) * acc[ms][2][i]) * w;
-                    const float v1 = (silu(acc[ms][1][i]) * acc[ms][3][i]) * w;
+                    const float v0 = (silu(clamp_act(acc[ms][0][i], a.clamp)) *
+                                      clamp_act(acc[ms][2][i], a.clamp)) * w;
+                    const float v1 = (silu(clamp_act(acc[ms][1][i], a.clamp)) *
+                                      clamp_act(acc[ms][3][i], a.clamp)) * w;
                     const float amax = max16(fmaxf(fabsf(v0), fabsf(v1)));
                     const uint32_t code = min(e8m0_ceil_code(fmaxf(amax, 1e-10f) / 448.0f), 253u);
                     const float inv = e8m0_inverse(code);
@@ -574,7 +576,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                     float m = 0.f;
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
-                        const float g = acc[ms][s][i], u = acc[ms][s + 2][i];
+                        const float g = clamp_act(acc[ms][s][i], a.clamp);
+                        const float u = clamp_act(acc[ms][s + 2][i], a.clamp);
                         const float v = (silu(g) * u) * w;
                         acc[ms][s][i] = v;
                         m = fmaxf(m, fabsf(v));
@@ -591,12 +594,12 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                     const int r = wm * 64 + ms * 16 + 4 * lg + i;
                     const float amax =
                         fmaxf(fmaxf(red[r], red[128 + r]), fmaxf(red[256 + r], red[384 + r]));
-                    const float sf = fmaxf(amax, 1e-10f) / 448.0f;
-                    const float rsf = __builtin_amdgcn_rcpf(sf);
+                    float rsf;
+                    const float sf = requant_sf(amax, a.pow2_scale, rsf);
 #pragma unroll
                     for (int s = 0; s < 2; ++s)
                         qt[r * 128 + wn * 32 + s * 16 + lr] =
-                            (uint8_t)requant_e4m3(acc[ms][s][i], sf, rsf);
+                            (uint8_t)requant_q(acc[ms][s][i], sf, rsf, a.pow2_scale);
                     if (wn == 0 && lr == 0)
                         a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
                 }

@@ -227,8 +227,10 @@ __global__ __launch_bounds__(256) void l1_mx(FwdArgs a)
             const int r = 16 * ms + 4 * lg + i;
             const int f = a.row_src[row0 + r];
             const float w = f >= 0 ? a.topk_w[f] : 0.f;
-            const float v0 = (silu(acc[ms][0][i]) * acc[ms][2][i]) * w;
-            const float v1 = (silu(acc[ms][1][i]) * acc[ms][3][i]) * w;
+            const float v0 = (silu(clamp_act(acc[ms][0][i], a.clamp)) *
+                              clamp_act(acc[ms][2][i], a.clamp)) * w;
+            const float v1 = (silu(clamp_act(acc[ms][1][i], a.clamp)) *
+                              clamp_act(acc[ms][3][i], a.clamp)) * w;
             const float amax = max16(fmaxf(fabsf(v0), fabsf(v1)));
             const uint32_t code = min(e8m0_ceil_code(fmaxf(amax, 1e-10f) / 448.0f), 253u);
             const float inv = e8m0_inverse(code);

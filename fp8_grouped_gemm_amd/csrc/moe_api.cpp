@@ -34,6 +34,16 @@ struct Config {
 // Beyond ~24 rows per expert the 128 x 256 LDS-staged MFMA tile takes over
 // (it needs H % 256 == 0 for its 256-column L2 tiles and I >= 256 for at
 // least two K blocks in L2; otherwise 64-row direct-load tiles).
+// Columns per intermediate scale of an FP8 plan (MXFP4: 32).
+int sf_gran(const moe_shape_t& s)
+{
+    if (s.recipe == MOE_RECIPE_MXFP4)
+        return 32;
+    if (s.act_sf_gran < 0)  // PR #440 "How it works": 128 where the decode tile fits, else 64
+        return (s.hidden % 512 == 0 && (2 * s.intermediate) % 512 == 0) ? 128 : 64;
+    return s.act_sf_gran == 64 ? 64 : 128;
+}
+
 // The LDS tile keeps NSTAGE - 1 K blocks in flight and needs that many per
 // layer: 2 for the FP8 recipe, 3 for FP8 x MXFP4.
 bool lds_tile_fits(const moe_shape_t& s)
@@ -51,7 +61,7 @@ Config choose_config(const moe_shape_t& s, int T)
         return Config{16, 0};
     if (rows <= 24.0)
         return Config{32, 0};
-    if (lds_tile_fits(s))
+    if (lds_tile_fits(s) && sf_gran(s) != 64)
         return Config{128, 1};
     return Config{64, 0};
 }
@@ -99,7 +109,7 @@ long long mblocks_expected(const moe_shape_t& s, long long T)
 // shape: T = 128 and 32 gain ~1.7 % in L2, T = 8 loses 7 %).
 bool choose_l2_wide(const moe_shape_t& s, int T, const Config& c)
 {
-    if (c.tile_m != 16 || T <= 0 || s.recipe != MOE_RECIPE_FP8_BLOCK128)
+    if (c.tile_m != 16 || T <= 0 || s.recipe != MOE_RECIPE_FP8_BLOCK128 || sf_gran(s) == 64)
         return false;
     const long long groups = mblocks_expected(s, T) * (((s.hidden + 255) / 256 + 1) / 2);
     return groups >= 4 * kMinItems;
@@ -184,8 +194,9 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     L.mbe = take(sizeof(int32_t) * (size_t)L.mb_cap);
     L.row_src = take(sizeof(int32_t) * (size_t)L.r_cap);
     L.src_row = take(sizeof(int32_t) * (size_t)std::max<long long>(TK, 1));
-    // f32 [R, I/128] (FP8 recipe) or UE8M0 bytes [R, I/32] (MXFP4): same size
-    L.h_sf = take(sizeof(float) * (size_t)L.r_cap * (I / 128));
+    // f32 [R, I/128] or [R, I/64] (FP8 recipe) or UE8M0 bytes [R, I/32]
+    // (MXFP4, the size of the per-128 f32 section)
+    L.h_sf = take(sizeof(float) * (size_t)L.r_cap * (I / (sf_gran(s) == 64 ? 64 : 128)));
     L.h = take((size_t)L.r_cap * I);
     L.partial = take(sizeof(uint16_t) * (size_t)K * T * H);
     // Split-K scratch: L1's f32 partials part[slice][slot][2I], slot
@@ -194,7 +205,7 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     L.l2_wide = choose_l2_wide(s, T, c);
     L.part = take(sizeof(float) * splitk_floats(s, T));
     // Single-launch counters: L2 done, 3 spare, one ready count per row block.
-    L.single = c.kernel == 0 && L.split_l1 == 1 &&
+    L.single = c.kernel == 0 && L.split_l1 == 1 && sf_gran(s) != 64 &&
                ((s.flags & MOE_FLAG_SINGLE_LAUNCH) ||
                 (kSingleLaunchDefault && !(s.flags & MOE_FLAG_SPLIT_LAUNCH)));
     L.n_sync = moe::kSyncReady + L.mb_cap;
@@ -231,10 +242,22 @@ int validate_shape(const moe_shape_t* s)
         return MOE_ERR_INVALID_ARG;
     if (s->weight_layout == MOE_WEIGHTS_PACKED && s->hidden % 256)
         return MOE_ERR_UNSUPPORTED_SHAPE;
-    if (s->flags & ~(MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_SPLIT_LAUNCH | MOE_FLAG_TEST_NO_WAIT |
-                     MOE_FLAG_TEST_SMALL_GRID))
+    if (s->flags & ~(MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_SPLIT_LAUNCH | MOE_FLAG_POW2_SCALE |
+                     MOE_FLAG_TEST_NO_WAIT | MOE_FLAG_TEST_SMALL_GRID))
         return MOE_ERR_INVALID_ARG;
+    if (s->act_sf_gran != 0 && s->act_sf_gran != 64 && s->act_sf_gran != 128 && s->act_sf_gran != -1)
+        return MOE_ERR_INVALID_ARG;
+    if (!(s->activation_clamp == s->activation_clamp))  // NaN
+        return MOE_ERR_INVALID_ARG;
+    if (sf_gran(*s) == 64) {  // per-64 plans: direct-load tiles, split launches
+        if (s->tile_m == 128)
+            return MOE_ERR_UNSUPPORTED_SHAPE;
+        if (s->flags & MOE_FLAG_SINGLE_LAUNCH)
+            return MOE_ERR_INVALID_ARG;
+    }
     if (s->recipe == MOE_RECIPE_MXFP4) {
+        if (s->act_sf_gran != 0 || (s->flags & MOE_FLAG_POW2_SCALE))
+            return MOE_ERR_INVALID_ARG;
         // the MXFP4 kernels address x with 32-bit buffer offsets
         if ((long long)s->max_tokens * s->hidden > 0x7FFFFFFFLL)
             return MOE_ERR_UNSUPPORTED_SHAPE;
@@ -362,6 +385,7 @@ int moe_plan_info(moe_plan_t plan, int32_t T, moe_tile_info_t* info)
     info->l1_split = L.split_l1;
     info->single_launch = L.single ? 1 : 0;
     info->l2_group_tiles = L.l2_wide ? 2 : 1;
+    info->act_sf_gran = sf_gran(plan->shape);
     return MOE_OK;
 }
 
@@ -496,6 +520,9 @@ int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, 
     a.sync = at<int32_t>(workspace, L.sync);
     a.status = at<int32_t>(workspace, L.status);
     a.spin_limit = (s.flags & MOE_FLAG_TEST_NO_WAIT) ? -1 : kSpinLimit;
+    a.clamp = s.activation_clamp > 0.f ? s.activation_clamp : 0.f;
+    a.pow2_scale = (s.flags & MOE_FLAG_POW2_SCALE) ? 1 : 0;
+    a.sf_gran64 = sf_gran(s) == 64 ? 1 : 0;
     a.grid_cap = (s.flags & MOE_FLAG_TEST_SMALL_GRID) ? 4 : 0;
     if (L.single) {
         if (moe::launch_fused(a, st) != hipSuccess || !mark(2) || !mark(3) || !mark(4))
@@ -624,6 +651,28 @@ int moe_prepare_weights_mx(moe_plan_t plan, const uint8_t* w1, const uint8_t* w1
     if (moe::launch_pack_mx(w1, w1_sf, w2, w2_sf, w1_packed, w1_sf_packed, w2_packed, w2_sf_packed,
                             s.num_experts, s.hidden, s.intermediate,
                             static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_quantize_act(moe_plan_t plan, int32_t T, const uint16_t* x_bf16, uint8_t* x, void* x_sf,
+                     void* stream)
+{
+    if (!plan)
+        return MOE_ERR_INVALID_ARG;
+    const moe_shape_t& s = plan->shape;
+    if (T < 0 || T > s.max_tokens)
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!x_bf16 || !x || !x_sf || reinterpret_cast<uintptr_t>(x_bf16) % 16 ||
+        reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(x_sf) % 4)
+        return MOE_ERR_INVALID_ARG;
+    int rc = device_ok();
+    if (rc != MOE_OK)
+        return rc;
+    if (moe::launch_quantize_act(x_bf16, T, s.hidden, x, x_sf, s.recipe == MOE_RECIPE_MXFP4,
+                                 static_cast<hipStream_t>(stream)) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
 }

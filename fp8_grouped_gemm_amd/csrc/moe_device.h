@@ -111,6 +111,36 @@ __device__ __forceinline__ uint32_t requant_e4m3(float v, float sf, float rsf)
     return f32_to_e4m3_hw(v / sf);
 }
 
+// Requant scale of a block with the given amax: the raw max(amax, 1e-10)/448
+// or, with pow2, the smallest power of two at or above it (PR #383's choice).
+// rsf: the hardware reciprocal of the raw scale (requant_q brackets it) or
+// the exact inverse of the power of two.
+__device__ __forceinline__ float requant_sf(float amax, bool pow2, float& rsf)
+{
+    const float s = fmaxf(amax, 1e-10f) / 448.0f;
+    if (pow2) {
+        const uint32_t c = min(e8m0_ceil_code(s), 253u);
+        rsf = e8m0_inverse(c);
+        return __uint_as_float(c << 23);
+    }
+    rsf = __builtin_amdgcn_rcpf(s);
+    return s;
+}
+
+// e4m3 code of v / sf for a scale from requant_sf (a power-of-two scale
+// divides exactly by multiplying with its inverse).
+__device__ __forceinline__ uint32_t requant_q(float v, float sf, float rsf, bool pow2)
+{
+    return pow2 ? f32_to_e4m3_hw(v * rsf) : requant_e4m3(v, sf, rsf);
+}
+
+// Activation clamp of gate / up before the SwiGLU ("MegaMoE SM90
+// Implementation Design" §10.1); c <= 0: none.
+__device__ __forceinline__ float clamp_act(float v, float c)
+{
+    return c > 0.f ? fminf(fmaxf(v, -c), c) : v;
+}
+
 // SiLU with the hardware exp2 and reciprocal (a few ulp from
 // g / (1 + expf(-g)); g -> -inf gives -0, g -> +inf gives g).
 __device__ __forceinline__ float silu(float g)

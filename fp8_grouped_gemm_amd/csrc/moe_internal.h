@@ -65,6 +65,12 @@ struct FwdArgs {
     // FP8 x MXFP4 recipe (mx = 1): UE8M0 scale codes, one per 32 K values,
     // x_sfq [T,H/32], w1_sfq [E,2I,H/32], w2_sfq [E,H,I/32], h_sfq [R,I/32];
     // w1/w2 hold packed e2m1 pairs.  The f32 scale pointers are unused.
+    // Recipe options: activation clamp of gate/up before the SwiGLU (<= 0:
+    // none), power-of-two requant scales, per-64 intermediate scales (h_sf
+    // [R, I/64] and the dual-half L2) -- the last two for the FP8 recipe.
+    float clamp;
+    int32_t pow2_scale;
+    int32_t sf_gran64;
     int32_t mx;
     const uint8_t* x_sfq;
     const uint8_t* w1_sfq;
@@ -89,6 +95,8 @@ hipError_t launch_l1_mx(const FwdArgs& a, hipStream_t s);  // direct tiles, tile
 hipError_t launch_l2_mx(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s);
+hipError_t launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* q, void* sf, bool mx,
+                               hipStream_t s);
 hipError_t launch_pack(const uint8_t* w1, const uint8_t* w2, uint8_t* w1p, uint8_t* w2p, int E,
                        int H, int I, hipStream_t s);
 hipError_t launch_pack_mx(const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2,

@@ -63,6 +63,8 @@ extern "C" {
                                      launch ("07 · MegaMoE" §5-6) */
 #define MOE_FLAG_SPLIT_LAUNCH 2   /* one launch per step; neither flag: the library's
                                      choice (see moe_plan_info's single_launch) */
+#define MOE_FLAG_POW2_SCALE 4     /* FP8 recipe: requant scales rounded up to a power of
+                                     two (DeepGEMM PR #440 "How it works", #383's choice) */
 #define MOE_FLAG_TEST_NO_WAIT 256 /* test-only: the single launch's waits give up at
                                      once, so MOE_STATUS_WAIT_TIMEOUT is set and y is
                                      invalid; exercises the timeout path */
@@ -94,6 +96,14 @@ typedef struct moe_shape {
     int32_t flags;         /* MOE_FLAG_* bits, 0 = defaults */
     int32_t recipe;        /* MOE_RECIPE_*; MXFP4 plans: no single launch,
                               max_tokens * H < 2^31, tile_m 128 needs H, I >= 384 */
+    int32_t act_sf_gran;   /* FP8 recipe: columns per intermediate (h) scale: 0 or 128,
+                              64 (L2 then scales each 128-K block as two 64-K halves,
+                              design doc §5.4), or -1 for the rule of PR #440 "How it
+                              works" (128 when H % 512 == 0 and 2I % 512 == 0, else 64).
+                              Per-64 plans use direct-load tiles (tile_m <= 64) and
+                              split launches.  MXFP4 plans: 0 (their blocks are 32). */
+    float activation_clamp; /* > 0: gate and up are clamped to [-c, c] before the
+                               SwiGLU (design doc §10.1); <= 0: no clamp */
 } moe_shape_t;
 
 typedef struct moe_plan* moe_plan_t;
@@ -111,6 +121,7 @@ typedef struct moe_tile_info {
     int32_t single_launch; /* 1: L1, L2 and combine run as one launch */
     int32_t l2_group_tiles; /* L2 tiles (of l2_tile_n columns) per workgroup: 2 for
                                16-row tiles when at least 1024 workgroups remain, else 1 */
+    int32_t act_sf_gran;    /* columns per intermediate (h) scale: 128 or 64 (FP8), 32 (MXFP4) */
 } moe_tile_info_t;
 
 /* Byte offsets of the workspace sections used by a forward with T tokens.
@@ -120,7 +131,8 @@ typedef struct moe_tile_info {
  *   row_src  int32 [pool_rows]    flat slot f = t*K + j held by a pool row, -1 = padding
  *   src_row  int32 [T*K]          pool row of slot f, -1 = skipped slot
  *   h        uint8 [pool_rows, I] e4m3 SwiGLU output (valid rows only)
- *   h_sf     f32   [pool_rows, I/128]  (MXFP4 plans: uint8 UE8M0 [pool_rows, I/32])
+ *   h_sf     f32   [pool_rows, I/128]  (per-64 plans: [pool_rows, I/64];
+ *                                       MXFP4 plans: uint8 UE8M0 [pool_rows, I/32])
  *   partial  uint16 [K, T, H]     bf16 L2 output of slot (t, j) at [j][t]
  *   status   int32 [4]            status[0] = MOE_STATUS_* bits, status[1] = #ids >= E */
 typedef struct moe_ws_layout {
@@ -256,6 +268,20 @@ int moe_prepare_weights_mx(moe_plan_t plan, const uint8_t* w1, const uint8_t* w1
                            const uint8_t* w2, const uint8_t* w2_sf, uint8_t* w1_packed,
                            uint8_t* w1_sf_packed, uint8_t* w2_packed, uint8_t* w2_sf_packed,
                            void* stream);
+
+/*
+ * Activation quantisation, the step the pages leave to the caller before each
+ * call ("07 · MegaMoE" §3 copies FP8 x and its scales into the buffer):
+ *   x_bf16 uint16 [T, H] bf16 (16-byte aligned), written to
+ *   FP8 plans:   x uint8 [T, H] e4m3, x_sf f32 [T, H/128];
+ *                per 1x128 block sf = max(amax, 1e-10)/448, q = e4m3(v / sf)
+ *                (correctly rounded division; RNE, saturating)
+ *   MXFP4 plans: x uint8 [T, H] e4m3, x_sf uint8 [T, H/32] UE8M0 codes;
+ *                per 1x32 block sf = the smallest power of two >= that
+ * x 16-byte aligned.  T == 0 is a no-op.  Same errors as moe_forward.
+ */
+int moe_quantize_act(moe_plan_t plan, int32_t num_tokens, const uint16_t* x_bf16, uint8_t* x,
+                     void* x_sf, void* stream);
 
 /*
  * Routing planner alone (step 1) with an explicit row alignment in [1, 1024]

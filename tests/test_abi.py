@@ -351,3 +351,55 @@ def test_mx_recipe_validation_and_choices():
     finally:
         moe.moe_plan_destroy(p)
         moe.moe_plan_destroy(q)
+
+
+def test_recipe_options_validation_and_rule():
+    # act_sf_gran: 0/128, 64, -1 (PR #440 rule); per-64 plans: no LDS tile,
+    # no single launch; MXFP4 plans: no per-64 or power-of-two flag; NaN clamp
+    for kw, code in ((dict(act_sf_gran=32), moe.MOE_ERR_INVALID_ARG),
+                     (dict(act_sf_gran=64, tile_m=128), moe.MOE_ERR_UNSUPPORTED_SHAPE),
+                     (dict(act_sf_gran=64, flags=moe.MOE_FLAG_SINGLE_LAUNCH), moe.MOE_ERR_INVALID_ARG),
+                     (dict(activation_clamp=float("nan")), moe.MOE_ERR_INVALID_ARG),
+                     (dict(act_sf_gran=64, recipe=moe.MOE_RECIPE_MXFP4), moe.MOE_ERR_INVALID_ARG),
+                     (dict(flags=moe.MOE_FLAG_POW2_SCALE, recipe=moe.MOE_RECIPE_MXFP4),
+                      moe.MOE_ERR_INVALID_ARG)):
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_plan_create(4096, 2048, 256, 6, 8192, **kw)
+        assert ei.value.code == code, kw
+    for (H, I), want in (((4096, 2048), 128), ((7168, 3072), 128), ((256, 128), 64),
+                         ((640, 384), 64)):
+        p = moe.moe_plan_create(H, I, 16, 2, 4096, act_sf_gran=-1)
+        try:
+            info = moe.moe_plan_info(p, 4096)
+            assert info["act_sf_gran"] == want, (H, I)
+            if want == 64:  # direct tiles only
+                assert info["tile_m"] <= 64
+        finally:
+            moe.moe_plan_destroy(p)
+    # per-64 needs twice the h_sf bytes; the workspace grows accordingly
+    a = moe.moe_plan_create(4096, 2048, 256, 6, 128)
+    b = moe.moe_plan_create(4096, 2048, 256, 6, 128, act_sf_gran=64)
+    try:
+        la, lb = moe.moe_workspace_layout(a, 128), moe.moe_workspace_layout(b, 128)
+        assert lb["h"] - lb["h_sf"] >= 2 * (la["h"] - la["h_sf"]) - 256
+        assert moe.moe_plan_info(b, 128)["single_launch"] == 0
+    finally:
+        moe.moe_plan_destroy(a)
+        moe.moe_plan_destroy(b)
+
+
+def test_quantize_act_rejects_invalid_calls_on_host():
+    L = moe.lib()
+    p = moe.moe_plan_create(256, 128, 4, 2, 8)
+    try:
+        x, q, sf = ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20)
+        assert L.moe_quantize_act(p, 9, x, q, sf, None) == moe.MOE_ERR_INVALID_ARG  # T > max
+        assert L.moe_quantize_act(p, 4, None, q, sf, None) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_quantize_act(p, 4, ctypes.c_void_p((1 << 20) + 2), q, sf, None) == \
+            moe.MOE_ERR_INVALID_ARG
+        assert L.moe_quantize_act(p, 4, x, q, ctypes.c_void_p((3 << 20) + 1), None) == \
+            moe.MOE_ERR_INVALID_ARG
+        assert L.moe_quantize_act(p, 0, x, q, sf, None) == moe.MOE_OK  # no-op
+        assert L.moe_quantize_act(None, 4, x, q, sf, None) == moe.MOE_ERR_INVALID_ARG
+    finally:
+        moe.moe_plan_destroy(p)

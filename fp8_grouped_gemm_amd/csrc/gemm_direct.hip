@@ -7,6 +7,9 @@
 // with sa the 1x128 activation scale and sb the 128x128 weight scale.
 // L1 epilogue (§10.1; DeepGEMM PR #440 "How it works" for the raw scale):
 //   h = silu(g) * u * topk_w,  sf = max(amax_128, 1e-10) / 448,  q = e4m3(h / sf)
+// with the plan's options: gate/up clamped to [-c, c] first (§10.1), sf
+// rounded up to a power of two (PR #440 on #383), or one scale per 64
+// columns (§5.4, then L2 multiplies each 128-K block as two 64-K halves).
 // L2 epilogue (§11.1): bf16(acc) stored at partial[j][t] for the slot
 // (t, j) the pool row holds.
 //
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(WV * 64, MT == 2 && PK && !G64 ? 2 : 1) void l2_dir
 // ------------------------------------------------- L1 split-K epilogue
 
 // Finishes a 16-row L1 tile whose K range ran as S workgroups: adds the S
-// f32 partials in slice order, then the same SwiGLU x topk_w, per-128 amax
+// f32 partials in slice order, then the same SwiGLU x topk_w, per-128 (or 64) amax
 // and e4m3 requant as the l1_direct epilogue.  Thread t: row t/16, gate
 // columns 8*(t%16) .. +8 of the tile's 128-column block and the matching up
 // columns; the 16 threads of a row share one wave quarter.

@@ -18,6 +18,9 @@
  *      (design doc §11.1);
  *   5. combine: per token, f32 sum of its slots' BF16 partials, cast to
  *      BF16 (design doc §11.2; "07 · MegaMoE" §9).
+ * Variants a plan can select: the FP8 x MXFP4 recipe of the SM100 kernel
+ * (moe_forward_mx; e2m1 weights, UE8M0 scales per 32), an activation clamp,
+ * power-of-two or per-64 intermediate scales; moe_quantize_act prepares x.
  *
  * Conventions for every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller, row-major,

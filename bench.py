@@ -63,20 +63,31 @@ def algorithmic_bytes(cfg, idx, mx=False):
     }
 
 
+def kernel_source_digest(paths):
+    """Digest of the code in the given sources: comments and whitespace are
+    dropped first, so a changed comment leaves the measured counters valid
+    and any changed code does not."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in paths:
+        text = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(cfg, weights):
     """HBM bytes per launch of the L1 step from the committed rocprofv3
     counter summary (FETCH_SIZE / WRITE_SIZE scaled by a plain copy's
     readings), or None when no summary matches this workload or the kernel
     sources changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "flash_decode_l1_traffic.json")
     if cfg.name != "flash_decode" or weights != "packed" or not os.path.exists(path):
         return None
     d = json.load(open(path))
-    h = hashlib.sha256()
-    for f in d["source_files"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest()[:16] != d["source_sha256_16"]:
+    if kernel_source_digest(d["source_files"]) != d["source_code_digest"]:
         return None
     return d["l1_step_traffic_bytes"]
 

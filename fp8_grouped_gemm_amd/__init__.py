@@ -24,6 +24,7 @@ MOE_WEIGHTS_PACKED = 1
 MOE_FLAG_SINGLE_LAUNCH = 1
 MOE_FLAG_SPLIT_LAUNCH = 2
 MOE_FLAG_POW2_SCALE = 4
+MOE_FLAG_DIRECT_TILES = 8
 MOE_FLAG_TEST_NO_WAIT = 256
 MOE_FLAG_TEST_SMALL_GRID = 512
 MOE_RECIPE_FP8_BLOCK128 = 0

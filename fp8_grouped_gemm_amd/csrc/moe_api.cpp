@@ -31,9 +31,10 @@ struct Config {
 // Rows per tile from the expected rows per expert T*K/E: the smallest tile
 // that holds an average expert's rows reads each expert's weights once
 // while padding as few MFMA rows as possible (decode: 16).
-// Beyond ~24 rows per expert the 128 x 256 LDS-staged MFMA tile takes over
-// (it needs H % 256 == 0 for its 256-column L2 tiles and I >= 256 for at
-// least two K blocks in L2; otherwise 64-row direct-load tiles).
+// Beyond ~24 rows per expert the LDS-staged MFMA tiles take over, 64 x 256
+// up to kRowsLds64 rows per expert and 128 x 256 above (they need H % 256 ==
+// 0 for their 256-column L2 tiles and enough K blocks, lds_tile_fits;
+// otherwise 64-row direct-load tiles).
 // Columns per intermediate scale of an FP8 plan (MXFP4: 32).
 int sf_gran(const moe_shape_t& s)
 {
@@ -52,18 +53,24 @@ bool lds_tile_fits(const moe_shape_t& s)
     return s.hidden % 256 == 0 && s.hidden / 128 >= min_kb && s.intermediate / 128 >= min_kb;
 }
 
+constexpr double kRowsLds64 = 64.0;
+
 Config choose_config(const moe_shape_t& s, int T)
 {
+    const bool lds = lds_tile_fits(s) && sf_gran(s) != 64;
+    const bool lds64 = lds && !(s.flags & MOE_FLAG_DIRECT_TILES);
     if (s.tile_m > 0)
-        return Config{s.tile_m, s.tile_m == 128 ? 1 : 0};
+        return Config{s.tile_m, s.tile_m == 128 || (s.tile_m == 64 && lds64) ? 1 : 0};
     const double rows = (double)T * s.top_k / s.num_experts;
     if (rows <= 12.0)
         return Config{16, 0};
     if (rows <= 24.0)
         return Config{32, 0};
-    if (lds_tile_fits(s) && sf_gran(s) != 64)
-        return Config{128, 1};
-    return Config{64, 0};
+    if (!lds)
+        return Config{64, 0};
+    if (rows <= kRowsLds64)
+        return Config{64, lds64 ? 1 : 0};
+    return Config{128, 1};
 }
 
 struct Layout {
@@ -243,7 +250,7 @@ int validate_shape(const moe_shape_t* s)
     if (s->weight_layout == MOE_WEIGHTS_PACKED && s->hidden % 256)
         return MOE_ERR_UNSUPPORTED_SHAPE;
     if (s->flags & ~(MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_SPLIT_LAUNCH | MOE_FLAG_POW2_SCALE |
-                     MOE_FLAG_TEST_NO_WAIT | MOE_FLAG_TEST_SMALL_GRID))
+                     MOE_FLAG_DIRECT_TILES | MOE_FLAG_TEST_NO_WAIT | MOE_FLAG_TEST_SMALL_GRID))
         return MOE_ERR_INVALID_ARG;
     if (s->act_sf_gran != 0 && s->act_sf_gran != 64 && s->act_sf_gran != 128 && s->act_sf_gran != -1)
         return MOE_ERR_INVALID_ARG;

@@ -68,6 +68,9 @@ extern "C" {
                                      choice (see moe_plan_info's single_launch) */
 #define MOE_FLAG_POW2_SCALE 4     /* FP8 recipe: requant scales rounded up to a power of
                                      two (DeepGEMM PR #440 "How it works", #383's choice) */
+#define MOE_FLAG_DIRECT_TILES 8   /* 64-row tiles use the direct-load kernels even where
+                                     the LDS-staged 64-row kernel fits (so that
+                                     MOE_FLAG_SINGLE_LAUNCH can apply to them) */
 #define MOE_FLAG_TEST_NO_WAIT 256 /* test-only: the single launch's waits give up at
                                      once, so MOE_STATUS_WAIT_TIMEOUT is set and y is
                                      invalid; exercises the timeout path */

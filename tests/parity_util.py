@@ -72,13 +72,13 @@ def run_oracle(h, tokens=None, want=()):
                               h["w2"], h["w2_sf"], tokens=tokens, want=want)
 
 
-def run_gpu(inp, tile_m=0, max_tokens=None, runner=None, weight_layout=0):
+def run_gpu(inp, tile_m=0, max_tokens=None, runner=None, weight_layout=0, flags=0):
     T, H = inp["x"].shape
     E, twoI, _ = inp["w1"].shape
     K = inp["topk_idx"].shape[1]
     if runner is None:
         runner = moe.MoEForward(H, twoI // 2, E, K, max_tokens or T, tile_m=tile_m,
-                                weight_layout=weight_layout)
+                                weight_layout=weight_layout, flags=flags)
     w1, w2 = runner.prepare(inp["w1"], inp["w2"])
     y = runner.forward(inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_w"], w1,
                        inp["w1_sf"], w2, inp["w2_sf"])

@@ -146,6 +146,25 @@ def test_tile128_needs_two_k_blocks_per_layer():
     moe.moe_plan_destroy(moe.moe_plan_create(256, 256, 8, 2, 64, tile_m=128))
 
 
+def test_tile64_kernel_choice():
+    # 64-row tiles run on the LDS-staged kernel where it fits, on the
+    # direct-load kernel where it does not (H % 256 != 0, one K block, per-64
+    # scales) or when the plan asks for direct tiles
+    cases = [((512, 384, 16, 4), {}, 1),
+             ((512, 384, 16, 4), dict(flags=moe.MOE_FLAG_DIRECT_TILES), 0),
+             ((384, 256, 8, 2), {}, 0),
+             ((256, 128, 8, 2), {}, 0),
+             ((512, 384, 16, 4), dict(act_sf_gran=64), 0),
+             ((512, 384, 16, 4), dict(recipe=moe.MOE_RECIPE_MXFP4), 1),
+             ((512, 256, 16, 4), dict(recipe=moe.MOE_RECIPE_MXFP4), 0)]  # MX: 3 K blocks
+    for shape, kw, kernel in cases:
+        p = moe.moe_plan_create(*shape, 256, tile_m=64, **kw)
+        try:
+            assert moe.moe_plan_info(p, 256)["kernel"] == kernel, (shape, kw)
+        finally:
+            moe.moe_plan_destroy(p)
+
+
 def test_plan_flags_and_single_launch_choice():
     with pytest.raises(moe.MoEError) as e:
         moe.moe_plan_create(256, 128, 8, 2, 64, flags=1 << 5)            # unknown bit

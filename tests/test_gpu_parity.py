@@ -88,9 +88,9 @@ def test_route_zero_tokens():
 # ---------------------------------------------------------------- forward
 
 
-def forward_and_check(host, dev, tile_m, what, check_intermediates=True):
-    say(f"forward {what}: tile_m={tile_m}")
-    y, runner = run_gpu(dev, tile_m=tile_m)
+def forward_and_check(host, dev, tile_m, what, check_intermediates=True, flags=0):
+    say(f"forward {what}: tile_m={tile_m} flags={flags}")
+    y, runner = run_gpu(dev, tile_m=tile_m, flags=flags)
     T = dev["x"].shape[0]
     K = dev["topk_idx"].shape[1]
     ref = run_oracle(host, want=("h", "partial", "acc1"))
@@ -174,6 +174,7 @@ def test_forward_ragged_multi_tile_shapes():
     host, dev = small_case(203, 512, 384, 16, 4, 12)
     for tile_m in (16, 32, 64, 128):
         forward_and_check(host, dev, tile_m, f"ragged tile {tile_m}")
+    forward_and_check(host, dev, 64, "ragged tile 64 direct", flags=moe.MOE_FLAG_DIRECT_TILES)
 
 
 def test_forward_single_token_and_hot_expert():
@@ -184,6 +185,7 @@ def test_forward_single_token_and_hot_expert():
     host, dev = small_case(T, 256, 256, 8, 2, 14, mask={(t, 0): 2 for t in range(T)})
     for tile_m in (16, 64, 128):
         forward_and_check(host, dev, tile_m, f"hot expert tile {tile_m}")
+    forward_and_check(host, dev, 64, "hot expert tile 64 direct", flags=moe.MOE_FLAG_DIRECT_TILES)
 
 
 def test_forward_deterministic_and_workspace_reuse():
@@ -197,13 +199,16 @@ def test_forward_deterministic_and_workspace_reuse():
     check_y(y2.cpu().numpy(), run_oracle(host2)["y"], what="reuse, larger call")
 
 
-@pytest.mark.parametrize("tile_m", [16, 32, 64, 128])
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128, "64d"])
 def test_packed_weights_match_row_major_bitwise(tile_m):
     # packed weights only change where the kernels read each fragment from:
     # same arithmetic in the same order, so y is bit-identical
     host, dev = small_case(203, 512, 384, 16, 4, 17)
-    y_row, _ = run_gpu(dev, tile_m=tile_m)
-    y_pk, runner = run_gpu(dev, tile_m=tile_m, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    flags = moe.MOE_FLAG_DIRECT_TILES if tile_m == "64d" else 0  # 64-row direct-load tiles
+    tile_m = 64 if tile_m == "64d" else tile_m
+    y_row, _ = run_gpu(dev, tile_m=tile_m, flags=flags)
+    y_pk, runner = run_gpu(dev, tile_m=tile_m, weight_layout=moe.MOE_WEIGHTS_PACKED, flags=flags)
+    assert moe.moe_plan_info(runner.plan, 203)["kernel"] == (0 if flags or tile_m < 64 else 1)
     assert torch.equal(y_row, y_pk)
     check_y(y_pk.cpu().numpy(), run_oracle(host)["y"], what=f"packed tile {tile_m}")
 
@@ -252,8 +257,9 @@ def test_forward_small_token_counts_split_k():
 # ------------------------------- 128-row tiles: persistent LDS kernels
 
 
+@pytest.mark.parametrize("tile", [64, 128])
 @pytest.mark.parametrize("case", ["ragged", "hot", "many_blocks", "tiny_rows"])
-def test_tile128_persistent_small_grid_matches_full_grid(case):
+def test_lds_tiles_persistent_small_grid_matches_full_grid(case, tile):
     # With the test flag the persistent kernels run on 4 workgroups, so each
     # walks many tiles (copies of the next tile overlap the current tile's
     # epilogue, metadata slots rotate); the arithmetic per tile is the same,
@@ -268,22 +274,51 @@ def test_tile128_persistent_small_grid_matches_full_grid(case):
     else:  # one K block more than the minimum, masked slots, a token with no slot
         host, dev = small_case(45, 256, 256, 6, 3, 23, mask={(0, 0): -1, (0, 1): -1, (0, 2): -1,
                                                              (5, 1): -3})
-    y_full, r_full = _run_flags(dev, 0, 128)
-    y_small, r_small = _run_flags(dev, moe.MOE_FLAG_TEST_SMALL_GRID, 128)
+    y_full, r_full = _run_flags(dev, 0, tile)
+    y_small, r_small = _run_flags(dev, moe.MOE_FLAG_TEST_SMALL_GRID, tile)
     T = dev["x"].shape[0]
     assert moe.moe_plan_info(r_small.plan, T)["kernel"] == 1
     assert torch.equal(y_full, y_small), case
-    check_y(y_small.cpu().numpy(), run_oracle(host)["y"], what=f"tile 128 small grid {case}")
+    check_y(y_small.cpu().numpy(), run_oracle(host)["y"], what=f"tile {tile} small grid {case}")
 
 
-def test_tile128_full_size_packed_small_grid():
+@pytest.mark.parametrize("case", ["ragged", "hot", "tiny_rows"])
+def test_tile64_lds_matches_direct_tiles_and_tile128_bitwise(case):
+    # Every kernel computes each row with the same MFMAs, the same per-K-block
+    # promotion and the same epilogue arithmetic; only the tiling (and hence
+    # the padding rows) differs, so y is bit-identical across them.
+    if case == "ragged":
+        host, dev = small_case(203, 512, 384, 16, 4, 12)
+    elif case == "hot":
+        T = 150
+        host, dev = small_case(T, 256, 256, 8, 2, 14, mask={(t, 0): 2 for t in range(T)})
+    else:
+        host, dev = small_case(45, 256, 256, 6, 3, 23, mask={(0, 0): -1, (5, 1): -3})
+    T = dev["x"].shape[0]
+    y64, r64 = _run_flags(dev, 0, 64)
+    assert moe.moe_plan_info(r64.plan, T)["kernel"] == 1
+    y64d, r64d = _run_flags(dev, moe.MOE_FLAG_DIRECT_TILES, 64)
+    assert moe.moe_plan_info(r64d.plan, T)["kernel"] == 0
+    y128, _ = _run_flags(dev, 0, 128)
+    assert torch.equal(y64, y64d), case
+    assert torch.equal(y64, y128), case
+    y64p, _ = _run_flags(dev, 0, 64, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert torch.equal(y64, y64p), case
+    check_y(y64.cpu().numpy(), run_oracle(host)["y"], what=f"tile 64 LDS {case}")
+
+
+@pytest.mark.parametrize("tile", [0, 128])
+def test_lds_tiles_full_size_packed_small_grid(tile):
     # The flash-prefill workload on 4 workgroups (every workgroup walks
-    # ~1400 L1 tiles) against the full grid, packed weights.
+    # ~1000 L1 tiles) against the full grid, packed weights: the library's
+    # choice (64-row LDS tiles, ~48 rows per expert) and 128-row tiles.
     cfg = wl.CONFIGS["flash_prefill"]
     inp = gpu_inputs(cfg, wl.default_seed(cfg))
-    y_full, r = _run_flags(inp, 0, weight_layout=moe.MOE_WEIGHTS_PACKED)
-    assert moe.moe_plan_info(r.plan, cfg.T)["kernel"] == 1
-    y_small, _ = _run_flags(inp, moe.MOE_FLAG_TEST_SMALL_GRID, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    y_full, r = _run_flags(inp, 0, tile, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    info = moe.moe_plan_info(r.plan, cfg.T)
+    assert info["kernel"] == 1 and info["tile_m"] == (tile or 64)
+    y_small, _ = _run_flags(inp, moe.MOE_FLAG_TEST_SMALL_GRID, tile,
+                            weight_layout=moe.MOE_WEIGHTS_PACKED)
     assert torch.equal(y_full, y_small)
     del inp
     torch.cuda.empty_cache()
@@ -322,8 +357,10 @@ def test_single_launch_matches_split_launch_bitwise(case):
     else:
         T = 150
         host, dev = small_case(T, 256, 256, 8, 2, 14, mask={(t, 0): 2 for t in range(T)})
-    y_split, r_split = _run_flags(dev, moe.MOE_FLAG_SPLIT_LAUNCH, tile)
-    y_one, r_one = _run_flags(dev, moe.MOE_FLAG_SINGLE_LAUNCH, tile)
+    # (64-row tiles: the direct-load kernels, which the single launch is built from)
+    direct = moe.MOE_FLAG_DIRECT_TILES if tile == 64 else 0
+    y_split, r_split = _run_flags(dev, moe.MOE_FLAG_SPLIT_LAUNCH | direct, tile)
+    y_one, r_one = _run_flags(dev, moe.MOE_FLAG_SINGLE_LAUNCH | direct, tile)
     T = dev["x"].shape[0]
     assert moe.moe_plan_info(r_split.plan, T)["single_launch"] == 0
     assert moe.moe_plan_info(r_one.plan, T)["single_launch"] == 1

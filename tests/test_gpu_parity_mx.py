@@ -34,13 +34,14 @@ def mx_case(T, H, I, E, K, seed, mask=None, skew=False):
     return host, {k: v.cuda() for k, v in inp.items()}
 
 
-def run_gpu_mx(dev, tile_m=0, max_tokens=None, runner=None, weight_layout=0):
+def run_gpu_mx(dev, tile_m=0, max_tokens=None, runner=None, weight_layout=0, flags=0):
     T, H = dev["x"].shape
     E, twoI, _ = dev["w1"].shape
     K = dev["topk_idx"].shape[1]
     if runner is None:
         runner = moe.MoEForward(H, twoI // 2, E, K, max_tokens or T, tile_m=tile_m,
-                                recipe=moe.MOE_RECIPE_MXFP4, weight_layout=weight_layout)
+                                recipe=moe.MOE_RECIPE_MXFP4, weight_layout=weight_layout,
+                                flags=flags)
     w1, w1_sf, w2, w2_sf = runner.prepare_mx(dev["w1"], dev["w1_sf"], dev["w2"], dev["w2_sf"])
     y = runner.forward(dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_w"], w1, w1_sf, w2,
                        w2_sf)
@@ -131,44 +132,55 @@ def test_mx_forward_deterministic_and_auto_tile():
     check_y(y1.cpu().numpy(), run_oracle_mx(host)["y"], what="auto tile")
 
 
-@pytest.mark.parametrize("tile_m", [16, 32, 64])
+@pytest.mark.parametrize("tile_m", [16, 32, 64, "64d"])
 def test_mx_packed_weights_match_row_major_bitwise(tile_m):
     # the packed layout only changes where each operand byte is read from:
-    # same MFMAs in the same order, so y is bit-identical
+    # same MFMAs in the same order, so y is bit-identical ("64d": 64-row
+    # direct-load tiles; plain 64: the LDS-staged 64-row tile)
     host, dev = mx_case(37, 512, 384, 16, 4, 211, mask={(5, 1): -1, (20, 3): 40})
-    y_row, _ = run_gpu_mx(dev, tile_m=tile_m)
-    y_pk, _ = run_gpu_mx(dev, tile_m=tile_m, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    flags = moe.MOE_FLAG_DIRECT_TILES if tile_m == "64d" else 0
+    tile_m = 64 if tile_m == "64d" else tile_m
+    y_row, _ = run_gpu_mx(dev, tile_m=tile_m, flags=flags)
+    y_pk, r = run_gpu_mx(dev, tile_m=tile_m, weight_layout=moe.MOE_WEIGHTS_PACKED, flags=flags)
+    assert moe.moe_plan_info(r.plan, 37)["kernel"] == (0 if flags or tile_m < 64 else 1)
     assert torch.equal(y_row, y_pk)
     check_y(y_pk.cpu().numpy(), run_oracle_mx(host)["y"], what=f"packed tile {tile_m}")
 
 
+@pytest.mark.parametrize("tile", [64, 128])
 @pytest.mark.parametrize("case", ["hot", "ragged"])
-def test_mx_lds_tile_128(case):
-    # LDS-staged persistent 128-row tiles: intermediates against the oracle,
-    # packed weights bit-identical to row-major, and a 4-workgroup grid (each
-    # workgroup walking many tiles across tile boundaries) bit-identical to
-    # the full grid
+def test_mx_lds_tiles(case, tile):
+    # LDS-staged persistent 64- and 128-row tiles: intermediates against the
+    # oracle, packed weights bit-identical to row-major, a 4-workgroup grid
+    # (each workgroup walking many tiles across tile boundaries)
+    # bit-identical to the full grid, and (64 rows) the direct-load 64-row
+    # tiles bit-identical too
     if case == "hot":
         host, dev = mx_case(300, 512, 384, 4, 3, 411, skew=True)
     else:
         host, dev = mx_case(157, 768, 512, 6, 2, 412, mask={(3, 0): -1, (40, 1): 77})
-    y, runner = check_case(host, dev, 128, f"LDS tile 128 {case}")
+    y, runner = check_case(host, dev, tile, f"LDS tile {tile} {case}")
     assert moe.moe_plan_info(runner.plan, dev["x"].shape[0])["kernel"] == 1
-    y_pk, _ = run_gpu_mx(dev, tile_m=128, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    y_pk, _ = run_gpu_mx(dev, tile_m=tile, weight_layout=moe.MOE_WEIGHTS_PACKED)
     assert torch.equal(y, y_pk)
     T, H = dev["x"].shape
     E, twoI, _ = dev["w1"].shape
-    small = moe.MoEForward(H, twoI // 2, E, dev["topk_idx"].shape[1], T, tile_m=128,
+    small = moe.MoEForward(H, twoI // 2, E, dev["topk_idx"].shape[1], T, tile_m=tile,
                            recipe=moe.MOE_RECIPE_MXFP4, flags=moe.MOE_FLAG_TEST_SMALL_GRID)
     y_small, _ = run_gpu_mx(dev, runner=small)
     assert torch.equal(y, y_small)
+    if tile == 64:
+        y_direct, rd = run_gpu_mx(dev, tile_m=64, flags=moe.MOE_FLAG_DIRECT_TILES)
+        assert moe.moe_plan_info(rd.plan, T)["kernel"] == 0
+        assert torch.equal(y, y_direct)
 
 
 def test_mx_flash_prefill_full_size_sampled():
     cfg = wl.CONFIGS["flash_prefill"]
     dev = wl.make_inputs_mx(cfg, wl.default_seed(cfg), "cuda")
     y, runner = run_gpu_mx(dev, weight_layout=moe.MOE_WEIGHTS_PACKED)
-    assert moe.moe_plan_info(runner.plan, cfg.T)["tile_m"] == 128
+    info = moe.moe_plan_info(runner.plan, cfg.T)  # ~48 rows per expert
+    assert info["tile_m"] == 64 and info["kernel"] == 1
     toks = [0, 1, 517, 1024, 1999, cfg.T - 1]
     E = cfg.E
     idx = dev["topk_idx"].cpu().numpy()

@@ -74,7 +74,7 @@ extern "C" {
 #define MOE_FLAG_TEST_NO_WAIT 256 /* test-only: the single launch's waits give up at
                                      once, so MOE_STATUS_WAIT_TIMEOUT is set and y is
                                      invalid; exercises the timeout path */
-#define MOE_FLAG_TEST_SMALL_GRID 512 /* test-only: the persistent 128-row-tile kernels
+#define MOE_FLAG_TEST_SMALL_GRID 512 /* test-only: the persistent LDS-tile kernels
                                         launch at most 4 workgroups, so each walks many
                                         tiles (same results as the full grid) */
 
@@ -96,8 +96,11 @@ typedef struct moe_shape {
     int32_t num_experts;   /* E */
     int32_t top_k;         /* K */
     int32_t max_tokens;    /* largest T any call on this plan may pass */
-    int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128
-                              (128: H % 256 == 0 and I >= 256; MXFP4: I >= 384) */
+    int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128.
+                              64 and 128 run the LDS-staged kernel where it fits
+                              (H % 256 == 0, H and I >= 256 (MXFP4: 384), per-128
+                              scales); 128 requires it, 64 otherwise (or with
+                              MOE_FLAG_DIRECT_TILES) runs the direct-load kernel */
     int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
     int32_t flags;         /* MOE_FLAG_* bits, 0 = defaults */
     int32_t recipe;        /* MOE_RECIPE_*; MXFP4 plans: no single launch,

@@ -254,7 +254,7 @@ def test_forward_small_token_counts_split_k():
     torch.cuda.empty_cache()
 
 
-# ------------------------------- 128-row tiles: persistent LDS kernels
+# ------------------------------- 64- and 128-row tiles: persistent LDS kernels
 
 
 @pytest.mark.parametrize("tile", [64, 128])

@@ -314,7 +314,7 @@ def main():
         dom = max(("l1", "l2"), key=lambda n: avg[n])
         dom_bytes = alg[dom]
         kernel_name = (("MXFP4 " if mx else "") + ("L1 step: GEMM gate+up, SwiGLU x topk_w, e4m3 requant "
-                        f"({'direct-load tiles' if info['kernel'] == 0 else 'LDS-staged tiles'}, "
+                        f"({('direct-load', 'LDS-staged', 'shared-A')[info['kernel']]} tiles, "
                         f"tile_m {info['tile_m']})") if dom == "l1" else
                        ("MXFP4 " if mx else "") + f"L2 step: GEMM down (tile_m {info['tile_m']})")
     achieved = dom_bytes / (avg[dom] * 1e-6) / 1e9

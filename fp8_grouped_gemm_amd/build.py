@@ -9,8 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_fp8.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["moe_api.cpp", "route.hip", "gemm_direct.hip", "gemm_lds.hip", "gemm_mx.hip", "pack.hip",
-           "quant.hip"]
+SOURCES = ["moe_api.cpp", "route.hip", "gemm_direct.hip", "gemm_lds.hip", "gemm_sa.hip",
+           "gemm_mx.hip", "pack.hip", "quant.hip"]
 PEAKS_LIB = os.path.join(HERE, "libmoe_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]
 

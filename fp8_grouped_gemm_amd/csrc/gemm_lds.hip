@@ -49,6 +49,7 @@
 // amax; sf = the smallest power of two >= max(amax, 1e-10)/448.
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_lds.h"
 
 namespace moe {
 
@@ -79,66 +80,6 @@ struct LdsCfg {
 };
 static_assert(LdsCfg<false, 128>::SMEM <= 160 * 1024 && LdsCfg<true, 128>::SMEM <= 160 * 1024,
               "LDS");
-
-// s_waitcnt with vmcnt = n (n < 16) and no wait on expcnt / lgkmcnt
-// (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
-#define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0xF70 | (n))
-
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15] (the immediate must
-// be a constant).
-__device__ __forceinline__ void wait_vmcnt(int n)
-{
-    switch (n) {
-    case 0: MOE_WAIT_VMCNT(0); break;
-    case 1: MOE_WAIT_VMCNT(1); break;
-    case 2: MOE_WAIT_VMCNT(2); break;
-    case 3: MOE_WAIT_VMCNT(3); break;
-    case 4: MOE_WAIT_VMCNT(4); break;
-    case 5: MOE_WAIT_VMCNT(5); break;
-    case 6: MOE_WAIT_VMCNT(6); break;
-    case 7: MOE_WAIT_VMCNT(7); break;
-    case 8: MOE_WAIT_VMCNT(8); break;
-    case 9: MOE_WAIT_VMCNT(9); break;
-    case 10: MOE_WAIT_VMCNT(10); break;
-    case 11: MOE_WAIT_VMCNT(11); break;
-    case 12: MOE_WAIT_VMCNT(12); break;
-    case 13: MOE_WAIT_VMCNT(13); break;
-    case 14: MOE_WAIT_VMCNT(14); break;
-    default: MOE_WAIT_VMCNT(0); break;  // (never larger here; waiting for all is safe)
-    }
-}
-
-// Asynchronous copy global -> LDS of 16 (or 4) bytes per lane to
-// lds_base + 16 * lane (4 * lane).  lds_base is wave-uniform (read from the
-// first lane into the scalar register M0 takes).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory", "m0");
-}
-
-// 32-bit LDS offset of a __shared__ object (what M0 expects).
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p)
-{
-    const __attribute__((address_space(3))) uint8_t* lp =
-        (const __attribute__((address_space(3))) uint8_t*)p;
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lp);
-}
-
-__device__ __forceinline__ v8i lds_frag(const uint8_t* sub_base, int lane)
-{
-    const uint4 lo = *reinterpret_cast<const uint4*>(sub_base + lane * 16);
-    const uint4 hi = *reinterpret_cast<const uint4*>(sub_base + 1024 + lane * 16);
-    return pack_frag(lo, hi);
-}
 
 // Address of the 16 bytes lane `lane` copies for weight subtile `sub`
 // (packed order w4 * 4 + s, see pack.hip), half `half`, K block kb.
@@ -707,8 +648,8 @@ static hipError_t launch_lds_bm(const FwdArgs& a, hipStream_t s)
 {
     if (a.BM == 128)
         return a.mx ? launch_lds<L1, true, 128>(a, s) : launch_lds<L1, false, 128>(a, s);
-    if (a.BM == 64)
-        return a.mx ? launch_lds<L1, true, 64>(a, s) : launch_lds<L1, false, 64>(a, s);
+    if (a.BM == 64 && a.mx)  // (FP8 64-row tiles run the shared-A kernel)
+        return launch_lds<L1, true, 64>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,283 @@
+// L1 / L2 grouped FP8 GEMMs on 64-row tiles with the activation rows shared
+// through LDS ("shared-A" tiles, prefill shapes with ~24-64 routed rows per
+// expert).
+//
+// Same arithmetic as the direct-load and LDS-staged kernels ("MegaMoE SM90
+// Implementation Design" §5.3 promotion per 128-K block, §10.1 / §11.1
+// epilogues): for every K block kb, p = 16x16x128 e4m3 MFMA with C = 0, then
+//   acc = fmaf(sa[row, kb] * sb[col block, kb], p, acc).
+//
+// gfx950 mapping.  A workgroup is 4 waves over one tile of 64 pool rows:
+// L1 128 gate + 128 up columns (wave w: gate columns [32w, 32w+32) and the
+// same up columns), L2 256 output columns (wave w: [64w, 64w+64)).  Each
+// wave streams its own weight subtiles straight into registers, one K block
+// ahead, as the decode tiles do (each weight byte is read by exactly one
+// wave).  The tile's 64 activation rows (and their scales) are the operand
+// every wave needs: instead of four register copies per workgroup they are
+// copied once per K block global -> LDS (gfx950's global_load_lds, in MFMA
+// fragment order) into a three-stage ring, and each wave reads its fragments
+// from there after one barrier.  That keeps a wave within 256 VGPRs, so two
+// workgroups share a compute unit and one's epilogue runs under the other's
+// weight stream.  (A third register set, two blocks ahead, spills.)
+//
+// Waits.  The copies are inline assembly the compiler does not count, so the
+// wait for K block kb's activation copies is explicit: vector-memory
+// operations retire in order, and after kb's copies each wave has issued
+// kb's 8 weight loads and, when block kb + 1 has been fetched, that block's
+// 3 copies and 8 weight loads (the weight scales may be scalar loads, which
+// vmcnt does not count, so they are left out: waiting for fewer outstanding
+// operations than allowed is always safe).  The compiler's own wait before
+// the MFMAs covers the weight registers.
+#include "moe_device.h"
+#include "moe_direct.h"
+#include "moe_internal.h"
+#include "moe_lds.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int SA_BM = 64;
+constexpr int SA_NS = 3;                    // activation stages
+constexpr int SA_A = SA_BM * 128;           // 8 KiB: 4 m-subtiles x 2 halves x 1 KiB
+constexpr int SA_STAGE = SA_A + 4 * 256;    // + one 256-byte scale copy per wave
+constexpr int SA_WLOADS = 8;                // weight loads per wave and K block
+constexpr int SA_COPIES = 3;                // activation copies per wave and K block
+
+}  // namespace
+
+template <bool L1, bool PK>
+__global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t stage_mem[SA_NS * SA_STAGE];
+    const int H = a.H, I = a.I, K = a.K, T = a.T;
+    const int NT = L1 ? I / 128 : H / 256;
+    const int nkb = L1 ? H / 128 : I / 128;
+    const int mb = blockIdx.x / NT;
+    const int nt = blockIdx.x - mb * NT;
+    const int e = a.mblock_expert[mb];
+    if (e < 0)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int row0 = mb * SA_BM;
+    const uint32_t stage_lds = lds_addr(stage_mem);
+
+    // Activation copies: wave w copies m-subtile w (rows row0 + 16 w + lr),
+    // both 64-byte halves, and the scale of row 16 w + (lane & 15).  A
+    // padding row (row_src < 0) copies a valid row (L1: token 0; L2: the
+    // block's first row, which always holds a slot): its products reach
+    // only that padding row of the accumulator, which is never stored.
+    const int fr = a.row_src[row0 + 16 * wave + lr];
+    const uint8_t* asrc;
+    const float* ssrc;
+    if constexpr (L1) {
+        const size_t tok = fr >= 0 ? (size_t)(fr / K) : 0;
+        asrc = a.x + tok * H + 16 * lg;
+        ssrc = a.x_sf + tok * (H / 128);
+    } else {
+        const size_t r = fr >= 0 ? (size_t)(row0 + 16 * wave + lr) : (size_t)row0;
+        asrc = a.h + r * I + 16 * lg;
+        ssrc = a.h_sf + r * (I / 128);
+    }
+
+    // Weights: subtile s of this wave (L1: s = 0,1 gate, 2,3 up).
+    const uint8_t* bptr[4];
+    constexpr size_t kstride = PK ? 32768 : 128;
+    const float* sfg;
+    const float* sfu;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        if constexpr (L1) {
+            if constexpr (PK) {
+                bptr[s] = a.w1 + (size_t)e * 2 * I * H + (size_t)nt * nkb * 32768 +
+                          (wave * 4 + s) * 2048 + lane * 16;
+            } else {
+                const int n = (s >= 2 ? I : 0) + nt * 128 + wave * 32 + (s & 1) * 16 + lr;
+                bptr[s] = a.w1 + ((size_t)e * 2 * I + n) * H + lg * 16;
+            }
+        } else {
+            if constexpr (PK) {
+                bptr[s] = a.w2 + (size_t)e * H * I + (size_t)nt * nkb * 32768 +
+                          (wave * 4 + s) * 2048 + lane * 16;
+            } else {
+                const int n = nt * 256 + wave * 64 + s * 16 + lr;
+                bptr[s] = a.w2 + ((size_t)e * H + n) * I + lg * 16;
+            }
+        }
+    }
+    if constexpr (L1) {
+        sfg = a.w1_sf + ((size_t)e * (2 * I / 128) + nt) * nkb;
+        sfu = a.w1_sf + ((size_t)e * (2 * I / 128) + I / 128 + nt) * nkb;
+    } else {
+        sfg = a.w2_sf + ((size_t)e * (H / 128) + (nt * 256 + wave * 64) / 128) * nkb;
+        sfu = sfg;
+    }
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    struct Blk {
+        Frag2 fb[4];
+        float sg, su;
+    };
+    int fetched = -1;  // last K block fetched
+    auto fetch = [&](Blk& b, int kb) {
+        const uint32_t st = stage_lds + (kb % SA_NS) * SA_STAGE;
+        dma16(asrc + (size_t)kb * 128, st + (wave * 2) * 1024);
+        dma16(asrc + (size_t)kb * 128 + 64, st + (wave * 2 + 1) * 1024);
+        dma4(ssrc + kb, st + SA_A + wave * 256);
+        b.sg = sfg[kb];
+        b.su = L1 ? sfu[kb] : b.sg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            b.fb[s] = load_wfrag<PK>(bptr[s] + kb * kstride);
+        fetched = kb;
+    };
+    int kb_m = 0;  // K block the next multiply takes
+    auto mul = [&](const Blk& b) {
+        // block kb_m's activation copies have landed (every wave's), and
+        // every wave is done reading the stage the next fetch overwrites
+        if (fetched > kb_m)
+            MOE_WAIT_VMCNT(SA_WLOADS + SA_COPIES + SA_WLOADS);
+        else
+            MOE_WAIT_VMCNT(SA_WLOADS);
+        __syncthreads();
+        const uint8_t* st = stage_mem + (kb_m % SA_NS) * SA_STAGE;
+        const float* s_lds = reinterpret_cast<const float*>(st + SA_A);
+        v8i af[4];
+        float sa[4][4];
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+            af[ms] = lds_frag(st + ms * 2048, lane);
+            const float4 s4 = *reinterpret_cast<const float4*>(s_lds + ms * 64 + 4 * lg);
+            sa[ms][0] = s4.x;
+            sa[ms][1] = s4.y;
+            sa[ms][2] = s4.z;
+            sa[ms][3] = s4.w;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const v8i bv = pack_frag(b.fb[s].lo, b.fb[s].hi);
+            const float sb = (L1 && s >= 2) ? b.su : b.sg;
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                const v4f p = mfma_16x16x128_e4m3(af[ms], bv, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[i], acc[ms][s][i]);
+            }
+        }
+        ++kb_m;
+    };
+    // The ring has three stages and a fetch runs one block ahead of the
+    // multiply, so the stage a fetch writes was last read two multiplies
+    // ago, before the barrier of the one in between.
+    kloop<Blk>(0, nkb, fetch, mul);
+
+    if constexpr (L1) {
+        // ---- SwiGLU x topk_w, per-row amax over the 128 columns, e4m3
+        // requant, coalesced store through LDS (as the direct tiles).
+        __shared__ float red[4][SA_BM];
+        __shared__ uint8_t qt[SA_BM][128];
+        float hv[4][2][4];
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int f = a.row_src[row0 + 16 * ms + 4 * lg + i];
+                const float w = f >= 0 ? a.topk_w[f] : 0.f;
+                float m = 0.f;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const float g = clamp_act(acc[ms][s][i], a.clamp);
+                    const float u = clamp_act(acc[ms][s + 2][i], a.clamp);
+                    const float v = (silu(g) * u) * w;
+                    hv[ms][s][i] = v;
+                    m = fmaxf(m, fabsf(v));
+                }
+                m = max16(m);
+                if (lr == 0)
+                    red[wave][16 * ms + 4 * lg + i] = m;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * ms + 4 * lg + i;
+                const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+                float rsf;
+                const float sf = requant_sf(amax, a.pow2_scale, rsf);
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    qt[r][wave * 32 + s * 16 + lr] =
+                        (uint8_t)requant_q(hv[ms][s][i], sf, rsf, a.pow2_scale);
+                if (wave == 0 && lr == 0)
+                    a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
+            }
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < SA_BM * 8; c += 256) {
+            const int r = c >> 3, col = (c & 7) * 16;
+            if (a.row_src[row0 + r] >= 0)
+                *reinterpret_cast<uint4*>(a.h + (size_t)(row0 + r) * I + nt * 128 + col) =
+                    *reinterpret_cast<const uint4*>(&qt[r][col]);
+        }
+    } else {
+        // ---- bf16, staged in LDS one 32-row half at a time, 16-byte stores
+        // to the (slot, token) row of the partial buffer.
+        __shared__ uint16_t ot[SA_BM / 2][256 + 8];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        ot[16 * mh + 4 * lg + i][wave * 64 + s * 16 + lr] =
+                            f32_to_bf16(acc[2 * hf + mh][s][i]);
+            __syncthreads();
+            for (int c = threadIdx.x; c < (SA_BM / 2) * 32; c += 256) {
+                const int r = c >> 5, col = (c & 31) * 8;
+                const int f = a.row_src[row0 + 32 * hf + r];
+                if (f >= 0) {
+                    const int t = f / K, j = f - t * K;
+                    uint4 v;
+                    v.x = (uint32_t)ot[r][col + 0] | ((uint32_t)ot[r][col + 1] << 16);
+                    v.y = (uint32_t)ot[r][col + 2] | ((uint32_t)ot[r][col + 3] << 16);
+                    v.z = (uint32_t)ot[r][col + 4] | ((uint32_t)ot[r][col + 5] << 16);
+                    v.w = (uint32_t)ot[r][col + 6] | ((uint32_t)ot[r][col + 7] << 16);
+                    *reinterpret_cast<uint4*>(a.partial + ((size_t)j * T + t) * H + nt * 256 + col) = v;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <bool L1>
+static hipError_t launch_sa(const FwdArgs& a, hipStream_t s)
+{
+    const int NT = L1 ? a.I / 128 : a.H / 256;
+    const long long grid = (long long)a.num_mblocks * NT;
+    if (a.BM != SA_BM || (!L1 && a.H % 256) || a.mx || (L1 ? a.H : a.I) < 256)
+        return hipErrorInvalidValue;
+    if (grid <= 0)
+        return hipSuccess;
+    auto kern = a.packed ? gemm_sa<L1, true> : gemm_sa<L1, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_l1_sa(const FwdArgs& a, hipStream_t s) { return launch_sa<true>(a, s); }
+hipError_t launch_l2_sa(const FwdArgs& a, hipStream_t s) { return launch_sa<false>(a, s); }
+
+}  // namespace moe

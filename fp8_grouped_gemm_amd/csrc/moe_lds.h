@@ -1,0 +1,72 @@
+// Helpers of the kernels that stage operands through LDS with gfx950's
+// asynchronous global -> LDS copies (global_load_lds_dword[x4]) and count
+// their completion by hand: the copies are inline assembly, invisible to the
+// compiler's own wait insertion, so each kernel waits on vmcnt itself.
+#pragma once
+
+#include "moe_device.h"
+
+namespace moe {
+
+// s_waitcnt with vmcnt = n (n < 64) and no wait on expcnt / lgkmcnt
+// (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in
+// bits [15:14]).
+#define MOE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0xF70 | ((n) & 15) | (((n) >> 4) << 14))
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15] (the immediate must
+// be a constant).
+__device__ __forceinline__ void wait_vmcnt(int n)
+{
+    switch (n) {
+    case 0: MOE_WAIT_VMCNT(0); break;
+    case 1: MOE_WAIT_VMCNT(1); break;
+    case 2: MOE_WAIT_VMCNT(2); break;
+    case 3: MOE_WAIT_VMCNT(3); break;
+    case 4: MOE_WAIT_VMCNT(4); break;
+    case 5: MOE_WAIT_VMCNT(5); break;
+    case 6: MOE_WAIT_VMCNT(6); break;
+    case 7: MOE_WAIT_VMCNT(7); break;
+    case 8: MOE_WAIT_VMCNT(8); break;
+    case 9: MOE_WAIT_VMCNT(9); break;
+    case 10: MOE_WAIT_VMCNT(10); break;
+    case 11: MOE_WAIT_VMCNT(11); break;
+    case 12: MOE_WAIT_VMCNT(12); break;
+    case 13: MOE_WAIT_VMCNT(13); break;
+    case 14: MOE_WAIT_VMCNT(14); break;
+    default: MOE_WAIT_VMCNT(0); break;  // (never larger here; waiting for all is safe)
+    }
+}
+
+// Asynchronous copy global -> LDS of 16 (or 4) bytes per lane to
+// lds_base + 16 * lane (4 * lane).  lds_base is wave-uniform (read from the
+// first lane into the scalar register M0 takes).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
+
+// 32-bit LDS offset of a __shared__ object (what M0 expects).
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p)
+{
+    const __attribute__((address_space(3))) uint8_t* lp =
+        (const __attribute__((address_space(3))) uint8_t*)p;
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lp);
+}
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* sub_base, int lane)
+{
+    const uint4 lo = *reinterpret_cast<const uint4*>(sub_base + lane * 16);
+    const uint4 hi = *reinterpret_cast<const uint4*>(sub_base + 1024 + lane * 16);
+    return pack_frag(lo, hi);
+}
+
+}  // namespace moe

@@ -208,7 +208,8 @@ def test_packed_weights_match_row_major_bitwise(tile_m):
     tile_m = 64 if tile_m == "64d" else tile_m
     y_row, _ = run_gpu(dev, tile_m=tile_m, flags=flags)
     y_pk, runner = run_gpu(dev, tile_m=tile_m, weight_layout=moe.MOE_WEIGHTS_PACKED, flags=flags)
-    assert moe.moe_plan_info(runner.plan, 203)["kernel"] == (0 if flags or tile_m < 64 else 1)
+    want = 0 if flags or tile_m < 64 else (2 if tile_m == 64 else 1)  # 2: shared-A, 1: LDS
+    assert moe.moe_plan_info(runner.plan, 203)["kernel"] == want
     assert torch.equal(y_row, y_pk)
     check_y(y_pk.cpu().numpy(), run_oracle(host)["y"], what=f"packed tile {tile_m}")
 
@@ -254,10 +255,10 @@ def test_forward_small_token_counts_split_k():
     torch.cuda.empty_cache()
 
 
-# ------------------------------- 64- and 128-row tiles: persistent LDS kernels
+# ---------------- 128-row tiles (persistent LDS kernel), 64-row shared-A tiles
 
 
-@pytest.mark.parametrize("tile", [64, 128])
+@pytest.mark.parametrize("tile", [128])
 @pytest.mark.parametrize("case", ["ragged", "hot", "many_blocks", "tiny_rows"])
 def test_lds_tiles_persistent_small_grid_matches_full_grid(case, tile):
     # With the test flag the persistent kernels run on 4 workgroups, so each
@@ -283,7 +284,7 @@ def test_lds_tiles_persistent_small_grid_matches_full_grid(case, tile):
 
 
 @pytest.mark.parametrize("case", ["ragged", "hot", "tiny_rows"])
-def test_tile64_lds_matches_direct_tiles_and_tile128_bitwise(case):
+def test_tile64_shared_a_matches_direct_tiles_and_tile128_bitwise(case):
     # Every kernel computes each row with the same MFMAs, the same per-K-block
     # promotion and the same epilogue arithmetic; only the tiling (and hence
     # the padding rows) differs, so y is bit-identical across them.
@@ -296,7 +297,7 @@ def test_tile64_lds_matches_direct_tiles_and_tile128_bitwise(case):
         host, dev = small_case(45, 256, 256, 6, 3, 23, mask={(0, 0): -1, (5, 1): -3})
     T = dev["x"].shape[0]
     y64, r64 = _run_flags(dev, 0, 64)
-    assert moe.moe_plan_info(r64.plan, T)["kernel"] == 1
+    assert moe.moe_plan_info(r64.plan, T)["kernel"] == 2
     y64d, r64d = _run_flags(dev, moe.MOE_FLAG_DIRECT_TILES, 64)
     assert moe.moe_plan_info(r64d.plan, T)["kernel"] == 0
     y128, _ = _run_flags(dev, 0, 128)
@@ -304,22 +305,25 @@ def test_tile64_lds_matches_direct_tiles_and_tile128_bitwise(case):
     assert torch.equal(y64, y128), case
     y64p, _ = _run_flags(dev, 0, 64, weight_layout=moe.MOE_WEIGHTS_PACKED)
     assert torch.equal(y64, y64p), case
-    check_y(y64.cpu().numpy(), run_oracle(host)["y"], what=f"tile 64 LDS {case}")
+    check_y(y64.cpu().numpy(), run_oracle(host)["y"], what=f"tile 64 shared-A {case}")
 
 
-@pytest.mark.parametrize("tile", [0, 128])
-def test_lds_tiles_full_size_packed_small_grid(tile):
-    # The flash-prefill workload on 4 workgroups (every workgroup walks
-    # ~1000 L1 tiles) against the full grid, packed weights: the library's
-    # choice (64-row LDS tiles, ~48 rows per expert) and 128-row tiles.
+def test_lds_tiles_full_size_packed_small_grid():
+    # The flash-prefill workload on 128-row tiles on 4 workgroups (every
+    # workgroup walks ~700 L1 tiles) against the full grid, packed weights,
+    # and both against the library's choice there (64-row shared-A tiles,
+    # ~48 rows per expert): the same arithmetic per row, so bit-identical.
     cfg = wl.CONFIGS["flash_prefill"]
     inp = gpu_inputs(cfg, wl.default_seed(cfg))
-    y_full, r = _run_flags(inp, 0, tile, weight_layout=moe.MOE_WEIGHTS_PACKED)
-    info = moe.moe_plan_info(r.plan, cfg.T)
-    assert info["kernel"] == 1 and info["tile_m"] == (tile or 64)
-    y_small, _ = _run_flags(inp, moe.MOE_FLAG_TEST_SMALL_GRID, tile,
+    y_full, r = _run_flags(inp, 0, 128, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert moe.moe_plan_info(r.plan, cfg.T)["kernel"] == 1
+    y_small, _ = _run_flags(inp, moe.MOE_FLAG_TEST_SMALL_GRID, 128,
                             weight_layout=moe.MOE_WEIGHTS_PACKED)
     assert torch.equal(y_full, y_small)
+    y_auto, ra = _run_flags(inp, 0, 0, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    info = moe.moe_plan_info(ra.plan, cfg.T)
+    assert info["kernel"] == 2 and info["tile_m"] == 64
+    assert torch.equal(y_full, y_auto)
     del inp
     torch.cuda.empty_cache()
 

@@ -1,5 +1,5 @@
-// L1 / L2 grouped FP8 GEMMs for large row tiles (prefill): 128 (or 64) pool
-// rows x 256 columns per tile, operands staged through LDS, one persistent
+// L1 / L2 grouped FP8 GEMMs for large row tiles (prefill): 128 pool rows x
+// 256 columns per tile, operands staged through LDS, one persistent
 // workgroup per compute unit.
 //
 // Same arithmetic as the direct-load kernels ("MegaMoE SM90 Implementation
@@ -8,7 +8,7 @@
 //   acc = fmaf(sa[row, kb] * sb[col block, kb], p, acc).
 //
 // gfx950 mapping.  A workgroup is 8 waves, 2 (rows) x 4 (columns); wave
-// (wm, wn) owns 64 (32) rows x 64 columns: for L1 the gate columns
+// (wm, wn) owns 64 rows x 64 columns: for L1 the gate columns
 // [128 n + 32 wn, +32) and the same up columns (gate and up of one element
 // meet in one lane, and the workgroup owns the whole 128-wide requant
 // block), for L2 the columns [256 n + 64 wn, +64).  Those are exactly the
@@ -55,7 +55,8 @@ namespace moe {
 
 namespace {
 
-constexpr int BN = 256;
+constexpr int BM = 128, BN = 256;
+constexpr int A_BYTES = BM * 128;   // 16 KiB: 8 m-subtiles x 2 halves x 1 KiB
 constexpr int S_BYTES = 8 * 256;    // one 256-byte scale copy per wave
 // Per-tile metadata slot: row_src of the 128 rows, top-k weight per row
 // (L1), the tile's expert replicated over 64 lanes.
@@ -64,22 +65,18 @@ constexpr int NMETA = 4;
 constexpr int META_W = 512, META_E = 1024;
 constexpr int kThreads = 512;
 
-// Stage geometry per recipe and tile height BM (128 or 64 rows).  A = BM/16
-// m-subtiles x 2 halves x 1 KiB: BM/64 copies per wave.  FP8: B = 16
-// n-subtiles x 2 halves x 1 KiB, 4 copies per wave; MXFP4: B = 16 subtiles
-// x 1 KiB of e2m1, 2 copies per wave; plus one scale copy per wave.
-template <bool MX, int BM>
+// Stage geometry per recipe.  FP8: B = 16 n-subtiles x 2 halves x 1 KiB,
+// copies per wave and block = 2 A + 4 B + 1 scale.  MXFP4: B = 16 subtiles
+// x 1 KiB of e2m1, 2 A + 2 B + 1 scale.
+template <bool MX>
 struct LdsCfg {
-    static constexpr int A_BYTES = BM * 128;
-    static constexpr int A_COPIES = BM / 64;
     static constexpr int B_BYTES = MX ? BN * 64 : BN * 128;
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int NSTAGE = MX ? 4 : 3;
-    static constexpr int COPIES = A_COPIES + (MX ? 2 : 4) + 1;
+    static constexpr int COPIES = MX ? 2 + 2 + 1 : 2 + 4 + 1;
     static constexpr int SMEM = NSTAGE * STAGE + NMETA * META;
 };
-static_assert(LdsCfg<false, 128>::SMEM <= 160 * 1024 && LdsCfg<true, 128>::SMEM <= 160 * 1024,
-              "LDS");
+static_assert(LdsCfg<false>::SMEM <= 160 * 1024 && LdsCfg<true>::SMEM <= 160 * 1024, "LDS");
 
 // Address of the 16 bytes lane `lane` copies for weight subtile `sub`
 // (packed order w4 * 4 + s, see pack.hip), half `half`, K block kb.
@@ -128,18 +125,14 @@ __device__ __forceinline__ const uint8_t* weight_src_mx(const FwdArgs& a, int e,
 
 }  // namespace
 
-// L1 (gate + up) when L1 is true, L2 (down) otherwise; BM = 128 or 64
-// rows per tile.  Needs at least NSTAGE - 1 K blocks (the plan enforces it).
-// With 64-row tiles the waves' A rows, metadata and scale copies that would
-// lie in rows 64..127 repeat rows 0..63 instead (nothing reads them).
-template <bool L1, bool PK, bool MX, int BM>
+// L1 (gate + up) when L1 is true, L2 (down) otherwise.  Needs at least two
+// K blocks (H >= 256 and I >= 256; the plan enforces it).
+template <bool L1, bool PK, bool MX>
 __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 {
-    using C = LdsCfg<MX, BM>;
-    constexpr int A_BYTES = C::A_BYTES, B_BYTES = C::B_BYTES, STAGE = C::STAGE;
-    constexpr int NSTAGE = C::NSTAGE, kCopiesPerBlock = C::COPIES;
-    constexpr int MS = BM / 32;       // m-subtiles per wave row half
-    constexpr int NSUB = BM / 16;     // m-subtiles per tile
+    using C = LdsCfg<MX>;
+    constexpr int B_BYTES = C::B_BYTES, STAGE = C::STAGE, NSTAGE = C::NSTAGE;
+    constexpr int kCopiesPerBlock = C::COPIES;
     extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
     const int H = a.H, I = a.I, K = a.K, T = a.T;
     const int NT = L1 ? I / 128 : H / 256;
@@ -193,12 +186,10 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         const int role = (wave == 5) ? 0 : (wave == 6) ? 1 : (wave == 7) ? 4 : wave;
         if (role <= 1 || (!L1 && role <= 3)) {
             const int h = role & 1;
-            const int hs = BM == 128 ? h : 0;  // 64-row tiles: repeat rows 0..63
-            dma4(a.row_src + rown + 64 * hs + lane, slot_lds(k + 1) + 256 * h);
+            dma4(a.row_src + rown + 64 * h + lane, slot_lds(k + 1) + 256 * h);
         } else if (role <= 3) {
             const int h = role - 2;
-            const int hs = BM == 128 ? h : 0;
-            const int f = reinterpret_cast<const int32_t*>(slot(k))[64 * hs + lane];
+            const int f = reinterpret_cast<const int32_t*>(slot(k))[64 * h + lane];
             dma4(a.topk_w + (f >= 0 ? f : 0), slot_lds(k) + META_W + 256 * h);
         } else {
             dma4(a.mblock_expert + rown / BM, slot_lds(k + 1) + META_E);
@@ -232,22 +223,19 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         const int row0 = mb * BM;
         i_e = e;
         i_nt = nt;
-        // A: with 128-row tiles wave v copies m-subtile v, both halves (rows
-        // row0 + 16 v + lr); with 64 rows, m-subtile v / 2, half v % 2.
+        // A: wave v copies m-subtile v, both halves: rows row0 + 16 v + lr.
         // Padding rows (f < 0) copy a valid row instead (L1: token 0; L2:
         // the block's first row, which always holds a routed slot), so their
         // lanes share cache lines with others; their products land only in
         // padding rows of the accumulator, which are never stored.
-        const int msub = BM == 128 ? wave : wave >> 1;
-        const int f = reinterpret_cast<const int32_t*>(slot(k))[msub * 16 + lr];
-        const int r = f >= 0 ? row0 + msub * 16 + lr : row0;
+        const int f = reinterpret_cast<const int32_t*>(slot(k))[wave * 16 + lr];
+        const int r = f >= 0 ? row0 + wave * 16 + lr : row0;
 #pragma unroll
-        for (int j = 0; j < C::A_COPIES; ++j) {
-            const int half = BM == 128 ? j : (wave & 1);
+        for (int j = 0; j < 2; ++j) {
             if constexpr (L1)
-                a_src[j] = a.x + (size_t)(f >= 0 ? f / K : 0) * H + half * 64 + 16 * lg;
+                a_src[j] = a.x + (size_t)(f >= 0 ? f / K : 0) * H + j * 64 + 16 * lg;
             else
-                a_src[j] = a.h + (size_t)r * I + half * 64 + 16 * lg;
+                a_src[j] = a.h + (size_t)r * I + j * 64 + 16 * lg;
         }
         if constexpr (MX) {
             // UE8M0 codes of K block kb, 4 bytes per lane: waves 0-1 the
@@ -257,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             // waves 6-7 a spare copy of row 0's codes (every wave issues the
             // same copies).
             const int HS = H / 32, IS = I / 32;
-            const int rr = wave < 2 && wave * 64 < BM ? wave * 64 + lane : lane;
+            const int rr = wave < 2 ? wave * 64 + lane : lane;
             const int fr = reinterpret_cast<const int32_t*>(slot(k))[rr];
             if (wave < 2 || wave >= 6) {
                 const bool spare = wave >= 6;
@@ -292,14 +280,10 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                 else
                     s_src = a.w2_sf + ((size_t)e * (H / 128) + 2 * nt + q) * nkb;
             } else {
-                // activation scale of row 16 v + (lane & 15) (64-row tiles:
-                // m-subtile v % 4, whose row is f2 / r2)
-                const int f2 = BM == 128 ? f : reinterpret_cast<const int32_t*>(slot(k))[(wave & 3) * 16 + lr];
-                const int r2 = BM == 128 ? r : (f2 >= 0 ? row0 + (wave & 3) * 16 + lr : row0);
                 if constexpr (L1)
-                    s_src = a.x_sf + (size_t)(f2 >= 0 ? f2 / K : 0) * (H / 128);
+                    s_src = a.x_sf + (size_t)(f >= 0 ? f / K : 0) * (H / 128);
                 else
-                    s_src = a.h_sf + (size_t)r2 * (I / 128);
+                    s_src = a.h_sf + (size_t)r * (I / 128);
             }
         }
     };
@@ -319,8 +303,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         const uint32_t st = smem_base + (i_j % NSTAGE) * STAGE;
         const int kb = i_kb;
 #pragma unroll
-        for (int j = 0; j < C::A_COPIES; ++j)
-            dma16(a_src[j] + (size_t)kb * 128, st + (wave * C::A_COPIES + j) * 1024);
+        for (int j = 0; j < 2; ++j)
+            dma16(a_src[j] + (size_t)kb * 128, st + (wave * 2 + j) * 1024);
         if constexpr (MX) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -353,8 +337,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         tile_at(tile_of(0), mb0, nt0);
         const int row0 = mb0 * BM;
         if (role <= 3)
-            dma4(a.row_src + row0 + (BM == 128 ? 64 * (role & 1) : 0) + lane,
-                 slot_lds(0) + 256 * (role & 1));
+            dma4(a.row_src + row0 + 64 * (role & 1) + lane, slot_lds(0) + 256 * (role & 1));
         else
             dma4(a.mblock_expert + row0 / BM, slot_lds(0) + META_E);
         MOE_WAIT_VMCNT(0);
@@ -368,10 +351,9 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     for (int q = 0; q < NSTAGE - 2; ++q)
         pend[q] = issue_next();
 
-    // wave (wm, wn): rows wm * BM / 2 + [0, BM / 2) = m-subtiles wm * MS + ms
-    v4f acc[MS][4];
+    v4f acc[4][4];
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
+    for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -415,13 +397,13 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             // codes: activation row r at byte 4 r + lg, weight subtile bytes
             // after them (packed: per lane; row-major: 4 per subtile row).
             const uint8_t* s_lds = st + A_BYTES + B_BYTES;
-            v8i af[MS];
+            v8i af[4];
             uint4 bf[4];
-            int sa[MS], sb[4];
+            int sa[4], sb[4];
 #pragma unroll
-            for (int ms = 0; ms < MS; ++ms) {
-                af[ms] = lds_frag(st + ((wm * MS + ms) * 2) * 1024, lane);
-                sa[ms] = s_lds[((wm * MS + ms) * 16 + lr) * 4 + lg];
+            for (int ms = 0; ms < 4; ++ms) {
+                af[ms] = lds_frag(st + ((wm * 4 + ms) * 2) * 1024, lane);
+                sa[ms] = s_lds[(wm * 64 + ms * 16 + lr) * 4 + lg];
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -433,17 +415,17 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int ms = 0; ms < MS; ++ms)
+                for (int ms = 0; ms < 4; ++ms)
                     acc[ms][s] = mfma_16x16x128_e4m3_e2m1(af[ms], e2m1_operand(bf[s]), acc[ms][s],
                                                           sa[ms], sb[s]);
         } else {
-            v8i af[MS], bf[4];
-            float sa[MS][4];
+            v8i af[4], bf[4];
+            float sa[4][4];
             const float* s_lds = reinterpret_cast<const float*>(st + A_BYTES + B_BYTES);
 #pragma unroll
-            for (int ms = 0; ms < MS; ++ms) {
-                af[ms] = lds_frag(st + ((wm * MS + ms) * 2) * 1024, lane);
-                const float4 s4 = *reinterpret_cast<const float4*>(s_lds + (wm * MS + ms) * 64 + 4 * lg);
+            for (int ms = 0; ms < 4; ++ms) {
+                af[ms] = lds_frag(st + ((wm * 4 + ms) * 2) * 1024, lane);
+                const float4 s4 = *reinterpret_cast<const float4*>(s_lds + (wm * 4 + ms) * 64 + 4 * lg);
                 sa[ms][0] = s4.x;
                 sa[ms][1] = s4.y;
                 sa[ms][2] = s4.z;
@@ -461,12 +443,12 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const float sb = (L1 && s >= 2) ? su : sg;
-                v4f p[MS];
+                v4f p[4];
 #pragma unroll
-                for (int ms = 0; ms < MS; ++ms)
+                for (int ms = 0; ms < 4; ++ms)
                     p[ms] = mfma_16x16x128_e4m3(af[ms], bf[s], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int ms = 0; ms < MS; ++ms)
+                for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[ms][i], acc[ms][s][i]);
@@ -493,13 +475,13 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             // requantisation block of each of its rows: amax over them, the
             // power-of-two scale as a UE8M0 code, codes staged in LDS.
             const float* m_w = reinterpret_cast<const float*>(slot(m_k) + META_W);
-            uint8_t* qt = ep;  // [BM][128]
+            uint8_t* qt = ep;  // [128][128]
             const int IS = I / 32;
 #pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
+            for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = (wm * MS + ms) * 16 + 4 * lg + i;
+                    const int r = wm * 64 + ms * 16 + 4 * lg + i;
                     const bool valid = m_rs[r] >= 0;
                     const float w = valid ? m_w[r] : 0.f;
                     const float v0 = (silu(clamp_act(acc[ms][0][i], a.clamp)) *
@@ -521,16 +503,16 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                     *reinterpret_cast<const uint4*>(qt + r * 128 + col);
             }
         } else if constexpr (L1) {
-            // acc[ms][s]: rows 16 (wm MS + ms) + 4 lg + i; s = 0,1 gate column
+            // acc[ms][s]: rows wm*64 + 16 ms + 4 lg + i; s = 0,1 gate column
             // 32 wn + 16 s + lr of the block, s = 2,3 the matching up column.
             const float* m_w = reinterpret_cast<const float*>(slot(m_k) + META_W);
             float* red = reinterpret_cast<float*>(ep);  // [4][128]
-            uint8_t* qt = ep + 2048;                    // [BM][128]
+            uint8_t* qt = ep + 2048;                    // [128][128]
 #pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
+            for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = (wm * MS + ms) * 16 + 4 * lg + i;
+                    const int r = wm * 64 + ms * 16 + 4 * lg + i;
                     const float w = m_rs[r] >= 0 ? m_w[r] : 0.f;
                     float m = 0.f;
 #pragma unroll
@@ -547,10 +529,10 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                 }
             __syncthreads();
 #pragma unroll
-            for (int ms = 0; ms < MS; ++ms)
+            for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = (wm * MS + ms) * 16 + 4 * lg + i;
+                    const int r = wm * 64 + ms * 16 + 4 * lg + i;
                     const float amax =
                         fmaxf(fmaxf(red[r], red[128 + r]), fmaxf(red[256 + r], red[384 + r]));
                     float rsf;
@@ -563,23 +545,22 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                         a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
                 }
             __syncthreads();
-            // BM rows x 128 bytes, 16 bytes per thread (rows without a slot
-            // are written too: nothing reads them).
+            // BM rows x 128 bytes, 16 bytes per thread, two per thread (rows
+            // without a slot are written too: nothing reads them).
             for (int c = threadIdx.x; c < BM * 8; c += kThreads) {
                 const int r = c >> 3, col = (c & 7) * 16;
                 *reinterpret_cast<uint4*>(a.h + (size_t)(row0 + r) * I + nt * 128 + col) =
                     *reinterpret_cast<const uint4*>(qt + r * 128 + col);
             }
         } else {
-            // acc[ms][s]: rows 16 (wm MS + ms) + 4 lg + i, column 64 wn +
-            // 16 s + lr; staged as bf16 one half (BM / 2 rows: the waves of
-            // one wm) at a time (<= 32 KiB).
-            uint16_t* ot = reinterpret_cast<uint16_t*>(ep);  // [BM / 2][256]
+            // acc[ms][s]: rows wm*64 + 16 ms + 4 lg + i, column 64 wn + 16 s
+            // + lr; staged as bf16 one 64-row half at a time (32 KiB).
+            uint16_t* ot = reinterpret_cast<uint16_t*>(ep);  // [64][256]
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 if (wm == hf) {
 #pragma unroll
-                    for (int ms = 0; ms < MS; ++ms)
+                    for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
                         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -588,9 +569,9 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                                     f32_to_bf16(acc[ms][s][i]);
                 }
                 __syncthreads();
-                for (int c = threadIdx.x; c < (BM / 2) * 32; c += kThreads) {
+                for (int c = threadIdx.x; c < 64 * 32; c += kThreads) {
                     const int r = c >> 5, col = (c & 31) * 8;
-                    const int f = m_rs[hf * (BM / 2) + r];
+                    const int f = m_rs[hf * 64 + r];
                     if (f >= 0) {
                         const int tt = f / K, jslot = f - tt * K;
                         *reinterpret_cast<uint4*>(a.partial + ((size_t)jslot * T + tt) * H +
@@ -603,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         }
         drain = true;
 #pragma unroll
-        for (int ms = 0; ms < MS; ++ms)
+        for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -612,9 +593,11 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     }
 }
 
-template <bool L1, bool MX, int BM>
+template <bool L1, bool MX>
 static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
 {
+    if (a.BM != BM)  // (64-row tiles run the shared-A kernels of gemm_sa.hip)
+        return hipErrorInvalidValue;
     const int NT = L1 ? a.I / 128 : a.H / 256;
     const long long n_tiles = (long long)a.num_mblocks * NT;
     const int nkb = L1 ? a.H / 128 : a.I / 128;
@@ -622,7 +605,7 @@ static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
         return hipSuccess;
     // a tile's metadata copy must land before that tile's first block is
     // issued, NSTAGE - 1 blocks ahead of the multiply
-    if (nkb < LdsCfg<MX, BM>::NSTAGE - 1)
+    if (nkb < LdsCfg<MX>::NSTAGE - 1)
         return hipErrorInvalidValue;
     int dev = 0, cus = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -634,8 +617,8 @@ static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
     if (a.grid_cap > 0 && g > a.grid_cap)
         g = a.grid_cap;
     const dim3 grid((unsigned)g);
-    const size_t smem = (size_t)LdsCfg<MX, BM>::SMEM;
-    auto kern = a.packed ? gemm_lds<L1, true, MX, BM> : gemm_lds<L1, false, MX, BM>;
+    const size_t smem = (size_t)LdsCfg<MX>::SMEM;
+    auto kern = a.packed ? gemm_lds<L1, true, MX> : gemm_lds<L1, false, MX>;
     err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (err != hipSuccess)
         return err;
@@ -643,17 +626,13 @@ static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <bool L1>
-static hipError_t launch_lds_bm(const FwdArgs& a, hipStream_t s)
+hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s)
 {
-    if (a.BM == 128)
-        return a.mx ? launch_lds<L1, true, 128>(a, s) : launch_lds<L1, false, 128>(a, s);
-    if (a.BM == 64 && a.mx)  // (FP8 64-row tiles run the shared-A kernel)
-        return launch_lds<L1, true, 64>(a, s);
-    return hipErrorInvalidValue;
+    return a.mx ? launch_lds<true, true>(a, s) : launch_lds<true, false>(a, s);
 }
-
-hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s) { return launch_lds_bm<true>(a, s); }
-hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s) { return launch_lds_bm<false>(a, s); }
+hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s)
+{
+    return a.mx ? launch_lds<false, true>(a, s) : launch_lds<false, false>(a, s);
+}
 
 }  // namespace moe

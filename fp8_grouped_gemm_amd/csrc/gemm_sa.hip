@@ -263,17 +263,219 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
     }
 }
 
+// FP8 x MXFP4 recipe (e4m3 activations, e2m1 weights, UE8M0 scales per 32
+// K values; "07 · MegaMoE" §0): the same tile with the block-scaled MFMA
+// (mfma_16x16x128_e4m3_e2m1), which applies both operands' codes and
+// accumulates in f32.  A wave's weight fragments of one K block are 4 x 16
+// bytes of e2m1 plus 4 scale bytes per lane (~170 VGPRs in all: three
+// workgroups fit a compute unit).  Each stage holds the 64 rows' e4m3
+// fragments and each row's 4 UE8M0 codes of the block.  L1's epilogue
+// requantises per 32 columns, one wave's gate columns.
+namespace {
+constexpr int SX_NS = 3;
+constexpr int SX_A = 64 * 128;
+constexpr int SX_STAGE = SX_A + 4 * 256;
+constexpr int SX_WLOADS = 8;  // 4 fragment loads + 4 scale-byte loads per wave and block
+}  // namespace
+
+template <bool L1, bool PK>
+__global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t stage_mem[SX_NS * SX_STAGE];
+    const int H = a.H, I = a.I, K = a.K, T = a.T;
+    const int HS = H / 32, IS = I / 32;
+    const int NT = L1 ? I / 128 : H / 256;
+    const int nkb = L1 ? H / 128 : I / 128;
+    const int mb = blockIdx.x / NT;
+    const int nt = blockIdx.x - mb * NT;
+    const int e = a.mblock_expert[mb];
+    if (e < 0)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int row0 = mb * 64;
+    const uint32_t stage_lds = lds_addr(stage_mem);
+
+    // Activation copies as in gemm_sa; the scale copy moves the row's 4
+    // codes of the block (one 4-byte word).
+    const int fr = a.row_src[row0 + 16 * wave + lr];
+    const uint8_t* asrc;
+    const uint8_t* ssrc;
+    if constexpr (L1) {
+        const size_t tok = fr >= 0 ? (size_t)(fr / K) : 0;
+        asrc = a.x + tok * H + 16 * lg;
+        ssrc = a.x_sfq + tok * HS;
+    } else {
+        const size_t r = fr >= 0 ? (size_t)(row0 + 16 * wave + lr) : (size_t)row0;
+        asrc = a.h + r * I + 16 * lg;
+        ssrc = a.h_sfq + r * IS;
+    }
+
+    // Weight subtile s of this wave (L1: 0,1 gate, 2,3 up): this lane's 16
+    // bytes of K block kb at wl + woff[s] + kb * wk, its scale byte at
+    // sl + soff[s] + kb * sk (one per-lane base, wave-uniform offsets).
+    const uint8_t* wl;
+    const uint8_t* sl;
+    uint32_t woff[4], soff[4];
+    uint32_t wk, sk;
+    const uint8_t* wbase = L1 ? a.w1 : a.w2;
+    const uint8_t* sbase = L1 ? a.w1_sfq : a.w2_sfq;
+    if constexpr (PK) {
+        const size_t t0 = ((size_t)e * NT + nt) * nkb;
+        wl = wbase + t0 * 16384 + wave * 4096 + lane * 16;
+        sl = sbase + t0 * 1024 + wave * 256 + lane;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            woff[s] = s * 1024;
+            soff[s] = s * 64;
+        }
+        wk = 16384;
+        sk = 1024;
+    } else {
+        const uint32_t KB = (L1 ? H : I) / 2, KS = L1 ? HS : IS;  // row bytes
+        const size_t row0w = L1 ? (size_t)e * 2 * I + nt * 128 + wave * 32 + lr
+                                : (size_t)e * H + nt * 256 + wave * 64 + lr;
+        wl = wbase + row0w * KB + lg * 16;
+        sl = sbase + row0w * KS + lg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t dr = L1 ? (s >= 2 ? I : 0) + (s & 1) * 16 : s * 16;
+            woff[s] = dr * KB;
+            soff[s] = dr * KS;
+        }
+        wk = 64;
+        sk = 4;
+    }
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc[ms][s] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    struct Blk {
+        uint4 fb[4];
+        int sb[4];
+    };
+    int fetched = -1;
+    auto fetch = [&](Blk& b, int kb) {
+        const uint32_t st = stage_lds + (kb % SX_NS) * SX_STAGE;
+        dma16(asrc + (size_t)kb * 128, st + (wave * 2) * 1024);
+        dma16(asrc + (size_t)kb * 128 + 64, st + (wave * 2 + 1) * 1024);
+        dma4(ssrc + (size_t)kb * 4, st + SX_A + wave * 256);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            b.fb[s] = *reinterpret_cast<const uint4*>(wl + woff[s] + (size_t)kb * wk);
+            b.sb[s] = sl[soff[s] + (size_t)kb * sk];
+        }
+        fetched = kb;
+    };
+    int kb_m = 0;
+    auto mul = [&](const Blk& b) {
+        if (fetched > kb_m)
+            MOE_WAIT_VMCNT(SX_WLOADS + SA_COPIES + SX_WLOADS);
+        else
+            MOE_WAIT_VMCNT(SX_WLOADS);
+        __syncthreads();
+        const uint8_t* st = stage_mem + (kb_m % SX_NS) * SX_STAGE;
+        const uint8_t* s_lds = st + SX_A;  // row 16 ms + r: bytes 256 ms + 4 r + [0, 4)
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+            const v8i av = lds_frag(st + ms * 2048, lane);
+            const int sa = s_lds[ms * 256 + 4 * lr + lg];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                acc[ms][s] = mfma_16x16x128_e4m3_e2m1(av, e2m1_operand(b.fb[s]), acc[ms][s], sa,
+                                                      b.sb[s]);
+        }
+        ++kb_m;
+    };
+    // One block ahead, two register sets (a third, two blocks ahead, made
+    // the kernel spill and measured no faster); the ring's three stages
+    // suffice as in gemm_sa.
+    kloop<Blk>(0, nkb, fetch, mul);
+
+    if constexpr (L1) {
+        // ---- SwiGLU x topk_w; wave w's 32 gate columns are one
+        // requantisation block of each row: its amax, the power-of-two
+        // scale as a UE8M0 code, codes staged in LDS for row stores.
+        __shared__ uint8_t qt[64][128];
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * ms + 4 * lg + i;
+                const int f = a.row_src[row0 + r];
+                const float w = f >= 0 ? a.topk_w[f] : 0.f;
+                const float v0 = (silu(clamp_act(acc[ms][0][i], a.clamp)) *
+                                  clamp_act(acc[ms][2][i], a.clamp)) * w;
+                const float v1 = (silu(clamp_act(acc[ms][1][i], a.clamp)) *
+                                  clamp_act(acc[ms][3][i], a.clamp)) * w;
+                const float amax = max16(fmaxf(fabsf(v0), fabsf(v1)));
+                const uint32_t code = min(e8m0_ceil_code(fmaxf(amax, 1e-10f) / 448.0f), 253u);
+                const float inv = e8m0_inverse(code);
+                qt[r][wave * 32 + lr] = (uint8_t)f32_to_e4m3_hw(v0 * inv);
+                qt[r][wave * 32 + 16 + lr] = (uint8_t)f32_to_e4m3_hw(v1 * inv);
+                if (lr == 0 && f >= 0)
+                    a.h_sfq[(size_t)(row0 + r) * IS + nt * 4 + wave] = (uint8_t)code;
+            }
+        __syncthreads();
+        for (int c = threadIdx.x; c < 64 * 8; c += 256) {
+            const int r = c >> 3, col = (c & 7) * 16;
+            if (a.row_src[row0 + r] >= 0)
+                *reinterpret_cast<uint4*>(a.h + (size_t)(row0 + r) * I + nt * 128 + col) =
+                    *reinterpret_cast<const uint4*>(&qt[r][col]);
+        }
+    } else {
+        __shared__ uint16_t ot[32][256 + 8];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int mh = 0; mh < 2; ++mh)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        ot[16 * mh + 4 * lg + i][wave * 64 + s * 16 + lr] =
+                            f32_to_bf16(acc[2 * hf + mh][s][i]);
+            __syncthreads();
+            for (int c = threadIdx.x; c < 32 * 32; c += 256) {
+                const int r = c >> 5, col = (c & 31) * 8;
+                const int f = a.row_src[row0 + 32 * hf + r];
+                if (f >= 0) {
+                    const int t = f / K, j = f - t * K;
+                    uint4 v;
+                    v.x = (uint32_t)ot[r][col + 0] | ((uint32_t)ot[r][col + 1] << 16);
+                    v.y = (uint32_t)ot[r][col + 2] | ((uint32_t)ot[r][col + 3] << 16);
+                    v.z = (uint32_t)ot[r][col + 4] | ((uint32_t)ot[r][col + 5] << 16);
+                    v.w = (uint32_t)ot[r][col + 6] | ((uint32_t)ot[r][col + 7] << 16);
+                    *reinterpret_cast<uint4*>(a.partial + ((size_t)j * T + t) * H + nt * 256 + col) = v;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
 template <bool L1>
 static hipError_t launch_sa(const FwdArgs& a, hipStream_t s)
 {
     const int NT = L1 ? a.I / 128 : a.H / 256;
     const long long grid = (long long)a.num_mblocks * NT;
-    if (a.BM != SA_BM || (!L1 && a.H % 256) || a.mx || (L1 ? a.H : a.I) < 256)
+    // FP8 needs two K blocks per layer, MXFP4 three
+    if (a.BM != SA_BM || (!L1 && a.H % 256) || (L1 ? a.H : a.I) < (a.mx ? 384 : 256))
         return hipErrorInvalidValue;
     if (grid <= 0)
         return hipSuccess;
-    auto kern = a.packed ? gemm_sa<L1, true> : gemm_sa<L1, false>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, a);
+    if (a.mx) {
+        auto kern = a.packed ? gemm_sa_mx<L1, true> : gemm_sa_mx<L1, false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, a);
+    } else {
+        auto kern = a.packed ? gemm_sa<L1, true> : gemm_sa<L1, false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

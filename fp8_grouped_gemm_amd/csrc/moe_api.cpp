@@ -31,11 +31,11 @@ struct Config {
 // Rows per tile from the expected rows per expert T*K/E: the smallest tile
 // that holds an average expert's rows reads each expert's weights once
 // while padding as few MFMA rows as possible (decode: 16).
-// Beyond ~24 rows per expert the LDS-using MFMA tiles take over: 64 rows up
-// to kRowsLds64 rows per expert (FP8: the shared-A tile of gemm_sa.hip;
-// MXFP4: the LDS-staged tile) and the 128 x 256 LDS-staged tile above (they
-// need H % 256 == 0 for their 256-column L2 tiles and enough K blocks,
-// lds_tile_fits; otherwise 64-row direct-load tiles).
+// Beyond ~24 rows per expert the LDS-using MFMA tiles take over: the 64-row
+// shared-A tile of gemm_sa.hip up to kRowsLds64 rows per expert and the
+// 128 x 256 LDS-staged tile above (they need H % 256 == 0 for their
+// 256-column L2 tiles and enough K blocks, lds_tile_fits; otherwise 64-row
+// direct-load tiles).
 // Columns per intermediate scale of an FP8 plan (MXFP4: 32).
 int sf_gran(const moe_shape_t& s)
 {
@@ -60,9 +60,8 @@ Config choose_config(const moe_shape_t& s, int T)
 {
     const bool lds = lds_tile_fits(s) && sf_gran(s) != 64;
     const bool lds64 = lds && !(s.flags & MOE_FLAG_DIRECT_TILES);
-    // 64-row tiles where the LDS tiles fit: FP8 the shared-A tile (kernel 2),
-    // MXFP4 the LDS-staged tile (kernel 1)
-    const int k64 = !lds64 ? 0 : s.recipe == MOE_RECIPE_MXFP4 ? 1 : 2;
+    // 64-row tiles where the LDS tiles fit: the shared-A tile (kernel 2)
+    const int k64 = lds64 ? 2 : 0;
     if (s.tile_m > 0)
         return Config{s.tile_m, s.tile_m == 128 ? 1 : s.tile_m == 64 ? k64 : 0};
     const double rows = (double)T * s.top_k / s.num_experts;

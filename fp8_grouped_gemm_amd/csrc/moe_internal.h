@@ -95,7 +95,7 @@ hipError_t launch_l1_mx(const FwdArgs& a, hipStream_t s);  // direct tiles, tile
 hipError_t launch_l2_mx(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s);
-hipError_t launch_l1_sa(const FwdArgs& a, hipStream_t s);  // 64-row shared-A tiles, FP8
+hipError_t launch_l1_sa(const FwdArgs& a, hipStream_t s);  // 64-row shared-A tiles
 hipError_t launch_l2_sa(const FwdArgs& a, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* q, void* sf, bool mx,
                                hipStream_t s);

@@ -69,8 +69,8 @@ extern "C" {
 #define MOE_FLAG_POW2_SCALE 4     /* FP8 recipe: requant scales rounded up to a power of
                                      two (DeepGEMM PR #440 "How it works", #383's choice) */
 #define MOE_FLAG_DIRECT_TILES 8   /* 64-row tiles use the direct-load kernels even where
-                                     the shared-A / LDS-staged 64-row kernels fit (so
-                                     that MOE_FLAG_SINGLE_LAUNCH can apply to them) */
+                                     the shared-A 64-row kernel fits (so that
+                                     MOE_FLAG_SINGLE_LAUNCH can apply to them) */
 #define MOE_FLAG_TEST_NO_WAIT 256 /* test-only: the single launch's waits give up at
                                      once, so MOE_STATUS_WAIT_TIMEOUT is set and y is
                                      invalid; exercises the timeout path */
@@ -99,7 +99,7 @@ typedef struct moe_shape {
     int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128.
                               Where the LDS tiles fit (H % 256 == 0, H and I >= 256
                               (MXFP4: 384), per-128 scales) 128 runs the LDS-staged
-                              kernel and 64 the shared-A kernel (MXFP4: LDS-staged);
+                              kernel and 64 the shared-A kernel;
                               128 requires it, 64 otherwise (or with
                               MOE_FLAG_DIRECT_TILES) runs the direct-load kernel */
     int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
@@ -126,7 +126,7 @@ typedef struct moe_tile_info {
     int32_t l1_tile_n;   /* L1 output columns per tile (gate + up) */
     int32_t l2_tile_n;   /* L2 output columns per tile */
     int32_t kernel;      /* 0 = direct-load tile kernel, 1 = LDS-staged tile kernel,
-                            2 = shared-A tile kernel (FP8, 64 rows) */
+                            2 = shared-A tile kernel (64 rows) */
     int32_t l1_split;    /* workgroups sharing one L1 tile's K range (1 = no split;
                             16-row tiles with fewer tiles than compute units) */
     int32_t single_launch; /* 1: L1, L2 and combine run as one launch */

@@ -147,16 +147,15 @@ def test_tile128_needs_two_k_blocks_per_layer():
 
 
 def test_tile64_kernel_choice():
-    # 64-row tiles run on the shared-A kernel (FP8; MXFP4: the LDS-staged
-    # kernel) where the LDS tiles fit, on the direct-load kernel where they
-    # do not (H % 256 != 0, one K block, per-64 scales) or when the plan asks
-    # for direct tiles
+    # 64-row tiles run on the shared-A kernel where the LDS tiles fit, on
+    # the direct-load kernel where they do not (H % 256 != 0, too few K
+    # blocks, per-64 scales) or when the plan asks for direct tiles
     cases = [((512, 384, 16, 4), {}, 2),
              ((512, 384, 16, 4), dict(flags=moe.MOE_FLAG_DIRECT_TILES), 0),
              ((384, 256, 8, 2), {}, 0),
              ((256, 128, 8, 2), {}, 0),
              ((512, 384, 16, 4), dict(act_sf_gran=64), 0),
-             ((512, 384, 16, 4), dict(recipe=moe.MOE_RECIPE_MXFP4), 1),
+             ((512, 384, 16, 4), dict(recipe=moe.MOE_RECIPE_MXFP4), 2),
              ((512, 256, 16, 4), dict(recipe=moe.MOE_RECIPE_MXFP4), 0)]  # MX: 3 K blocks
     for shape, kw, kernel in cases:
         p = moe.moe_plan_create(*shape, 256, tile_m=64, **kw)

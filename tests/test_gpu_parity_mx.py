@@ -136,13 +136,13 @@ def test_mx_forward_deterministic_and_auto_tile():
 def test_mx_packed_weights_match_row_major_bitwise(tile_m):
     # the packed layout only changes where each operand byte is read from:
     # same MFMAs in the same order, so y is bit-identical ("64d": 64-row
-    # direct-load tiles; plain 64: the LDS-staged 64-row tile)
+    # direct-load tiles; plain 64: the shared-A 64-row tile)
     host, dev = mx_case(37, 512, 384, 16, 4, 211, mask={(5, 1): -1, (20, 3): 40})
     flags = moe.MOE_FLAG_DIRECT_TILES if tile_m == "64d" else 0
     tile_m = 64 if tile_m == "64d" else tile_m
     y_row, _ = run_gpu_mx(dev, tile_m=tile_m, flags=flags)
     y_pk, r = run_gpu_mx(dev, tile_m=tile_m, weight_layout=moe.MOE_WEIGHTS_PACKED, flags=flags)
-    assert moe.moe_plan_info(r.plan, 37)["kernel"] == (0 if flags or tile_m < 64 else 1)
+    assert moe.moe_plan_info(r.plan, 37)["kernel"] == (0 if flags or tile_m < 64 else 2)
     assert torch.equal(y_row, y_pk)
     check_y(y_pk.cpu().numpy(), run_oracle_mx(host)["y"], what=f"packed tile {tile_m}")
 
@@ -150,17 +150,17 @@ def test_mx_packed_weights_match_row_major_bitwise(tile_m):
 @pytest.mark.parametrize("tile", [64, 128])
 @pytest.mark.parametrize("case", ["hot", "ragged"])
 def test_mx_lds_tiles(case, tile):
-    # LDS-staged persistent 64- and 128-row tiles: intermediates against the
-    # oracle, packed weights bit-identical to row-major, a 4-workgroup grid
-    # (each workgroup walking many tiles across tile boundaries)
-    # bit-identical to the full grid, and (64 rows) the direct-load 64-row
-    # tiles bit-identical too
+    # The 64-row shared-A tile and the persistent 128-row LDS tile:
+    # intermediates against the oracle, packed weights bit-identical to
+    # row-major, (128) a 4-workgroup grid (each workgroup walking many tiles
+    # across tile boundaries) bit-identical to the full grid, and (64) the
+    # direct-load 64-row tiles bit-identical too
     if case == "hot":
         host, dev = mx_case(300, 512, 384, 4, 3, 411, skew=True)
     else:
         host, dev = mx_case(157, 768, 512, 6, 2, 412, mask={(3, 0): -1, (40, 1): 77})
     y, runner = check_case(host, dev, tile, f"LDS tile {tile} {case}")
-    assert moe.moe_plan_info(runner.plan, dev["x"].shape[0])["kernel"] == 1
+    assert moe.moe_plan_info(runner.plan, dev["x"].shape[0])["kernel"] == (2 if tile == 64 else 1)
     y_pk, _ = run_gpu_mx(dev, tile_m=tile, weight_layout=moe.MOE_WEIGHTS_PACKED)
     assert torch.equal(y, y_pk)
     T, H = dev["x"].shape
@@ -179,8 +179,8 @@ def test_mx_flash_prefill_full_size_sampled():
     cfg = wl.CONFIGS["flash_prefill"]
     dev = wl.make_inputs_mx(cfg, wl.default_seed(cfg), "cuda")
     y, runner = run_gpu_mx(dev, weight_layout=moe.MOE_WEIGHTS_PACKED)
-    info = moe.moe_plan_info(runner.plan, cfg.T)  # ~48 rows per expert
-    assert info["tile_m"] == 64 and info["kernel"] == 1
+    info = moe.moe_plan_info(runner.plan, cfg.T)  # ~48 rows per expert: shared-A tiles
+    assert info["tile_m"] == 64 and info["kernel"] == 2
     toks = [0, 1, 517, 1024, 1999, cfg.T - 1]
     E = cfg.E
     idx = dev["topk_idx"].cpu().numpy()

@@ -641,9 +641,13 @@ __global__ __launch_bounds__(256) void combine_kernel(FwdArgs a)
 template <int MT, bool PK>
 __global__ __launch_bounds__(256) void fused_direct(FwdArgs a)
 {
-    const int n1 = a.num_mblocks * (a.I / 128);
+    // Items of the row blocks that hold routed slots only (the planner's
+    // used-row count): the pool's capacity T*K + E*(BM - 1) rows is mostly
+    // empty at small T, and every item costs a claim on the shared queue.
+    const int used_mb = min(a.num_mblocks, a.status[2] / (16 * MT));
+    const int n1 = used_mb * (a.I / 128);
     const int NT2 = (a.H + 255) / 256;
-    const int n2 = a.num_mblocks * NT2;
+    const int n2 = used_mb * NT2;
     const int n3 = (int)(((long long)a.T * (a.H / 8) + 255) / 256);
     const int total = n1 + n2 + n3;
     int32_t* queue = a.sync + kSyncQueue;

@@ -206,16 +206,35 @@ __global__ __launch_bounds__(kRouteThreads) void route_small(RouteArgs a)
         seg = (total + a.row_align - 1) / a.row_align * a.row_align;
         a.counts[x] = total;
     }
-    scan[x] = seg;
-    __syncthreads();
-    for (int d = 1; d < kRouteThreads; d <<= 1) {
-        int v = (x >= d) ? scan[x - d] : 0;
-        __syncthreads();
-        scan[x] += v;
-        __syncthreads();
+    // Inclusive prefix sum of seg over the block: within each wave by
+    // shuffles, then the 16 wave totals by wave 0 (integer adds: the same
+    // result in any order).
+    __shared__ int32_t wave_sum[kWaves];
+    int incl = seg;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d)
+            incl += v;
     }
+    if (lane == 63)
+        wave_sum[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < kWaves ? wave_sum[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < kWaves; d <<= 1) {
+            const int v = __shfl_up(w, d);
+            if (lane >= d)
+                w += v;
+        }
+        if (lane < kWaves)
+            wave_sum[lane] = w;  // inclusive over waves 0 .. lane
+    }
+    __syncthreads();
+    scan[x] = incl + (wave > 0 ? wave_sum[wave - 1] : 0);
     const int start = scan[x] - seg;
-    const int used = scan[kRouteThreads - 1];
+    const int used = wave_sum[kWaves - 1];
     if (x < a.E) {
         a.offsets[x] = start;
         for (int r = start + total; r < start + seg; ++r)

@@ -92,9 +92,10 @@ def measured_traffic(cfg, weights):
     return d["l1_step_traffic_bytes"]
 
 
-def time_oracle_sample(inp, cfg, n_tokens, seed, mx=False):
+def time_oracle_sample(inp, cfg, n_tokens, seed, mx=False, threads=None):
     """CPU oracle on a bounded sample of tokens; returns (us per layer
-    extrapolated to T tokens, threads, seconds, sample description)."""
+    extrapolated to T tokens, threads, seconds, sample description).
+    threads: worker threads (default: every core this process may run on)."""
     import numpy as np
 
     import oracle
@@ -105,7 +106,8 @@ def time_oracle_sample(inp, cfg, n_tokens, seed, mx=False):
     sel = lambda t: [t[e].cpu().numpy() if e in need else None for e in range(cfg.E)]
     args = (inp["x"].cpu().numpy(), inp["x_sf"].cpu().numpy(), idx, inp["topk_w"].cpu().numpy(),
             sel(inp["w1"]), sel(inp["w1_sf"]), sel(inp["w2"]), sel(inp["w2_sf"]))
-    threads = len(os.sched_getaffinity(0))
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     (oracle.moe_forward_mx if mx else oracle.moe_forward)(*args, tokens=toks, nthreads=threads)
     dt = time.perf_counter() - t0
@@ -177,6 +179,8 @@ def main():
                     help="override the workload's token count (same shapes and routing recipe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=128)
+    ap.add_argument("--cpu-sample-tokens-1t", type=int, default=2,
+                    help="tokens in the one-thread oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(the reference kernel for scaling HBM byte counters) and exit")
@@ -406,6 +410,11 @@ def main():
         line["cpu_baseline"] = {"value": round(us, 1), "unit": "us", "cores": threads,
                                 "kind": "oracle", "sample": sample,
                                 "seconds": round(secs, 2)}
+        if args.cpu_sample_tokens_1t > 0:  # the same oracle on one thread, smaller sample
+            us1, _, secs1, sample1 = time_oracle_sample(inp, cfg, args.cpu_sample_tokens_1t,
+                                                        seed, mx, threads=1)
+            line["cpu_baseline"]["one_thread"] = {"value": round(us1, 1), "unit": "us",
+                                                  "sample": sample1, "seconds": round(secs1, 2)}
     print(json.dumps(line), flush=True)
 
 

@@ -107,7 +107,7 @@ def test_pow2_scales(tile_m):
     assert np.all(m == 0.5)  # every scale a power of two
 
 
-@pytest.mark.parametrize("tile_m", [16, 128])
+@pytest.mark.parametrize("tile_m", [16, 64, 128])
 def test_activation_clamp_fp8(tile_m):
     host, dev = small_case(160, 512, 384, 6, 3, 503)
     clamp = 0.05  # well inside the range of gate/up here: the clamp is active
@@ -118,7 +118,7 @@ def test_activation_clamp_fp8(tile_m):
     assert not torch.equal(y, y0)
 
 
-@pytest.mark.parametrize("tile_m", [16, 128])
+@pytest.mark.parametrize("tile_m", [16, 64, 128])
 def test_activation_clamp_mxfp4(tile_m):
     cfg = wl.custom_config(160, 512, 384, 6, 3)
     inp = wl.make_inputs_mx(cfg, 504, "cpu")

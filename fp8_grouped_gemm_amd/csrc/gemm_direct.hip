@@ -516,9 +516,10 @@ __global__ __launch_bounds__(WV * 64, MT == 2 && PK && !G64 ? 2 : 1) void l2_dir
 // and e4m3 requant as the l1_direct epilogue.  Thread t: row t/16, gate
 // columns 8*(t%16) .. +8 of the tile's 128-column block and the matching up
 // columns; the 16 threads of a row share one wave quarter.
+template <int S>
 __global__ __launch_bounds__(256) void l1_splitk_epilogue(FwdArgs a)
 {
-    const int I = a.I, NT = I / 128, S = a.split_l1;
+    const int I = a.I, NT = I / 128;
     const int mb = blockIdx.x / NT;
     const int nt = blockIdx.x - mb * NT;
     if (a.mblock_expert[mb] < 0)
@@ -531,7 +532,8 @@ __global__ __launch_bounds__(256) void l1_splitk_epilogue(FwdArgs a)
     for (int q = 0; q < 8; ++q)
         g[q] = u[q] = 0.f;
     if (f >= 0) {
-        for (int k = 0; k < S; ++k) {
+#pragma unroll
+        for (int k = 0; k < S; ++k) {  // all S slices' loads in flight together
             const float* row = a.splitk_part + ((size_t)k * a.splitk_slots + f) * 2 * I;
             const float4 g0 = *reinterpret_cast<const float4*>(row + c0);
             const float4 g1 = *reinterpret_cast<const float4*>(row + c0 + 4);
@@ -597,12 +599,7 @@ __device__ __forceinline__ void combine_chunk(const FwdArgs& a, int blk, int n_l
 #pragma unroll
     for (int q = 0; q < 8; ++q)
         s[q] = 0.f;
-    for (int j = 0; j < a.K; ++j) {
-        const int e = a.idx[t * a.K + j];
-        if (e < 0 || e >= a.E)
-            continue;
-        const uint16_t* prow = a.partial + ((size_t)j * a.T + t) * a.H + c;
-        const uint4 v = *reinterpret_cast<const uint4*>(prow);
+    auto add = [&](const uint4& v) {
         s[0] += bf16_to_f32(v.x & 0xFFFFu);
         s[1] += bf16_to_f32(v.x >> 16);
         s[2] += bf16_to_f32(v.y & 0xFFFFu);
@@ -611,6 +608,33 @@ __device__ __forceinline__ void combine_chunk(const FwdArgs& a, int blk, int n_l
         s[5] += bf16_to_f32(v.z >> 16);
         s[6] += bf16_to_f32(v.w & 0xFFFFu);
         s[7] += bf16_to_f32(v.w >> 16);
+    };
+    const uint16_t* prow = a.partial + (size_t)t * a.H + c;  // slot j: + j * T * H
+    const size_t jstride = (size_t)a.T * a.H;
+    if (a.K <= 8) {
+        // every slot's row is loaded (a masked slot's stale row is not
+        // added), so all K loads are in flight together; the sum still runs
+        // over the valid slots in ascending j
+        bool ok[8];
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < a.K) {
+                const int e = a.idx[t * a.K + j];
+                ok[j] = e >= 0 && e < a.E;
+                v[j] = *reinterpret_cast<const uint4*>(prow + j * jstride);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < a.K && ok[j])
+                add(v[j]);
+    } else {
+        for (int j = 0; j < a.K; ++j) {
+            const int e = a.idx[t * a.K + j];
+            if (e >= 0 && e < a.E)
+                add(*reinterpret_cast<const uint4*>(prow + j * jstride));
+        }
     }
     uint4 o;
     o.x = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
@@ -702,11 +726,16 @@ static hipError_t launch_l1_t(const FwdArgs& a, hipStream_t s)
     case 16:
         if (a.split_l1 > 1) {
             switch (a.split_l1) {
-            case 2: hipLaunchKernelGGL((l1_direct<1, 2, PK>), dim3(tiles * 2), dim3(256), 0, s, a); break;
-            case 4: hipLaunchKernelGGL((l1_direct<1, 4, PK>), dim3(tiles * 4), dim3(256), 0, s, a); break;
+            case 2:
+                hipLaunchKernelGGL((l1_direct<1, 2, PK>), dim3(tiles * 2), dim3(256), 0, s, a);
+                hipLaunchKernelGGL(l1_splitk_epilogue<2>, dim3(tiles), dim3(256), 0, s, a);
+                break;
+            case 4:
+                hipLaunchKernelGGL((l1_direct<1, 4, PK>), dim3(tiles * 4), dim3(256), 0, s, a);
+                hipLaunchKernelGGL(l1_splitk_epilogue<4>, dim3(tiles), dim3(256), 0, s, a);
+                break;
             default: return hipErrorInvalidValue;
             }
-            hipLaunchKernelGGL(l1_splitk_epilogue, dim3(tiles), dim3(256), 0, s, a);
         } else {
             hipLaunchKernelGGL((l1_direct<1, 1, PK>), dim3(tiles), dim3(256), 0, s, a);
         }

@@ -1,6 +1,7 @@
-// L1 / L2 grouped FP8 GEMMs on 64-row tiles with the activation rows shared
+// L1 / L2 grouped GEMMs on 64-row tiles with the activation rows shared
 // through LDS ("shared-A" tiles, prefill shapes with ~24-64 routed rows per
-// expert).
+// expert), for the FP8 recipe (gemm_sa) and the FP8 x MXFP4 recipe
+// (gemm_sa_mx, further below).
 //
 // Same arithmetic as the direct-load and LDS-staged kernels ("MegaMoE SM90
 // Implementation Design" §5.3 promotion per 128-K block, §10.1 / §11.1
@@ -24,9 +25,10 @@
 // wait for K block kb's activation copies is explicit: vector-memory
 // operations retire in order, and after kb's copies each wave has issued
 // kb's 8 weight loads and, when block kb + 1 has been fetched, that block's
-// 3 copies and 8 weight loads (the weight scales may be scalar loads, which
-// vmcnt does not count, so they are left out: waiting for fewer outstanding
-// operations than allowed is always safe).  The compiler's own wait before
+// 3 copies and 8 weight loads.  The weight-scale loads are left out of the
+// count (the compiler may make them scalar loads, which vmcnt does not
+// count): a count that omits operations issued after the copies only makes
+// the wait longer, which is always safe.  The compiler's own wait before
 // the MFMAs covers the weight registers.
 #include "moe_device.h"
 #include "moe_direct.h"

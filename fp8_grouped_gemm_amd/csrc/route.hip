@@ -139,9 +139,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_assign(RouteArgs a)
     const int key = valid ? e : -1;
     // Rank among the earlier lanes of this wave with the same expert.
     int rank = 0;
-    for (int j = 0; j < 64; ++j) {
-        const int other = __shfl(key, j);
-        rank += (j < lane && other == key) ? 1 : 0;
+    if (__ballot(valid)) {  // a wave with no routed slot (past the last one) skips it
+        for (int j = 0; j < 64; ++j) {
+            const int other = __shfl(key, j);
+            rank += (j < lane && other == key) ? 1 : 0;
+        }
     }
     if (valid)
         atomicAdd(&wave_cnt[wave * a.E + e], 1);
@@ -185,9 +187,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_small(RouteArgs a)
     const bool valid = e >= 0 && e < a.E;
     const int key = valid ? e : -1;
     int rank = 0;
-    for (int j = 0; j < 64; ++j) {
-        const int other = __shfl(key, j);
-        rank += (j < lane && other == key) ? 1 : 0;
+    if (__ballot(valid)) {  // a wave with no routed slot (past the last one) skips it
+        for (int j = 0; j < 64; ++j) {
+            const int other = __shfl(key, j);
+            rank += (j < lane && other == key) ? 1 : 0;
+        }
     }
     if (valid)
         atomicAdd(&wave_cnt[wave * a.E + e], 1);

@@ -257,6 +257,7 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
             const int f = a.row_src[row0 + 16 * ms + 4 * lg + i];
             wrow[ms][i] = f >= 0 ? a.topk_w[f] : 0.f;
         }
+    clamp_acc<MT * 4>(&acc[0][0], a.clamp);
 #pragma unroll
     for (int ms = 0; ms < MT; ++ms) {
 #pragma unroll
@@ -264,8 +265,8 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
             float m = 0.f;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const float g = clamp_act(acc[ms][s][i], a.clamp);
-                const float u = clamp_act(acc[ms][s + 2][i], a.clamp);
+                const float g = acc[ms][s][i];
+                const float u = acc[ms][s + 2][i];
                 const float v = (silu(g) * u) * wrow[ms][i];
                 hv[ms][s][i] = v;
                 m = fmaxf(m, fabsf(v));

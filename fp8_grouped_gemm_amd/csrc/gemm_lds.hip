@@ -475,6 +475,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             // requantisation block of each of its rows: amax over them, the
             // power-of-two scale as a UE8M0 code, codes staged in LDS.
             const float* m_w = reinterpret_cast<const float*>(slot(m_k) + META_W);
+            clamp_acc<16>(&acc[0][0], a.clamp);
             uint8_t* qt = ep;  // [128][128]
             const int IS = I / 32;
 #pragma unroll
@@ -484,10 +485,10 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                     const int r = wm * 64 + ms * 16 + 4 * lg + i;
                     const bool valid = m_rs[r] >= 0;
                     const float w = valid ? m_w[r] : 0.f;
-                    const float v0 = (silu(clamp_act(acc[ms][0][i], a.clamp)) *
-                                      clamp_act(acc[ms][2][i], a.clamp)) * w;
-                    const float v1 = (silu(clamp_act(acc[ms][1][i], a.clamp)) *
-                                      clamp_act(acc[ms][3][i], a.clamp)) * w;
+                    const float v0 = (silu(acc[ms][0][i]) *
+                                      acc[ms][2][i]) * w;
+                    const float v1 = (silu(acc[ms][1][i]) *
+                                      acc[ms][3][i]) * w;
                     const float amax = max16(fmaxf(fabsf(v0), fabsf(v1)));
                     const uint32_t code = min(e8m0_ceil_code(fmaxf(amax, 1e-10f) / 448.0f), 253u);
                     const float inv = e8m0_inverse(code);
@@ -506,6 +507,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             // acc[ms][s]: rows wm*64 + 16 ms + 4 lg + i; s = 0,1 gate column
             // 32 wn + 16 s + lr of the block, s = 2,3 the matching up column.
             const float* m_w = reinterpret_cast<const float*>(slot(m_k) + META_W);
+            clamp_acc<16>(&acc[0][0], a.clamp);
             float* red = reinterpret_cast<float*>(ep);  // [4][128]
             uint8_t* qt = ep + 2048;                    // [128][128]
 #pragma unroll
@@ -517,8 +519,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                     float m = 0.f;
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
-                        const float g = clamp_act(acc[ms][s][i], a.clamp);
-                        const float u = clamp_act(acc[ms][s + 2][i], a.clamp);
+                        const float g = acc[ms][s][i];
+                        const float u = acc[ms][s + 2][i];
                         const float v = (silu(g) * u) * w;
                         acc[ms][s][i] = v;
                         m = fmaxf(m, fabsf(v));

@@ -219,6 +219,7 @@ __global__ __launch_bounds__(256) void l1_mx(FwdArgs a)
     // ---- epilogue: SwiGLU x topk_w, per-row amax over this wave's 32
     // columns (one requantisation block), power-of-two scale, e4m3 codes
     // staged in LDS for 16-byte row stores.
+    clamp_acc<MT * 4>(&acc[0][0], a.clamp);
     __shared__ uint8_t qt[BM][128];
 #pragma unroll
     for (int ms = 0; ms < MT; ++ms) {
@@ -227,10 +228,10 @@ __global__ __launch_bounds__(256) void l1_mx(FwdArgs a)
             const int r = 16 * ms + 4 * lg + i;
             const int f = a.row_src[row0 + r];
             const float w = f >= 0 ? a.topk_w[f] : 0.f;
-            const float v0 = (silu(clamp_act(acc[ms][0][i], a.clamp)) *
-                              clamp_act(acc[ms][2][i], a.clamp)) * w;
-            const float v1 = (silu(clamp_act(acc[ms][1][i], a.clamp)) *
-                              clamp_act(acc[ms][3][i], a.clamp)) * w;
+            const float v0 = (silu(acc[ms][0][i]) *
+                              acc[ms][2][i]) * w;
+            const float v1 = (silu(acc[ms][1][i]) *
+                              acc[ms][3][i]) * w;
             const float amax = max16(fmaxf(fabsf(v0), fabsf(v1)));
             const uint32_t code = min(e8m0_ceil_code(fmaxf(amax, 1e-10f) / 448.0f), 253u);
             const float inv = e8m0_inverse(code);

@@ -188,6 +188,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
         __shared__ float red[4][SA_BM];
         __shared__ uint8_t qt[SA_BM][128];
         float hv[4][2][4];
+        clamp_acc<16>(&acc[0][0], a.clamp);
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
 #pragma unroll
@@ -197,8 +198,8 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
                 float m = 0.f;
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const float g = clamp_act(acc[ms][s][i], a.clamp);
-                    const float u = clamp_act(acc[ms][s + 2][i], a.clamp);
+                    const float g = acc[ms][s][i];
+                    const float u = acc[ms][s + 2][i];
                     const float v = (silu(g) * u) * w;
                     hv[ms][s][i] = v;
                     m = fmaxf(m, fabsf(v));
@@ -403,6 +404,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
         // ---- SwiGLU x topk_w; wave w's 32 gate columns are one
         // requantisation block of each row: its amax, the power-of-two
         // scale as a UE8M0 code, codes staged in LDS for row stores.
+        clamp_acc<16>(&acc[0][0], a.clamp);
         __shared__ uint8_t qt[64][128];
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms)
@@ -411,10 +413,10 @@ __global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
                 const int r = 16 * ms + 4 * lg + i;
                 const int f = a.row_src[row0 + r];
                 const float w = f >= 0 ? a.topk_w[f] : 0.f;
-                const float v0 = (silu(clamp_act(acc[ms][0][i], a.clamp)) *
-                                  clamp_act(acc[ms][2][i], a.clamp)) * w;
-                const float v1 = (silu(clamp_act(acc[ms][1][i], a.clamp)) *
-                                  clamp_act(acc[ms][3][i], a.clamp)) * w;
+                const float v0 = (silu(acc[ms][0][i]) *
+                                  acc[ms][2][i]) * w;
+                const float v1 = (silu(acc[ms][1][i]) *
+                                  acc[ms][3][i]) * w;
                 const float amax = max16(fmaxf(fabsf(v0), fabsf(v1)));
                 const uint32_t code = min(e8m0_ceil_code(fmaxf(amax, 1e-10f) / 448.0f), 253u);
                 const float inv = e8m0_inverse(code);

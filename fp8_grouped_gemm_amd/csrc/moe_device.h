@@ -141,6 +141,20 @@ __device__ __forceinline__ float clamp_act(float v, float c)
     return c > 0.f ? fminf(fmaxf(v, -c), c) : v;
 }
 
+// clamp_act applied in place to N accumulator vectors: one branch on the
+// (workgroup-uniform) bound instead of a select per value.
+template <int N>
+__device__ __forceinline__ void clamp_acc(v4f* acc, float c)
+{
+    if (c > 0.f) {
+#pragma unroll
+        for (int q = 0; q < N; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[q][i] = fminf(fmaxf(acc[q][i], -c), c);
+    }
+}
+
 // SiLU with the hardware exp2 and reciprocal (a few ulp from
 // g / (1 + expf(-g)); g -> -inf gives -0, g -> +inf gives g).
 __device__ __forceinline__ float silu(float g)
@@ -163,13 +177,23 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b)
     return __uint_as_float(b << 16);
 }
 
-// Max over the 16 lanes that share (lane / 16).
+// v from another lane of the same 16-lane row, by a DPP row permutation.
+template <int CTRL>
+__device__ __forceinline__ float row_perm(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                      0xF, 0xF, false));
+}
+
+// Max over the 16 lanes that share (lane / 16), all of them active: swap
+// neighbours, swap pairs, mirror each 8-lane half, mirror the row (DPP, no
+// LDS round trip; max is exact, so the pairing does not change the value).
 __device__ __forceinline__ float max16(float v)
 {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, row_perm<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fmaxf(v, row_perm<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fmaxf(v, row_perm<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, row_perm<0x140>(v));  // row_mirror
     return v;
 }
 

@@ -508,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             // 32 wn + 16 s + lr of the block, s = 2,3 the matching up column.
             const float* m_w = reinterpret_cast<const float*>(slot(m_k) + META_W);
             clamp_acc<16>(&acc[0][0], a.clamp);
-            float* red = reinterpret_cast<float*>(ep);  // [4][128]
+            float* red = reinterpret_cast<float*>(ep);  // [128][4]: row, then wave wn
             uint8_t* qt = ep + 2048;                    // [128][128]
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms)
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                     }
                     m = max16(m);
                     if (lr == 0)
-                        red[wn * 128 + r] = m;
+                        red[r * 4 + wn] = m;
                 }
             __syncthreads();
 #pragma unroll
@@ -535,8 +535,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = wm * 64 + ms * 16 + 4 * lg + i;
-                    const float amax =
-                        fmaxf(fmaxf(red[r], red[128 + r]), fmaxf(red[256 + r], red[384 + r]));
+                    const float4 rm = *reinterpret_cast<const float4*>(red + r * 4);
+                    const float amax = fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
                     float rsf;
                     const float sf = requant_sf(amax, a.pow2_scale, rsf);
 #pragma unroll

@@ -101,13 +101,19 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_hw(float v)
 // y (1 - 2^-20) and y (1 + 2^-20); the encoder is monotone, so when both ends
 // give the same code, so does the quotient.  Only otherwise (y within ~2^-20
 // of a rounding boundary of the e4m3 grid) is the division done.
+// (f32_to_e4m3_hw's NaN test is made once, on y: for a NaN y both bracket
+// ends clamp to -448, agree, and the code is 0x7F.)
 __device__ __forceinline__ uint32_t requant_e4m3(float v, float sf, float rsf)
 {
     const float y = v * rsf;
-    const uint32_t lo = f32_to_e4m3_hw(y * (1.0f - 0x1p-20f));
-    const uint32_t hi = f32_to_e4m3_hw(y * (1.0f + 0x1p-20f));
+    auto sat = [](float x) {
+        const float c = __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+    };
+    const uint32_t lo = sat(y * (1.0f - 0x1p-20f));
+    const uint32_t hi = sat(y * (1.0f + 0x1p-20f));
     if (lo == hi)
-        return lo;
+        return y != y ? 0x7Fu : lo;
     return f32_to_e4m3_hw(v / sf);
 }
 

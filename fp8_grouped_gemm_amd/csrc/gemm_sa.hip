@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
     if constexpr (L1) {
         // ---- SwiGLU x topk_w, per-row amax over the 128 columns, e4m3
         // requant, coalesced store through LDS (as the direct tiles).
-        __shared__ float red[4][SA_BM];
+        __shared__ __align__(16) float red[SA_BM][4];  // row, then wave
         __shared__ uint8_t qt[SA_BM][128];
         float hv[4][2][4];
         clamp_acc<16>(&acc[0][0], a.clamp);
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
                 }
                 m = max16(m);
                 if (lr == 0)
-                    red[wave][16 * ms + 4 * lg + i] = m;
+                    red[16 * ms + 4 * lg + i][wave] = m;
             }
         }
         __syncthreads();
@@ -215,7 +215,8 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * ms + 4 * lg + i;
-                const float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+                const float4 rm = *reinterpret_cast<const float4*>(red[r]);
+                const float amax = fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
                 float rsf;
                 const float sf = requant_sf(amax, a.pow2_scale, rsf);
 #pragma unroll

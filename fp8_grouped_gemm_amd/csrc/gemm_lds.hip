@@ -556,8 +556,21 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             }
         } else {
             // acc[ms][s]: rows wm*64 + 16 ms + 4 lg + i, column 64 wn + 16 s
-            // + lr; staged as bf16 one 64-row half at a time (32 KiB).
-            uint16_t* ot = reinterpret_cast<uint16_t*>(ep);  // [64][256]
+            // + lr.  Every wave rounds its values to bf16 at once; the rows
+            // are then staged one 64-row half at a time (33 KiB: rows padded
+            // to 264 columns, so the four row groups of a wave's write fall
+            // on different LDS banks).
+            constexpr int OT = 256 + 8;
+            static_assert(64 * OT * 2 <= STAGE, "a staged half fits one stage");
+            uint16_t* ot = reinterpret_cast<uint16_t*>(ep);  // [64][OT]
+            uint16_t hb[4][4][4];
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        hb[ms][s][i] = f32_to_bf16(acc[ms][s][i]);
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 if (wm == hf) {
@@ -567,8 +580,8 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                         for (int s = 0; s < 4; ++s)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                ot[(ms * 16 + 4 * lg + i) * 256 + wn * 64 + s * 16 + lr] =
-                                    f32_to_bf16(acc[ms][s][i]);
+                                ot[(ms * 16 + 4 * lg + i) * OT + wn * 64 + s * 16 + lr] =
+                                    hb[ms][s][i];
                 }
                 __syncthreads();
                 for (int c = threadIdx.x; c < 64 * 32; c += kThreads) {
@@ -578,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                         const int tt = f / K, jslot = f - tt * K;
                         *reinterpret_cast<uint4*>(a.partial + ((size_t)jslot * T + tt) * H +
                                                   nt * 256 + col) =
-                            *reinterpret_cast<const uint4*>(ot + r * 256 + col);
+                            *reinterpret_cast<const uint4*>(ot + r * OT + col);
                     }
                 }
                 __syncthreads();

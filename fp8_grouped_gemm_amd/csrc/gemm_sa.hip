@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
     } else {
         // ---- bf16, staged in LDS one 32-row half at a time, 16-byte stores
         // to the (slot, token) row of the partial buffer.
-        __shared__ uint16_t ot[SA_BM / 2][256 + 8];
+        __shared__ __align__(16) uint16_t ot[SA_BM / 2][256 + 8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -254,11 +254,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
                 const int f = a.row_src[row0 + 32 * hf + r];
                 if (f >= 0) {
                     const int t = f / K, j = f - t * K;
-                    uint4 v;
-                    v.x = (uint32_t)ot[r][col + 0] | ((uint32_t)ot[r][col + 1] << 16);
-                    v.y = (uint32_t)ot[r][col + 2] | ((uint32_t)ot[r][col + 3] << 16);
-                    v.z = (uint32_t)ot[r][col + 4] | ((uint32_t)ot[r][col + 5] << 16);
-                    v.w = (uint32_t)ot[r][col + 6] | ((uint32_t)ot[r][col + 7] << 16);
+                    const uint4 v = *reinterpret_cast<const uint4*>(&ot[r][col]);  // 8 bf16
                     *reinterpret_cast<uint4*>(a.partial + ((size_t)j * T + t) * H + nt * 256 + col) = v;
                 }
             }
@@ -434,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
                     *reinterpret_cast<const uint4*>(&qt[r][col]);
         }
     } else {
-        __shared__ uint16_t ot[32][256 + 8];
+        __shared__ __align__(16) uint16_t ot[32][256 + 8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -451,11 +447,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
                 const int f = a.row_src[row0 + 32 * hf + r];
                 if (f >= 0) {
                     const int t = f / K, j = f - t * K;
-                    uint4 v;
-                    v.x = (uint32_t)ot[r][col + 0] | ((uint32_t)ot[r][col + 1] << 16);
-                    v.y = (uint32_t)ot[r][col + 2] | ((uint32_t)ot[r][col + 3] << 16);
-                    v.z = (uint32_t)ot[r][col + 4] | ((uint32_t)ot[r][col + 5] << 16);
-                    v.w = (uint32_t)ot[r][col + 6] | ((uint32_t)ot[r][col + 7] << 16);
+                    const uint4 v = *reinterpret_cast<const uint4*>(&ot[r][col]);  // 8 bf16
                     *reinterpret_cast<uint4*>(a.partial + ((size_t)j * T + t) * H + nt * 256 + col) = v;
                 }
             }

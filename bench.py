@@ -218,7 +218,7 @@ def main():
     import torch
 
     import fp8_grouped_gemm_amd as moe
-    from fp8_grouped_gemm_amd import workload as wl
+    import workload as wl
 
     if args.copy_calibration:
         n = args.copy_calibration << 20

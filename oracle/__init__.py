@@ -53,8 +53,18 @@ def lib():
             [ctypes.c_int] * 5
             + [_u8p, _f32p, _i32p, _f32p]
             + [ctypes.POINTER(ctypes.c_void_p)] * 4
-            + [ctypes.c_int, _i32p, _u16p, _f32p, _f32p, _u8p, _f32p, _u16p,
+            + [ctypes.c_int, _i32p, _u16p, _f32p, _f32p, _f32p, _f32p, _u8p, _f32p, _u16p,
                ctypes.c_int, ctypes.c_float, ctypes.c_int])
+        L.orc_moe_l2_combine.restype = ctypes.c_int
+        L.orc_moe_l2_combine.argtypes = (
+            [ctypes.c_int] * 5 + [_i32p] + [ctypes.POINTER(ctypes.c_void_p)] * 2
+            + [ctypes.c_int, _i32p, _u8p, _f32p, _u16p, _u16p, _f32p, ctypes.c_int,
+               ctypes.c_int])
+        L.orc_moe_l2_combine_mx.restype = ctypes.c_int
+        L.orc_moe_l2_combine_mx.argtypes = (
+            [ctypes.c_int] * 5 + [_i32p] + [ctypes.POINTER(ctypes.c_void_p)] * 2
+            + [ctypes.c_int, _i32p, _u8p, _u8p, _u16p, _u16p, _f32p, ctypes.c_int,
+               ctypes.c_int])
         L.orc_max_threads.restype = ctypes.c_int
         L.orc_requant_block_pow2.restype = None
         L.orc_requant_block_pow2.argtypes = [_f32p, ctypes.c_int, _u8p, _f32p]
@@ -75,7 +85,7 @@ def lib():
             [ctypes.c_int] * 5
             + [_u8p, _u8p, _i32p, _f32p]
             + [ctypes.POINTER(ctypes.c_void_p)] * 4
-            + [ctypes.c_int, _i32p, _u16p, _f32p, _f32p, _u8p, _u8p, _u16p,
+            + [ctypes.c_int, _i32p, _u16p, _f32p, _f32p, _f32p, _f32p, _u8p, _u8p, _u16p,
                ctypes.c_int, ctypes.c_float, ctypes.c_int])
         _lib = L
     return _lib
@@ -182,7 +192,11 @@ def moe_forward(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
 
     w1, w1_sf, w2, w2_sf: sequences indexed by expert (arrays or None for
     experts no listed token uses).  tokens: optional list of token ids.
-    want: subset of {"acc1", "h", "partial", "y_f32"} extra outputs.
+    want: subset of {"acc1", "acc1_mag", "hval", "h", "partial", "y_f32"} extra
+    outputs ("acc1_mag": per L1 output the sum over K blocks of |scale product|
+    times the block's sum of |products|, the magnitude a bound on rounding
+    inside a block scales with; "hval": the f32 SwiGLU output before
+    requantisation).
     Returns dict with "y" (uint16 bf16 bits [n,H]) and requested extras,
     indexed by position in the token list (slot-major: row p*K + j).
     """
@@ -229,6 +243,8 @@ def moe_forward(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
     y = np.zeros((n, H), np.uint16)
     y_f32 = np.zeros((n, H), np.float32) if "y_f32" in want else None
     acc1 = np.zeros((n * K, 2 * I), np.float32) if "acc1" in want else None
+    acc1_mag = np.zeros((n * K, 2 * I), np.float32) if "acc1_mag" in want else None
+    hval = np.zeros((n * K, I), np.float32) if "hval" in want else None
     h = np.zeros((n * K, I), np.uint8) if "h" in want else None
     G = 64 if flags & ORC_SF_GRAN64 else 128
     h_sf = np.zeros((n * K, I // G), np.float32) if "h" in want else None
@@ -236,20 +252,98 @@ def moe_forward(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=None,
     rc = lib().orc_moe_forward(
         T, H, I, E, K, _p(x, _u8p), _p(x_sf, _f32p), _p(idx, _i32p), _p(wts, _f32p),
         p1, p1s, p2, p2s, n, _p(toks, _i32p), _p(y, _u16p), _p(y_f32, _f32p),
-        _p(acc1, _f32p), _p(h, _u8p), _p(h_sf, _f32p), _p(partial, _u16p),
-        int(flags), float(clamp), int(nthreads))
+        _p(acc1, _f32p), _p(acc1_mag, _f32p), _p(hval, _f32p), _p(h, _u8p), _p(h_sf, _f32p),
+        _p(partial, _u16p), int(flags), float(clamp), int(nthreads))
     if rc < 0:
         raise ValueError("oracle: invalid shape or missing expert weights")
     out = {"y": y, "n_bad": rc}
-    if y_f32 is not None:
-        out["y_f32"] = y_f32
-    if acc1 is not None:
-        out["acc1"] = acc1
-    if h is not None:
-        out["h"] = h
-        out["h_sf"] = h_sf
+    for k, v in (("y_f32", y_f32), ("acc1", acc1), ("acc1_mag", acc1_mag), ("hval", hval),
+                 ("h", h), ("h_sf", h_sf), ("partial", partial)):
+        if v is not None:
+            out[k] = v
+    return out
+
+
+def _ptr_array(seq, dt, keep):
+    arr = (ctypes.c_void_p * len(seq))()
+    for e, a in enumerate(seq):
+        if a is None:
+            arr[e] = None
+        else:
+            a = np.ascontiguousarray(a, dtype=dt)
+            keep.append(a)
+            arr[e] = a.ctypes.data
+    return arr
+
+
+def moe_l2_combine(topk_idx, w2, w2_sf, h, h_sf, *, tokens=None, flags=0, want=(),
+                   nthreads=0):
+    """Oracle steps 5-6 (L2 + combine) from a given intermediate.
+
+    h [n*K, I] e4m3 codes and h_sf [n*K, I/G] f32 scales (G = 64 with
+    ORC_SF_GRAN64, else 128), rows indexed like moe_forward's outputs (slot j
+    of the p-th listed token at row p*K + j; rows of skipped slots unread).
+    w2, w2_sf: per-expert sequences as for moe_forward.  want: subset of
+    {"partial", "o_mag"}.  Returns dict with "y" [n,H] bf16 bits and extras.
+    """
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, K = idx.shape
+    E = len(w2)
+    h = np.ascontiguousarray(h, dtype=np.uint8)
+    h_sf = np.ascontiguousarray(h_sf, dtype=np.float32)
+    I = h.shape[1]
+    H = next(a.shape[0] for a in w2 if a is not None)
+    keep = []
+    p2, p2s = _ptr_array(w2, np.uint8, keep), _ptr_array(w2_sf, np.float32, keep)
+    toks = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    n = T if toks is None else toks.size
+    assert h.shape[0] == n * K and h_sf.shape[0] == n * K
+    y = np.zeros((n, H), np.uint16)
+    partial = np.zeros((n * K, H), np.uint16) if "partial" in want else None
+    o_mag = np.zeros((n * K, H), np.float32) if "o_mag" in want else None
+    rc = lib().orc_moe_l2_combine(T, H, I, E, K, _p(idx, _i32p), p2, p2s, n, _p(toks, _i32p),
+                                  _p(h, _u8p), _p(h_sf, _f32p), _p(y, _u16p),
+                                  _p(partial, _u16p), _p(o_mag, _f32p), int(flags),
+                                  int(nthreads))
+    if rc < 0:
+        raise ValueError("oracle: invalid shape or missing expert weights")
+    out = {"y": y, "n_bad": rc}
     if partial is not None:
         out["partial"] = partial
+    if o_mag is not None:
+        out["o_mag"] = o_mag
+    return out
+
+
+def moe_l2_combine_mx(topk_idx, w2, w2_sf, h, h_sf, *, tokens=None, want=(), nthreads=0):
+    """moe_l2_combine for the MXFP4 recipe: h_sf [n*K, I/32] UE8M0 codes,
+    per expert w2 [H, I/2] packed e2m1 and w2_sf [H, I/32] codes."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, K = idx.shape
+    E = len(w2)
+    h = np.ascontiguousarray(h, dtype=np.uint8)
+    h_sf = np.ascontiguousarray(h_sf, dtype=np.uint8)
+    I = h.shape[1]
+    H = next(a.shape[0] for a in w2 if a is not None)
+    keep = []
+    p2, p2s = _ptr_array(w2, np.uint8, keep), _ptr_array(w2_sf, np.uint8, keep)
+    toks = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    n = T if toks is None else toks.size
+    assert h.shape[0] == n * K and h_sf.shape[0] == n * K
+    y = np.zeros((n, H), np.uint16)
+    partial = np.zeros((n * K, H), np.uint16) if "partial" in want else None
+    o_mag = np.zeros((n * K, H), np.float32) if "o_mag" in want else None
+    rc = lib().orc_moe_l2_combine_mx(T, H, I, E, K, _p(idx, _i32p), p2, p2s, n,
+                                     _p(toks, _i32p), _p(h, _u8p), _p(h_sf, _u8p),
+                                     _p(y, _u16p), _p(partial, _u16p), _p(o_mag, _f32p), 0,
+                                     int(nthreads))
+    if rc < 0:
+        raise ValueError("oracle: invalid shape or missing expert weights")
+    out = {"y": y, "n_bad": rc}
+    if partial is not None:
+        out["partial"] = partial
+    if o_mag is not None:
+        out["o_mag"] = o_mag
     return out
 
 
@@ -293,19 +387,21 @@ def moe_forward_mx(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, tokens=No
     y = np.zeros((n, H), np.uint16)
     y_f32 = np.zeros((n, H), np.float32) if "y_f32" in want else None
     acc1 = np.zeros((n * K, 2 * I), np.float32) if "acc1" in want else None
+    acc1_mag = np.zeros((n * K, 2 * I), np.float32) if "acc1_mag" in want else None
+    hval = np.zeros((n * K, I), np.float32) if "hval" in want else None
     h = np.zeros((n * K, I), np.uint8) if "h" in want else None
     h_sf = np.zeros((n * K, I // 32), np.uint8) if "h" in want else None
     partial = np.zeros((n * K, H), np.uint16) if "partial" in want else None
     rc = lib().orc_moe_forward_mx(
         T, H, I, E, K, _p(x, _u8p), _p(x_sf, _u8p), _p(idx, _i32p), _p(wts, _f32p),
         p1, p1s, p2, p2s, n, _p(toks, _i32p), _p(y, _u16p), _p(y_f32, _f32p),
-        _p(acc1, _f32p), _p(h, _u8p), _p(h_sf, _u8p), _p(partial, _u16p),
-        int(flags), float(clamp), int(nthreads))
+        _p(acc1, _f32p), _p(acc1_mag, _f32p), _p(hval, _f32p), _p(h, _u8p), _p(h_sf, _u8p),
+        _p(partial, _u16p), int(flags), float(clamp), int(nthreads))
     if rc < 0:
         raise ValueError("oracle: invalid shape or missing expert weights")
     out = {"y": y, "n_bad": rc}
-    for k, v in (("y_f32", y_f32), ("acc1", acc1), ("h", h), ("h_sf", h_sf),
-                 ("partial", partial)):
+    for k, v in (("y_f32", y_f32), ("acc1", acc1), ("acc1_mag", acc1_mag), ("hval", hval),
+                 ("h", h), ("h_sf", h_sf), ("partial", partial)):
         if v is not None:
             out[k] = v
     return out

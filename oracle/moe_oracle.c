@@ -197,14 +197,46 @@ int orc_route(int T, int K, int E, int row_align, const int32_t* idx,
 
 /* ----------------------------------------------------- block-scaled GEMM */
 
+/* Decoded values of every e4m3 code and every e2m1 nibble, filled once from
+ * orc_e4m3_decode / orc_e2m1_decode (a table of the decoder's own values, so
+ * the sums below read exactly what the decoder defines, only faster). */
+float orc_e2m1_decode(uint8_t code);
+static double g_e4m3[256];
+static double g_e2m1[16];
+static int g_tables_ready;
+
+static void init_tables(void)
+{
+    if (g_tables_ready)
+        return;
+    for (int c = 0; c < 256; ++c)
+        g_e4m3[c] = (double)orc_e4m3_decode((uint8_t)c);
+    for (int c = 0; c < 16; ++c)
+        g_e2m1[c] = (double)orc_e2m1_decode((uint8_t)c);
+    g_tables_ready = 1;
+}
+
 /* Exact sum over one 128-wide K block of decoded e4m3 products.  Every
  * e4m3 value is an integer multiple of 2^-9 below 2^9, so each product is
- * a multiple of 2^-18 below 2^18 and 128 of them sum exactly in binary64. */
+ * a multiple of 2^-18 below 2^18 and 128 of them sum exactly in binary64
+ * (in any order). */
 double orc_block_dot_e4m3(const uint8_t* a, const uint8_t* b, int n)
+{
+    init_tables();
+    double s = 0.0;
+    for (int c = 0; c < n; ++c)
+        s += g_e4m3[a[c]] * g_e4m3[b[c]];
+    return s;
+}
+
+/* The same block's sum of |products| (exact for the same reason): the
+ * magnitude an error bound on a rounded accumulation of the block scales
+ * with. */
+static double block_abs_dot_e4m3(const uint8_t* a, const uint8_t* b, int n)
 {
     double s = 0.0;
     for (int c = 0; c < n; ++c)
-        s += (double)orc_e4m3_decode(a[c]) * (double)orc_e4m3_decode(b[c]);
+        s += fabs(g_e4m3[a[c]] * g_e4m3[b[c]]);
     return s;
 }
 
@@ -214,7 +246,7 @@ static double block_dot_f32_e4m3(const float* a, const uint8_t* b, int n)
 {
     double s = 0.0;
     for (int c = 0; c < n; ++c)
-        s += (double)a[c] * (double)orc_e4m3_decode(b[c]);
+        s += (double)a[c] * g_e4m3[b[c]];
     return s;
 }
 
@@ -230,6 +262,33 @@ static float scaled_row_dot(const uint8_t* a, const float* sa, const uint8_t* b,
         float s = sa[kb] * sb[kb];
         acc = fmaf(s, p, acc);
     }
+    return acc;
+}
+
+/* The same element together with its magnitude: *mag = the sum over K
+ * blocks of |sa*sb| * (sum of |products| of the block), in binary64 (not
+ * part of the forward; tests scale the error bound of an accumulation that
+ * rounds inside a block by it).  The returned value is scaled_row_dot's:
+ * the same block sums, promoted in the same order. */
+static float scaled_row_dot_mag(const uint8_t* a, const float* sa, const uint8_t* b,
+                                const float* sb, int kblocks, double* mag)
+{
+    float acc = 0.0f;
+    double m = 0.0;
+    for (int kb = 0; kb < kblocks; ++kb) {
+        const uint8_t* ak = a + 128 * kb;
+        const uint8_t* bk = b + 128 * kb;
+        double ps = 0.0, pm = 0.0;
+        for (int c = 0; c < 128; ++c) {
+            const double pr = g_e4m3[ak[c]] * g_e4m3[bk[c]];
+            ps += pr;
+            pm += fabs(pr);
+        }
+        float s = sa[kb] * sb[kb];
+        acc = fmaf(s, (float)ps, acc);
+        m += fabs((double)sa[kb] * (double)sb[kb]) * pm;
+    }
+    *mag = m;
     return acc;
 }
 
@@ -304,10 +363,10 @@ float orc_e2m1_decode(uint8_t code)
 }
 
 /* Element k of a row of packed e2m1 pairs. */
-static float e2m1_at(const uint8_t* row, int k)
+static double e2m1_at(const uint8_t* row, int k)
 {
     uint8_t b = row[k >> 1];
-    return orc_e2m1_decode((k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 0xF));
+    return g_e2m1[(k & 1) ? (b >> 4) : (b & 0xF)];
 }
 
 /* UE8M0: value 2^(code - 127); code 0xFF is NaN. */
@@ -337,13 +396,28 @@ uint8_t orc_e8m0_ceil(float s)
 double orc_mx_dot(const uint8_t* a, const uint8_t* sa, const uint8_t* b_packed,
                   const uint8_t* sb, int n)
 {
+    init_tables();
     double s = 0.0;
     for (int blk = 0; blk < n / 32; ++blk) {
         if (sa[blk] == 0xFF || sb[blk] == 0xFF)
             return NAN;
         double p = 0.0;
         for (int c = 32 * blk; c < 32 * blk + 32; ++c)
-            p += (double)orc_e4m3_decode(a[c]) * (double)e2m1_at(b_packed, c);
+            p += g_e4m3[a[c]] * e2m1_at(b_packed, c);
+        s += ldexp(p, (int)sa[blk] + (int)sb[blk] - 254);
+    }
+    return s;
+}
+
+/* Its magnitude: sum over 32-blocks of 2^(scales) * (sum of |products|). */
+static double mx_mag(const uint8_t* a, const uint8_t* sa, const uint8_t* b_packed,
+                     const uint8_t* sb, int n)
+{
+    double s = 0.0;
+    for (int blk = 0; blk < n / 32; ++blk) {
+        double p = 0.0;
+        for (int c = 32 * blk; c < 32 * blk + 32; ++c)
+            p += fabs(g_e4m3[a[c]] * e2m1_at(b_packed, c));
         s += ldexp(p, (int)sa[blk] + (int)sb[blk] - 254);
     }
     return s;
@@ -435,6 +509,55 @@ enum {
     ORC_SF_GRAN64 = 8   /* FP8 recipe: per-64 intermediate scales, dual-half L2 */
 };
 
+/* L2 of one routed slot (design doc §11.1; per-64 halves: §5.4): for each
+ * output column n, acc = the block-scaled dot product of the requantised row
+ * (q, per-G scales qs) with W2[e] row n, then one bf16 rounding.
+ *   part_f32[n] = the bf16-rounded value as f32 (the combine's input), or the
+ *                 f32 value itself with ORC_NO_BF16
+ *   partial[n]  = bf16 bits (optional), mag[n] = scaled_row_mag (optional)
+ * With ORC_NO_REQUANT the unquantised f32 row hv is used instead of q/qs. */
+static void l2_slot(int H, int I, int G, const uint8_t* q, const float* qs, const float* hv,
+                    const uint8_t* w2e, const float* w2se, int flags, float* part_f32,
+                    uint16_t* partial, float* mag)
+{
+    const int IB = I / 128;
+    for (int n = 0; n < H; ++n) {
+        const uint8_t* wr = w2e + (size_t)n * I;
+        const float* ws = w2se + (size_t)(n / 128) * IB;
+        float acc = 0.0f;
+        if (flags & ORC_NO_REQUANT) {
+            for (int ib = 0; ib < IB; ++ib) {
+                float pdot = (float)block_dot_f32_e4m3(hv + 128 * ib, wr + 128 * ib, 128);
+                acc = fmaf(ws[ib], pdot, acc);
+            }
+        } else if (G == 64) {
+            /* design doc §5.4: each 128-K block as two 64-K halves */
+            double m = 0.0;
+            for (int kb = 0; kb < IB; ++kb) {
+                float p_lo = (float)orc_block_dot_e4m3(q + 128 * kb, wr + 128 * kb, 64);
+                float p_hi = (float)orc_block_dot_e4m3(q + 128 * kb + 64, wr + 128 * kb + 64, 64);
+                acc = fmaf(qs[2 * kb] * ws[kb], p_lo, acc);
+                acc = fmaf(qs[2 * kb + 1] * ws[kb], p_hi, acc);
+                if (mag)
+                    m += fabs((double)qs[2 * kb] * ws[kb]) * block_abs_dot_e4m3(q + 128 * kb, wr + 128 * kb, 64) +
+                         fabs((double)qs[2 * kb + 1] * ws[kb]) *
+                             block_abs_dot_e4m3(q + 128 * kb + 64, wr + 128 * kb + 64, 64);
+            }
+            if (mag)
+                mag[n] = (float)m;
+        } else if (mag) {
+            double m;
+            acc = scaled_row_dot_mag(q, qs, wr, ws, IB, &m);
+            mag[n] = (float)m;
+        } else {
+            acc = scaled_row_dot(q, qs, wr, ws, IB);
+        }
+        part_f32[n] = (flags & ORC_NO_BF16) ? acc : orc_bf16_to_f32(orc_bf16_rne(acc));
+        if (partial)
+            partial[n] = orc_bf16_rne(acc);
+    }
+}
+
 /* Forward for a list of tokens.
  *   x [T,H] e4m3, x_sf [T,H/128] f32, idx/w [T,K]
  *   w1[e] -> [2I,H] e4m3 (gate rows then up rows), w1_sf[e] -> [2I/128,H/128]
@@ -444,7 +567,10 @@ enum {
  * Outputs, indexed by position p in the token list (all optional but y):
  *   y [n_tok,H] bf16 (or y_f32 [n_tok,H] when ORC_NO_BF16)
  *   acc1 [n_tok*K, 2I] f32 L1 accumulator before SwiGLU
- *   h [n_tok*K, I] e4m3, h_sf [n_tok*K, I/128]
+ *   acc1_mag [n_tok*K, 2I] its magnitude (scaled_row_mag; not part of the
+ *            forward: the scale of a bound on rounding inside the blocks)
+ *   hval [n_tok*K, I] f32 SwiGLU x top-k weight, before requantisation
+ *   h [n_tok*K, I] e4m3, h_sf [n_tok*K, I/G]
  *   partial [n_tok*K, H] bf16 (skipped slots left untouched)
  * Returns the number of slots with an id >= E, or -1 when a needed expert
  * pointer is NULL or a shape is invalid. */
@@ -455,14 +581,16 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
                     const uint8_t* const* w2, const float* const* w2_sf,
                     int n_tok, const int32_t* toks,
                     uint16_t* y, float* y_f32,
-                    float* acc1, uint8_t* h, float* h_sf, uint16_t* partial,
+                    float* acc1, float* acc1_mag, float* hval,
+                    uint8_t* h, float* h_sf, uint16_t* partial,
                     int flags, float clamp, int nthreads)
 {
     if (H % 128 || I % 128 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || T < 0)
         return -1;
     if (!toks)
         n_tok = T;
-    const int HB = H / 128, IB = I / 128;
+    init_tables();
+    const int HB = H / 128;
     const int G = (flags & ORC_SF_GRAN64) ? 64 : 128;  /* intermediate scale block */
     const int NG = I / G;
     int bad = check_tokens(T, E, K, idx, n_tok, toks, (const void* const*)w1,
@@ -494,12 +622,20 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
         const float* xs = x_sf + (size_t)t * HB;
         for (int n = 0; n < 2 * I; ++n) {
             const float* ws = w1_sf[e] + (size_t)(n / 128) * HB;
-            a1[n] = scaled_row_dot(xr, xs, w1[e] + (size_t)n * H, ws, HB);
+            if (acc1_mag) {
+                double m;
+                a1[n] = scaled_row_dot_mag(xr, xs, w1[e] + (size_t)n * H, ws, HB, &m);
+                acc1_mag[(size_t)ps * 2 * I + n] = (float)m;
+            } else {
+                a1[n] = scaled_row_dot(xr, xs, w1[e] + (size_t)n * H, ws, HB);
+            }
         }
         if (acc1)
             memcpy(acc1 + (size_t)ps * 2 * I, a1, sizeof(float) * 2 * I);
         for (int i = 0; i < I; ++i)
             hv[i] = orc_swiglu(clamp_act(a1[i], clamp), clamp_act(a1[I + i], clamp), w[t * K + j]);
+        if (hval)
+            memcpy(hval + (size_t)ps * I, hv, sizeof(float) * I);
         if (!(flags & ORC_NO_REQUANT)) {
             for (int ib = 0; ib < NG; ++ib) {
                 if (flags & ORC_POW2_SCALE)
@@ -512,31 +648,8 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
             if (h_sf)
                 memcpy(h_sf + (size_t)ps * NG, qs, sizeof(float) * NG);
         }
-        for (int n = 0; n < H; ++n) {
-            const uint8_t* wr = w2[e] + (size_t)n * I;
-            const float* ws = w2_sf[e] + (size_t)(n / 128) * IB;
-            float acc = 0.0f;
-            if (flags & ORC_NO_REQUANT) {
-                for (int ib = 0; ib < IB; ++ib) {
-                    float pdot = (float)block_dot_f32_e4m3(hv + 128 * ib, wr + 128 * ib, 128);
-                    acc = fmaf(ws[ib], pdot, acc);
-                }
-            } else if (G == 64) {
-                /* design doc §5.4: each 128-K block as two 64-K halves */
-                for (int kb = 0; kb < IB; ++kb) {
-                    float p_lo = (float)orc_block_dot_e4m3(q + 128 * kb, wr + 128 * kb, 64);
-                    float p_hi = (float)orc_block_dot_e4m3(q + 128 * kb + 64, wr + 128 * kb + 64, 64);
-                    acc = fmaf(qs[2 * kb] * ws[kb], p_lo, acc);
-                    acc = fmaf(qs[2 * kb + 1] * ws[kb], p_hi, acc);
-                }
-            } else {
-                acc = scaled_row_dot(q, qs, wr, ws, IB);
-            }
-            float o = (flags & ORC_NO_BF16) ? acc : orc_bf16_to_f32(orc_bf16_rne(acc));
-            part_f32[(size_t)ps * H + n] = o;
-            if (partial)
-                partial[(size_t)ps * H + n] = orc_bf16_rne(acc);
-        }
+        l2_slot(H, I, G, q, qs, hv, w2[e], w2_sf[e], flags, part_f32 + (size_t)ps * H,
+                partial ? partial + (size_t)ps * H : NULL, NULL);
         free(a1);
         free(hv);
         free(q);
@@ -544,6 +657,58 @@ int orc_moe_forward(int T, int H, int I, int E, int K,
     }
 
     combine(T, H, E, K, idx, n_tok, toks, part_f32, y, y_f32);
+    free(part_f32);
+    return bad;
+}
+
+/* Steps 5-6 alone (L2 + combine), started from a given requantised
+ * intermediate instead of the one step 4 computes: h [n_tok*K, I] e4m3 and
+ * h_sf [n_tok*K, I/G] (G = 64 with ORC_SF_GRAN64, else 128), indexed like
+ * the forward's outputs (slot j of the p-th listed token at row p*K + j;
+ * rows of skipped slots are not read).  Fed the forward's own h and h_sf it
+ * returns the forward's y and partials bit for bit.  Outputs: y [n_tok,H]
+ * bf16, partial [n_tok*K,H] bf16 and o_mag [n_tok*K,H] (the L2 magnitude,
+ * as acc1_mag), the last two optional.  Same return values as the forward. */
+int orc_moe_l2_combine(int T, int H, int I, int E, int K,
+                       const int32_t* idx,
+                       const uint8_t* const* w2, const float* const* w2_sf,
+                       int n_tok, const int32_t* toks,
+                       const uint8_t* h, const float* h_sf,
+                       uint16_t* y, uint16_t* partial, float* o_mag,
+                       int flags, int nthreads)
+{
+    if (H % 128 || I % 128 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || T < 0 ||
+        (flags & (ORC_NO_REQUANT | ORC_NO_BF16)))
+        return -1;
+    if (!toks)
+        n_tok = T;
+    init_tables();
+    const int G = (flags & ORC_SF_GRAN64) ? 64 : 128;
+    const int NG = I / G;
+    int bad = check_tokens(T, E, K, idx, n_tok, toks, (const void* const*)w2,
+                           (const void* const*)w2_sf, (const void* const*)w2,
+                           (const void* const*)w2_sf);
+    if (bad < 0)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+    float* part_f32 = (float*)calloc((size_t)n_tok * K * H, sizeof(float));
+    if (!part_f32)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ps = 0; ps < n_tok * K; ++ps) {
+        int p = ps / K, j = ps % K;
+        int t = toks ? toks[p] : p;
+        int e = idx[t * K + j];
+        if (e < 0 || e >= E)
+            continue;
+        l2_slot(H, I, G, h + (size_t)ps * I, h_sf + (size_t)ps * NG, NULL, w2[e], w2_sf[e],
+                flags, part_f32 + (size_t)ps * H, partial ? partial + (size_t)ps * H : NULL,
+                o_mag ? o_mag + (size_t)ps * H : NULL);
+    }
+    combine(T, H, E, K, idx, n_tok, toks, part_f32, y, NULL);
     free(part_f32);
     return bad;
 }
@@ -557,12 +722,34 @@ int orc_max_threads(void)
 #endif
 }
 
+/* L2 of one routed slot of the MXFP4 recipe: per output column the MX dot
+ * product of the requantised row (q, UE8M0 codes qs per 32) with W2[e] row
+ * n, rounded once to f32, then to bf16 (outputs as l2_slot). */
+static void l2_slot_mx(int H, int I, const uint8_t* q, const uint8_t* qs, const float* hv,
+                       const uint8_t* w2e, const uint8_t* w2se, int flags, float* part_f32,
+                       uint16_t* partial, float* mag)
+{
+    const int IS = I / 32;
+    for (int n = 0; n < H; ++n) {
+        const uint8_t* wr = w2e + (size_t)n * (I / 2);
+        const uint8_t* ws = w2se + (size_t)n * IS;
+        float acc = (flags & ORC_NO_REQUANT) ? (float)mx_dot_f32(hv, wr, ws, I)
+                                             : (float)orc_mx_dot(q, qs, wr, ws, I);
+        if (mag)
+            mag[n] = (float)mx_mag(q, qs, wr, ws, I);
+        part_f32[n] = (flags & ORC_NO_BF16) ? acc : orc_bf16_to_f32(orc_bf16_rne(acc));
+        if (partial)
+            partial[n] = orc_bf16_rne(acc);
+    }
+}
+
 /* Forward of the FP8 x MXFP4 recipe, same structure and outputs as
  * orc_moe_forward:
  *   x [T,H] e4m3, x_sf [T,H/32] UE8M0, idx/w [T,K]
  *   w1[e] -> [2I,H/2] packed e2m1 (gate rows then up rows), w1_sf[e] -> [2I,H/32]
  *   w2[e] -> [H,I/2] packed e2m1, w2_sf[e] -> [H,I/32]
- *   acc1 [n*K,2I] f32, h [n*K,I] e4m3, h_sf [n*K,I/32] UE8M0, partial [n*K,H]
+ *   acc1 [n*K,2I] f32, acc1_mag [n*K,2I] (mx_mag), hval [n*K,I] f32,
+ *   h [n*K,I] e4m3, h_sf [n*K,I/32] UE8M0, partial [n*K,H]
  * ORC_NO_REQUANT feeds the f32 SwiGLU output to L2 unquantised; ORC_NO_BF16
  * keeps partials and y in f32. */
 int orc_moe_forward_mx(int T, int H, int I, int E, int K,
@@ -572,13 +759,15 @@ int orc_moe_forward_mx(int T, int H, int I, int E, int K,
                        const uint8_t* const* w2, const uint8_t* const* w2_sf,
                        int n_tok, const int32_t* toks,
                        uint16_t* y, float* y_f32,
-                       float* acc1, uint8_t* h, uint8_t* h_sf, uint16_t* partial,
+                       float* acc1, float* acc1_mag, float* hval,
+                       uint8_t* h, uint8_t* h_sf, uint16_t* partial,
                        int flags, float clamp, int nthreads)
 {
     if (H % 32 || I % 32 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || T < 0)
         return -1;
     if (!toks)
         n_tok = T;
+    init_tables();
     const int HS = H / 32, IS = I / 32;
     int bad = check_tokens(T, E, K, idx, n_tok, toks, (const void* const*)w1,
                            (const void* const*)w1_sf, (const void* const*)w2,
@@ -605,13 +794,19 @@ int orc_moe_forward_mx(int T, int H, int I, int E, int K,
         uint8_t* qs = (uint8_t*)malloc(IS);
         const uint8_t* xr = x + (size_t)t * H;
         const uint8_t* xs = x_sf + (size_t)t * HS;
-        for (int n = 0; n < 2 * I; ++n)
+        for (int n = 0; n < 2 * I; ++n) {
             a1[n] = (float)orc_mx_dot(xr, xs, w1[e] + (size_t)n * (H / 2),
                                       w1_sf[e] + (size_t)n * HS, H);
+            if (acc1_mag)
+                acc1_mag[(size_t)ps * 2 * I + n] =
+                    (float)mx_mag(xr, xs, w1[e] + (size_t)n * (H / 2), w1_sf[e] + (size_t)n * HS, H);
+        }
         if (acc1)
             memcpy(acc1 + (size_t)ps * 2 * I, a1, sizeof(float) * 2 * I);
         for (int i = 0; i < I; ++i)
             hv[i] = orc_swiglu(clamp_act(a1[i], clamp), clamp_act(a1[I + i], clamp), w[t * K + j]);
+        if (hval)
+            memcpy(hval + (size_t)ps * I, hv, sizeof(float) * I);
         if (!(flags & ORC_NO_REQUANT)) {
             for (int ib = 0; ib < IS; ++ib)
                 orc_requant_block_mx(hv + 32 * ib, 32, q + 32 * ib, qs + ib);
@@ -620,22 +815,60 @@ int orc_moe_forward_mx(int T, int H, int I, int E, int K,
             if (h_sf)
                 memcpy(h_sf + (size_t)ps * IS, qs, IS);
         }
-        for (int n = 0; n < H; ++n) {
-            const uint8_t* wr = w2[e] + (size_t)n * (I / 2);
-            const uint8_t* ws = w2_sf[e] + (size_t)n * IS;
-            float acc = (flags & ORC_NO_REQUANT) ? (float)mx_dot_f32(hv, wr, ws, I)
-                                                 : (float)orc_mx_dot(q, qs, wr, ws, I);
-            float o = (flags & ORC_NO_BF16) ? acc : orc_bf16_to_f32(orc_bf16_rne(acc));
-            part_f32[(size_t)ps * H + n] = o;
-            if (partial)
-                partial[(size_t)ps * H + n] = orc_bf16_rne(acc);
-        }
+        l2_slot_mx(H, I, q, qs, hv, w2[e], w2_sf[e], flags, part_f32 + (size_t)ps * H,
+                   partial ? partial + (size_t)ps * H : NULL, NULL);
         free(a1);
         free(hv);
         free(q);
         free(qs);
     }
     combine(T, H, E, K, idx, n_tok, toks, part_f32, y, y_f32);
+    free(part_f32);
+    return bad;
+}
+
+/* Steps 5-6 of the MXFP4 recipe from a given intermediate: h [n_tok*K, I]
+ * e4m3, h_sf [n_tok*K, I/32] UE8M0 codes; outputs and returns as
+ * orc_moe_l2_combine. */
+int orc_moe_l2_combine_mx(int T, int H, int I, int E, int K,
+                          const int32_t* idx,
+                          const uint8_t* const* w2, const uint8_t* const* w2_sf,
+                          int n_tok, const int32_t* toks,
+                          const uint8_t* h, const uint8_t* h_sf,
+                          uint16_t* y, uint16_t* partial, float* o_mag,
+                          int flags, int nthreads)
+{
+    if (H % 32 || I % 32 || H <= 0 || I <= 0 || E <= 0 || K <= 0 || T < 0 ||
+        (flags & (ORC_NO_REQUANT | ORC_NO_BF16)))
+        return -1;
+    if (!toks)
+        n_tok = T;
+    init_tables();
+    const int IS = I / 32;
+    int bad = check_tokens(T, E, K, idx, n_tok, toks, (const void* const*)w2,
+                           (const void* const*)w2_sf, (const void* const*)w2,
+                           (const void* const*)w2_sf);
+    if (bad < 0)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+    float* part_f32 = (float*)calloc((size_t)n_tok * K * H, sizeof(float));
+    if (!part_f32)
+        return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int ps = 0; ps < n_tok * K; ++ps) {
+        int p = ps / K, j = ps % K;
+        int t = toks ? toks[p] : p;
+        int e = idx[t * K + j];
+        if (e < 0 || e >= E)
+            continue;
+        l2_slot_mx(H, I, h + (size_t)ps * I, h_sf + (size_t)ps * IS, NULL, w2[e], w2_sf[e],
+                   flags, part_f32 + (size_t)ps * H, partial ? partial + (size_t)ps * H : NULL,
+                   o_mag ? o_mag + (size_t)ps * H : NULL);
+    }
+    combine(T, H, E, K, idx, n_tok, toks, part_f32, y, NULL);
     free(part_f32);
     return bad;
 }

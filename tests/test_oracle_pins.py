@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from fp8_grouped_gemm_amd import workload as wl
+import workload as wl
 
 # --------------------------------------------------------------- helpers
 

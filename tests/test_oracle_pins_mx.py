@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from fp8_grouped_gemm_amd import workload as wl
+import workload as wl
 
 # OCP Microscaling Formats (MX) v1.0, E2M1 element values for codes 0..7
 E2M1_TABLE = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from fp8_grouped_gemm_amd import workload as wl
+import workload as wl
 from test_oracle_pins import (DEC, _bf16_bits, _e4m3, _f32, bf16_bits_to_f64, dequant_blocks,
                               rel_l2, small_inputs)
 

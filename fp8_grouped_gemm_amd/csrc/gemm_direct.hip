@@ -143,7 +143,7 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
     const int mb = tile / NT;
     const int nt = tile - mb * NT;
     const int e = a.mblock_expert[mb];
-    if (e < 0)
+    if (e < 0 || e >= a.E)
         return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -363,7 +363,7 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
     const int mb = tile / NG;
     const int g = tile - mb * NG;
     const int e = a.mblock_expert[mb];
-    if (e < 0)
+    if (e < 0 || e >= a.E)
         return;
     if constexpr (CO)
         wait_count(a.sync + kSyncReady + mb, a.I / 128, a, hint);
@@ -623,9 +623,9 @@ __device__ __forceinline__ void combine_chunk(const FwdArgs& a, int blk, int n_l
     const uint16_t* prow = a.partial + (size_t)t * a.H + c;  // slot j: + j * T * H
     const size_t jstride = (size_t)a.T * a.H;
     if (a.K <= 8) {
-        // every slot's row is loaded (a masked slot's stale row is not
-        // added), so all K loads are in flight together; the sum still runs
-        // over the valid slots in ascending j
+        // the rows of all valid slots are loaded before any is added, so
+        // their loads are in flight together (a masked slot's row is neither
+        // read nor added); the sum runs over the valid slots in ascending j
         bool ok[8];
         uint4 v[8];
 #pragma unroll
@@ -633,7 +633,8 @@ __device__ __forceinline__ void combine_chunk(const FwdArgs& a, int blk, int n_l
             if (j < a.K) {
                 const int e = a.idx[t * a.K + j];
                 ok[j] = e >= 0 && e < a.E;
-                v[j] = *reinterpret_cast<const uint4*>(prow + j * jstride);
+                if (ok[j])
+                    v[j] = *reinterpret_cast<const uint4*>(prow + j * jstride);
             }
         }
 #pragma unroll

@@ -73,9 +73,16 @@ struct LdsCfg {
     static constexpr int B_BYTES = MX ? BN * 64 : BN * 128;
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int NSTAGE = MX ? 4 : 3;
-    static constexpr int COPIES = MX ? 2 + 2 + 1 : 2 + 4 + 1;
+    // copies each wave issues per K block: the loops of issue_next run
+    // exactly these counts, and the vmcnt waits are sized by their sum
+    static constexpr int A_COPIES = A_BYTES / 1024 / 8;     // 1 KiB each, 8 waves
+    static constexpr int B_COPIES = B_BYTES / 1024 / 8;
+    static constexpr int S_COPIES = S_BYTES / 256 / 8;      // one 256-byte scale copy
+    static constexpr int COPIES = A_COPIES + B_COPIES + S_COPIES;
     static constexpr int SMEM = NSTAGE * STAGE + NMETA * META;
 };
+static_assert(LdsCfg<false>::COPIES == 2 + 4 + 1 && LdsCfg<true>::COPIES == 2 + 2 + 1,
+              "copy counts per wave and K block");
 static_assert(LdsCfg<false>::SMEM <= 160 * 1024 && LdsCfg<true>::SMEM <= 160 * 1024, "LDS");
 
 // Address of the 16 bytes lane `lane` copies for weight subtile `sub`
@@ -142,6 +149,11 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int lr = lane & 15, lg = lane >> 4;
+    const int TK = T * K;
+    // Every index read from a metadata slot is range-checked before it forms
+    // an address: a slot read before its copy landed (or never written)
+    // then costs a wrong result, never an access outside the buffers.
+    auto slot_f = [&](int f) { return (f >= 0 && f < TK) ? f : -1; };
     const uint32_t smem_base = lds_addr(smem);
     uint8_t* meta_base = smem + NSTAGE * STAGE;
     const uint32_t meta_lds = smem_base + NSTAGE * STAGE;
@@ -189,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             dma4(a.row_src + rown + 64 * h + lane, slot_lds(k + 1) + 256 * h);
         } else if (role <= 3) {
             const int h = role - 2;
-            const int f = reinterpret_cast<const int32_t*>(slot(k))[64 * h + lane];
+            const int f = slot_f(reinterpret_cast<const int32_t*>(slot(k))[64 * h + lane]);
             dma4(a.topk_w + (f >= 0 ? f : 0), slot_lds(k) + META_W + 256 * h);
         } else {
             dma4(a.mblock_expert + rown / BM, slot_lds(k + 1) + META_E);
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         }
         const int e = __builtin_amdgcn_readfirstlane(
             reinterpret_cast<const int32_t*>(slot(k) + META_E)[lane]);
-        if (e < 0) {
+        if (e < 0 || e >= a.E) {
             i_done = true;
             return;
         }
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         // the block's first row, which always holds a routed slot), so their
         // lanes share cache lines with others; their products land only in
         // padding rows of the accumulator, which are never stored.
-        const int f = reinterpret_cast<const int32_t*>(slot(k))[wave * 16 + lr];
+        const int f = slot_f(reinterpret_cast<const int32_t*>(slot(k))[wave * 16 + lr]);
         const int r = f >= 0 ? row0 + wave * 16 + lr : row0;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
             // same copies).
             const int HS = H / 32, IS = I / 32;
             const int rr = wave < 2 ? wave * 64 + lane : lane;
-            const int fr = reinterpret_cast<const int32_t*>(slot(k))[rr];
+            const int fr = slot_f(reinterpret_cast<const int32_t*>(slot(k))[rr]);
             if (wave < 2 || wave >= 6) {
                 const bool spare = wave >= 6;
                 if constexpr (L1)
@@ -302,20 +314,21 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
         }
         const uint32_t st = smem_base + (i_j % NSTAGE) * STAGE;
         const int kb = i_kb;
+        static_assert(C::A_COPIES == 2 && C::S_COPIES == 1, "the loops below");
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < C::A_COPIES; ++j)
             dma16(a_src[j] + (size_t)kb * 128, st + (wave * 2 + j) * 1024);
         if constexpr (MX) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int q = wave * 2 + j;
+            for (int j = 0; j < C::B_COPIES; ++j) {
+                const int q = wave * C::B_COPIES + j;
                 dma16(weight_src_mx<L1, PK>(a, i_e, i_nt, kb, q, lane), st + A_BYTES + q * 1024);
             }
             dma4(s_src_mx + (size_t)kb * s_stride, st + A_BYTES + B_BYTES + wave * 256);
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int q = wave * 4 + j, sub = q >> 1, half = q & 1;
+            for (int j = 0; j < C::B_COPIES; ++j) {
+                const int q = wave * C::B_COPIES + j, sub = q >> 1, half = q & 1;
                 dma16(weight_src<L1, PK>(a, i_e, i_nt, kb, sub, half, lane), st + A_BYTES + q * 1024);
             }
             dma4(s_src + kb, st + A_BYTES + B_BYTES + wave * 256);
@@ -483,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = wm * 64 + ms * 16 + 4 * lg + i;
-                    const bool valid = m_rs[r] >= 0;
+                    const bool valid = slot_f(m_rs[r]) >= 0;
                     const float w = valid ? m_w[r] : 0.f;
                     const float v0 = (silu(acc[ms][0][i]) *
                                       acc[ms][2][i]) * w;
@@ -515,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = wm * 64 + ms * 16 + 4 * lg + i;
-                    const float w = m_rs[r] >= 0 ? m_w[r] : 0.f;
+                    const float w = slot_f(m_rs[r]) >= 0 ? m_w[r] : 0.f;
                     float m = 0.f;
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
@@ -586,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                 __syncthreads();
                 for (int c = threadIdx.x; c < 64 * 32; c += kThreads) {
                     const int r = c >> 5, col = (c & 31) * 8;
-                    const int f = m_rs[hf * 64 + r];
+                    const int f = slot_f(m_rs[hf * 64 + r]);
                     if (f >= 0) {
                         const int tt = f / K, jslot = f - tt * K;
                         *reinterpret_cast<uint4*>(a.partial + ((size_t)jslot * T + tt) * H +

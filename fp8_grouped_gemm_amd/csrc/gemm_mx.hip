@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void l1_mx(FwdArgs a)
     const int mb = blockIdx.x / NT;
     const int nt = blockIdx.x - mb * NT;
     const int e = a.mblock_expert[mb];
-    if (e < 0)
+    if (e < 0 || e >= a.E)
         return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void l2_mx(FwdArgs a)
     const int mb = blockIdx.x / NT;
     const int nt = blockIdx.x - mb * NT;
     const int e = a.mblock_expert[mb];
-    if (e < 0)
+    if (e < 0 || e >= a.E)
         return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

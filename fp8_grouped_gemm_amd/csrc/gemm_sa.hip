@@ -43,8 +43,12 @@ constexpr int SA_BM = 64;
 constexpr int SA_NS = 3;                    // activation stages
 constexpr int SA_A = SA_BM * 128;           // 8 KiB: 4 m-subtiles x 2 halves x 1 KiB
 constexpr int SA_STAGE = SA_A + 4 * 256;    // + one 256-byte scale copy per wave
-constexpr int SA_WLOADS = 8;                // weight loads per wave and K block
-constexpr int SA_COPIES = 3;                // activation copies per wave and K block
+constexpr int SA_SUBTILES = 4;              // weight subtiles per wave
+constexpr int SA_WLOADS = SA_SUBTILES * 2;  // weight loads per wave and K block (load_wfrag: 2)
+constexpr int SA_ACOPIES = 2;               // activation copies per wave and K block (2 halves)
+constexpr int SA_SCOPIES = 1;               //   + the activation scales
+constexpr int SA_COPIES = SA_ACOPIES + SA_SCOPIES;
+static_assert(SA_A == 4 * SA_ACOPIES * 1024, "four waves copy the A stage");
 
 }  // namespace
 
@@ -58,20 +62,23 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
     const int mb = blockIdx.x / NT;
     const int nt = blockIdx.x - mb * NT;
     const int e = a.mblock_expert[mb];
-    if (e < 0)
+    if (e < 0 || e >= a.E)
         return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int row0 = mb * SA_BM;
     const uint32_t stage_lds = lds_addr(stage_mem);
+    // slot indices are range-checked before they form addresses
+    const int TK = T * K;
+    auto slot_f = [&](int f) { return (f >= 0 && f < TK) ? f : -1; };
 
     // Activation copies: wave w copies m-subtile w (rows row0 + 16 w + lr),
     // both 64-byte halves, and the scale of row 16 w + (lane & 15).  A
     // padding row (row_src < 0) copies a valid row (L1: token 0; L2: the
     // block's first row, which always holds a slot): its products reach
     // only that padding row of the accumulator, which is never stored.
-    const int fr = a.row_src[row0 + 16 * wave + lr];
+    const int fr = slot_f(a.row_src[row0 + 16 * wave + lr]);
     const uint8_t* asrc;
     const float* ssrc;
     if constexpr (L1) {
@@ -131,13 +138,15 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
     int fetched = -1;  // last K block fetched
     auto fetch = [&](Blk& b, int kb) {
         const uint32_t st = stage_lds + (kb % SA_NS) * SA_STAGE;
-        dma16(asrc + (size_t)kb * 128, st + (wave * 2) * 1024);
-        dma16(asrc + (size_t)kb * 128 + 64, st + (wave * 2 + 1) * 1024);
+#pragma unroll
+        for (int j = 0; j < SA_ACOPIES; ++j)
+            dma16(asrc + (size_t)kb * 128 + 64 * j, st + (wave * 2 + j) * 1024);
+        static_assert(SA_SCOPIES == 1, "one scale copy below");
         dma4(ssrc + kb, st + SA_A + wave * 256);
         b.sg = sfg[kb];
         b.su = L1 ? sfu[kb] : b.sg;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < SA_SUBTILES; ++s)
             b.fb[s] = load_wfrag<PK>(bptr[s] + kb * kstride);
         fetched = kb;
     };
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
         for (int ms = 0; ms < 4; ++ms) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int f = a.row_src[row0 + 16 * ms + 4 * lg + i];
+                const int f = slot_f(a.row_src[row0 + 16 * ms + 4 * lg + i]);
                 const float w = f >= 0 ? a.topk_w[f] : 0.f;
                 float m = 0.f;
 #pragma unroll
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
         __syncthreads();
         for (int c = threadIdx.x; c < SA_BM * 8; c += 256) {
             const int r = c >> 3, col = (c & 7) * 16;
-            if (a.row_src[row0 + r] >= 0)
+            if (slot_f(a.row_src[row0 + r]) >= 0)
                 *reinterpret_cast<uint4*>(a.h + (size_t)(row0 + r) * I + nt * 128 + col) =
                     *reinterpret_cast<const uint4*>(&qt[r][col]);
         }
@@ -251,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
             __syncthreads();
             for (int c = threadIdx.x; c < (SA_BM / 2) * 32; c += 256) {
                 const int r = c >> 5, col = (c & 31) * 8;
-                const int f = a.row_src[row0 + 32 * hf + r];
+                const int f = slot_f(a.row_src[row0 + 32 * hf + r]);
                 if (f >= 0) {
                     const int t = f / K, j = f - t * K;
                     const uint4 v = *reinterpret_cast<const uint4*>(&ot[r][col]);  // 8 bf16
@@ -275,7 +284,7 @@ namespace {
 constexpr int SX_NS = 3;
 constexpr int SX_A = 64 * 128;
 constexpr int SX_STAGE = SX_A + 4 * 256;
-constexpr int SX_WLOADS = 8;  // 4 fragment loads + 4 scale-byte loads per wave and block
+constexpr int SX_WLOADS = 2 * SA_SUBTILES;  // per subtile a fragment and a scale byte
 }  // namespace
 
 template <bool L1, bool PK>
@@ -289,17 +298,19 @@ __global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
     const int mb = blockIdx.x / NT;
     const int nt = blockIdx.x - mb * NT;
     const int e = a.mblock_expert[mb];
-    if (e < 0)
+    if (e < 0 || e >= a.E)
         return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int row0 = mb * 64;
     const uint32_t stage_lds = lds_addr(stage_mem);
+    const int TK = T * K;
+    auto slot_f = [&](int f) { return (f >= 0 && f < TK) ? f : -1; };
 
     // Activation copies as in gemm_sa; the scale copy moves the row's 4
     // codes of the block (one 4-byte word).
-    const int fr = a.row_src[row0 + 16 * wave + lr];
+    const int fr = slot_f(a.row_src[row0 + 16 * wave + lr]);
     const uint8_t* asrc;
     const uint8_t* ssrc;
     if constexpr (L1) {
@@ -362,11 +373,12 @@ __global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
     int fetched = -1;
     auto fetch = [&](Blk& b, int kb) {
         const uint32_t st = stage_lds + (kb % SX_NS) * SX_STAGE;
-        dma16(asrc + (size_t)kb * 128, st + (wave * 2) * 1024);
-        dma16(asrc + (size_t)kb * 128 + 64, st + (wave * 2 + 1) * 1024);
+#pragma unroll
+        for (int j = 0; j < SA_ACOPIES; ++j)
+            dma16(asrc + (size_t)kb * 128 + 64 * j, st + (wave * 2 + j) * 1024);
         dma4(ssrc + (size_t)kb * 4, st + SX_A + wave * 256);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < SA_SUBTILES; ++s) {
             b.fb[s] = *reinterpret_cast<const uint4*>(wl + woff[s] + (size_t)kb * wk);
             b.sb[s] = sl[soff[s] + (size_t)kb * sk];
         }
@@ -408,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * ms + 4 * lg + i;
-                const int f = a.row_src[row0 + r];
+                const int f = slot_f(a.row_src[row0 + r]);
                 const float w = f >= 0 ? a.topk_w[f] : 0.f;
                 const float v0 = (silu(acc[ms][0][i]) *
                                   acc[ms][2][i]) * w;
@@ -425,7 +437,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
         __syncthreads();
         for (int c = threadIdx.x; c < 64 * 8; c += 256) {
             const int r = c >> 3, col = (c & 7) * 16;
-            if (a.row_src[row0 + r] >= 0)
+            if (slot_f(a.row_src[row0 + r]) >= 0)
                 *reinterpret_cast<uint4*>(a.h + (size_t)(row0 + r) * I + nt * 128 + col) =
                     *reinterpret_cast<const uint4*>(&qt[r][col]);
         }
@@ -444,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa_mx(FwdArgs a)
             __syncthreads();
             for (int c = threadIdx.x; c < 32 * 32; c += 256) {
                 const int r = c >> 5, col = (c & 31) * 8;
-                const int f = a.row_src[row0 + 32 * hf + r];
+                const int f = slot_f(a.row_src[row0 + 32 * hf + r]);
                 if (f >= 0) {
                     const int t = f / K, j = f - t * K;
                     const uint4 v = *reinterpret_cast<const uint4*>(&ot[r][col]);  // 8 bf16

@@ -8,6 +8,7 @@
 
 #include "moe_peaks.h"
 #include "moe_device.h"
+#include "moe_direct.h"
 
 namespace {
 
@@ -82,6 +83,41 @@ __global__ void __launch_bounds__(256) mfma_fp8_loop(int iters, float* __restric
     out[blockIdx.x * 256 + threadIdx.x] = (t.x + t.y) + (t.z + t.w);
 }
 
+// One 16 x 16 x 128 product per wave, with the operands loaded exactly as
+// the GEMM kernels load them: lane l = 16 g + r reads bytes [16 g, 16 g + 16)
+// and [64 + 16 g, 64 + 16 g + 16) of A row r; for e4m3 B the same bytes of
+// B row (output column) r; for e2m1 B the 16 bytes [16 g, 16 g + 16) of its
+// packed row (K values 32 g .. 32 g + 31), with the UE8M0 code of K block g
+// of the row / column as each operand's scale.  Lane l writes column r,
+// rows 4 g + i of its tile.  Waves past the last tile do nothing.
+template <bool MX>
+__global__ void __launch_bounds__(256) mfma_block_probe(const uint8_t* __restrict__ A,
+                                                        const uint8_t* __restrict__ B,
+                                                        const uint8_t* __restrict__ SA,
+                                                        const uint8_t* __restrict__ SB,
+                                                        int n_tiles, float* __restrict__ out)
+{
+    const int tile = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (tile >= n_tiles)
+        return;
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const size_t row = (size_t)tile * 16 + r;
+    const moe::Frag2 fa = moe::load_frag(A + row * 128 + 16 * g);
+    const moe::v8i av = moe::pack_frag(fa.lo, fa.hi);
+    moe::v4f d;
+    if constexpr (MX) {
+        const uint4 fb = *reinterpret_cast<const uint4*>(B + row * 64 + 16 * g);
+        d = moe::mfma_16x16x128_e4m3_e2m1(av, moe::e2m1_operand(fb), moe::v4f{0.f, 0.f, 0.f, 0.f},
+                                          SA[row * 4 + g], SB[row * 4 + g]);
+    } else {
+        const moe::Frag2 fb = moe::load_frag(B + row * 128 + 16 * g);
+        d = moe::mfma_16x16x128_e4m3(av, moe::pack_frag(fb.lo, fb.hi), moe::v4f{0.f, 0.f, 0.f, 0.f});
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        out[((size_t)tile * 16 + 4 * g + i) * 16 + r] = d[i];
+}
+
 int device_is_gfx950()
 {
     int dev = 0;
@@ -132,5 +168,27 @@ extern "C" int moe_peak_mfma_fp8(int32_t blocks, int32_t iters, float* out, void
         return dev;
     hipLaunchKernelGGL(mfma_fp8_loop, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                        iters, out);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" int moe_probe_mfma_block(int32_t mode, int32_t n_tiles, const uint8_t* a,
+                                    const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                                    float* out, void* stream)
+{
+    if (!a || !b || !out || n_tiles < 1 || n_tiles > (1 << 20) ||
+        (mode != MOE_PROBE_E4M3 && mode != MOE_PROBE_E4M3_E2M1) ||
+        (reinterpret_cast<uintptr_t>(a) & 15) || (reinterpret_cast<uintptr_t>(b) & 15))
+        return MOE_ERR_INVALID_ARG;
+    if (mode == MOE_PROBE_E4M3_E2M1 && (!sa || !sb))
+        return MOE_ERR_INVALID_ARG;
+    const int dev = device_is_gfx950();
+    if (dev != MOE_OK)
+        return dev;
+    const dim3 grid((unsigned)((n_tiles + 3) / 4));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mode == MOE_PROBE_E4M3_E2M1)
+        hipLaunchKernelGGL(mfma_block_probe<true>, grid, dim3(256), 0, s, a, b, sa, sb, n_tiles, out);
+    else
+        hipLaunchKernelGGL(mfma_block_probe<false>, grid, dim3(256), 0, s, a, b, sa, sb, n_tiles, out);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -11,7 +11,9 @@ from .build import PEAKS_LIB
 
 MOE_PEAK_READ_PLAIN = 0
 MOE_PEAK_READ_NONTEMPORAL = 1
-EXPORTED_SYMBOLS = ("moe_peak_stream_read", "moe_peak_mfma_fp8")
+MOE_PROBE_E4M3 = 0
+MOE_PROBE_E4M3_E2M1 = 1
+EXPORTED_SYMBOLS = ("moe_peak_stream_read", "moe_peak_mfma_fp8", "moe_probe_mfma_block")
 MFMA_FLOP_PER_WAVE_ROUND = 8 * 2 * 16 * 16 * 128
 
 _lib = None
@@ -27,6 +29,7 @@ def lib():
         vp, i32 = ctypes.c_void_p, ctypes.c_int32
         L.moe_peak_stream_read.argtypes = [vp, ctypes.c_size_t, i32, i32, i32, vp, vp]
         L.moe_peak_mfma_fp8.argtypes = [i32, i32, vp, vp]
+        L.moe_probe_mfma_block.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp]
         for name in EXPORTED_SYMBOLS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -56,3 +59,13 @@ def mfma_fp8(blocks, iters, out, stream=None):
 
 def mfma_flop(blocks, iters):
     return blocks * 4 * iters * MFMA_FLOP_PER_WAVE_ROUND
+
+
+def probe_mfma_block(mode, a, b, out, sa=None, sb=None, stream=None):
+    """One 16x16x128 MFMA per tile (moe_probe_mfma_block); a, b, sa, sb, out
+    device tensors shaped as the header documents."""
+    n_tiles = a.shape[0]
+    rc = lib().moe_probe_mfma_block(mode, n_tiles, _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
+                                    _ptr(out), _stream(stream))
+    if rc != MOE_OK:
+        raise MoEError(rc, "moe_probe_mfma_block")

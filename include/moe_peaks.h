@@ -53,6 +53,29 @@ int moe_peak_stream_read(const void* buf, size_t bytes, int32_t blocks, int32_t 
  * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_NOT_GFX950, MOE_ERR_HIP. */
 int moe_peak_mfma_fp8(int32_t blocks, int32_t iters, float* out, void* stream);
 
+/* Probe modes of moe_probe_mfma_block. */
+#define MOE_PROBE_E4M3 0       /* v_mfma_f32_16x16x128_f8f6f4, e4m3 x e4m3 */
+#define MOE_PROBE_E4M3_E2M1 1  /* the block-scaled form, e4m3 x e2m1, UE8M0 per 32 */
+
+/* Precision probe of the GEMMs' matrix instruction: for each of n_tiles
+ * tiles, D = A B^T over one 128-wide K block with C = 0, the operands loaded
+ * from memory exactly as the GEMM kernels load them.  The MoE parity tests
+ * compare D with the exact dot products to measure how far the hardware's
+ * accumulation inside one instruction is from the exact sum (the error the
+ * oracle's exact block sums do not have).
+ *   mode MOE_PROBE_E4M3:      a [n_tiles,16,128] e4m3, b [n_tiles,16,128] e4m3
+ *                             (row n of b = output column n); sa, sb unused
+ *   mode MOE_PROBE_E4M3_E2M1: a as above, b [n_tiles,16,64] packed e2m1
+ *                             (element k in byte k/2, even k in the low
+ *                             nibble), sa / sb [n_tiles,16,4] UE8M0 codes of
+ *                             the four 32-wide K blocks of each row / column
+ *   out float [n_tiles,16,16], out[t][m][n] = sum_k A[t][m][k] B[t][n][k]
+ *                             (times the block scales), written.
+ * a and b 16-byte aligned; 1 <= n_tiles <= 2^20.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_NOT_GFX950, MOE_ERR_HIP. */
+int moe_probe_mfma_block(int32_t mode, int32_t n_tiles, const uint8_t* a, const uint8_t* b,
+                         const uint8_t* sa, const uint8_t* sb, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

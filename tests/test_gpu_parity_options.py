@@ -1,16 +1,17 @@
 """GPU parity of the recipe options against the oracle: per-64 intermediate
 scales (dual-half L2), power-of-two requant scales, the activation clamp
-(both recipes, direct and LDS tiles, split-K, single launch), and the
-activation quantisation entry point (codes and scales bit-exact: both sides
-take every rounding decision in f32 the same way)."""
+(both recipes, direct and LDS tiles, split-K, single launch) -- each through
+parity_util.verify with the oracle's matching option -- and the activation
+quantisation entry point (codes and scales bit-exact: both sides take every
+rounding decision in f32 the same way)."""
 import numpy as np
 import pytest
 import torch
 
 import fp8_grouped_gemm_amd as moe
 import oracle
-from fp8_grouped_gemm_amd import workload as wl
-from parity_util import check_y, say, small_case
+import workload as wl
+from parity_util import host_copy_for_oracle, host_dict, say, small_case, verify
 
 pytestmark = pytest.mark.gpu
 
@@ -28,38 +29,13 @@ def run_opts(dev, tile_m=0, flags=0, gran=0, clamp=0.0, mx=False):
     return y, r
 
 
-def oracle_opts(host, flags=0, clamp=0.0, want=(), tokens=None, mx=False):
-    fn = oracle.moe_forward_mx if mx else oracle.moe_forward
-    return fn(host["x"], host["x_sf"], host["idx"], host["w"], host["w1"], host["w1_sf"],
-              host["w2"], host["w2_sf"], flags=flags, clamp=clamp, want=want, tokens=tokens)
-
-
-def check_h(runner, host, ref, T, K, gran, what):
-    # dequantised h per routed slot within the bound of the FP8 parity tests;
-    # the scales agree to ~1e-3 (raw) or exactly up to one power of two
-    DEC = np.array([oracle.e4m3_decode(c) for c in range(256)])
-    src_row = runner.view("src_row", T).cpu().numpy()
-    h = runner.view("h", T).cpu().numpy()
-    h_sf = runner.view("h_sf", T).cpu().numpy()
-    assert h_sf.shape[1] == h.shape[1] // gran
-    for f in range(T * K):
-        r = src_row[f]
-        if r < 0:
-            continue
-        g = DEC[h[r]].reshape(-1, gran) * h_sf[r][:, None]
-        o = DEC[ref["h"][f]].reshape(-1, gran) * ref["h_sf"][f][:, None]
-        assert np.linalg.norm(g - o) <= 2e-2 * np.linalg.norm(o) + 1e-30, (what, f)
-
-
 @pytest.mark.parametrize("tile_m", [16, 32, 64])
 def test_per64_scales_all_direct_tiles(tile_m):
     host, dev = small_case(45, 512, 384, 12, 3, 501, mask={(0, 1): -1, (7, 2): 99}, skew=True)
     y, r = run_opts(dev, tile_m=tile_m, gran=64)
     info = moe.moe_plan_info(r.plan, 45)
     assert info["act_sf_gran"] == 64 and info["l2_group_tiles"] == 1
-    ref = oracle_opts(host, flags=oracle.ORC_SF_GRAN64, want=("h",))
-    check_y(y.cpu().numpy(), ref["y"], what=f"per-64 tile {tile_m}")
-    check_h(r, host, ref, 45, 3, 64, f"per-64 tile {tile_m}")
+    verify(y, r, host, f"per-64 tile {tile_m}", oflags=oracle.ORC_SF_GRAN64)
     # against the per-128 recipe: a different (still accurate) result
     y128, _ = run_opts(dev, tile_m=tile_m)
     assert not torch.equal(y, y128)
@@ -71,7 +47,7 @@ def test_per64_rule_and_split_k():
     host, dev = small_case(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, wl.default_seed(cfg))
     y, r = run_opts(dev, gran=-1)
     assert moe.moe_plan_info(r.plan, cfg.T)["act_sf_gran"] == 64
-    check_y(y.cpu().numpy(), oracle_opts(host, flags=oracle.ORC_SF_GRAN64)["y"], what="tiny rule")
+    verify(y, r, host, "tiny rule", oflags=oracle.ORC_SF_GRAN64)
     # one and two tokens at the flash shape: L1 split-K with per-64 scales
     base = wl.CONFIGS["flash_decode"]
     full = wl.make_inputs(wl.custom_config(2, base.H, base.I, base.E, base.K),
@@ -82,15 +58,8 @@ def test_per64_rule_and_split_k():
             inp[k] = full[k][:T].contiguous()
         y, r = run_opts(inp, gran=64)
         assert moe.moe_plan_info(r.plan, T)["l1_split"] > 1
-        E = base.E
-        idx = inp["topk_idx"].cpu().numpy()
-        need = sorted({int(e) for e in idx.reshape(-1)})
-        sel = lambda t: [t[e].cpu().numpy() if e in need else None for e in range(E)]
-        h = dict(x=inp["x"].cpu().numpy(), x_sf=inp["x_sf"].cpu().numpy(), idx=idx,
-                 w=inp["topk_w"].cpu().numpy(), w1=sel(inp["w1"]), w1_sf=sel(inp["w1_sf"]),
-                 w2=sel(inp["w2"]), w2_sf=sel(inp["w2_sf"]))
-        check_y(y.cpu().numpy(), oracle_opts(h, flags=oracle.ORC_SF_GRAN64)["y"],
-                per_token_tol=1e-2, what=f"per-64 split-K T={T}")
+        h = host_copy_for_oracle(inp, list(range(T)))
+        verify(y, r, h, f"per-64 split-K T={T}", oflags=oracle.ORC_SF_GRAN64)
     del full
 
 
@@ -98,9 +67,7 @@ def test_per64_rule_and_split_k():
 def test_pow2_scales(tile_m):
     host, dev = small_case(160, 512, 384, 6, 3, 502, mask={(3, 0): -1})
     y, r = run_opts(dev, tile_m=tile_m, flags=moe.MOE_FLAG_POW2_SCALE)
-    ref = oracle_opts(host, flags=oracle.ORC_POW2_SCALE, want=("h",))
-    check_y(y.cpu().numpy(), ref["y"], what=f"pow2 tile {tile_m}")
-    check_h(r, host, ref, 160, 3, 128, f"pow2 tile {tile_m}")
+    verify(y, r, host, f"pow2 tile {tile_m}", oflags=oracle.ORC_POW2_SCALE)
     sf = r.view("h_sf", 160).cpu().numpy()
     used = sf[r.view("src_row", 160).cpu().numpy()[r.view("src_row", 160).cpu().numpy() >= 0]]
     m, _ = np.frexp(used.astype(np.float64))
@@ -112,8 +79,7 @@ def test_activation_clamp_fp8(tile_m):
     host, dev = small_case(160, 512, 384, 6, 3, 503)
     clamp = 0.05  # well inside the range of gate/up here: the clamp is active
     y, r = run_opts(dev, tile_m=tile_m, clamp=clamp)
-    ref = oracle_opts(host, clamp=clamp)
-    check_y(y.cpu().numpy(), ref["y"], what=f"clamp tile {tile_m}")
+    verify(y, r, host, f"clamp tile {tile_m}", clamp=clamp)
     y0, _ = run_opts(dev, tile_m=tile_m)
     assert not torch.equal(y, y0)
 
@@ -122,16 +88,10 @@ def test_activation_clamp_fp8(tile_m):
 def test_activation_clamp_mxfp4(tile_m):
     cfg = wl.custom_config(160, 512, 384, 6, 3)
     inp = wl.make_inputs_mx(cfg, 504, "cpu")
-    E = cfg.E
-    host = dict(x=inp["x"].numpy(), x_sf=inp["x_sf"].numpy(), idx=inp["topk_idx"].numpy(),
-                w=inp["topk_w"].numpy(), w1=[inp["w1"][e].numpy() for e in range(E)],
-                w1_sf=[inp["w1_sf"][e].numpy() for e in range(E)],
-                w2=[inp["w2"][e].numpy() for e in range(E)],
-                w2_sf=[inp["w2_sf"][e].numpy() for e in range(E)])
+    host = host_dict(inp)
     dev = {k: v.cuda() for k, v in inp.items()}
-    y, _ = run_opts(dev, tile_m=tile_m, clamp=0.05, mx=True)
-    check_y(y.cpu().numpy(), oracle_opts(host, clamp=0.05, mx=True)["y"],
-            what=f"MX clamp tile {tile_m}")
+    y, r = run_opts(dev, tile_m=tile_m, clamp=0.05, mx=True)
+    verify(y, r, host, f"MX clamp tile {tile_m}", clamp=0.05)
 
 
 def test_single_launch_with_pow2_and_clamp_matches_split_launches():
@@ -142,8 +102,7 @@ def test_single_launch_with_pow2_and_clamp_matches_split_launches():
                          clamp=kw["clamp"])
     assert moe.moe_plan_info(r2.plan, 300)["single_launch"] == 1
     assert torch.equal(y_split, y_one)
-    check_y(y_one.cpu().numpy(),
-            oracle_opts(host, flags=oracle.ORC_POW2_SCALE, clamp=0.04)["y"], what="single pow2")
+    verify(y_one, r2, host, "single launch pow2 + clamp", oflags=oracle.ORC_POW2_SCALE, clamp=0.04)
 
 
 # ---------------------------------------------------- activation quantisation

@@ -2,13 +2,19 @@
 
 One step = one moe_forward (planner, L1 GEMM + SwiGLU/requant epilogue, L2
 GEMM, combine) over one batch of seeded synthetic inputs already resident
-in HBM.  Prints ONE JSON line.  The default workload is the DeepSeek
-"Flash"-shaped decode layer: T=128 tokens, hidden 4096, intermediate 2048,
-256 experts all resident, top-6, uniform routing.
+in HBM.  Prints ONE JSON line.  The headline workload is the largest
+single-GPU configuration, the DeepSeek "Pro"-shaped prefill layer: T=8192
+tokens, hidden 7168, intermediate 3072, 384 experts all resident (25 GB of
+e4m3 weights), top-6, uniform routing.  The same line carries one entry per
+further workload ("workloads": flash_decode, flash_prefill, skewed), each
+with its own timing, rooflines and CPU-oracle baseline, and the pages'
+8xH100 EP8 per-layer figures as context ("pages_context"; another machine
+and a multi-GPU layer with communication, so vs_baseline stays null).
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--tokens T] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--tokens T]
+                  [--extra-workloads a,b,c | --no-extra] [--no-cpu-baseline]
                   [--flush MIB] [--no-peaks] [--launch auto|single|split]
-                  [--weights packed|row_major]
+                  [--weights packed|row_major] [--recipe fp8|mxfp4]
 
 Beside the timed steps it measures, unless told not to, (a) the same call
 with caches flushed before each call (3 observations of K calls; median of
@@ -78,18 +84,81 @@ def kernel_source_digest(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg, weights):
-    """HBM bytes per launch of the L1 step from the committed rocprofv3
-    counter summary (FETCH_SIZE / WRITE_SIZE scaled by a plain copy's
-    readings), or None when no summary matches this workload or the kernel
-    sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "flash_decode_l1_traffic.json")
-    if cfg.name != "flash_decode" or weights != "packed" or not os.path.exists(path):
+def measured_traffic(cfg, weights, recipe, dom):
+    """HBM bytes per launch of the dominant step from the committed rocprofv3
+    counter summary profiles/<workload>_<step>_traffic.json (FETCH_SIZE /
+    WRITE_SIZE scaled by a plain copy's readings), or None when no summary
+    matches this workload, layout and recipe, or the kernel sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{cfg.name}_{dom}_traffic.json")
+    if weights != "packed" or recipe != "fp8" or not os.path.exists(path):
         return None
     d = json.load(open(path))
     if kernel_source_digest(d["source_files"]) != d["source_code_digest"]:
         return None
-    return d["l1_step_traffic_bytes"]
+    return d["step_traffic_bytes"]
+
+
+def _counter_means(d, counter):
+    """Mean value per kernel name of one counter over the dispatches in the
+    rocprofv3 CSV output under directory d."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def write_traffic_summary(args):
+    """profiles/<workload>_<step>_traffic.json from counter runs: per kernel
+    of the step the mean FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by
+    what the same counters read for a plain 1 GiB device copy (bytes per
+    KiB of counter), summed over the step's kernels."""
+    fetch_dir, write_dir, cf_dir, cw_dir = args.traffic_summary
+    match = [m for m in args.kernel_match.split(",") if m]
+    cal_bytes = 1 << 30
+
+    def copy_kib(d, counter):
+        v = {k: x for k, x in _counter_means(d, counter).items() if "moe::" not in k}
+        return max(v.values())  # the 1 GiB copy is the largest non-library dispatch
+
+    ff = cal_bytes / (copy_kib(cf_dir, "FETCH_SIZE") * 1024)
+    wf = cal_bytes / (copy_kib(cw_dir, "WRITE_SIZE") * 1024)
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    kernels = {k: {"fetch_size_kib": fetch[k], "write_size_kib": write.get(k, 0.0)}
+               for k in fetch if any(m in k for m in match)}
+    if not kernels:
+        raise SystemExit(f"no kernel matching {match} in {fetch_dir}")
+    total = sum((v["fetch_size_kib"] * ff + v["write_size_kib"] * wf) * 1024
+                for v in kernels.values())
+    sources = [x for x in args.sources.split(",") if x]
+    out = {
+        "what": f"HBM traffic per launch of the {args.workload} {args.step.upper()} step, "
+                f"{args.weights} weights, {args.recipe}",
+        "command_fetch": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE "
+                         "--kernel-include-regex \"moe::\" --output-format csv -d OUT -o out -- "
+                         "python3 $GRAFT_REPO_ROOT/bench.py "
+                         f"--workload {args.workload} --steps 2 --warmup 1 --no-extra "
+                         "--no-cpu-baseline --no-peaks --flush 0",
+        "command_write": "the same with --pmc WRITE_SIZE",
+        "command_calibration": "the same counters without the kernel filter over: python3 "
+                               "$GRAFT_REPO_ROOT/bench.py --copy-calibration 1024",
+        "command_summary": "python3 bench.py --traffic-summary FETCH_OUT WRITE_OUT COPY_FETCH_OUT "
+                           f"COPY_WRITE_OUT --workload {args.workload} --step {args.step} "
+                           f"--kernel-match '{args.kernel_match}' --sources {args.sources}",
+        "copy_calibration": {"bytes_per_dispatch": cal_bytes, "fetch_factor": ff,
+                             "write_factor": wf},
+        "kernels": kernels,
+        "source_files": sources,
+        "source_code_digest": kernel_source_digest(sources),
+        "step_traffic_bytes": total,
+    }
+    path = os.path.join(ROOT, "profiles", f"{args.workload}_{args.step}_traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps({"written": path, "step_traffic_bytes": total}), flush=True)
 
 
 def time_oracle_sample(inp, cfg, n_tokens, seed, mx=False, threads=None):
@@ -168,19 +237,47 @@ def measure_peaks(torch, dev, stream, read_gib=4, reps=3):
     }
 
 
+# The pages' own per-layer figures (DeepGEMM PR #440 "Performance": fused
+# MegaMoE vs the split #383 path, bench_kineto device time, 8xH100 under
+# 8-way expert parallelism, per tokens/rank).  Another machine, and a layer
+# that includes NVLink dispatch and combine: context, not a target.
+PAGES_CONTEXT = {
+    "source": "DeepGEMM PR #440 'Performance' tables: 8xH100 EP8, fused #440 / split #383, "
+              "us per layer per rank, includes NVLink dispatch/combine",
+    "flash_fused_us": {"64": 351, "128": 353, "256": 388, "512": 423, "2048": 757, "8192": 2556},
+    "flash_split_us": {"64": 368, "128": 363, "256": 417, "512": 545, "2048": 1174, "8192": 3702},
+    "pro_fused_us": {"64": 1123, "128": 1134, "256": 1182, "512": 1237, "2048": 1978,
+                     "8192": 6477},
+    "pro_split_us": {"64": 1184, "128": 1173, "256": 1237, "512": 1291, "2048": 2809,
+                     "8192": 8601},
+}
+
+# Tokens of each workload the CPU oracle computes for its baseline: the
+# whole workload where that is under ~15 s on the GPU machine's 16 host threads,
+# else a seeded sample of ~10-15 s (pro prefill: 512 tokens took 4.8 s).
+CPU_SAMPLE_TOKENS = {"tiny": 64, "flash_decode": 128, "flash_decode_ep8": 128,
+                     "flash_prefill": 2048, "skewed": 2048, "pro_prefill": 1536}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="flash_decode")
+    ap.add_argument("--workload", default="pro_prefill")
+    ap.add_argument("--extra-workloads", default="flash_decode,flash_prefill,skewed",
+                    help="comma-separated workloads timed after the headline one, each an "
+                         "entry of the line's 'workloads' object")
+    ap.add_argument("--no-extra", action="store_true", help="time the headline workload only")
+    ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the workload's token count (same shapes and routing recipe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=4, metavar="N",
                     help="record the per-stage HIP events on every N-th timed step (1: all)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=128)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens in the oracle sample (0 = the workload's default)")
     ap.add_argument("--cpu-sample-tokens-1t", type=int, default=2,
                     help="tokens in the one-thread oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -193,6 +290,17 @@ def main():
                          "medians and the range (0 = skip)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the streaming-read and FP8 MFMA ceilings")
+    ap.add_argument("--traffic-summary", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="only summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output "
+                         "directories (of this workload, and of --copy-calibration 1024) into "
+                         "profiles/<workload>_<step>_traffic.json and exit; needs --step, "
+                         "--kernel-match and --sources")
+    ap.add_argument("--step", choices=("l1", "l2"), default="l1")
+    ap.add_argument("--kernel-match", default="",
+                    help="substrings (comma-separated) of the step's kernel names in the CSVs")
+    ap.add_argument("--sources", default="",
+                    help="comma-separated source files whose code the counters belong to")
     ap.add_argument("--peaks-only", action="store_true",
                     help="only measure the streaming-read and FP8 MFMA ceilings, print them "
                          "as one JSON line and exit")
@@ -230,6 +338,10 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_dispatch": n}), flush=True)
         return
 
+    if args.traffic_summary:
+        write_traffic_summary(args)
+        return
+
     if args.peaks_only:
         dev = torch.device("cuda:0")
         torch.cuda.set_device(dev)
@@ -238,12 +350,56 @@ def main():
         return
 
     cfg = wl.CONFIGS[args.workload]
-    seed = wl.default_seed(cfg) if args.seed is None else args.seed
     if args.tokens is not None:
         cfg = wl.custom_config(args.tokens, cfg.H, cfg.I, cfg.E, cfg.K, cfg.skew,
                                name=f"{cfg.name}_T{args.tokens}")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    seed = args.seed if args.seed is not None else wl.default_seed(wl.CONFIGS[args.workload])
+    line = run_workload(args, cfg, seed, args.steps, args.warmup, args.flush, cpu_1t=True)
+    if not args.no_peaks:
+        print("[bench] measuring the read and MFMA ceilings", file=sys.stderr, flush=True)
+        pk = measure_peaks(torch, dev, torch.cuda.current_stream())
+        line["achievable"] = pk
+        add_achievable(line, pk)
+    extras = [] if args.no_extra else [w for w in args.extra_workloads.split(",") if w]
+    if extras:
+        line["workloads"] = {}
+    for name in extras:
+        e = run_workload(args, wl.CONFIGS[name], wl.default_seed(wl.CONFIGS[name]),
+                         args.extra_steps, max(2, args.warmup // 2), 0, cpu_1t=False)
+        if "achievable" in line:
+            add_achievable(e, line["achievable"])
+        keep = ("value", "unit", "steps", "config", "tflops", "hbm_gbs_algorithmic",
+                "pct_hbm_roof", "pct_mfma_roof", "pct_binding_roof", "binding_roof", "roof_us",
+                "kernel_us", "algorithmic_bytes", "active_experts", "routed_rows", "roofline",
+                "pct_hbm_achievable", "pct_mfma_achievable", "cpu_baseline")
+        line["workloads"][name] = {k: e[k] for k in keep if k in e}
+    line["pages_context"] = PAGES_CONTEXT
+    print(json.dumps(line), flush=True)
+
+
+def add_achievable(line, pk):
+    """Roofline fractions against the measured ceilings as well."""
+    rl = line["roofline"]
+    rl["achievable_peak"] = pk["hbm_read_gbs"]
+    rl["frac_of_achievable"] = round(rl["achieved"] / pk["hbm_read_gbs"], 4)
+    us = line["value"]
+    line["pct_hbm_achievable"] = round(100 * line["_t_bytes"] / (pk["hbm_read_gbs"] * 1e3) / us, 2)
+    line["pct_mfma_achievable"] = round(100 * line["_t_flops"] / (pk["mfma_fp8_tflops"] * 1e6) / us,
+                                        2)
+    del line["_t_bytes"], line["_t_flops"]
+
+
+def run_workload(args, cfg, seed, steps, warmup, flush, cpu_1t):
+    """Time `steps` forwards of workload cfg (after `warmup`), return its
+    JSON object (headline fields, stage times, rooflines, cold-cache times
+    when flush > 0, CPU-oracle baseline unless disabled)."""
+    import torch
+
+    import fp8_grouped_gemm_amd as moe
+    import workload as wl
+    dev = torch.device("cuda:0")
     print(f"[bench] drawing {cfg} seed {seed} on the GPU", file=sys.stderr, flush=True)
     mx = args.recipe == "mxfp4"
     if cfg.H % 256:
@@ -275,17 +431,17 @@ def main():
     fwd_args = (inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_w"], w1, w1_sf,
                 w2, w2_sf, y, runner.workspace)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         forward(runner.plan, cfg.T, *fwd_args, stream=stream)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] warmup done, timing {steps} steps", file=sys.stderr, flush=True)
 
     # Stage events go on every `--event-every`-th timed step only: each event
     # recorded between two launches costs the step ~3.7 us (measured: 924 vs
     # 943 us per flash-decode layer with events on no step / every step), so
     # the other steps run as a caller would run them.
     every_n = max(1, args.event_every)
-    event_steps = [k for k in range(args.steps) if k % every_n == 0]
+    event_steps = [k for k in range(steps) if k % every_n == 0]
     evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for k in event_steps}
     # torch creates the HIP event on first record(); do that once so the
     # library can record the same events between its launches.
@@ -297,7 +453,7 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for k in range(args.steps):
+    for k in range(steps):
         if k in evs:
             forward_timed(runner.plan, cfg.T, *fwd_args, stream, evs[k])
         else:
@@ -312,7 +468,7 @@ def main():
         for i, n in enumerate(names):
             per[n].append(evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3)
     avg = {n: sum(v) / len(v) for n, v in per.items()}
-    us_per_layer = total_ms * 1e3 / args.steps
+    us_per_layer = total_ms * 1e3 / steps
 
     alg = algorithmic_bytes(cfg, inp["topk_idx"], mx)
     flops = 2.0 * alg["rows"] * 3 * cfg.H * cfg.I
@@ -341,9 +497,9 @@ def main():
         "value": round(us_per_layer, 2),
         "unit": "us",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(total_ms / args.steps, 4),
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(total_ms / steps, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -362,6 +518,8 @@ def main():
         "pct_hbm_roof": round(100 * t_hbm / us_per_layer, 2),
         "pct_mfma_roof": round(100 * t_mfma / us_per_layer, 2),
         "pct_binding_roof": round(100 * max(t_hbm, t_mfma) / us_per_layer, 2),
+        "binding_roof": "hbm" if t_hbm >= t_mfma else "mfma",
+        "roof_us": {"hbm": round(t_hbm, 1), "mfma": round(t_mfma, 1)},
         "kernel_us": {n: round(v, 2) for n, v in avg.items()},
         "event_steps": len(event_steps),
         "algorithmic_bytes": {n: alg[n] for n in names},
@@ -375,21 +533,21 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (measured_traffic(cfg, args.weights)
-                        if dom == "l1" and not single and not mx else None),
+            "traffic": (None if single else
+                        measured_traffic(cfg, args.weights, args.recipe, dom)),
             "algorithmic_bytes": dom_bytes,
         },
         "cpu_baseline": None,
     }
-    if args.flush:
+    if flush:
         print("[bench] cold-cache observations", file=sys.stderr, flush=True)
-        scratch = torch.empty(args.flush << 20, dtype=torch.uint8, device=dev)
+        scratch = torch.empty(flush << 20, dtype=torch.uint8, device=dev)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         medians, every = [], []
         for _ in range(3):
             obs = []
-            for _ in range(args.steps):
+            for _ in range(steps):
                 scratch.fill_(1)
                 e0.record(stream)
                 forward(runner.plan, cfg.T, *fwd_args, stream=stream)
@@ -400,34 +558,29 @@ def main():
             medians.append(obs[len(obs) // 2])
             every += obs
         medians.sort()
-        line["cold"] = {"flush_mib": args.flush, "median_us": round(medians[1], 2),
+        line["cold"] = {"flush_mib": flush, "median_us": round(medians[1], 2),
                         "observation_medians_us": [round(m, 2) for m in medians],
                         "min_us": round(min(every), 2), "max_us": round(max(every), 2),
-                        "steps_per_observation": args.steps}
+                        "steps_per_observation": steps}
         del scratch
-    if not args.no_peaks:
-        print("[bench] measuring the read and MFMA ceilings", file=sys.stderr, flush=True)
-        pk = measure_peaks(torch, dev, stream)
-        line["achievable"] = pk
-        rl = line["roofline"]
-        rl["achievable_peak"] = pk["hbm_read_gbs"]
-        rl["frac_of_achievable"] = round(rl["achieved"] / pk["hbm_read_gbs"], 4)
-        t_hbm_meas = bytes_total / (pk["hbm_read_gbs"] * 1e9) * 1e6
-        t_mfma_meas = flops / (pk["mfma_fp8_tflops"] * 1e12) * 1e6
-        line["pct_hbm_achievable"] = round(100 * t_hbm_meas / us_per_layer, 2)
-        line["pct_mfma_achievable"] = round(100 * t_mfma_meas / us_per_layer, 2)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
-        us, threads, secs, sample = time_oracle_sample(inp, cfg, args.cpu_sample_tokens, seed, mx)
+        n_cpu = args.cpu_sample_tokens or CPU_SAMPLE_TOKENS.get(cfg.name, 64)
+        us, threads, secs, sample = time_oracle_sample(inp, cfg, n_cpu, seed, mx)
         line["cpu_baseline"] = {"value": round(us, 1), "unit": "us", "cores": threads,
                                 "kind": "oracle", "sample": sample,
                                 "seconds": round(secs, 2)}
-        if args.cpu_sample_tokens_1t > 0:  # the same oracle on one thread, smaller sample
+        if cpu_1t and args.cpu_sample_tokens_1t > 0:  # one thread, smaller sample
             us1, _, secs1, sample1 = time_oracle_sample(inp, cfg, args.cpu_sample_tokens_1t,
                                                         seed, mx, threads=1)
             line["cpu_baseline"]["one_thread"] = {"value": round(us1, 1), "unit": "us",
                                                   "sample": sample1, "seconds": round(secs1, 2)}
-    print(json.dumps(line), flush=True)
+    line["_t_bytes"] = bytes_total
+    line["_t_flops"] = flops
+    del inp, runner, w1, w2, w1_sf, w2_sf, fwd_args, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return line
 
 
 if __name__ == "__main__":

@@ -33,7 +33,7 @@ MOE_RECIPE_MXFP4 = 1
 EXPORTED_SYMBOLS = (
     "moe_plan_create", "moe_plan_destroy", "moe_plan_info", "moe_workspace_bytes",
     "moe_workspace_layout", "moe_forward", "moe_forward_timed", "moe_forward_mx",
-    "moe_forward_mx_timed", "moe_route",
+    "moe_forward_mx_timed", "moe_forward_noalloc", "moe_route",
     "moe_route_workspace_bytes", "moe_prepare_weights", "moe_prepare_weights_mx",
     "moe_quantize_act",
     "moe_read_status", "moe_strerror", "moe_version",
@@ -90,6 +90,7 @@ def lib():
         L.moe_forward.argtypes = [_vp, _i32] + [_vp] * 10 + [ctypes.c_size_t, _vp]
         L.moe_forward_timed.argtypes = [_vp, _i32] + [_vp] * 10 + [ctypes.c_size_t, _vp,
                                                                    ctypes.POINTER(_vp)]
+        L.moe_forward_noalloc.argtypes = [_vp, _i32] + [_vp] * 10
         L.moe_forward_mx.argtypes = L.moe_forward.argtypes
         L.moe_forward_mx_timed.argtypes = L.moe_forward_timed.argtypes
         L.moe_route.argtypes = ([_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp,
@@ -194,6 +195,19 @@ def moe_forward_timed(plan, num_tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2
                                  _ptr(topk_w), _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
                                  _ptr(y), _ptr(workspace), ws_bytes, _stream(stream), ev)
     _check(rc, "moe_forward_timed")
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_forward_noalloc(plan, num_tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
+                        stream=None):
+    """moe_forward with the library's static per-GPU scratch instead of a
+    workspace (no device allocation; calls overlapping on one GPU race)."""
+    rc = lib().moe_forward_noalloc(plan, num_tokens, _ptr(x), _ptr(x_sf), _ptr(topk_idx),
+                                   _ptr(topk_w), _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
+                                   _ptr(y), _stream(stream))
+    _check(rc, "moe_forward_noalloc")
 
 
 def moe_forward_mx(plan, num_tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/moe_fp8.h"
@@ -317,6 +318,35 @@ int device_ok()
     return cached[dev];
 }
 
+// Scratch of moe_forward_noalloc: every section a forward keeps in its
+// workspace (plan, pool maps, h, h_sf, partials, counters), in a static
+// device array of fixed size instead of a caller's allocation.  Each GPU the
+// library runs on holds its own copy until the process ends.  Host code uses
+// the array only through the device address hipGetSymbolAddress returns
+// (the array's name is a host-side stand-in, not a device address); that
+// address is looked up once per device, with the device current, and kept.
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch(void** out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return MOE_ERR_HIP;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return MOE_OK;
+}
+
 moe::RouteArgs route_args(const moe_shape_t& s, int T, const Layout& L, void* ws,
                           const int32_t* idx, int row_align, int32_t* counts,
                           int32_t* offsets, int32_t* row_src, int r_cap, int32_t* src_row,
@@ -444,6 +474,25 @@ struct FwdOperands {
     uint16_t* y;
 };
 
+bool misaligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) != 0; }
+
+// Host-side checks of a forward's operands (no HIP call).
+int check_operands(const FwdOperands& op)
+{
+    if (!op.x || !op.x_sf || !op.topk_idx || !op.topk_w || !op.w1 || !op.w1_sf || !op.w2 ||
+        !op.w2_sf || !op.y)
+        return MOE_ERR_INVALID_ARG;
+    // The kernels move 16-byte vectors of x, the weights and y.
+    if (misaligned(op.x, 16) || misaligned(op.w1, 16) || misaligned(op.w2, 16) ||
+        misaligned(op.y, 16))
+        return MOE_ERR_INVALID_ARG;
+    // MXFP4 scale codes are copied 4 bytes at a time by the LDS tiles (f32
+    // scales are naturally aligned)
+    if (misaligned(op.x_sf, 4) || misaligned(op.w1_sf, 4) || misaligned(op.w2_sf, 4))
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
 int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, void* workspace,
                  size_t workspace_bytes, void* stream, void* const* step_events)
 {
@@ -456,18 +505,10 @@ int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, 
         return MOE_ERR_INVALID_ARG;
     if (T == 0)
         return MOE_OK;
-    if (!op.x || !op.x_sf || !op.topk_idx || !op.topk_w || !op.w1 || !op.w1_sf || !op.w2 ||
-        !op.w2_sf || !op.y || !workspace)
+    if (check_operands(op) != MOE_OK || !workspace)
         return MOE_ERR_INVALID_ARG;
-    // The kernels move 16-byte vectors of x, the weights, y and the
-    // workspace sections (which sit at 256-byte offsets).
-    auto misaligned = [](const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) != 0; };
-    if (misaligned(workspace, 256) || misaligned(op.x, 16) || misaligned(op.w1, 16) ||
-        misaligned(op.w2, 16) || misaligned(op.y, 16))
-        return MOE_ERR_INVALID_ARG;
-    // MXFP4 scale codes are copied 4 bytes at a time by the LDS tiles (f32
-    // scales are naturally aligned)
-    if (misaligned(op.x_sf, 4) || misaligned(op.w1_sf, 4) || misaligned(op.w2_sf, 4))
+    // the workspace sections sit at 256-byte offsets and move as 16-byte vectors
+    if (misaligned(workspace, 256))
         return MOE_ERR_INVALID_ARG;
     const Layout L = make_layout(s, T);
     if (workspace_bytes < L.total)
@@ -579,6 +620,32 @@ int moe_forward(moe_plan_t plan, int32_t T, const uint8_t* x, const float* x_sf,
 {
     return moe_forward_timed(plan, T, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
                              workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_forward_noalloc(moe_plan_t plan, int32_t T, const uint8_t* x, const float* x_sf,
+                        const int32_t* topk_idx, const float* topk_w, const uint8_t* w1,
+                        const float* w1_sf, const uint8_t* w2, const float* w2_sf, uint16_t* y,
+                        void* stream)
+{
+    // every check before the first HIP call
+    if (!plan)
+        return MOE_ERR_INVALID_ARG;
+    const moe_shape_t& s = plan->shape;
+    if (s.recipe != MOE_RECIPE_FP8_BLOCK128 || T < 0 || T > s.max_tokens)
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    const FwdOperands op{x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y};
+    if (check_operands(op) != MOE_OK)
+        return MOE_ERR_INVALID_ARG;
+    if (make_layout(s, T).total > kNoAllocScratchBytes)
+        return MOE_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    const int rc = noalloc_scratch(&ws);
+    if (rc != MOE_OK)
+        return rc;
+    return forward_impl(plan, MOE_RECIPE_FP8_BLOCK128, T, op, ws, kNoAllocScratchBytes, stream,
+                        nullptr);
 }
 
 int moe_forward_mx_timed(moe_plan_t plan, int32_t T, const uint8_t* x, const uint8_t* x_sf,

@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller, row-major,
  *     densely packed.  The library never allocates or frees device memory;
- *     all scratch lives in a caller-provided workspace.
+ *     all scratch lives in a caller-provided workspace (moe_forward_noalloc:
+ *     in a static device array of the library, see there).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued asynchronously; no entry point synchronises the host, except
  *     moe_read_status, which says so.
@@ -204,6 +205,34 @@ int moe_forward_timed(moe_plan_t plan, int32_t num_tokens,
                       const uint8_t* w2, const float* w2_sf,
                       uint16_t* y, void* workspace, size_t workspace_bytes, void* stream,
                       void* const* step_events);
+
+/*
+ * moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same steps, kernels and results as moe_forward (bit-identical y), with the
+ * workspace replaced by a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * that the library owns: one per GPU, alive until the process ends.  No
+ * call allocates or frees device memory.  The caller still passes inputs,
+ * output and stream; operands as documented at moe_forward (FP8 plans only).
+ *   - A call whose workspace (moe_workspace_bytes(plan, T)) exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE_TOO_SMALL before
+ *     any HIP call (up to 404 tokens of the flash-decode shape, hidden 4096,
+ *     intermediate 2048, 256 experts, top-6; 142 of the pro shape).
+ *   - Every call on one GPU uses that GPU's one array, which keeps the last
+ *     call's contents (each call rewrites what it reads): calls that overlap
+ *     on one GPU (other streams, other threads) race and give undefined y.
+ *   - MOE_ERR_INVALID_ARG for non-FP8 plans, null or misaligned operands, T
+ *     out of range; MOE_ERR_HIP if the scratch address cannot be found.
+ * The first call on a device also looks up the array's device address
+ * (hipGetSymbolAddress, no allocation).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_forward_noalloc(moe_plan_t plan, int32_t num_tokens,
+                        const uint8_t* x, const float* x_sf,
+                        const int32_t* topk_idx, const float* topk_w,
+                        const uint8_t* w1, const float* w1_sf,
+                        const uint8_t* w2, const float* w2_sf,
+                        uint16_t* y, void* stream);
 
 /*
  * Full forward of the FP8 x MXFP4 recipe (plans with recipe =

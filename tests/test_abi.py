@@ -422,3 +422,32 @@ def test_quantize_act_rejects_invalid_calls_on_host():
         assert L.moe_quantize_act(None, 4, x, q, sf, None) == moe.MOE_ERR_INVALID_ARG
     finally:
         moe.moe_plan_destroy(p)
+
+
+def test_noalloc_host_validation_without_gpu():
+    # every rejection of moe_forward_noalloc happens before its first HIP call
+    L = moe.lib()
+    a = ctypes.c_void_p(0x1000)
+    p = moe.moe_plan_create(4096, 2048, 256, 6, 8192)
+    pmx = moe.moe_plan_create(4096, 2048, 256, 6, 64, recipe=moe.MOE_RECIPE_MXFP4)
+    try:
+        assert L.moe_forward_noalloc(p, 8193, *([a] * 9), None) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_forward_noalloc(p, -1, *([a] * 9), None) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_forward_noalloc(p, 0, *([None] * 9), None) == moe.MOE_OK  # no-op
+        for i in range(9):
+            args = [a] * 9
+            args[i] = None
+            assert L.moe_forward_noalloc(p, 8, *args, None) == moe.MOE_ERR_INVALID_ARG, i
+        for i in (0, 4, 6, 8):  # x, w1, w2, y need 16-byte alignment
+            args = [a] * 9
+            args[i] = ctypes.c_void_p(0x1008)
+            assert L.moe_forward_noalloc(p, 8, *args, None) == moe.MOE_ERR_INVALID_ARG, i
+        # the static scratch holds the workspace of up to 404 flash-decode tokens
+        assert moe.moe_workspace_bytes(p, 404) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+        assert moe.moe_workspace_bytes(p, 405) > moe.MOE_NOALLOC_SCRATCH_BYTES
+        assert L.moe_forward_noalloc(p, 405, *([a] * 9), None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+        assert L.moe_forward_noalloc(pmx, 8, *([a] * 9), None) == moe.MOE_ERR_INVALID_ARG
+        assert L.moe_forward_noalloc(None, 8, *([a] * 9), None) == moe.MOE_ERR_INVALID_ARG
+    finally:
+        moe.moe_plan_destroy(p)
+        moe.moe_plan_destroy(pmx)

@@ -152,17 +152,35 @@ typedef struct moe_ws_layout {
     size_t total;
 } moe_ws_layout_t;
 
-/* Validate a shape and create a plan (host only, no HIP call). */
+/* Validate a shape and create a plan (host only, no HIP call).  The pages
+ * reject unsupported shapes on the host before anything launches: hidden and
+ * intermediate multiples of 128, the architecture checked at dispatch
+ * ("07 · MegaMoE" §0), intermediate size bounded when the buffer is sized
+ * (DeepGEMM PR #440 "What a per-rank token count changes").  Here: the
+ * constraints at the top of this file and those noted per field of
+ * moe_shape_t; MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED_SHAPE otherwise,
+ * *out then NULL.  The plan is host memory owned by the caller until
+ * moe_plan_destroy (which accepts NULL and always returns MOE_OK). */
 int moe_plan_create(const moe_shape_t* shape, moe_plan_t* out);
 int moe_plan_destroy(moe_plan_t plan);
 
-/* Tile configuration for a call with num_tokens tokens. */
+/* Tile configuration for a call with num_tokens tokens (host only).  As on
+ * the pages, the row tile is chosen per call from the call's token count
+ * (PR #440 "What a per-rank token count changes": block_m flips 64 -> 128
+ * with the routed rows per expert, and the library reports the chosen
+ * configuration); the pool segments are aligned to it ("07 · MegaMoE" §4).
+ * MOE_ERR_INVALID_ARG for a null plan or info, or num_tokens outside
+ * [0, max_tokens]. */
 int moe_plan_info(moe_plan_t plan, int32_t num_tokens, moe_tile_info_t* info);
 
-/* Workspace bytes a call with num_tokens tokens needs.  The amount is
- * nondecreasing in num_tokens, so the value for max_tokens serves every
- * call on the plan.  No zeroing is required: every call rewrites what it
- * reads. */
+/* Workspace bytes a call with num_tokens tokens needs, and where its
+ * sections sit: the pages' buffer-size query, which returns the byte count
+ * and a slicer of the buffer into its regions (PR #440 "API, Tests, Files";
+ * the input, L1-pool, L2-pool and combine regions of "07 · MegaMoE" §3).
+ * Host only.  The amount is nondecreasing in num_tokens, so the value for
+ * max_tokens serves every call on the plan.  No zeroing is required: every
+ * call rewrites what it reads.  MOE_ERR_INVALID_ARG for a null plan or
+ * output, or num_tokens outside [0, max_tokens]. */
 int moe_workspace_bytes(moe_plan_t plan, int32_t num_tokens, size_t* bytes);
 int moe_workspace_layout(moe_plan_t plan, int32_t num_tokens, moe_ws_layout_t* layout);
 
@@ -339,13 +357,26 @@ int moe_route(moe_plan_t plan, int32_t num_tokens, const int32_t* topk_idx,
               int32_t row_align, int32_t* counts, int32_t* offsets,
               int32_t* row_src, int32_t row_src_len, int32_t* src_row,
               void* workspace, size_t workspace_bytes, void* stream);
+/* Scratch bytes of moe_route alone (its per-chunk count table and status
+ * word); same errors as moe_workspace_bytes. */
 int moe_route_workspace_bytes(moe_plan_t plan, int32_t num_tokens, size_t* bytes);
 
 /* Blocking: synchronises `stream`, then copies the 4-int status word of the
- * last call that used `workspace` into host_status[4]. */
+ * last call that used `workspace` into host_status[4] (MOE_STATUS_* bits,
+ * the number of ids >= E, the pool rows used).  The pages' kernels return
+ * nothing from the device and abort on a timed-out wait (PR #440 "Register
+ * inventory": the wait timeout and its handler); this library reports
+ * instead: an id the pages leave undefined (>= E) is skipped and counted,
+ * and a single-launch wait that gives up sets MOE_STATUS_WAIT_TIMEOUT.
+ * MOE_ERR_WORKSPACE_TOO_SMALL if the workspace cannot hold the status word
+ * of a call with num_tokens tokens; MOE_ERR_HIP if the copy fails. */
 int moe_read_status(moe_plan_t plan, int32_t num_tokens, const void* workspace,
                     size_t workspace_bytes, int32_t* host_status, void* stream);
 
+/* A static, human-readable name of a MOE_OK / MOE_ERR_* code ("unknown error"
+ * otherwise).  The pages raise on the host (PR #440 "API, Tests, Files": a
+ * token bound above capacity raises before any launch; fused-only keywords
+ * on the split arm raise a ValueError); a C ABI returns codes instead. */
 const char* moe_strerror(int code);
 
 /* Library version, for the binding's sanity check. */

@@ -304,9 +304,10 @@ def main():
     ap.add_argument("--peaks-only", action="store_true",
                     help="only measure the streaming-read and FP8 MFMA ceilings, print them "
                          "as one JSON line and exit")
-    ap.add_argument("--launch", choices=("auto", "single", "split"), default="auto",
+    ap.add_argument("--launch", choices=("auto", "single", "ring", "split"), default="auto",
                     help="single: L1, L2 and combine in one cooperative launch (direct "
-                         "tiles); split: one launch per step; auto: the library's choice")
+                         "tiles); ring: the same over the lag-ordered ring pool; split: "
+                         "one launch per step; auto: the library's choice")
     ap.add_argument("--tile-m", type=int, default=0, choices=(0, 16, 32, 64, 128),
                     help="rows per GEMM tile (0 = the library's choice per call)")
     ap.add_argument("--recipe", choices=("fp8", "mxfp4"), default="fp8",
@@ -407,7 +408,8 @@ def run_workload(args, cfg, seed, steps, warmup, flush, cpu_1t):
     inp = (wl.make_inputs_mx if mx else wl.make_inputs)(cfg, seed, dev)
     torch.cuda.synchronize()
     layout = moe.MOE_WEIGHTS_PACKED if args.weights == "packed" else moe.MOE_WEIGHTS_ROW_MAJOR
-    flags = {"auto": 0, "single": moe.MOE_FLAG_SINGLE_LAUNCH,
+    flags = {"auto": 0, "single": moe.MOE_FLAG_SINGLE_LAUNCH | moe.MOE_FLAG_DIRECT_TILES,
+             "ring": moe.MOE_FLAG_RING_POOL,
              "split": moe.MOE_FLAG_SPLIT_LAUNCH}[args.launch]
     runner = moe.MoEForward(cfg.H, cfg.I, cfg.E, cfg.K, cfg.T, tile_m=args.tile_m, device=dev,
                             weight_layout=layout,
@@ -480,7 +482,10 @@ def run_workload(args, cfg, seed, steps, warmup, flush, cpu_1t):
         dom = "l1"
         dom_bytes = alg["l1"] + alg["l2"] + alg["combine"]
         kernel_name = (f"single launch: L1 + L2 + combine (direct-load tiles, tile_m "
-                       f"{info['tile_m']})")
+                       f"{info['tile_m']}" +
+                       (f"; h in a ring of {info['ring_blocks']} row blocks, L2 "
+                        f"{info['l2_lag_units']} units behind L1)" if info["ring_blocks"]
+                        else ")"))
     else:
         dom = max(("l1", "l2"), key=lambda n: avg[n])
         dom_bytes = alg[dom]

@@ -25,6 +25,7 @@ MOE_FLAG_SINGLE_LAUNCH = 1
 MOE_FLAG_SPLIT_LAUNCH = 2
 MOE_FLAG_POW2_SCALE = 4
 MOE_FLAG_DIRECT_TILES = 8
+MOE_FLAG_RING_POOL = 16
 MOE_FLAG_TEST_NO_WAIT = 256
 MOE_FLAG_TEST_SMALL_GRID = 512
 MOE_RECIPE_FP8_BLOCK128 = 0
@@ -60,7 +61,8 @@ class moe_tile_info_t(ctypes.Structure):
                 ("pool_rows", ctypes.c_int32), ("l1_tile_n", ctypes.c_int32),
                 ("l2_tile_n", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("l1_split", ctypes.c_int32), ("single_launch", ctypes.c_int32),
-                ("l2_group_tiles", ctypes.c_int32), ("act_sf_gran", ctypes.c_int32)]
+                ("l2_group_tiles", ctypes.c_int32), ("act_sf_gran", ctypes.c_int32),
+                ("ring_blocks", ctypes.c_int32), ("l2_lag_units", ctypes.c_int32)]
 
 
 class moe_ws_layout_t(ctypes.Structure):
@@ -335,14 +337,16 @@ class MoEForward:
         info = moe_plan_info(self.plan, num_tokens)
         H, I, E, K = self.shape[:4]
         R = info["pool_rows"]
+        # ring-pool calls: h / h_sf hold ring_blocks row blocks
+        HR = info["ring_blocks"] * info["tile_m"] if info["ring_blocks"] > 0 else R
         spec = {
             "counts": (torch.int32, (E,)),
             "offsets": (torch.int32, (E + 1,)),
             "row_src": (torch.int32, (R,)),
             "src_row": (torch.int32, (num_tokens * K,)),
-            "h": (torch.uint8, (R, I)),
-            "h_sf": ((torch.uint8, (R, I // 32)) if self.recipe == MOE_RECIPE_MXFP4
-                     else (torch.float32, (R, I // info["act_sf_gran"]))),
+            "h": (torch.uint8, (HR, I)),
+            "h_sf": ((torch.uint8, (HR, I // 32)) if self.recipe == MOE_RECIPE_MXFP4
+                     else (torch.float32, (HR, I // info["act_sf_gran"]))),
             "partial": (torch.int16, (K, num_tokens, H)),
             "status": (torch.int32, (4,)),
         }[name]

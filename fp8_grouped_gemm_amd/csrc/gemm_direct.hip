@@ -91,6 +91,18 @@ __device__ __forceinline__ void st_co128(void* p, uint4 v)
     st_co64(p, (uint64_t)v.x | ((uint64_t)v.y << 32));
     st_co64(reinterpret_cast<uint8_t*>(p) + 8, (uint64_t)v.z | ((uint64_t)v.w << 32));
 }
+// 16 bytes of h read coherently (agent scope, two 8-byte loads): with a ring
+// pool the same h lines are written again later in the launch, so a copy
+// another XCD's L2 kept from the previous occupant of a slot may be stale.
+__device__ __forceinline__ uint4 ld_co128(const uint8_t* p)
+{
+    const uint64_t lo = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p + 8),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+}
+
 // Counts one finished tile: every thread's hand-off stores have completed
 // before the workgroup barrier, then one lane bumps the counter.
 __device__ __forceinline__ void count_done(int32_t* ctr)
@@ -149,6 +161,8 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
     const int lr = lane & 15, lg = lane >> 4;
     const int H = a.H, HB = H / 128, I = a.I, K = a.K;
     const int row0 = mb * BM;
+    // h / h_sf rows of this block: its pool rows, or its ring slot's
+    const int hrow0 = (CO && a.ring_blocks > 0) ? (mb % a.ring_blocks) * BM : row0;
     const int kb0 = ks * HB / S, kb1 = (ks + 1) * HB / S;
 
     // A operand rows: row0 + 16*ms + lr.  Padding rows (row_src < 0) read
@@ -294,8 +308,8 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
                     qt[r][wave * 32 + s * 16 + lr] =
                         (uint8_t)requant_q(hv[ms][s][i], sf, rsf, a.pow2_scale);
                 if ((a.sf_gran64 ? (wave & 1) == 0 : wave == 0) && lr == 0) {
-                    float* dst = a.sf_gran64 ? a.h_sf + (size_t)(row0 + r) * (I / 64) + nt * 2 + (wave >> 1)
-                                             : a.h_sf + (size_t)(row0 + r) * (I / 128) + nt;
+                    float* dst = a.sf_gran64 ? a.h_sf + (size_t)(hrow0 + r) * (I / 64) + nt * 2 + (wave >> 1)
+                                             : a.h_sf + (size_t)(hrow0 + r) * (I / 128) + nt;
                     if constexpr (CO)
                         st_co32f(dst, sf);
                     else
@@ -309,7 +323,7 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
     for (int c = threadIdx.x; c < BM * 8; c += 256) {
         const int r = c >> 3, col = (c & 7) * 16;
         if (a.row_src[row0 + r] >= 0) {
-            uint8_t* dst = a.h + (size_t)(row0 + r) * I + nt * 128 + col;
+            uint8_t* dst = a.h + (size_t)(hrow0 + r) * I + nt * 128 + col;
             const uint4 v = *reinterpret_cast<const uint4*>(&qt[r][col]);
             if constexpr (CO)
                 st_co128(dst, v);
@@ -370,6 +384,9 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int row0 = mb * BM;
+    // h / h_sf rows of this block: its pool rows, or its ring slot's
+    const bool ring = CO && a.ring_blocks > 0;
+    const int hrow0 = ring ? (mb % a.ring_blocks) * BM : row0;
     const int kb0 = 0, kb1 = IB;
     const int nt_w = g * NTG + (wave >> 2);               // this wave's 256-column tile
     const bool busy = nt_w < NT && nt_w * 256 + (wave & 3) * 64 < H;
@@ -380,16 +397,16 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
     bool avalid[MT];
 #pragma unroll
     for (int ms = 0; ms < MT; ++ms) {
-        const int r = row0 + 16 * ms + lr;
-        avalid[ms] = a.row_src[r] >= 0;
-        aptr[ms] = a.h + (size_t)r * I + lg * 16;
+        const int r = 16 * ms + lr;
+        avalid[ms] = a.row_src[row0 + r] >= 0;
+        aptr[ms] = a.h + (size_t)(hrow0 + r) * I + lg * 16;
     }
     const float* asf[MT][4];
 #pragma unroll
     for (int ms = 0; ms < MT; ++ms)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            asf[ms][i] = a.h_sf + (size_t)(row0 + 16 * ms + 4 * lg + i) * (G64 ? 2 * IB : IB);
+            asf[ms][i] = a.h_sf + (size_t)(hrow0 + 16 * ms + 4 * lg + i) * (G64 ? 2 * IB : IB);
     // A wave's 64 columns are either all inside H or all past it; an idle
     // wave re-reads column block 0 and stores nothing.
     const int ncol0 = busy ? nt * 256 + w4 * 64 : 0;
@@ -435,8 +452,16 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
             }
         b.sb = sfb[kb];
 #pragma unroll
-        for (int ms = 0; ms < MT; ++ms)
-            b.fa[ms] = avalid[ms] ? load_frag(aptr[ms] + kb * 128) : zero_frag();
+        for (int ms = 0; ms < MT; ++ms) {
+            if (!avalid[ms]) {
+                b.fa[ms] = zero_frag();
+            } else if (ring) {
+                b.fa[ms].lo = ld_co128(aptr[ms] + kb * 128);
+                b.fa[ms].hi = ld_co128(aptr[ms] + kb * 128 + 64);
+            } else {
+                b.fa[ms] = load_frag(aptr[ms] + kb * 128);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             b.fb[s] = load_wfrag<PK>(bptr[s] + kb * kstride);
@@ -510,8 +535,13 @@ template <int MT, bool PK, bool CO>
 __device__ __forceinline__ void l2_tile(const FwdArgs& a, int tile, int hint = 0)
 {
     l2_tile_body<MT, PK, CO>(a, tile, hint);
-    if constexpr (CO)
+    if constexpr (CO) {
         count_done(a.sync + kSyncL2Done);  // every L2 item counts, idle ones too
+        // ring pool: and per row block, for the L1 tiles that reuse its slot
+        if (a.ring_blocks > 0 && threadIdx.x == 0)
+            __hip_atomic_fetch_add(a.sync + kSyncReady + a.num_mblocks + tile / ((a.H + 255) / 256), 1,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 template <int MT, bool PK, int WV = 4, bool G64 = false>
@@ -730,6 +760,104 @@ __global__ __launch_bounds__(256) void fused_direct(FwdArgs a)
     }
 }
 
+// The single launch over a ring pool (DeepGEMM PR #440 "How it works",
+// "Ring sizing, recycling"): items are the route_stream's lag-ordered
+// stream, then the combine chunks.  Row block mb writes h / h_sf slot
+// mb % ring_blocks, so its L1 tiles first wait until the L2 tiles of the
+// slot's previous occupant, block mb - ring_blocks, are all finished (a
+// per-block count, bumped after the tile's loads have returned).  The
+// stream puts those L2 tiles before these L1 tiles whenever the ring holds
+// 8 (lag + group) + 1 blocks (the host sizes it 8 (lag + group) + 4), and
+// an L2 tile only waits for its own block's L1 tiles, earlier in the stream:
+// every wait is for smaller item numbers, as in fused_direct, and ends.
+// Claims run three deep: while an item runs, thread 0 claims the item after
+// next, reads the next item's table entry, and reads the count that the
+// item after this one will wait for.
+template <int MT, bool PK>
+__global__ __launch_bounds__(256) void fused_ring(FwdArgs a)
+{
+    const int used_mb = min(a.num_mblocks, a.status[2] / (16 * MT));
+    const int NT1 = a.I / 128, NT2 = (a.H + 255) / 256;
+    const int S = min(a.sync[kSyncStreamItems], used_mb * (NT1 + NT2));
+    const int n2 = used_mb * NT2;
+    const int n3 = (int)(((long long)a.T * (a.H / 8) + 255) / 256);
+    const int total = S + n3;
+    const int RB = a.ring_blocks;
+    int32_t* queue = a.sync + kSyncQueue;
+    const int32_t* l2_done = a.sync + kSyncReady + a.num_mblocks;
+    auto code_of = [&](int q) { return q < S ? a.item_tab[q] : -1; };
+    // counter item q (table entry code) waits for, and its target
+    auto wait_of = [&](int q, int code, int& target) -> const int32_t* {
+        if (q >= total)
+            return nullptr;
+        if (q >= S) {
+            target = n2;
+            return a.sync + kSyncL2Done;
+        }
+        const int tile = code & ~kItemL2;
+        if (code & kItemL2) {
+            target = NT1;
+            return a.sync + kSyncReady + tile / NT2;
+        }
+        const int mb = tile / NT1;
+        target = NT2;
+        return mb >= RB ? l2_done + (mb - RB) : nullptr;
+    };
+    __shared__ int s_cur[2], s_code[2], s_hint[2], s_nxt[2], s_ncode[2], s_nxt2[2];
+    if (threadIdx.x == 0) {
+        const int c0 = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int c1 = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int c2 = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_cur[0] = c0;
+        s_code[0] = code_of(c0);
+        s_hint[0] = 0;
+        s_nxt[0] = c1;
+        s_ncode[0] = code_of(c1);
+        s_nxt2[0] = c2;
+    }
+    __syncthreads();
+    int slot = 0;
+    for (;;) {
+        const int cur = s_cur[slot];
+        if (cur >= total)
+            break;
+        const int code = s_code[slot], hint = s_hint[slot];
+        const int nxt = s_nxt[slot], ncode = s_ncode[slot], nxt2 = s_nxt2[slot];
+        int claim = total, code2 = -1, nhint = 0;
+        if (threadIdx.x == 0) {
+            if (nxt2 < total)
+                claim = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            code2 = code_of(nxt2);
+            int tgt = 0;
+            if (const int32_t* c = wait_of(nxt, ncode, tgt))
+                nhint = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (cur < S) {
+            const int tile = code & ~kItemL2;
+            if (code & kItemL2) {
+                l2_tile<MT, PK, true>(a, tile, hint);
+            } else {
+                const int mb = tile / NT1;
+                if (mb >= RB)
+                    wait_count(l2_done + (mb - RB), NT2, a, hint);
+                l1_tile<MT, 1, PK, true>(a, tile);
+            }
+        } else {
+            combine_chunk<true>(a, cur - S, n2, hint);
+        }
+        slot ^= 1;
+        if (threadIdx.x == 0) {
+            s_cur[slot] = nxt;
+            s_code[slot] = ncode;
+            s_hint[slot] = nhint;
+            s_nxt[slot] = nxt2;
+            s_ncode[slot] = code2;
+            s_nxt2[slot] = claim;
+        }
+        __syncthreads();
+    }
+}
+
 template <bool PK>
 static hipError_t launch_l1_t(const FwdArgs& a, hipStream_t s)
 {
@@ -791,7 +919,7 @@ static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
 template <int MT, bool PK>
 static hipError_t launch_fused_t(const FwdArgs& a, hipStream_t s)
 {
-    auto kern = fused_direct<MT, PK>;
+    auto kern = a.ring_blocks > 0 ? fused_ring<MT, PK> : fused_direct<MT, PK>;
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err == hipSuccess)
@@ -804,7 +932,9 @@ static hipError_t launch_fused_t(const FwdArgs& a, hipStream_t s)
         return hipErrorInvalidConfiguration;
     const long long n = (long long)a.num_mblocks * (a.I / 128 + (a.H + 255) / 256) +
                         ((long long)a.T * (a.H / 8) + 255) / 256;
-    const long long cap = (long long)cus * per_cu;  // resident workgroups
+    long long cap = (long long)cus * per_cu;  // resident workgroups
+    if (a.grid_cap > 0 && cap > a.grid_cap)
+        cap = a.grid_cap;
     const unsigned grid = (unsigned)(n < cap ? n : cap);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
@@ -813,6 +943,11 @@ static hipError_t launch_fused_t(const FwdArgs& a, hipStream_t s)
 hipError_t launch_fused(const FwdArgs& a, hipStream_t s)
 {
     if (a.split_l1 != 1 || !a.sync || !a.status)
+        return hipErrorInvalidValue;
+    // ring pool: the stream tables, and a ring that holds the live set
+    if (a.ring_blocks > 0 &&
+        (!a.item_tab || a.lag_units < 1 ||
+         a.ring_blocks < kUnitBlocks * (a.lag_units + kStreamGroup) + 1))
         return hipErrorInvalidValue;
     switch (a.BM) {
     case 16: return a.packed ? launch_fused_t<1, true>(a, s) : launch_fused_t<1, false>(a, s);

@@ -59,7 +59,9 @@ constexpr double kRowsLds64 = 64.0;
 
 Config choose_config(const moe_shape_t& s, int T)
 {
-    const bool lds = lds_tile_fits(s) && sf_gran(s) != 64;
+    // ring-pool plans run the single launch, which has direct-load tiles only
+    const bool ring = (s.flags & MOE_FLAG_RING_POOL) != 0;
+    const bool lds = lds_tile_fits(s) && sf_gran(s) != 64 && !ring;
     const bool lds64 = lds && !(s.flags & MOE_FLAG_DIRECT_TILES);
     // 64-row tiles where the LDS tiles fit: the shared-A tile (kernel 2)
     const int k64 = lds64 ? 2 : 0;
@@ -82,11 +84,38 @@ struct Layout {
     int split_l1;
     bool l2_wide;
     bool single;  // L1 + L2 + combine in one launch
+    int ring_blocks, lag_units;  // ring pool: row blocks of h / h_sf, lag (0: full pool)
     int n_sync;
     size_t sync;
     size_t status, counts, offsets, blk, mbe, row_src, src_row, h_sf, h, partial;
-    size_t part, total;
+    size_t part, unit_mb, stream_start, stream_desc, item_tab, total;
 };
+
+// Ring pool sizing (DeepGEMM PR #440 "How it works", "Ring sizing,
+// recycling, and why that granularity"): a unit is up to kUnitBlocks row
+// blocks of one expert; the call's unit count is estimated from its token
+// count (T*K rows in blocks of tile_m), L2 trails L1 by lag = clamp(round(0.45
+// units), 8, 64) units in groups of kStreamGroup, so at most kUnitBlocks
+// (lag + group) blocks are live and the ring holds that plus kRingMargin.
+constexpr int kRingMargin = 4;
+
+struct RingSize {
+    int blocks, lag;
+};
+
+RingSize ring_size(long long TK, int tile_m)
+{
+    const long long per_unit = (long long)moe::kUnitBlocks * tile_m;
+    const long long units = std::max<long long>(1, (TK + per_unit - 1) / per_unit);
+    const int lag = (int)std::min<long long>(64, std::max<long long>(8, std::llround(0.45 * units)));
+    return RingSize{moe::kUnitBlocks * (lag + moe::kStreamGroup) + kRingMargin, lag};
+}
+
+// The live set of the lag order: blocks whose h a ring slot must still hold.
+bool ring_holds_live_set(int blocks, int lag)
+{
+    return blocks >= moe::kUnitBlocks * (lag + moe::kStreamGroup) + 1;
+}
 
 // Split-K across workgroups for the 16-row L1 tiles.  One workgroup per
 // (row block, column tile) streams that tile's whole weight block (~1 MiB at
@@ -131,7 +160,8 @@ bool choose_l2_wide(const moe_shape_t& s, int T, const Config& c)
 // L1 split factor of a call with T tokens and tile configuration c.
 int choose_split(const moe_shape_t& s, int T, const Config& c)
 {
-    if (c.tile_m != 16 || T <= 0 || s.recipe != MOE_RECIPE_FP8_BLOCK128)
+    if (c.tile_m != 16 || T <= 0 || s.recipe != MOE_RECIPE_FP8_BLOCK128 ||
+        (s.flags & MOE_FLAG_RING_POOL))
         return 1;
     const long long items = mblocks_expected(s, T) * (s.intermediate / 128);
     const int kblocks = s.hidden / 128;
@@ -207,22 +237,48 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     L.mbe = take(sizeof(int32_t) * (size_t)L.mb_cap);
     L.row_src = take(sizeof(int32_t) * (size_t)L.r_cap);
     L.src_row = take(sizeof(int32_t) * (size_t)std::max<long long>(TK, 1));
+    L.split_l1 = choose_split(s, T, c);
+    L.single = c.kernel == 0 && L.split_l1 == 1 && sf_gran(s) != 64 &&
+               ((s.flags & (MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_RING_POOL)) ||
+                (kSingleLaunchDefault && !(s.flags & MOE_FLAG_SPLIT_LAUNCH)));
+    // the single launch's L2 tiles are one 256-column tile per workgroup
+    L.l2_wide = choose_l2_wide(s, T, c) && !L.single;
+    // Ring pool: where the call's pool holds more row blocks than the ring,
+    // h / h_sf hold ring_blocks blocks (block mb at slot mb % ring_blocks);
+    // elsewhere the ring would be the whole pool and never wrap.
+    const bool ring_plan = L.single && (s.flags & MOE_FLAG_RING_POOL);
+    L.ring_blocks = L.lag_units = 0;
+    if (ring_plan) {
+        const RingSize rs = ring_size(TK, ra);
+        if (rs.blocks < L.mb_cap) {
+            L.ring_blocks = rs.blocks;
+            L.lag_units = rs.lag;
+        }
+    }
+    const size_t h_rows = L.ring_blocks > 0 ? (size_t)L.ring_blocks * ra : (size_t)L.r_cap;
     // f32 [R, I/128] or [R, I/64] (FP8 recipe) or UE8M0 bytes [R, I/32]
     // (MXFP4, the size of the per-128 f32 section)
-    L.h_sf = take(sizeof(float) * (size_t)L.r_cap * (I / (sf_gran(s) == 64 ? 64 : 128)));
-    L.h = take((size_t)L.r_cap * I);
+    L.h_sf = take(sizeof(float) * h_rows * (I / (sf_gran(s) == 64 ? 64 : 128)));
+    L.h = take(h_rows * I);
     L.partial = take(sizeof(uint16_t) * (size_t)K * T * H);
     // Split-K scratch: L1's f32 partials part[slice][slot][2I], slot
     // f = t*K + j.
-    L.split_l1 = choose_split(s, T, c);
-    L.l2_wide = choose_l2_wide(s, T, c);
     L.part = take(sizeof(float) * splitk_floats(s, T));
-    // Single-launch counters: L2 done, 3 spare, one ready count per row block.
-    L.single = c.kernel == 0 && L.split_l1 == 1 && sf_gran(s) != 64 &&
-               ((s.flags & MOE_FLAG_SINGLE_LAUNCH) ||
-                (kSingleLaunchDefault && !(s.flags & MOE_FLAG_SPLIT_LAUNCH)));
-    L.n_sync = moe::kSyncReady + L.mb_cap;
+    // Single-launch counters: L2 done, queue, 2 for the ring's stream, one
+    // L1-ready count per row block, and (ring plans) one L2-done count per
+    // row block.  Ring plans size the per-block sections for mbb >= mb_cap
+    // blocks, a bound that grows with T whatever the tile height.
+    const size_t mbb = (size_t)((TK + 15) / 16 + E);
+    L.n_sync = moe::kSyncReady + (ring_plan ? (int)(2 * mbb) : L.mb_cap);
     L.sync = take(sizeof(int32_t) * (size_t)L.n_sync);
+    L.unit_mb = L.stream_start = L.stream_desc = L.item_tab = 0;
+    if (ring_plan) {
+        const size_t NT1 = I / 128, NT2 = (H + 255) / 256;
+        L.unit_mb = take(sizeof(int32_t) * (mbb + 1));
+        L.stream_start = take(sizeof(int32_t) * (2 * mbb + 1));
+        L.stream_desc = take(sizeof(int32_t) * 2 * mbb);
+        L.item_tab = take(sizeof(int32_t) * mbb * (NT1 + NT2));
+    }
     L.total = o;
     return L;
 }
@@ -256,7 +312,8 @@ int validate_shape(const moe_shape_t* s)
     if (s->weight_layout == MOE_WEIGHTS_PACKED && s->hidden % 256)
         return MOE_ERR_UNSUPPORTED_SHAPE;
     if (s->flags & ~(MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_SPLIT_LAUNCH | MOE_FLAG_POW2_SCALE |
-                     MOE_FLAG_DIRECT_TILES | MOE_FLAG_TEST_NO_WAIT | MOE_FLAG_TEST_SMALL_GRID))
+                     MOE_FLAG_DIRECT_TILES | MOE_FLAG_RING_POOL | MOE_FLAG_TEST_NO_WAIT |
+                     MOE_FLAG_TEST_SMALL_GRID))
         return MOE_ERR_INVALID_ARG;
     if (s->act_sf_gran != 0 && s->act_sf_gran != 64 && s->act_sf_gran != 128 && s->act_sf_gran != -1)
         return MOE_ERR_INVALID_ARG;
@@ -279,6 +336,14 @@ int validate_shape(const moe_shape_t* s)
     }
     if ((s->flags & MOE_FLAG_SINGLE_LAUNCH) && (s->flags & MOE_FLAG_SPLIT_LAUNCH))
         return MOE_ERR_INVALID_ARG;
+    if (s->flags & MOE_FLAG_RING_POOL) {  // the single launch with direct-load tiles
+        if (s->flags & MOE_FLAG_SPLIT_LAUNCH)
+            return MOE_ERR_INVALID_ARG;
+        if (s->recipe != MOE_RECIPE_FP8_BLOCK128 || sf_gran(*s) == 64)
+            return MOE_ERR_INVALID_ARG;
+        if (s->tile_m == 128)
+            return MOE_ERR_UNSUPPORTED_SHAPE;
+    }
     return MOE_OK;
 }
 
@@ -428,6 +493,8 @@ int moe_plan_info(moe_plan_t plan, int32_t T, moe_tile_info_t* info)
     info->single_launch = L.single ? 1 : 0;
     info->l2_group_tiles = L.l2_wide ? 2 : 1;
     info->act_sf_gran = sf_gran(plan->shape);
+    info->ring_blocks = L.ring_blocks;
+    info->l2_lag_units = L.lag_units;
     return MOE_OK;
 }
 
@@ -513,6 +580,9 @@ int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, 
     const Layout L = make_layout(s, T);
     if (workspace_bytes < L.total)
         return MOE_ERR_WORKSPACE_TOO_SMALL;
+    // the ring must hold the lag order's live set (asserted before any launch)
+    if (L.ring_blocks > 0 && !ring_holds_live_set(L.ring_blocks, L.lag_units))
+        return MOE_ERR_UNSUPPORTED_SHAPE;
     int rc = device_ok();
     if (rc != MOE_OK)
         return rc;
@@ -560,6 +630,7 @@ int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, 
         a.h_sf = at<float>(workspace, L.h_sf);
     }
     a.row_src = at<int32_t>(workspace, L.row_src);
+    a.offsets = at<int32_t>(workspace, L.offsets);
     a.mblock_expert = at<int32_t>(workspace, L.mbe);
     a.num_mblocks = L.mb_cap;
     a.h = at<uint8_t>(workspace, L.h);
@@ -577,6 +648,16 @@ int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, 
     a.pow2_scale = (s.flags & MOE_FLAG_POW2_SCALE) ? 1 : 0;
     a.sf_gran64 = sf_gran(s) == 64 ? 1 : 0;
     a.grid_cap = (s.flags & MOE_FLAG_TEST_SMALL_GRID) ? 4 : 0;
+    if (L.ring_blocks > 0) {
+        a.ring_blocks = L.ring_blocks;
+        a.lag_units = L.lag_units;
+        a.unit_mb = at<int32_t>(workspace, L.unit_mb);
+        a.stream_start = at<int32_t>(workspace, L.stream_start);
+        a.stream_desc = at<int32_t>(workspace, L.stream_desc);
+        a.item_tab = at<int32_t>(workspace, L.item_tab);
+        if (moe::launch_route_stream(a, st) != hipSuccess)
+            return MOE_ERR_HIP;
+    }
     if (L.single) {
         if (moe::launch_fused(a, st) != hipSuccess || !mark(2) || !mark(3) || !mark(4))
             return MOE_ERR_HIP;

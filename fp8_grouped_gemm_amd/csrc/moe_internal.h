@@ -40,6 +40,7 @@ struct FwdArgs {
     const uint8_t* w2;
     const float* w2_sf;
     const int32_t* row_src;
+    const int32_t* offsets;        // [E+1] first pool row of each expert's segment
     const int32_t* mblock_expert;
     int32_t num_mblocks;
     uint8_t* h;
@@ -61,6 +62,24 @@ struct FwdArgs {
     int32_t* sync;
     int32_t* status;
     int32_t spin_limit;
+    // Lag-ordered ring pool of the single launch (ring_blocks > 0; DeepGEMM
+    // PR #440 "How it works", "Ring sizing, recycling"): h / h_sf hold
+    // ring_blocks row blocks, row block mb in slot mb % ring_blocks.  The
+    // planner's route_stream writes the unit table unit_mb[U + 1] (first row
+    // block of each unit of up to kUnitBlocks blocks of one expert; the
+    // last entry is the used row-block count) and the stream: entry p covers
+    // items [stream_start[p], stream_start[p + 1]) of unit stream_desc[p] &
+    // kStreamUnitMask, its L2 tiles when kStreamL2 is set, else its L1 tiles,
+    // and item_tab[q] names item q: its tile (row block x column tiles + column
+    // tile), with the top bit set for an L2 tile.  Where the used row blocks
+    // fit the ring, the stream is the single-wave order (every L1 unit, then
+    // every L2 unit) and no slot is reused.
+    int32_t ring_blocks;
+    int32_t lag_units;
+    int32_t* unit_mb;
+    int32_t* stream_start;
+    int32_t* stream_desc;
+    int32_t* item_tab;
     int32_t grid_cap;  // > 0: at most this many workgroups for the persistent kernels
     // FP8 x MXFP4 recipe (mx = 1): UE8M0 scale codes, one per 32 K values,
     // x_sfq [T,H/32], w1_sfq [E,2I,H/32], w2_sfq [E,H,I/32], h_sfq [R,I/32];
@@ -79,14 +98,23 @@ struct FwdArgs {
 };
 
 constexpr int kSyncL2Done = 0;
-constexpr int kSyncQueue = 1;  // next unclaimed item
-constexpr int kSyncReady = 4;
+constexpr int kSyncQueue = 1;        // next unclaimed item
+constexpr int kSyncStreamItems = 2;  // ring pool: L1 + L2 items of the stream
+constexpr int kSyncUnits = 3;        // ring pool: units in the stream
+constexpr int kSyncReady = 4;        // [num_mblocks]: L1 tiles finished per row block, then
+                                     // [num_mblocks]: L2 tiles finished per row block
+constexpr int kUnitBlocks = 8;       // row blocks per unit of the lag order
+constexpr int kStreamGroup = 4;      // units per L2 group of the lag order
+constexpr int32_t kStreamL2 = 1 << 30;
+constexpr int32_t kStreamUnitMask = kStreamL2 - 1;
+constexpr int32_t kItemL2 = INT32_MIN;  // item_tab: an L2 tile
 constexpr int32_t kStatusWaitTimeout = 2;  // == MOE_STATUS_WAIT_TIMEOUT
 
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxExperts = 1024;
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_route_stream(const FwdArgs& a, hipStream_t s);  // ring pool: lag-ordered stream
 hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s);
 hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s);
 hipError_t launch_fused(const FwdArgs& a, hipStream_t s);  // L1 + L2 + combine, direct tiles

@@ -278,6 +278,104 @@ __global__ __launch_bounds__(kRouteThreads) void route_small(RouteArgs a)
     }
 }
 
+// Stream of the single launch with a ring pool (DeepGEMM PR #440 "How it
+// works"): units of up to kUnitBlocks consecutive row blocks of one expert,
+// in pool order; the L2 tiles of unit group j (kStreamGroup units) follow
+// the L1 tiles of unit G j + G - 1 + lag (or, when that unit does not
+// exist, the last L1 unit).  In closed form, with U units, G = kStreamGroup
+// and L = lag: L1 of unit u is entry u + min(U, G max(0, floor((u - L) / G)))
+// and L2 of unit u is entry u + 1 + min(G floor(u / G) + G - 1 + L, U - 1).
+// One block: per-expert unit counts and their scan, the unit table, each
+// unit's two entries with their item counts (row blocks x column tiles),
+// the exclusive scan of those counts and the item table.
+__global__ __launch_bounds__(kRouteThreads) void route_stream(FwdArgs a)
+{
+    __shared__ int32_t scan[kRouteThreads];
+    const int tid = threadIdx.x;
+    const int BM = a.BM;
+    auto block_scan = [&](int v) {  // inclusive scan over the block
+        scan[tid] = v;
+        __syncthreads();
+        for (int d = 1; d < kRouteThreads; d <<= 1) {
+            const int w = tid >= d ? scan[tid - d] : 0;
+            __syncthreads();
+            scan[tid] += w;
+            __syncthreads();
+        }
+        return scan[tid];
+    };
+    int first = 0, nu = 0;
+    if (tid < a.E) {
+        first = a.offsets[tid] / BM;
+        const int nb = (a.offsets[tid + 1] - a.offsets[tid]) / BM;
+        nu = (nb + kUnitBlocks - 1) / kUnitBlocks;
+    }
+    const int ubase = block_scan(nu) - nu;
+    const int U = scan[kRouteThreads - 1];
+    __syncthreads();
+    for (int k = 0; k < nu; ++k)
+        a.unit_mb[ubase + k] = first + kUnitBlocks * k;
+    if (tid == 0)
+        a.unit_mb[U] = a.offsets[a.E] / BM;
+    __syncthreads();  // the unit table is visible to the whole block
+    // Used row blocks that fit the ring never share a slot: single-wave
+    // order (a lag of U units puts every L1 unit before every L2 unit).
+    // Otherwise the host's lag.  (Lengthening it on the device to the
+    // longest the ring holds for the routed unit sizes was measured slower:
+    // L1 tiles then wait on the slots' previous L2 tiles.)
+    const int RB = a.ring_blocks, G = kStreamGroup;
+    const int L = a.unit_mb[U] <= RB ? U : a.lag_units;
+    const int NT1 = a.I / 128, NT2 = (a.H + 255) / 256;
+    for (int u = tid; u < U; u += kRouteThreads) {
+        const int nbu = a.unit_mb[u + 1] - a.unit_mb[u];
+        const int c = u >= L ? (u - L) / G : 0;
+        const int p1 = u + min(U, G * c);
+        const int p2 = u + 1 + min(G * (u / G) + G - 1 + L, U - 1);
+        a.stream_start[p1] = nbu * NT1;
+        a.stream_desc[p1] = u;
+        a.stream_start[p2] = nbu * NT2;
+        a.stream_desc[p2] = u | kStreamL2;
+    }
+    __syncthreads();
+    // exclusive scan of the 2U item counts, in place, 1024 at a time
+    int carry = 0;
+    for (int base = 0; base < 2 * U; base += kRouteThreads) {
+        const int i = base + tid;
+        const int v = i < 2 * U ? a.stream_start[i] : 0;
+        const int incl = block_scan(v);
+        const int total = scan[kRouteThreads - 1];
+        if (i < 2 * U)
+            a.stream_start[i] = carry + incl - v;
+        carry += total;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        a.stream_start[2 * U] = carry;
+        a.sync[kSyncStreamItems] = carry;
+        a.sync[kSyncUnits] = U;
+    }
+    __syncthreads();
+    // item table: one wave per stream entry, its items in consecutive words
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int p = wave; p < 2 * U; p += kRouteThreads / 64) {
+        const int d = a.stream_desc[p];
+        const bool l2 = (d & kStreamL2) != 0;
+        const int tile0 = a.unit_mb[d & kStreamUnitMask] * (l2 ? NT2 : NT1);
+        const int q0 = a.stream_start[p], n = a.stream_start[p + 1] - q0;
+        for (int i = lane; i < n; i += 64)
+            a.item_tab[q0 + i] = (tile0 + i) | (l2 ? kItemL2 : 0);
+    }
+}
+
+hipError_t launch_route_stream(const FwdArgs& a, hipStream_t s)
+{
+    if (a.E > kRouteThreads || !a.offsets || !a.unit_mb || !a.stream_start || !a.stream_desc ||
+        !a.item_tab || !a.sync || a.ring_blocks <= 0 || a.lag_units < 1)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_stream, dim3(1), dim3(kRouteThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s)
 {
     if (a.NB == 1 && a.E <= 512) {

@@ -72,6 +72,18 @@ extern "C" {
 #define MOE_FLAG_DIRECT_TILES 8   /* 64-row tiles use the direct-load kernels even where
                                      the shared-A 64-row kernel fits (so that
                                      MOE_FLAG_SINGLE_LAUNCH can apply to them) */
+#define MOE_FLAG_RING_POOL 16     /* FP8 recipe with per-128 intermediate scales: L1,
+                                     L2 and the combine run as one launch in the lag
+                                     order of DeepGEMM PR #440 "How it works", and h /
+                                     h_sf become a ring of 8 (lag + 4) + 4 row blocks
+                                     ("Ring sizing, recycling, and why that
+                                     granularity") wherever the call's pool has more
+                                     row blocks than that (moe_plan_info reports
+                                     ring_blocks and l2_lag_units).  Direct-load tiles
+                                     (tile_m 16, 32 or 64), no L1 split.  Invalid with
+                                     MOE_FLAG_SPLIT_LAUNCH, MXFP4 or per-64 scales;
+                                     tile_m 128 is unsupported.  y is bitwise that of
+                                     MOE_FLAG_SINGLE_LAUNCH with the same tiles. */
 #define MOE_FLAG_TEST_NO_WAIT 256 /* test-only: the single launch's waits give up at
                                      once, so MOE_STATUS_WAIT_TIMEOUT is set and y is
                                      invalid; exercises the timeout path */
@@ -134,6 +146,16 @@ typedef struct moe_tile_info {
     int32_t l2_group_tiles; /* L2 tiles (of l2_tile_n columns) per workgroup: 2 for
                                16-row tiles when at least 1024 workgroups remain, else 1 */
     int32_t act_sf_gran;    /* columns per intermediate (h) scale: 128 or 64 (FP8), 32 (MXFP4) */
+    int32_t ring_blocks;    /* MOE_FLAG_RING_POOL calls whose pool has more row blocks
+                               than the ring: row blocks (of tile_m rows) that h and
+                               h_sf hold, block mb at slot mb % ring_blocks; the ring
+                               capacity PR #440's buffer query returns ("API, Tests,
+                               Files").  0: h and h_sf hold the whole pool */
+    int32_t l2_lag_units;   /* with ring_blocks > 0: units (up to 8 row blocks of one
+                               expert) that L2 trails L1 by, clamp(round(0.45 units),
+                               8, 64) for the call's T*K / (8 tile_m) units; a call
+                               whose used blocks fit the ring runs the single-wave
+                               order instead.  0 otherwise */
 } moe_tile_info_t;
 
 /* Byte offsets of the workspace sections used by a forward with T tokens.
@@ -145,6 +167,8 @@ typedef struct moe_tile_info {
  *   h        uint8 [pool_rows, I] e4m3 SwiGLU output (valid rows only)
  *   h_sf     f32   [pool_rows, I/128]  (per-64 plans: [pool_rows, I/64];
  *                                       MXFP4 plans: uint8 UE8M0 [pool_rows, I/32])
+ *            (ring-pool calls, moe_tile_info.ring_blocks > 0: ring_blocks * tile_m rows
+ *            in place of pool_rows, each slot holding the last row block that used it)
  *   partial  uint16 [K, T, H]     bf16 L2 output of slot (t, j) at [j][t]
  *   status   int32 [4]            status[0] = MOE_STATUS_* bits, status[1] = #ids >= E */
 typedef struct moe_ws_layout {

@@ -1,6 +1,7 @@
 """The C-ABI library loads, exports every declared symbol, and rejects invalid
 calls on the host before any HIP call (CPU only: no compute call is made)."""
 import ctypes
+import math
 import os
 import re
 
@@ -451,3 +452,87 @@ def test_noalloc_host_validation_without_gpu():
     finally:
         moe.moe_plan_destroy(p)
         moe.moe_plan_destroy(pmx)
+
+
+def _ring_expect(T, K, tile):
+    # DeepGEMM PR #440 "How it works": units of up to 8 row blocks, lag =
+    # clamp(round(0.45 units), 8, 64); "Ring sizing": 8 (lag + 4) + 4 slots
+    units = max(1, -(-(T * K) // (8 * tile)))
+    lag = min(64, max(8, math.floor(0.45 * units + 0.5)))
+    return 8 * (lag + 4) + 4, lag
+
+
+def test_ring_pool_plan_info_sizes_and_workspace():
+    H, I, E, K = 4096, 2048, 256, 6
+    ring = moe.moe_plan_create(H, I, E, K, 8192, flags=moe.MOE_FLAG_RING_POOL)
+    try:
+        last = 0
+        for T in (1, 2, 17, 128, 300, 1024, 2048, 4096, 5000, 8192):
+            info = moe.moe_plan_info(ring, T)
+            # the single launch with direct-load tiles, one L2 tile per workgroup
+            assert info["kernel"] == 0 and info["l1_split"] == 1, T
+            assert info["single_launch"] == 1 and info["l2_group_tiles"] == 1, T
+            blocks = info["pool_rows"] // info["tile_m"]
+            rb, lag = _ring_expect(T, K, info["tile_m"])
+            if rb < blocks:
+                assert (info["ring_blocks"], info["l2_lag_units"]) == (rb, lag), T
+                # the ring holds the live set 8 (lag + group) + 1
+                assert info["ring_blocks"] >= 8 * (info["l2_lag_units"] + 4) + 1
+            else:  # a ring the size of the pool never wraps
+                assert (info["ring_blocks"], info["l2_lag_units"]) == (0, 0), T
+            b = moe.moe_workspace_bytes(ring, T)
+            assert b >= last, T
+            last = b
+            if info["ring_blocks"] > 0:
+                # against the full pool with the same tiles, h and h_sf shrink
+                # from pool_rows to ring_blocks * tile_m rows
+                full = moe.moe_plan_create(H, I, E, K, 8192, tile_m=info["tile_m"],
+                                           flags=moe.MOE_FLAG_SINGLE_LAUNCH |
+                                           moe.MOE_FLAG_DIRECT_TILES)
+                try:
+                    saved = ((info["pool_rows"] - info["ring_blocks"] * info["tile_m"]) *
+                             (I + 4 * I // 128))
+                    assert moe.moe_workspace_bytes(full, T) - b >= saved // 2, T
+                finally:
+                    moe.moe_plan_destroy(full)
+        assert moe.moe_plan_info(ring, 2048)["ring_blocks"] == 124       # lag 11 at 64-row tiles
+        assert moe.moe_plan_info(ring, 8192)["l2_lag_units"] == 43
+    finally:
+        moe.moe_plan_destroy(ring)
+
+
+def test_ring_pool_flag_rejections():
+    R = moe.MOE_FLAG_RING_POOL
+    for kw, err in ((dict(flags=R | moe.MOE_FLAG_SPLIT_LAUNCH), moe.MOE_ERR_INVALID_ARG),
+                    (dict(flags=R, recipe=moe.MOE_RECIPE_MXFP4), moe.MOE_ERR_INVALID_ARG),
+                    (dict(flags=R, act_sf_gran=64), moe.MOE_ERR_INVALID_ARG),
+                    (dict(flags=R, act_sf_gran=-1), moe.MOE_ERR_INVALID_ARG),  # 2I % 512 != 0
+                    (dict(flags=R, tile_m=128), moe.MOE_ERR_UNSUPPORTED_SHAPE)):
+        H, I = (4096, 2048 + 128) if kw.get("act_sf_gran") == -1 else (4096, 2048)
+        with pytest.raises(moe.MoEError) as ex:
+            moe.moe_plan_create(H, I, 256, 6, 64, **kw)
+        assert ex.value.code == err, kw
+    # the shape rule that gives per-128 scales keeps the ring
+    p = moe.moe_plan_create(4096, 2048, 256, 6, 64, flags=R, act_sf_gran=-1)
+    moe.moe_plan_destroy(p)
+
+
+def test_ring_pool_over_capacity_rejected_before_any_launch():
+    # a token count one alignment above the plan's bound is refused on the
+    # host, before any HIP call (DeepGEMM PR #440 "API, Tests, Files")
+    L = moe.lib()
+    a = ctypes.c_void_p(0x1000)
+    p = moe.moe_plan_create(4096, 2048, 256, 6, 1024, flags=moe.MOE_FLAG_RING_POOL)
+    try:
+        for T in (1025, 1024 + 16, 1024 + 64):
+            assert L.moe_forward(p, T, *([a] * 9), a, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+            with pytest.raises(moe.MoEError):
+                moe.moe_plan_info(p, T)
+            with pytest.raises(moe.MoEError):
+                moe.moe_workspace_bytes(p, T)
+        # a workspace one byte short is refused before any HIP call too
+        need = moe.moe_workspace_bytes(p, 1024)
+        assert L.moe_forward(p, 1024, *([a] * 9), ctypes.c_void_p(0x100000), need - 1,
+                             None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    finally:
+        moe.moe_plan_destroy(p)

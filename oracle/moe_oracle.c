@@ -71,11 +71,19 @@
  *              acc) then acc = fmaf(sa[2kb+1] sb, p_hi, acc), p_lo / p_hi the
  *              exact 64-term sums rounded once to f32.
  *
- * Pins: every function here is checked by tests/test_oracle_pins.py against
- * closed forms, library codecs, an fp64 unquantised MoE, a dense SwiGLU FFN
- * written separately, brute-force routing and exact rational arithmetic.
- * Parity of the GPU result against this oracle beyond the stated tolerance
- * (f32 summation order inside the MFMA, expf ulps) is "parity unpinned".
+ * Steps 5-6 alone: orc_moe_l2_combine (and its MXFP4 form) start L2 from a
+ * given intermediate h / h_sf, so a test can feed it the GPU's own h and
+ * compare each later step with the GPU's; fed the forward's own h it
+ * returns the forward's partials and y bit for bit.  The forward can also
+ * return the L1 accumulator, its magnitude sum |a||b| scale per column (the
+ * scale of a bound on rounding inside a block), and the SwiGLU value before
+ * requantisation, for the same step-by-step comparison.
+ *
+ * Pins: every function here is checked against something other than itself
+ * (tests/test_oracle_pins*.py): closed forms, library codecs, an fp64
+ * unquantised MoE, a dense SwiGLU FFN written separately, brute-force
+ * routing, exact rational arithmetic, and the forward itself for the
+ * L2 + combine entries.  No function here is unpinned.
  */
 #include <math.h>
 #include <stddef.h>

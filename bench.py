@@ -314,6 +314,9 @@ def main():
                     help="fp8: e4m3 x e4m3 with f32 block scales (1x128, 128x128); mxfp4: "
                          "e4m3 activations x e2m1 weights with UE8M0 scales per 32 "
                          "(row-major weights)")
+    ap.add_argument("--act-sf-gran", type=int, default=0, choices=(0, 64, 128, -1),
+                    help="FP8 recipe: columns per intermediate scale (0/128: per-128, 64: "
+                         "per-64 with the dual-half L2, -1: the per-shape rule)")
     ap.add_argument("--weights", choices=("packed", "row_major"), default="packed",
                     help="expert weight layout the plan expects (packed = one-time "
                          "moe_prepare_weights re-layout, done before timing)")
@@ -414,7 +417,7 @@ def run_workload(args, cfg, seed, steps, warmup, flush, cpu_1t):
     runner = moe.MoEForward(cfg.H, cfg.I, cfg.E, cfg.K, cfg.T, tile_m=args.tile_m, device=dev,
                             weight_layout=layout,
                             recipe=moe.MOE_RECIPE_MXFP4 if mx else moe.MOE_RECIPE_FP8_BLOCK128,
-                            flags=flags)
+                            flags=flags, act_sf_gran=0 if mx else args.act_sf_gran)
     info = moe.moe_plan_info(runner.plan, cfg.T)
     y = torch.empty(cfg.T, cfg.H, dtype=torch.uint16, device=dev)
     stream = torch.cuda.current_stream()

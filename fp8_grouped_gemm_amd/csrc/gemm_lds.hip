@@ -134,9 +134,19 @@ __device__ __forceinline__ const uint8_t* weight_src_mx(const FwdArgs& a, int e,
 
 // L1 (gate + up) when L1 is true, L2 (down) otherwise.  Needs at least two
 // K blocks (H >= 256 and I >= 256; the plan enforces it).
-template <bool L1, bool PK, bool MX>
+// G64 (FP8 recipe): per-64 intermediate scales ("MegaMoE SM90 Implementation
+// Design" §5.4).  L1 requantises each 64-column half of its 128 gate/up
+// columns on its own (waves wn = 2b, 2b + 1 hold block b); L2's scale copy
+// carries both scales of each row and K block (lanes 0-15 the first, 32-47
+// the second; lanes 16-17 stay the weight scales), and each 128-K block is
+// multiplied as its two 64-K halves -- bytes 0-15 of every A fragment are K
+// 0-63, bytes 16-31 K 64-127, so a copy with one half zeroed gives that
+// half's sum -- each promoted with its own activation scale.
+template <bool L1, bool PK, bool MX, bool G64>
 __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 {
+    static_assert(!(MX && G64), "per-64 scales are an FP8-recipe option");
+    constexpr bool D64 = G64 && !L1;  // L2 multiplies dual halves
     using C = LdsCfg<MX>;
     constexpr int B_BYTES = C::B_BYTES, STAGE = C::STAGE, NSTAGE = C::NSTAGE;
     constexpr int kCopiesPerBlock = C::COPIES;
@@ -214,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     int i_e = 0, i_nt = 0;
     const uint8_t* a_src[2] = {nullptr, nullptr};
     const float* s_src = nullptr;
+    int s_step = 1;                     // floats between K blocks of s_src
     const uint8_t* s_src_mx = nullptr;  // MXFP4: this wave's 4 scale bytes per lane
     uint32_t s_stride = 0;              // bytes between K blocks of s_src_mx
     // Starts issuing tile k: reads its expert and row sources from its
@@ -291,11 +302,16 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                     s_src = a.w1_sf + ((size_t)e * (2 * I / 128) + (q ? I / 128 + nt : nt)) * nkb;
                 else
                     s_src = a.w2_sf + ((size_t)e * (H / 128) + 2 * nt + q) * nkb;
+                s_step = 1;
             } else {
-                if constexpr (L1)
+                if constexpr (L1) {
                     s_src = a.x_sf + (size_t)(f >= 0 ? f / K : 0) * (H / 128);
-                else
+                } else if constexpr (D64) {  // lanes 32-47: the second half's scale
+                    s_src = a.h_sf + (size_t)r * (I / 64) + (lg == 2 ? 1 : 0);
+                    s_step = 2;
+                } else {
                     s_src = a.h_sf + (size_t)r * (I / 128);
+                }
             }
         }
     };
@@ -331,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                 const int q = wave * C::B_COPIES + j, sub = q >> 1, half = q & 1;
                 dma16(weight_src<L1, PK>(a, i_e, i_nt, kb, sub, half, lane), st + A_BYTES + q * 1024);
             }
-            dma4(s_src + kb, st + A_BYTES + B_BYTES + wave * 256);
+            dma4(s_src + (size_t)kb * s_step, st + A_BYTES + B_BYTES + wave * 256);
         }
         int n = kCopiesPerBlock;
         if (kb == 0) {
@@ -433,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                                                           sa[ms], sb[s]);
         } else {
             v8i af[4], bf[4];
-            float sa[4][4];
+            float sa[4][4], sa2[D64 ? 4 : 1][4];
             const float* s_lds = reinterpret_cast<const float*>(st + A_BYTES + B_BYTES);
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) {
@@ -443,6 +459,14 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                 sa[ms][1] = s4.y;
                 sa[ms][2] = s4.z;
                 sa[ms][3] = s4.w;
+                if constexpr (D64) {  // the second half's scales, copied by lanes 32-47
+                    const float4 t4 =
+                        *reinterpret_cast<const float4*>(s_lds + (wm * 4 + ms) * 64 + 32 + 4 * lg);
+                    sa2[ms][0] = t4.x;
+                    sa2[ms][1] = t4.y;
+                    sa2[ms][2] = t4.z;
+                    sa2[ms][3] = t4.w;
+                }
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s)
@@ -456,15 +480,30 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const float sb = (L1 && s >= 2) ? su : sg;
-                v4f p[4];
+                if constexpr (D64) {
 #pragma unroll
-                for (int ms = 0; ms < 4; ++ms)
-                    p[ms] = mfma_16x16x128_e4m3(af[ms], bf[s], v4f{0.f, 0.f, 0.f, 0.f});
+                    for (int ms = 0; ms < 4; ++ms) {
+                        const v8i alo = {af[ms][0], af[ms][1], af[ms][2], af[ms][3], 0, 0, 0, 0};
+                        const v8i ahi = {0, 0, 0, 0, af[ms][4], af[ms][5], af[ms][6], af[ms][7]};
+                        const v4f plo = mfma_16x16x128_e4m3(alo, bf[s], v4f{0.f, 0.f, 0.f, 0.f});
+                        const v4f phi = mfma_16x16x128_e4m3(ahi, bf[s], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int ms = 0; ms < 4; ++ms)
+                        for (int i = 0; i < 4; ++i) {
+                            acc[ms][s][i] = fmaf(sa[ms][i] * sb, plo[i], acc[ms][s][i]);
+                            acc[ms][s][i] = fmaf(sa2[ms][i] * sb, phi[i], acc[ms][s][i]);
+                        }
+                    }
+                } else {
+                    v4f p[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[ms][i], acc[ms][s][i]);
+                    for (int ms = 0; ms < 4; ++ms)
+                        p[ms] = mfma_16x16x128_e4m3(af[ms], bf[s], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[ms][i], acc[ms][s][i]);
+                }
             }
         }
         ++j;
@@ -549,15 +588,21 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
                 for (int i = 0; i < 4; ++i) {
                     const int r = wm * 64 + ms * 16 + 4 * lg + i;
                     const float4 rm = *reinterpret_cast<const float4*>(red + r * 4);
-                    const float amax = fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
+                    // per-64 scales: waves wn = 2b, 2b + 1 hold block b of the tile
+                    const float amax = G64 ? (wn < 2 ? fmaxf(rm.x, rm.y) : fmaxf(rm.z, rm.w))
+                                           : fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
                     float rsf;
                     const float sf = requant_sf(amax, a.pow2_scale, rsf);
 #pragma unroll
                     for (int s = 0; s < 2; ++s)
                         qt[r * 128 + wn * 32 + s * 16 + lr] =
                             (uint8_t)requant_q(acc[ms][s][i], sf, rsf, a.pow2_scale);
-                    if (wn == 0 && lr == 0)
+                    if constexpr (G64) {
+                        if ((wn & 1) == 0 && lr == 0)
+                            a.h_sf[(size_t)(row0 + r) * (I / 64) + nt * 2 + (wn >> 1)] = sf;
+                    } else if (wn == 0 && lr == 0) {
                         a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
+                    }
                 }
             __syncthreads();
             // BM rows x 128 bytes, 16 bytes per thread, two per thread (rows
@@ -646,7 +691,11 @@ static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
         g = a.grid_cap;
     const dim3 grid((unsigned)g);
     const size_t smem = (size_t)LdsCfg<MX>::SMEM;
-    auto kern = a.packed ? gemm_lds<L1, true, MX> : gemm_lds<L1, false, MX>;
+    auto kern = a.packed ? gemm_lds<L1, true, MX, false> : gemm_lds<L1, false, MX, false>;
+    if constexpr (!MX) {
+        if (a.sf_gran64)
+            kern = a.packed ? gemm_lds<L1, true, false, true> : gemm_lds<L1, false, false, true>;
+    }
     err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (err != hipSuccess)
         return err;

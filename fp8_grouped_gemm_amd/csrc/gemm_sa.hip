@@ -52,10 +52,21 @@ static_assert(SA_A == 4 * SA_ACOPIES * 1024, "four waves copy the A stage");
 
 }  // namespace
 
-template <bool L1, bool PK>
+// G64: per-64 intermediate scales ("MegaMoE SM90 Implementation Design"
+// §5.4).  L1 requantises each 64-column half of its 128 gate/up columns on
+// its own (waves 2b and 2b + 1 hold block b); L2 copies both scales of each
+// row and K block (lanes 0-15 the first, 16-31 the second) and multiplies
+// each 128-K block as its two 64-K halves -- bytes 0-15 of every A fragment
+// are K 0-63, bytes 16-31 K 64-127, so a copy with one half zeroed gives
+// that half's sum -- each promoted with its own activation scale.  The
+// dual-half L2 needs more registers than two workgroups per compute unit
+// leave (18-32 VGPRs spill); one workgroup per unit fits without spills but
+// measured slower (flash-prefill L2 478 -> 589 us), so the spills stay.
+template <bool L1, bool PK, bool G64>
 __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t stage_mem[SA_NS * SA_STAGE];
+    constexpr bool D64 = G64 && !L1;  // L2 multiplies dual halves
     const int H = a.H, I = a.I, K = a.K, T = a.T;
     const int NT = L1 ? I / 128 : H / 256;
     const int nkb = L1 ? H / 128 : I / 128;
@@ -88,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
     } else {
         const size_t r = fr >= 0 ? (size_t)(row0 + 16 * wave + lr) : (size_t)row0;
         asrc = a.h + r * I + 16 * lg;
-        ssrc = a.h_sf + r * (I / 128);
+        ssrc = D64 ? a.h_sf + r * (I / 64) + (lg & 1) : a.h_sf + r * (I / 128);
     }
 
     // Weights: subtile s of this wave (L1: s = 0,1 gate, 2,3 up).
@@ -142,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
         for (int j = 0; j < SA_ACOPIES; ++j)
             dma16(asrc + (size_t)kb * 128 + 64 * j, st + (wave * 2 + j) * 1024);
         static_assert(SA_SCOPIES == 1, "one scale copy below");
-        dma4(ssrc + kb, st + SA_A + wave * 256);
+        dma4(ssrc + (D64 ? 2 * kb : kb), st + SA_A + wave * 256);
         b.sg = sfg[kb];
         b.su = L1 ? sfu[kb] : b.sg;
 #pragma unroll
@@ -161,27 +172,54 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
         __syncthreads();
         const uint8_t* st = stage_mem + (kb_m % SA_NS) * SA_STAGE;
         const float* s_lds = reinterpret_cast<const float*>(st + SA_A);
-        v8i af[4];
-        float sa[4][4];
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-            af[ms] = lds_frag(st + ms * 2048, lane);
-            const float4 s4 = *reinterpret_cast<const float4*>(s_lds + ms * 64 + 4 * lg);
-            sa[ms][0] = s4.x;
-            sa[ms][1] = s4.y;
-            sa[ms][2] = s4.z;
-            sa[ms][3] = s4.w;
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const v8i bv = pack_frag(b.fb[s].lo, b.fb[s].hi);
-            const float sb = (L1 && s >= 2) ? b.su : b.sg;
+        if constexpr (D64) {
+            // one m-subtile at a time (its fragment, both halves' scales),
+            // which keeps the dual-half multiply within the register budget
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) {
-                const v4f p = mfma_16x16x128_e4m3(af[ms], bv, v4f{0.f, 0.f, 0.f, 0.f});
+                const v8i af = lds_frag(st + ms * 2048, lane);
+                const float4 s4 = *reinterpret_cast<const float4*>(s_lds + ms * 64 + 4 * lg);
+                // the second half's scales, copied by lanes 16-31
+                const float4 t4 = *reinterpret_cast<const float4*>(s_lds + ms * 64 + 16 + 4 * lg);
+                const float sa[4] = {s4.x, s4.y, s4.z, s4.w}, sa2[4] = {t4.x, t4.y, t4.z, t4.w};
+                const v8i alo = {af[0], af[1], af[2], af[3], 0, 0, 0, 0};
+                const v8i ahi = {0, 0, 0, 0, af[4], af[5], af[6], af[7]};
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[i], acc[ms][s][i]);
+                for (int s = 0; s < 4; ++s) {
+                    const v8i bv = pack_frag(b.fb[s].lo, b.fb[s].hi);
+                    const float sb = b.sg;
+                    const v4f plo = mfma_16x16x128_e4m3(alo, bv, v4f{0.f, 0.f, 0.f, 0.f});
+                    const v4f phi = mfma_16x16x128_e4m3(ahi, bv, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[ms][s][i] = fmaf(sa[i] * sb, plo[i], acc[ms][s][i]);
+                        acc[ms][s][i] = fmaf(sa2[i] * sb, phi[i], acc[ms][s][i]);
+                    }
+                }
+            }
+        } else {
+            v8i af[4];
+            float sa[4][4];
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+                af[ms] = lds_frag(st + ms * 2048, lane);
+                const float4 s4 = *reinterpret_cast<const float4*>(s_lds + ms * 64 + 4 * lg);
+                sa[ms][0] = s4.x;
+                sa[ms][1] = s4.y;
+                sa[ms][2] = s4.z;
+                sa[ms][3] = s4.w;
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const v8i bv = pack_frag(b.fb[s].lo, b.fb[s].hi);
+                const float sb = (L1 && s >= 2) ? b.su : b.sg;
+#pragma unroll
+                for (int ms = 0; ms < 4; ++ms) {
+                    const v4f p = mfma_16x16x128_e4m3(af[ms], bv, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[ms][s][i] = fmaf(sa[ms][i] * sb, p[i], acc[ms][s][i]);
+                }
             }
         }
         ++kb_m;
@@ -225,15 +263,21 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * ms + 4 * lg + i;
                 const float4 rm = *reinterpret_cast<const float4*>(red[r]);
-                const float amax = fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
+                // per-64 scales: waves 2b, 2b + 1 hold block b of the tile
+                const float amax = G64 ? (wave < 2 ? fmaxf(rm.x, rm.y) : fmaxf(rm.z, rm.w))
+                                       : fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
                 float rsf;
                 const float sf = requant_sf(amax, a.pow2_scale, rsf);
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
                     qt[r][wave * 32 + s * 16 + lr] =
                         (uint8_t)requant_q(hv[ms][s][i], sf, rsf, a.pow2_scale);
-                if (wave == 0 && lr == 0)
+                if constexpr (G64) {
+                    if ((wave & 1) == 0 && lr == 0)
+                        a.h_sf[(size_t)(row0 + r) * (I / 64) + nt * 2 + (wave >> 1)] = sf;
+                } else if (wave == 0 && lr == 0) {
                     a.h_sf[(size_t)(row0 + r) * (I / 128) + nt] = sf;
+                }
             }
         }
         __syncthreads();
@@ -481,8 +525,11 @@ static hipError_t launch_sa(const FwdArgs& a, hipStream_t s)
     if (a.mx) {
         auto kern = a.packed ? gemm_sa_mx<L1, true> : gemm_sa_mx<L1, false>;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, a);
+    } else if (a.sf_gran64) {
+        auto kern = a.packed ? gemm_sa<L1, true, true> : gemm_sa<L1, false, true>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, a);
     } else {
-        auto kern = a.packed ? gemm_sa<L1, true> : gemm_sa<L1, false>;
+        auto kern = a.packed ? gemm_sa<L1, true, false> : gemm_sa<L1, false, false>;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, a);
     }
     return hipGetLastError();

@@ -61,7 +61,7 @@ Config choose_config(const moe_shape_t& s, int T)
 {
     // ring-pool plans run the single launch, which has direct-load tiles only
     const bool ring = (s.flags & MOE_FLAG_RING_POOL) != 0;
-    const bool lds = lds_tile_fits(s) && sf_gran(s) != 64 && !ring;
+    const bool lds = lds_tile_fits(s) && !ring;
     const bool lds64 = lds && !(s.flags & MOE_FLAG_DIRECT_TILES);
     // 64-row tiles where the LDS tiles fit: the shared-A tile (kernel 2)
     const int k64 = lds64 ? 2 : 0;
@@ -319,9 +319,7 @@ int validate_shape(const moe_shape_t* s)
         return MOE_ERR_INVALID_ARG;
     if (!(s->activation_clamp == s->activation_clamp))  // NaN
         return MOE_ERR_INVALID_ARG;
-    if (sf_gran(*s) == 64) {  // per-64 plans: direct-load tiles, split launches
-        if (s->tile_m == 128)
-            return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (sf_gran(*s) == 64) {  // per-64 plans: split launches
         if (s->flags & MOE_FLAG_SINGLE_LAUNCH)
             return MOE_ERR_INVALID_ARG;
     }

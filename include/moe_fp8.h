@@ -123,8 +123,9 @@ typedef struct moe_shape {
                               64 (L2 then scales each 128-K block as two 64-K halves,
                               design doc §5.4), or -1 for the rule of PR #440 "How it
                               works" (128 when H % 512 == 0 and 2I % 512 == 0, else 64).
-                              Per-64 plans use direct-load tiles (tile_m <= 64) and
-                              split launches.  MXFP4 plans: 0 (their blocks are 32). */
+                              Per-64 plans run every tile kind as split launches (no
+                              single launch, no ring pool).  MXFP4 plans: 0 (their
+                              blocks are 32). */
     float activation_clamp; /* > 0: gate and up are clamped to [-c, c] before the
                                SwiGLU (design doc §10.1); <= 0: no clamp */
 } moe_shape_t;

@@ -148,14 +148,14 @@ def test_tile128_needs_two_k_blocks_per_layer():
 
 
 def test_tile64_kernel_choice():
-    # 64-row tiles run on the shared-A kernel where the LDS tiles fit, on
-    # the direct-load kernel where they do not (H % 256 != 0, too few K
-    # blocks, per-64 scales) or when the plan asks for direct tiles
+    # 64-row tiles run on the shared-A kernel where the LDS tiles fit (per-64
+    # scales included), on the direct-load kernel where they do not (H % 256
+    # != 0, too few K blocks) or when the plan asks for direct tiles
     cases = [((512, 384, 16, 4), {}, 2),
              ((512, 384, 16, 4), dict(flags=moe.MOE_FLAG_DIRECT_TILES), 0),
              ((384, 256, 8, 2), {}, 0),
              ((256, 128, 8, 2), {}, 0),
-             ((512, 384, 16, 4), dict(act_sf_gran=64), 0),
+             ((512, 384, 16, 4), dict(act_sf_gran=64), 2),
              ((512, 384, 16, 4), dict(recipe=moe.MOE_RECIPE_MXFP4), 2),
              ((512, 256, 16, 4), dict(recipe=moe.MOE_RECIPE_MXFP4), 0)]  # MX: 3 K blocks
     for shape, kw, kernel in cases:
@@ -374,10 +374,9 @@ def test_mx_recipe_validation_and_choices():
 
 
 def test_recipe_options_validation_and_rule():
-    # act_sf_gran: 0/128, 64, -1 (PR #440 rule); per-64 plans: no LDS tile,
-    # no single launch; MXFP4 plans: no per-64 or power-of-two flag; NaN clamp
+    # act_sf_gran: 0/128, 64, -1 (PR #440 rule); per-64 plans: no single
+    # launch; MXFP4 plans: no per-64 or power-of-two flag; NaN clamp
     for kw, code in ((dict(act_sf_gran=32), moe.MOE_ERR_INVALID_ARG),
-                     (dict(act_sf_gran=64, tile_m=128), moe.MOE_ERR_UNSUPPORTED_SHAPE),
                      (dict(act_sf_gran=64, flags=moe.MOE_FLAG_SINGLE_LAUNCH), moe.MOE_ERR_INVALID_ARG),
                      (dict(activation_clamp=float("nan")), moe.MOE_ERR_INVALID_ARG),
                      (dict(act_sf_gran=64, recipe=moe.MOE_RECIPE_MXFP4), moe.MOE_ERR_INVALID_ARG),
@@ -392,10 +391,15 @@ def test_recipe_options_validation_and_rule():
         try:
             info = moe.moe_plan_info(p, 4096)
             assert info["act_sf_gran"] == want, (H, I)
-            if want == 64:  # direct tiles only
-                assert info["tile_m"] <= 64
         finally:
             moe.moe_plan_destroy(p)
+    # per-64 plans take the LDS tiles where they fit (128 rows at 4096 tokens)
+    p = moe.moe_plan_create(4096, 2048, 256, 6, 8192, act_sf_gran=64)
+    try:
+        assert moe.moe_plan_info(p, 8192)["kernel"] == 1
+        assert moe.moe_plan_info(p, 2048)["kernel"] == 2
+    finally:
+        moe.moe_plan_destroy(p)
     # per-64 needs twice the h_sf bytes; the workspace grows accordingly
     a = moe.moe_plan_create(4096, 2048, 256, 6, 128)
     b = moe.moe_plan_create(4096, 2048, 256, 6, 128, act_sf_gran=64)

@@ -41,6 +41,52 @@ def test_per64_scales_all_direct_tiles(tile_m):
     assert not torch.equal(y, y128)
 
 
+@pytest.mark.parametrize("tile_m", [64, 128])
+def test_per64_scales_lds_tiles(tile_m):
+    # the shared-A (64-row) and LDS-staged (128-row) tiles with per-64 h
+    # scales: L1 requantises each 64-column half on its own, L2 multiplies
+    # dual halves; same oracle reading as the direct tiles (bitwise equal to
+    # them), and the 128-row tile on a 4-workgroup grid walks many tiles
+    host, dev = small_case(300, 512, 384, 16, 4, 503, mask={(0, 1): -1, (9, 2): 77}, skew=True)
+    y, r = run_opts(dev, tile_m=tile_m, gran=64)
+    info = moe.moe_plan_info(r.plan, 300)
+    assert info["act_sf_gran"] == 64 and info["kernel"] == (2 if tile_m == 64 else 1), info
+    verify(y, r, host, f"per-64 LDS tile {tile_m}", oflags=oracle.ORC_SF_GRAN64)
+    y_direct, rd = run_opts(dev, tile_m=64, gran=64, flags=moe.MOE_FLAG_DIRECT_TILES)
+    assert moe.moe_plan_info(rd.plan, 300)["kernel"] == 0
+    assert torch.equal(y, y_direct), "per-64: LDS tile and direct tile differ"
+    if tile_m == 128:
+        y_small, _ = run_opts(dev, tile_m=128, gran=64, flags=moe.MOE_FLAG_TEST_SMALL_GRID)
+        assert torch.equal(y, y_small)
+
+
+@pytest.mark.parametrize("name", ["flash_prefill", "pro_prefill", "skewed"])
+def test_per64_full_size_sampled(name):
+    # configs 3-5 with per-64 h scales on the library's prefill tiles,
+    # sampled tokens through the whole chain
+    cfg = wl.CONFIGS[name]
+    seed = wl.default_seed(cfg)
+    inp = wl.make_inputs(cfg, seed, "cuda")
+    r = moe.MoEForward(cfg.H, cfg.I, cfg.E, cfg.K, cfg.T, weight_layout=moe.MOE_WEIGHTS_PACKED,
+                       act_sf_gran=64)
+    info = moe.moe_plan_info(r.plan, cfg.T)
+    say(f"per-64 {name}: tile {info['tile_m']} kernel {info['kernel']}")
+    assert info["act_sf_gran"] == 64 and info["kernel"] in (1, 2)
+    w1, w2 = r.prepare(inp["w1"], inp["w2"])
+    y = r.forward(inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_w"], w1, inp["w1_sf"], w2,
+                  inp["w2_sf"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    toks = sorted({0, cfg.T - 1, *rng.choice(cfg.T, 16, replace=False).tolist()})
+    host = host_copy_for_oracle(inp, toks)
+    del w1, w2
+    verify(y, r, host, f"per-64 {name} ({len(toks)} tokens)", tokens=toks,
+           oflags=oracle.ORC_SF_GRAN64)
+    r.close()
+    del inp
+    torch.cuda.empty_cache()
+
+
 def test_per64_rule_and_split_k():
     # -1: the rule of PR #440 (hidden 256 is not a multiple of 512 -> 64)
     cfg = wl.CONFIGS["tiny"]

@@ -861,7 +861,7 @@ __global__ __launch_bounds__(256) void fused_ring(FwdArgs a)
 template <bool PK>
 static hipError_t launch_l1_t(const FwdArgs& a, hipStream_t s)
 {
-    const unsigned tiles = a.num_mblocks * (a.I / 128);
+    const unsigned tiles = a.grid_mblocks * (a.I / 128);
     switch (a.BM) {
     case 16:
         if (a.split_l1 > 1) {
@@ -890,7 +890,7 @@ static hipError_t launch_l1_t(const FwdArgs& a, hipStream_t s)
 template <bool PK>
 static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
 {
-    const unsigned tiles = a.num_mblocks * ((a.H + 255) / 256);
+    const unsigned tiles = a.grid_mblocks * ((a.H + 255) / 256);
     if (a.sf_gran64) {  // per-64 intermediate scales: dual-half L2, 4-wave tiles
         switch (a.BM) {
         case 16: hipLaunchKernelGGL((l2_direct<1, PK, 4, true>), dim3(tiles), dim3(256), 0, s, a); break;
@@ -903,7 +903,7 @@ static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
     switch (a.BM) {
     case 16:
         if (a.l2_wide) {  // two 256-column tiles per workgroup, 8 waves
-            const unsigned groups = a.num_mblocks * (((a.H + 255) / 256 + 1) / 2);
+            const unsigned groups = a.grid_mblocks * (((a.H + 255) / 256 + 1) / 2);
             hipLaunchKernelGGL((l2_direct<1, PK, 8>), dim3(groups), dim3(512), 0, s, a);
         } else {
             hipLaunchKernelGGL((l2_direct<1, PK, 4>), dim3(tiles), dim3(256), 0, s, a);
@@ -930,7 +930,7 @@ static hipError_t launch_fused_t(const FwdArgs& a, hipStream_t s)
         return err;
     if (cus <= 0 || per_cu <= 0)
         return hipErrorInvalidConfiguration;
-    const long long n = (long long)a.num_mblocks * (a.I / 128 + (a.H + 255) / 256) +
+    const long long n = (long long)a.grid_mblocks * (a.I / 128 + (a.H + 255) / 256) +
                         ((long long)a.T * (a.H / 8) + 255) / 256;
     long long cap = (long long)cus * per_cu;  // resident workgroups
     if (a.grid_cap > 0 && cap > a.grid_cap)

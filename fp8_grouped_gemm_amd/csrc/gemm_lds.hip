@@ -672,7 +672,7 @@ static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
     if (a.BM != BM)  // (64-row tiles run the shared-A kernels of gemm_sa.hip)
         return hipErrorInvalidValue;
     const int NT = L1 ? a.I / 128 : a.H / 256;
-    const long long n_tiles = (long long)a.num_mblocks * NT;
+    const long long n_tiles = (long long)a.grid_mblocks * NT;
     const int nkb = L1 ? a.H / 128 : a.I / 128;
     if (n_tiles <= 0)
         return hipSuccess;

@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void l2_mx(FwdArgs a)
 template <bool PK>
 static hipError_t launch_l1_mx_t(const FwdArgs& a, hipStream_t s)
 {
-    const unsigned grid = a.num_mblocks * (a.I / 128);
+    const unsigned grid = a.grid_mblocks * (a.I / 128);
     switch (a.BM) {
     case 16: hipLaunchKernelGGL((l1_mx<1, PK>), dim3(grid), dim3(256), 0, s, a); break;
     case 32: hipLaunchKernelGGL((l1_mx<2, PK>), dim3(grid), dim3(256), 0, s, a); break;
@@ -370,7 +370,7 @@ static hipError_t launch_l1_mx_t(const FwdArgs& a, hipStream_t s)
 template <bool PK>
 static hipError_t launch_l2_mx_t(const FwdArgs& a, hipStream_t s)
 {
-    const unsigned grid = a.num_mblocks * ((a.H + 255) / 256);
+    const unsigned grid = a.grid_mblocks * ((a.H + 255) / 256);
     switch (a.BM) {
     case 16: hipLaunchKernelGGL((l2_mx<1, PK>), dim3(grid), dim3(256), 0, s, a); break;
     case 32: hipLaunchKernelGGL((l2_mx<2, PK>), dim3(grid), dim3(256), 0, s, a); break;

@@ -516,7 +516,7 @@ template <bool L1>
 static hipError_t launch_sa(const FwdArgs& a, hipStream_t s)
 {
     const int NT = L1 ? a.I / 128 : a.H / 256;
-    const long long grid = (long long)a.num_mblocks * NT;
+    const long long grid = (long long)a.grid_mblocks * NT;
     // FP8 needs two K blocks per layer, MXFP4 three
     if (a.BM != SA_BM || (!L1 && a.H % 256) || (L1 ? a.H : a.I) < (a.mx ? 384 : 256))
         return hipErrorInvalidValue;

@@ -631,6 +631,7 @@ int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, 
     a.offsets = at<int32_t>(workspace, L.offsets);
     a.mblock_expert = at<int32_t>(workspace, L.mbe);
     a.num_mblocks = L.mb_cap;
+    a.grid_mblocks = (int)std::min<long long>(L.mb_cap, std::max<long long>(1, (long long)T * s.top_k));
     a.h = at<uint8_t>(workspace, L.h);
     a.partial = at<uint16_t>(workspace, L.partial);
     a.y = op.y;

@@ -42,7 +42,11 @@ struct FwdArgs {
     const int32_t* row_src;
     const int32_t* offsets;        // [E+1] first pool row of each expert's segment
     const int32_t* mblock_expert;
-    int32_t num_mblocks;
+    int32_t num_mblocks;   // row blocks of the pool's capacity (array sizes)
+    // row blocks the launch grids cover: min(num_mblocks, T*K), since the
+    // routed slots fill at most one new block each; blocks past the used
+    // ones are empty and their workgroups would only read -1 and exit
+    int32_t grid_mblocks;
     uint8_t* h;
     float* h_sf;
     uint16_t* partial;

@@ -32,11 +32,15 @@ struct Config {
 // Rows per tile from the expected rows per expert T*K/E: the smallest tile
 // that holds an average expert's rows reads each expert's weights once
 // while padding as few MFMA rows as possible (decode: 16).
-// Beyond ~24 rows per expert the LDS-using MFMA tiles take over: the 64-row
-// shared-A tile of gemm_sa.hip up to kRowsLds64 rows per expert and the
-// 128 x 256 LDS-staged tile above (they need H % 256 == 0 for their
+// Beyond kRows32 rows per expert the LDS-using MFMA tiles take over: the
+// 64-row shared-A tile of gemm_sa.hip up to kRowsLds64 rows per expert and
+// the 128 x 256 LDS-staged tile above (they need H % 256 == 0 for their
 // 256-column L2 tiles and enough K blocks, lds_tile_fits; otherwise 64-row
-// direct-load tiles).
+// direct-load tiles).  kRows32: at ~24 rows a tenth of the experts already
+// overflow 32 rows, and the extra row blocks start a second, mostly idle
+// round of 32-row workgroups (measured on the EP8 share, 32 experts: 145 us
+// at 21 rows, 183 us at 24, against 152-155 us for the shared-A tile; on the
+// flash shape the two cross between 20 and 22.5 rows).
 // Columns per intermediate scale of an FP8 plan (MXFP4: 32).
 int sf_gran(const moe_shape_t& s)
 {
@@ -55,6 +59,9 @@ bool lds_tile_fits(const moe_shape_t& s)
     return s.hidden % 256 == 0 && s.hidden / 128 >= min_kb && s.intermediate / 128 >= min_kb;
 }
 
+constexpr double kRows16 = 10.0;     // FP8: 16-row tiles up to here (12 rows: 32-row 6 % faster)
+constexpr double kRows16Mx = 12.0;   // MXFP4: 16-row tiles up to here, then shared-A
+constexpr double kRows32 = 21.0;
 constexpr double kRowsLds64 = 64.0;
 
 Config choose_config(const moe_shape_t& s, int T)
@@ -68,9 +75,12 @@ Config choose_config(const moe_shape_t& s, int T)
     if (s.tile_m > 0)
         return Config{s.tile_m, s.tile_m == 128 ? 1 : s.tile_m == 64 ? k64 : 0};
     const double rows = (double)T * s.top_k / s.num_experts;
-    if (rows <= 12.0)
+    const bool mx = s.recipe == MOE_RECIPE_MXFP4;
+    if (rows <= (mx ? kRows16Mx : kRows16))
         return Config{16, 0};
-    if (rows <= 24.0)
+    // MXFP4: the shared-A tile beats the 32-row tile from 12 rows on
+    // (flash shape at 15 rows per expert: 693 vs 706 us; EP8 share: 104 vs 108)
+    if (rows <= kRows32 && !(mx && lds64))
         return Config{32, 0};
     if (!lds)
         return Config{64, 0};

@@ -177,9 +177,9 @@ def test_mx_large_prefill_sampled(name):
 
 def test_mx_flash_decode_ep8_share_every_token():
     # one GPU's expert share under 8-way expert parallelism: 32 experts,
-    # ~24 rows each (32-row direct tiles)
+    # ~24 rows each (64-row shared-A tiles)
     cfg = wl.CONFIGS["flash_decode_ep8"]
-    _mx_full_size(cfg, wl.default_seed(cfg), list(range(cfg.T)), tile=32)
+    _mx_full_size(cfg, wl.default_seed(cfg), list(range(cfg.T)), tile=64, kernel=2)
 
 
 @pytest.mark.parametrize("T", [1, 3, 128])

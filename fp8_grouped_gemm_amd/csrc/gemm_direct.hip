@@ -36,9 +36,9 @@ namespace {
 
 // Split-K partial store: each of the S K-slices of a tile writes its f32
 // sums to part[slice][slot][col] for the rows that hold a routed slot
-// (slot = row_src of the row); a later kernel adds the slices in slice
-// order.  Lane (lg, lr) holds rows 4*lg + i of column lr of each 16-column
-// subtile.
+// (slot = row_src of the row); the slice counted last adds the slices in
+// slice order (splitk_finish).  Lane (lg, lr) holds rows 4*lg + i of column
+// lr of each 16-column subtile.
 template <int MT>
 __device__ __forceinline__ void store_partial(const v4f (&acc)[MT][4], float* part, size_t ld,
                                               const int32_t* row_src, int row0, const int (&col)[4],
@@ -52,8 +52,9 @@ __device__ __forceinline__ void store_partial(const v4f (&acc)[MT][4], float* pa
             if (f < 0)
                 continue;
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                part[(size_t)f * ld + col[s]] = acc[ms][s][i];
+            for (int s = 0; s < 4; ++s)  // written through (sc1): another workgroup adds them
+                __hip_atomic_store(part + (size_t)f * ld + col[s], acc[ms][s][i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
 }
 
@@ -138,6 +139,76 @@ __device__ __forceinline__ void wait_count(const int32_t* ctr, int target, const
 }
 
 }  // namespace
+
+// ------------------------------------------------- L1 split-K finish
+
+// Finishes 16-row L1 tile `tile` whose K range ran as S workgroups: adds
+// the S f32 partials in slice order, then the same SwiGLU x topk_w, per-128
+// (or 64) amax and e4m3 requant as the unsplit epilogue.  Run by the
+// workgroup whose slice was counted last: the other slices were written
+// through (sc1) and completed before they were counted, and each of their
+// cache lines has that one producer, so ordinary loads see them.  Thread t:
+// row t/16, gate columns 8*(t%16) .. +8 of the tile's 128-column block and
+// the matching up columns; the 16 threads of a row share one wave quarter.
+template <int S>
+__device__ __forceinline__ void splitk_finish(const FwdArgs& a, int tile)
+{
+    const int I = a.I, NT = I / 128;
+    const int mb = tile / NT;
+    const int nt = tile - mb * NT;
+    const int r = mb * 16 + (threadIdx.x >> 4);
+    const int c0 = nt * 128 + (threadIdx.x & 15) * 8;
+    const int f = a.row_src[r];
+    float g[8], u[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        g[q] = u[q] = 0.f;
+    if (f >= 0 && f < a.splitk_slots) {
+#pragma unroll
+        for (int k = 0; k < S; ++k) {  // all S slices' loads in flight together
+            const float* row = a.splitk_part + ((size_t)k * a.splitk_slots + f) * 2 * I;
+            const float4 g0 = *reinterpret_cast<const float4*>(row + c0);
+            const float4 g1 = *reinterpret_cast<const float4*>(row + c0 + 4);
+            const float4 u0 = *reinterpret_cast<const float4*>(row + I + c0);
+            const float4 u1 = *reinterpret_cast<const float4*>(row + I + c0 + 4);
+            g[0] += g0.x; g[1] += g0.y; g[2] += g0.z; g[3] += g0.w;
+            g[4] += g1.x; g[5] += g1.y; g[6] += g1.z; g[7] += g1.w;
+            u[0] += u0.x; u[1] += u0.y; u[2] += u0.z; u[3] += u0.w;
+            u[4] += u1.x; u[5] += u1.y; u[6] += u1.z; u[7] += u1.w;
+        }
+    }
+    const bool valid = f >= 0 && f < a.splitk_slots;
+    const float w = valid ? a.topk_w[f] : 0.f;
+    float hv[8], m = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        hv[q] = (silu(clamp_act(g[q], a.clamp)) * clamp_act(u[q], a.clamp)) * w;
+        m = fmaxf(m, fabsf(hv[q]));
+    }
+    // the row's 16 threads cover 128 columns; per-64 scales: 8 threads each
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    if (!a.sf_gran64)
+        m = fmaxf(m, __shfl_xor(m, 8));
+    if (!valid)
+        return;
+    float rsf;
+    const float sf = requant_sf(m, a.pow2_scale, rsf);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        lo |= requant_q(hv[q], sf, rsf, a.pow2_scale) << (8 * q);
+        hi |= requant_q(hv[q + 4], sf, rsf, a.pow2_scale) << (8 * q);
+    }
+    *reinterpret_cast<uint2*>(a.h + (size_t)r * I + c0) = make_uint2(lo, hi);
+    if (a.sf_gran64) {
+        if ((threadIdx.x & 7) == 0)
+            a.h_sf[(size_t)r * (I / 64) + nt * 2 + ((threadIdx.x >> 3) & 1)] = sf;
+    } else if ((threadIdx.x & 15) == 0) {
+        a.h_sf[(size_t)r * NT + nt] = sf;
+    }
+}
 
 // ------------------------------------------------------------------- L1
 
@@ -254,7 +325,20 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
                             I + nt * 128 + wave * 32 + lr, I + nt * 128 + wave * 32 + 16 + lr};
         store_partial<MT>(acc, a.splitk_part + (size_t)ks * a.splitk_slots * 2 * I, 2 * (size_t)I,
                           a.row_src, row0, col, lg);
-        return;  // l1_splitk_epilogue finishes the tile
+        // Count the slice once its stores have completed; the tile's last
+        // slice to be counted finishes the tile (one counter per tile,
+        // zeroed by the planner).
+        static_assert(MT == 1, "split-K runs on 16-row tiles");
+        __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this lane's stores are done
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(a.sync + kSyncReady + tile, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        __syncthreads();
+        if (s_last)
+            splitk_finish<S>(a, tile);
+        return;
     }
     const bool epi = true;
 
@@ -550,74 +634,6 @@ __global__ __launch_bounds__(WV * 64, MT == 2 && PK && !G64 ? 2 : 1) void l2_dir
     l2_tile_body<MT, PK, false, WV, G64>(a, blockIdx.x, 0);
 }
 
-// ------------------------------------------------- L1 split-K epilogue
-
-// Finishes a 16-row L1 tile whose K range ran as S workgroups: adds the S
-// f32 partials in slice order, then the same SwiGLU x topk_w, per-128 (or 64) amax
-// and e4m3 requant as the l1_direct epilogue.  Thread t: row t/16, gate
-// columns 8*(t%16) .. +8 of the tile's 128-column block and the matching up
-// columns; the 16 threads of a row share one wave quarter.
-template <int S>
-__global__ __launch_bounds__(256) void l1_splitk_epilogue(FwdArgs a)
-{
-    const int I = a.I, NT = I / 128;
-    const int mb = blockIdx.x / NT;
-    const int nt = blockIdx.x - mb * NT;
-    if (a.mblock_expert[mb] < 0)
-        return;
-    const int r = mb * 16 + (threadIdx.x >> 4);
-    const int c0 = nt * 128 + (threadIdx.x & 15) * 8;
-    const int f = a.row_src[r];
-    float g[8], u[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-        g[q] = u[q] = 0.f;
-    if (f >= 0) {
-#pragma unroll
-        for (int k = 0; k < S; ++k) {  // all S slices' loads in flight together
-            const float* row = a.splitk_part + ((size_t)k * a.splitk_slots + f) * 2 * I;
-            const float4 g0 = *reinterpret_cast<const float4*>(row + c0);
-            const float4 g1 = *reinterpret_cast<const float4*>(row + c0 + 4);
-            const float4 u0 = *reinterpret_cast<const float4*>(row + I + c0);
-            const float4 u1 = *reinterpret_cast<const float4*>(row + I + c0 + 4);
-            g[0] += g0.x; g[1] += g0.y; g[2] += g0.z; g[3] += g0.w;
-            g[4] += g1.x; g[5] += g1.y; g[6] += g1.z; g[7] += g1.w;
-            u[0] += u0.x; u[1] += u0.y; u[2] += u0.z; u[3] += u0.w;
-            u[4] += u1.x; u[5] += u1.y; u[6] += u1.z; u[7] += u1.w;
-        }
-    }
-    const float w = f >= 0 ? a.topk_w[f] : 0.f;
-    float hv[8], m = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        hv[q] = (silu(clamp_act(g[q], a.clamp)) * clamp_act(u[q], a.clamp)) * w;
-        m = fmaxf(m, fabsf(hv[q]));
-    }
-    // the row's 16 threads cover 128 columns; per-64 scales: 8 threads each
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    if (!a.sf_gran64)
-        m = fmaxf(m, __shfl_xor(m, 8));
-    if (f < 0)
-        return;
-    float rsf;
-    const float sf = requant_sf(m, a.pow2_scale, rsf);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        lo |= requant_q(hv[q], sf, rsf, a.pow2_scale) << (8 * q);
-        hi |= requant_q(hv[q + 4], sf, rsf, a.pow2_scale) << (8 * q);
-    }
-    *reinterpret_cast<uint2*>(a.h + (size_t)r * I + c0) = make_uint2(lo, hi);
-    if (a.sf_gran64) {
-        if ((threadIdx.x & 7) == 0)
-            a.h_sf[(size_t)r * (I / 64) + nt * 2 + ((threadIdx.x >> 3) & 1)] = sf;
-    } else if ((threadIdx.x & 15) == 0) {
-        a.h_sf[(size_t)r * NT + nt] = sf;
-    }
-}
-
 // -------------------------------------------------------------- combine
 
 // y[t, n] = bf16( sum over active slots j ascending of f32(partial[j][t][n]) )
@@ -865,14 +881,14 @@ static hipError_t launch_l1_t(const FwdArgs& a, hipStream_t s)
     switch (a.BM) {
     case 16:
         if (a.split_l1 > 1) {
+            if (!a.sync)  // the slice counts
+                return hipErrorInvalidValue;
             switch (a.split_l1) {
-            case 2:
+            case 2:  // (the last slice of each tile finishes it)
                 hipLaunchKernelGGL((l1_direct16<2, PK>), dim3(tiles * 2), dim3(256), 0, s, a);
-                hipLaunchKernelGGL(l1_splitk_epilogue<2>, dim3(tiles), dim3(256), 0, s, a);
                 break;
             case 4:
                 hipLaunchKernelGGL((l1_direct16<4, PK>), dim3(tiles * 4), dim3(256), 0, s, a);
-                hipLaunchKernelGGL(l1_splitk_epilogue<4>, dim3(tiles), dim3(256), 0, s, a);
                 break;
             default: return hipErrorInvalidValue;
             }

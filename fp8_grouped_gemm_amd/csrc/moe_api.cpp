@@ -280,6 +280,9 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     // blocks, a bound that grows with T whatever the tile height.
     const size_t mbb = (size_t)((TK + 15) / 16 + E);
     L.n_sync = moe::kSyncReady + (ring_plan ? (int)(2 * mbb) : L.mb_cap);
+    // split-K L1: one slice count per tile of the launch grid's row blocks
+    if (L.split_l1 > 1)
+        L.n_sync = std::max<int>(L.n_sync, moe::kSyncReady + (int)std::min<long long>(L.mb_cap, std::max<long long>(TK, 1)) * (I / 128));
     L.sync = take(sizeof(int32_t) * (size_t)L.n_sync);
     L.unit_mb = L.stream_start = L.stream_desc = L.item_tab = 0;
     if (ring_plan) {

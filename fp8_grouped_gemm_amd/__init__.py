@@ -62,6 +62,7 @@ class moe_tile_info_t(ctypes.Structure):
                 ("l2_tile_n", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("l1_split", ctypes.c_int32), ("single_launch", ctypes.c_int32),
                 ("l2_group_tiles", ctypes.c_int32), ("act_sf_gran", ctypes.c_int32),
+                ("l2_split", ctypes.c_int32),
                 ("ring_blocks", ctypes.c_int32), ("l2_lag_units", ctypes.c_int32)]
 
 

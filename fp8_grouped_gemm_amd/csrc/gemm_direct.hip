@@ -437,6 +437,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(128))) void l1_
     l1_tile<1, S, PK, false>(a, blockIdx.x);
 }
 
+// Finishes 16-row L2 tile `tile` (row block x 256-column tile) whose K
+// range ran as S workgroups: adds the S f32 slices in slice order and
+// stores the bf16 partial rows, as the unsplit epilogue does.  Run by the
+// workgroup whose slice was counted last (the slices were written through
+// and completed before they were counted; each cache line has one
+// producer).  Thread t: row t/16, columns 16 (t%16) .. +16 of the tile.
+template <int S>
+__device__ __forceinline__ void l2_splitk_finish(const FwdArgs& a, int tile)
+{
+    const int H = a.H, NT = (H + 255) / 256;
+    const int mb = tile / NT;
+    const int nt = tile - mb * NT;
+    const int f = a.row_src[mb * 16 + (threadIdx.x >> 4)];
+    const int c0 = nt * 256 + (threadIdx.x & 15) * 16;
+    if (f < 0 || f >= a.splitk_slots || c0 >= H)
+        return;
+    float p[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        p[q] = 0.f;
+#pragma unroll
+    for (int k = 0; k < S; ++k) {  // all S slices' loads in flight together
+        const float* row = a.splitk_part + ((size_t)k * a.splitk_slots + f) * H + c0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float4 x = *reinterpret_cast<const float4*>(row + 4 * v);
+            p[4 * v] += x.x;
+            p[4 * v + 1] += x.y;
+            p[4 * v + 2] += x.z;
+            p[4 * v + 3] += x.w;
+        }
+    }
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        w[q] = (uint32_t)f32_to_bf16(p[2 * q]) | ((uint32_t)f32_to_bf16(p[2 * q + 1]) << 16);
+    const int t = f / a.K, j = f - t * a.K;
+    uint4* dst = reinterpret_cast<uint4*>(a.partial + ((size_t)j * a.T + t) * H + c0);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
 // ------------------------------------------------------------------- L2
 
 // L2 tile `tile`.  CO: the single-launch form (waits for the row block's
@@ -450,14 +492,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(128))) void l1_
 // fragment's bytes 0..15 are K 0..63 of every lane group, bytes 16..31 are
 // K 64..127, so zeroing one half leaves the other -- and each half is
 // promoted with its own activation scale.
-template <int MT, bool PK, bool CO, int WV = 4, bool G64 = false>
-__device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hint)
+// S > 1 (16-row 4-wave tiles of one or two tokens, never CO): item = tile
+// * S + K slice; each slice writes its f32 sums through to
+// splitk_part[slice][slot][H], and the slice counted last adds them in
+// slice order and stores the bf16 partials (l2_splitk_finish).
+template <int MT, bool PK, bool CO, int WV = 4, bool G64 = false, int S = 1>
+__device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int item, int hint)
 {
+    static_assert(!CO || S == 1, "the single launch does not split K");
+    static_assert(S == 1 || (MT == 1 && WV == 4), "split-K runs on 16-row 4-wave tiles");
     constexpr int BM = 16 * MT;
     constexpr int NTG = WV / 4;
     const int H = a.H, I = a.I, IB = I / 128, K = a.K, T = a.T;
     const int NT = (H + 255) / 256;  // H % 256 == 128: the last tile has 2 idle waves
     const int NG = (NT + NTG - 1) / NTG;
+    const int tile = item / S;  // S consecutive items share a tile
+    const int ks = item - tile * S;
     const int mb = tile / NG;
     const int g = tile - mb * NG;
     const int e = a.mblock_expert[mb];
@@ -471,7 +521,7 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
     // h / h_sf rows of this block: its pool rows, or its ring slot's
     const bool ring = CO && a.ring_blocks > 0;
     const int hrow0 = ring ? (mb % a.ring_blocks) * BM : row0;
-    const int kb0 = 0, kb1 = IB;
+    const int kb0 = ks * IB / S, kb1 = (ks + 1) * IB / S;
     const int nt_w = g * NTG + (wave >> 2);               // this wave's 256-column tile
     const bool busy = nt_w < NT && nt_w * 256 + (wave & 3) * 64 < H;
     const int nt = busy ? nt_w : 0;                       // idle waves read tile 0
@@ -582,6 +632,34 @@ __device__ __forceinline__ void l2_tile_body(const FwdArgs& a, int tile, int hin
     };
     kloop<Blk>(kb0, kb1, fetch, mul);
 
+    if constexpr (S > 1) {
+        // ---- K slice: its f32 sums written through, row by row (16 lanes =
+        // 64 bytes); counted once stored; the last slice finishes the tile
+        if (busy) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int f = a.row_src[row0 + 4 * lg + i];
+                if (f < 0 || f >= a.splitk_slots)
+                    continue;
+                float* dst = a.splitk_part + ((size_t)ks * a.splitk_slots + f) * H + ncol0 + lr;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    __hip_atomic_store(dst + s * 16, acc[0][s][i], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this lane's stores are done
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = __hip_atomic_fetch_add(a.sync + kSyncReady + a.grid_mblocks * (I / 128) + tile,
+                                            1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        __syncthreads();
+        if (s_last)
+            l2_splitk_finish<S>(a, tile);
+        return;
+    }
+
     // ---- epilogue: bf16, stage BM x 256 in LDS, 16-byte stores to the
     // (slot, token) row of the partial buffer.
     __shared__ uint16_t ot[BM][WV * 64 + 8];
@@ -628,10 +706,10 @@ __device__ __forceinline__ void l2_tile(const FwdArgs& a, int tile, int hint = 0
     }
 }
 
-template <int MT, bool PK, int WV = 4, bool G64 = false>
+template <int MT, bool PK, int WV = 4, bool G64 = false, int S = 1>
 __global__ __launch_bounds__(WV * 64, MT == 2 && PK && !G64 ? 2 : 1) void l2_direct(FwdArgs a)
 {
-    l2_tile_body<MT, PK, false, WV, G64>(a, blockIdx.x, 0);
+    l2_tile_body<MT, PK, false, WV, G64, S>(a, blockIdx.x, 0);
 }
 
 // -------------------------------------------------------------- combine
@@ -912,6 +990,18 @@ static hipError_t launch_l2_t(const FwdArgs& a, hipStream_t s)
         case 16: hipLaunchKernelGGL((l2_direct<1, PK, 4, true>), dim3(tiles), dim3(256), 0, s, a); break;
         case 32: hipLaunchKernelGGL((l2_direct<2, PK, 4, true>), dim3(tiles), dim3(256), 0, s, a); break;
         case 64: hipLaunchKernelGGL((l2_direct<4, PK, 4, true>), dim3(tiles), dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    if (a.split_l2 > 1) {  // 16-row 4-wave tiles, K over split_l2 workgroups
+        if (a.BM != 16 || a.l2_wide || !a.sync)
+            return hipErrorInvalidValue;
+        switch (a.split_l2 * (a.sf_gran64 ? -1 : 1)) {
+        case 2: hipLaunchKernelGGL((l2_direct<1, PK, 4, false, 2>), dim3(tiles * 2), dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((l2_direct<1, PK, 4, false, 4>), dim3(tiles * 4), dim3(256), 0, s, a); break;
+        case -2: hipLaunchKernelGGL((l2_direct<1, PK, 4, true, 2>), dim3(tiles * 2), dim3(256), 0, s, a); break;
+        case -4: hipLaunchKernelGGL((l2_direct<1, PK, 4, true, 4>), dim3(tiles * 4), dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
         }
         return hipGetLastError();

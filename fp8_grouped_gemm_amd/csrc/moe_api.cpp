@@ -91,7 +91,7 @@ Config choose_config(const moe_shape_t& s, int T)
 
 struct Layout {
     int tile_m, kernel, r_cap, mb_cap, NB;
-    int split_l1;
+    int split_l1, split_l2;
     bool l2_wide;
     bool single;  // L1 + L2 + combine in one launch
     int ring_blocks, lag_units;  // ring pool: row blocks of h / h_sf, lag (0: full pool)
@@ -133,9 +133,10 @@ bool ring_holds_live_set(int blocks, int lag)
 // of the flash-decode shape) as long as there are at least as many tiles as
 // compute units.  With fewer (a single token: 6 row blocks x 16 tiles) each
 // tile's K range is split over S workgroups, S the smallest power of two
-// (<= 4, <= the K blocks) that reaches kMinItems.  L2 is never split: its
-// slices would have to be added by the combine, which costs more than the
-// split saves (measured).
+// (<= 4, <= the K blocks) that reaches kMinItems.  The 16-row L2 tiles
+// split by the same rule; in both steps the slice counted last adds the
+// slices (adding them in the combine instead cost as much as the split
+// saved, measured).
 constexpr long long kMinItems = 256;  // MI355X compute units
 
 // Whether direct-tile calls run L1, L2 and the combine as one launch when
@@ -167,14 +168,21 @@ bool choose_l2_wide(const moe_shape_t& s, int T, const Config& c)
     return groups >= 4 * kMinItems;
 }
 
-// L1 split factor of a call with T tokens and tile configuration c.
-int choose_split(const moe_shape_t& s, int T, const Config& c)
+// K split factor of the L1 (l2 = false) or L2 step of a call with T tokens
+// and tile configuration c.
+int choose_split(const moe_shape_t& s, int T, const Config& c, bool l2 = false)
 {
     if (c.tile_m != 16 || T <= 0 || s.recipe != MOE_RECIPE_FP8_BLOCK128 ||
         (s.flags & MOE_FLAG_RING_POOL))
         return 1;
-    const long long items = mblocks_expected(s, T) * (s.intermediate / 128);
-    const int kblocks = s.hidden / 128;
+    const long long tiles = l2 ? (s.hidden + 255) / 256 : s.intermediate / 128;
+    const long long items = mblocks_expected(s, T) * tiles;
+    const int kblocks = (l2 ? s.intermediate : s.hidden) / 128;
+    // L2 splits only below half a grid's worth of tiles: at the flash shape
+    // one token (96 tiles) gains 2.7 us, two tokens (192 tiles, split 2)
+    // lose 0.7 us (measured)
+    if (l2 && 2 * items >= kMinItems)
+        return 1;
     int S = 1;
     while (S < 4 && 2 * S <= kblocks && items * S < kMinItems)
         S *= 2;
@@ -197,27 +205,33 @@ long long pool_rows(const moe_shape_t& s, long long T, int ra)
 // bisection.
 size_t splitk_floats(const moe_shape_t& s, int T)
 {
-    const size_t width = 2 * (size_t)s.intermediate * (size_t)s.top_k;
-    auto S = [&](int t) { return choose_split(s, t, choose_config(s, t)); };
-    auto need = [&](int t) -> size_t {
-        const int v = S(t);
-        return v > 1 ? (size_t)v * (size_t)t * width : 0;
-    };
-    size_t best = need(T);
-    for (int v = 2; v <= 4; v *= 2) {
-        // last t in [1, T] with S(t) >= v (S is nonincreasing in t while the
-        // tiles are 16 rows; once they are not, S is 1)
-        if (T < 1 || S(1) < v)
-            continue;
-        int lo = 1, hi = T;
-        while (lo < hi) {
-            const int mid = lo + (hi - lo + 1) / 2;
-            if (S(mid) >= v)
-                lo = mid;
-            else
-                hi = mid - 1;
+    // L1 slices hold 2I floats per slot, L2 slices H; the two steps use the
+    // buffer one after the other
+    size_t best = 0;
+    for (int l2 = 0; l2 < 2; ++l2) {
+        const size_t width = (l2 ? (size_t)s.hidden : 2 * (size_t)s.intermediate) *
+                             (size_t)s.top_k;
+        auto S = [&](int t) { return choose_split(s, t, choose_config(s, t), l2 != 0); };
+        auto need = [&](int t) -> size_t {
+            const int v = S(t);
+            return v > 1 ? (size_t)v * (size_t)t * width : 0;
+        };
+        best = std::max(best, need(T));
+        for (int v = 2; v <= 4; v *= 2) {
+            // last t in [1, T] with S(t) >= v (S is nonincreasing in t while
+            // the tiles are 16 rows; once they are not, S is 1)
+            if (T < 1 || S(1) < v)
+                continue;
+            int lo = 1, hi = T;
+            while (lo < hi) {
+                const int mid = lo + (hi - lo + 1) / 2;
+                if (S(mid) >= v)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            best = std::max(best, need(lo));
         }
-        best = std::max(best, need(lo));
     }
     return best;
 }
@@ -248,11 +262,13 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     L.row_src = take(sizeof(int32_t) * (size_t)L.r_cap);
     L.src_row = take(sizeof(int32_t) * (size_t)std::max<long long>(TK, 1));
     L.split_l1 = choose_split(s, T, c);
-    L.single = c.kernel == 0 && L.split_l1 == 1 && sf_gran(s) != 64 &&
+    L.split_l2 = choose_split(s, T, c, true);
+    L.single = c.kernel == 0 && L.split_l1 == 1 && L.split_l2 == 1 && sf_gran(s) != 64 &&
                ((s.flags & (MOE_FLAG_SINGLE_LAUNCH | MOE_FLAG_RING_POOL)) ||
                 (kSingleLaunchDefault && !(s.flags & MOE_FLAG_SPLIT_LAUNCH)));
-    // the single launch's L2 tiles are one 256-column tile per workgroup
-    L.l2_wide = choose_l2_wide(s, T, c) && !L.single;
+    // the single launch's and the split L2's tiles are one 256-column tile
+    // per workgroup
+    L.l2_wide = choose_l2_wide(s, T, c) && !L.single && L.split_l2 == 1;
     // Ring pool: where the call's pool holds more row blocks than the ring,
     // h / h_sf hold ring_blocks blocks (block mb at slot mb % ring_blocks);
     // elsewhere the ring would be the whole pool and never wrap.
@@ -280,9 +296,10 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     // blocks, a bound that grows with T whatever the tile height.
     const size_t mbb = (size_t)((TK + 15) / 16 + E);
     L.n_sync = moe::kSyncReady + (ring_plan ? (int)(2 * mbb) : L.mb_cap);
-    // split-K L1: one slice count per tile of the launch grid's row blocks
-    if (L.split_l1 > 1)
-        L.n_sync = std::max<int>(L.n_sync, moe::kSyncReady + (int)std::min<long long>(L.mb_cap, std::max<long long>(TK, 1)) * (I / 128));
+    // split-K: one slice count per tile of the launch grid's row blocks, L1
+    // tiles then L2 tiles
+    if (L.split_l1 > 1 || L.split_l2 > 1)
+        L.n_sync = std::max<int>(L.n_sync, moe::kSyncReady + (int)std::min<long long>(L.mb_cap, std::max<long long>(TK, 1)) * (I / 128 + (H + 255) / 256));
     L.sync = take(sizeof(int32_t) * (size_t)L.n_sync);
     L.unit_mb = L.stream_start = L.stream_desc = L.item_tab = 0;
     if (ring_plan) {
@@ -501,6 +518,7 @@ int moe_plan_info(moe_plan_t plan, int32_t T, moe_tile_info_t* info)
     info->l2_tile_n = 256;
     info->kernel = L.kernel;
     info->l1_split = L.split_l1;
+    info->l2_split = L.split_l2;
     info->single_launch = L.single ? 1 : 0;
     info->l2_group_tiles = L.l2_wide ? 2 : 1;
     info->act_sf_gran = sf_gran(plan->shape);
@@ -650,6 +668,7 @@ int forward_impl(moe_plan_t plan, int recipe, int32_t T, const FwdOperands& op, 
     a.y = op.y;
     a.src_row = at<int32_t>(workspace, L.src_row);
     a.split_l1 = L.split_l1;
+    a.split_l2 = L.split_l2;
     a.l2_wide = L.l2_wide ? 1 : 0;
     a.splitk_slots = T * s.top_k;
     a.splitk_part = at<float>(workspace, L.part);

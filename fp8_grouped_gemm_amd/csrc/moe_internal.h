@@ -56,6 +56,10 @@ struct FwdArgs {
     // off) and their f32 partial sums, part[slice][slot][2I] for the
     // splitk_slots = T*K routed slots (slot f = t*K + j).
     int32_t split_l1;
+    // L2 likewise for 16-row tiles of one or two tokens: K slices per tile
+    // (1 = off), f32 sums in splitk_part[slice][slot][H]; the per-tile slice
+    // counts follow the L1 ones in sync (kSyncReady + grid_mblocks * I/128)
+    int32_t split_l2;
     int32_t l2_wide;  // 16-row L2 tiles: 1 = 8-wave workgroups over two 256-column tiles
     int32_t splitk_slots;
     float* splitk_part;

@@ -147,6 +147,8 @@ typedef struct moe_tile_info {
     int32_t l2_group_tiles; /* L2 tiles (of l2_tile_n columns) per workgroup: 2 for
                                16-row tiles when at least 1024 workgroups remain, else 1 */
     int32_t act_sf_gran;    /* columns per intermediate (h) scale: 128 or 64 (FP8), 32 (MXFP4) */
+    int32_t l2_split;       /* workgroups sharing one L2 tile's K range (1 = no split;
+                               16-row tiles with fewer tiles than compute units) */
     int32_t ring_blocks;    /* MOE_FLAG_RING_POOL calls whose pool has more row blocks
                                than the ring: row blocks (of tile_m rows) that h and
                                h_sf hold, block mb at slot mb % ring_blocks; the ring

@@ -216,6 +216,19 @@ def test_split_k_choice_and_workspace_monotone_every_T(shape):
                 assert (g == 2) == (rows * ((H // 256 + 1) // 2) >= 1024), (T, g)
             else:
                 assert g == 1
+            # L2 splits K by the same rule over its 256-column tiles
+            S2 = info["l2_split"]
+            assert S2 in (1, 2, 4) and S2 <= max(1, I // 128), (T, S2)
+            if info["tile_m"] != 16 or T == 0:
+                assert S2 == 1
+            else:
+                rows = max((T * K + 15) // 16, min(T * K, E))
+                tiles2 = rows * ((H + 255) // 256)
+                assert (S2 == 1) == (2 * tiles2 >= 256 or I // 128 < 2), (T, S2, tiles2)
+                if S2 > 1:  # the smallest power of two reaching 256 items, within limits
+                    assert tiles2 * S2 >= 256 or S2 == 4 or 2 * S2 > I // 128, (T, S2, tiles2)
+                if S2 > 1:
+                    assert g == 1 and info["single_launch"] == 0
             b = moe.moe_workspace_bytes(p, T)
             assert b >= last_b, T
             last_b = b

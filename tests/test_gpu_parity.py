@@ -193,12 +193,12 @@ def test_packed_weights_full_size_decode_bitwise():
 
 def test_forward_small_token_counts_split_k():
     # Flash-decode shapes with one or two tokens: fewer (row block, column
-    # tile) pairs than compute units, so each L1 tile's K range is split over
-    # 4 or 2 workgroups (f32 partials per routed slot, added in slice order
-    # by the epilogue kernel); from three tokens on there is no split.  At
-    # 32 tokens the L2 workgroups each take two column tiles.  Every token is
-    # checked against the oracle; packed and row-major weights must agree bit
-    # for bit.
+    # tile) pairs than compute units, so each L1 tile's K range is split
+    # over 4 or 2 workgroups, and at one token each L2 tile's over 4 (f32
+    # partials per routed slot, added in slice order by the slice counted
+    # last); from three tokens on there is no split.  At 32 tokens the L2 workgroups each take two column tiles.
+    # Every token is checked against the oracle; packed and row-major
+    # weights must agree bit for bit.
     base = wl.CONFIGS["flash_decode"]
     full = gpu_inputs(wl.custom_config(32, base.H, base.I, base.E, base.K), wl.default_seed(base))
     for T, (split, l2g) in {1: (4, 1), 2: (2, 1), 3: (1, 1), 8: (1, 1), 32: (1, 2)}.items():
@@ -208,9 +208,9 @@ def test_forward_small_token_counts_split_k():
         y_row, runner = run_gpu(inp)
         info = moe.moe_plan_info(runner.plan, T)
         say(f"  T={T}: tile {info['tile_m']}, L1 split {info['l1_split']}, "
-            f"L2 tiles/workgroup {info['l2_group_tiles']}")
+            f"L2 split {info['l2_split']}, L2 tiles/workgroup {info['l2_group_tiles']}")
         assert info["tile_m"] == 16 and info["l1_split"] == split
-        assert info["l2_group_tiles"] == l2g
+        assert info["l2_split"] == (4 if T == 1 else 1) and info["l2_group_tiles"] == l2g
         y_pk, r_pk = run_gpu(inp, weight_layout=moe.MOE_WEIGHTS_PACKED)
         assert torch.equal(y_row, y_pk), T
         host = host_copy_for_oracle(inp, list(range(T)))
@@ -310,12 +310,12 @@ def _run_flags(inp, flags, tile_m=0, weight_layout=0):
 def test_single_launch_matches_split_launch_bitwise(case):
     # Same tiles, same arithmetic in the same order; only the hand-off
     # between L1, L2 and the combine changes, so y is bit-identical.  (The
-    # single launch runs when L1 does not split K, i.e. 16-row tiles need at
-    # least 256 L1 tiles: hence the wide case.)
+    # single launch runs when neither GEMM splits K, i.e. 16-row tiles need
+    # at least 256 L1 and 256 L2 tiles: hence the wide case.)
     cfg = wl.CONFIGS["tiny"]
     tile = int(case[-2:])
     if case.startswith("wide"):
-        host, dev = small_case(300, 256, 512, 64, 4, 21)
+        host, dev = small_case(300, 1024, 512, 64, 4, 21)
     elif case.startswith("tiny"):
         host, dev = small_case(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, wl.default_seed(cfg))
     elif case.startswith("ragged"):

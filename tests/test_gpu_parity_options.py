@@ -141,9 +141,12 @@ def test_activation_clamp_mxfp4(tile_m):
 
 
 def test_single_launch_with_pow2_and_clamp_matches_split_launches():
-    host, dev = small_case(300, 256, 512, 64, 4, 505)
+    # (hidden 1024: enough L2 tiles that the split launches split no K range)
+    host, dev = small_case(300, 1024, 512, 64, 4, 505)
     kw = dict(flags=moe.MOE_FLAG_POW2_SCALE, clamp=0.04)
     y_split, r1 = run_opts(dev, tile_m=16, **kw)
+    info = moe.moe_plan_info(r1.plan, 300)
+    assert info["l1_split"] == 1 and info["l2_split"] == 1, info
     y_one, r2 = run_opts(dev, tile_m=16, flags=kw["flags"] | moe.MOE_FLAG_SINGLE_LAUNCH,
                          clamp=kw["clamp"])
     assert moe.moe_plan_info(r2.plan, 300)["single_launch"] == 1

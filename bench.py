@@ -380,7 +380,8 @@ def main():
                 "pct_hbm_achievable", "pct_mfma_achievable", "cpu_baseline")
         line["workloads"][name] = {k: e[k] for k in keep if k in e}
     line["pages_context"] = PAGES_CONTEXT
-    print(json.dumps(line), flush=True)
+    # (keys starting with "_" are internal: figures add_achievable needs)
+    print(json.dumps({k: v for k, v in line.items() if not k.startswith("_")}), flush=True)
 
 
 def add_achievable(line, pk):

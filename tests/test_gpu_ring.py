@@ -188,3 +188,26 @@ def test_ring_full_size_flash_prefill_bitwise():
     ctrl.close()
     del inp, w1, w2
     torch.cuda.empty_cache()
+
+
+def test_ring_wait_timeout_is_reported_and_next_call_is_clean():
+    # The test flag makes every wait of the ring's single launch give up at
+    # once (L1 tiles waiting for a slot's previous L2 tiles included): the
+    # call completes and flags MOE_STATUS_WAIT_TIMEOUT; a normal ring plan on
+    # the same inputs then runs clean and matches the full-pool control.
+    T, H, I, E, K, tile, layout = SHAPES["t16"]
+    _, dev = small_case(T, H, I, E, K, 93)
+    bad = moe.MoEForward(H, I, E, K, T, tile_m=tile, flags=RING | moe.MOE_FLAG_TEST_NO_WAIT)
+    assert moe.moe_plan_info(bad.plan, T)["ring_blocks"] > 0
+    _forward(bad, dev, dev["topk_idx"], dev["w1"], dev["w2"])
+    st = moe.moe_read_status(bad.plan, T, bad.workspace)
+    assert st[0] & moe.MOE_STATUS_WAIT_TIMEOUT
+    ring = moe.MoEForward(H, I, E, K, T, tile_m=tile, flags=RING)
+    ctrl = moe.MoEForward(H, I, E, K, T, tile_m=tile, flags=CONTROL)
+    y_r = _forward(ring, dev, dev["topk_idx"], dev["w1"], dev["w2"])
+    y_c = _forward(ctrl, dev, dev["topk_idx"], dev["w1"], dev["w2"])
+    st = moe.moe_read_status(ring.plan, T, ring.workspace)
+    assert not (st[0] & moe.MOE_STATUS_WAIT_TIMEOUT)
+    assert torch.equal(y_r, y_c)
+    for r in (bad, ring, ctrl):
+        r.close()

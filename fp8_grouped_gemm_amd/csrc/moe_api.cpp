@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -63,6 +64,12 @@ constexpr double kRows16 = 10.0;     // FP8: 16-row tiles up to here (12 rows: 3
 constexpr double kRows16Mx = 12.0;   // MXFP4: 16-row tiles up to here, then shared-A
 constexpr double kRows32 = 21.0;
 constexpr double kRowsLds64 = 64.0;
+// MXFP4: the 128-row LDS tile leads only between kRowsLds64 and this many
+// rows per expert; beyond it the shared-A tile is 4-20 % faster (flash shape
+// at 96 / 120 / 192 rows: 1222 vs 1317, 1516 vs 1463, 2462 vs 2103 us;
+// pro shape at 96 / 128 / 256 rows: 4165 vs 4441, 6034 vs 5330, 10002 vs
+// 8936 us; FP8 keeps the LDS tile: pro 8342 vs 10619 us).
+constexpr double kRowsLds128Mx = 108.0;
 
 Config choose_config(const moe_shape_t& s, int T)
 {
@@ -84,7 +91,7 @@ Config choose_config(const moe_shape_t& s, int T)
         return Config{32, 0};
     if (!lds)
         return Config{64, 0};
-    if (rows <= kRowsLds64)
+    if (rows <= kRowsLds64 || (mx && lds64 && rows > kRowsLds128Mx))
         return Config{64, k64};
     return Config{128, 1};
 }
@@ -236,6 +243,23 @@ size_t splitk_floats(const moe_shape_t& s, int T)
     return best;
 }
 
+// Largest tile height the choice takes at any token count <= T.  The
+// MXFP4 choice is not monotone in T (the 128-row tile between 64 and 108
+// rows per expert, the 64-row tile beyond), and a workspace sized for T must
+// serve every smaller call, so the pool sections are sized for this height.
+int max_tile_upto(const moe_shape_t& s, int T)
+{
+    int m = choose_config(s, T).tile_m;
+    for (double x : {kRows16, kRows16Mx, kRows32, kRowsLds64, kRowsLds128Mx}) {
+        // last token count with at most x rows per expert, and the next
+        const long long t = (long long)std::floor(x * s.num_experts / s.top_k);
+        for (long long u = t; u <= t + 1; ++u)
+            if (u >= 1 && u <= T)
+                m = std::max(m, choose_config(s, (int)u).tile_m);
+    }
+    return m;
+}
+
 Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
 {
     Layout L{};
@@ -246,6 +270,11 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     const long long TK = (long long)T * s.top_k;
     L.r_cap = (int)pool_rows(s, T, ra);
     L.mb_cap = L.r_cap / ra;
+    // the pool sections' size (>= r_cap: see max_tile_upto)
+    const size_t r_alloc = row_align_override > 0
+                               ? (size_t)L.r_cap
+                               : (size_t)std::max<long long>(L.r_cap,
+                                                             pool_rows(s, T, max_tile_upto(s, T)));
     L.NB = (int)std::max<long long>((TK + moe::kRouteThreads - 1) / moe::kRouteThreads, 1);
     const int E = s.num_experts, H = s.hidden, I = s.intermediate, K = s.top_k;
     size_t o = 0;
@@ -259,7 +288,7 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
     L.offsets = take(sizeof(int32_t) * (E + 1));
     L.blk = take(sizeof(int32_t) * (size_t)L.NB * (E + 1));
     L.mbe = take(sizeof(int32_t) * (size_t)L.mb_cap);
-    L.row_src = take(sizeof(int32_t) * (size_t)L.r_cap);
+    L.row_src = take(sizeof(int32_t) * r_alloc);
     L.src_row = take(sizeof(int32_t) * (size_t)std::max<long long>(TK, 1));
     L.split_l1 = choose_split(s, T, c);
     L.split_l2 = choose_split(s, T, c, true);
@@ -281,7 +310,7 @@ Layout make_layout(const moe_shape_t& s, int T, int row_align_override = 0)
             L.lag_units = rs.lag;
         }
     }
-    const size_t h_rows = L.ring_blocks > 0 ? (size_t)L.ring_blocks * ra : (size_t)L.r_cap;
+    const size_t h_rows = L.ring_blocks > 0 ? (size_t)L.ring_blocks * ra : r_alloc;
     // f32 [R, I/128] or [R, I/64] (FP8 recipe) or UE8M0 bytes [R, I/32]
     // (MXFP4, the size of the per-128 f32 section)
     L.h_sf = take(sizeof(float) * h_rows * (I / (sf_gran(s) == 64 ? 64 : 128)));

@@ -363,10 +363,13 @@ def test_mx_recipe_validation_and_choices():
     try:
         for T in (1, 2, 8, 128, 1024, 8192):
             info = moe.moe_plan_info(p, T)
-            # at these token counts the same tile choice as FP8 (MXFP4
-            # leaves 32-row tiles out where the shared-A tile fits), no
+            # at these token counts the same tile choice as FP8 up to 1024
+            # tokens (MXFP4 leaves 32-row tiles out where the shared-A tile
+            # fits, and takes it again beyond 108 rows per expert), no
             # split-K, one L2 tile per workgroup
-            assert info["tile_m"] == moe.moe_plan_info(q, T)["tile_m"], T
+            want = (64, 2) if T == 8192 else (moe.moe_plan_info(q, T)["tile_m"],
+                                                moe.moe_plan_info(q, T)["kernel"])
+            assert (info["tile_m"], info["kernel"]) == want, T
             assert info["l1_split"] == 1 and info["l2_group_tiles"] == 1 and \
                 info["single_launch"] == 0, T
             # same workspace as the FP8 plan (h_sf: I/32 bytes = I/128 floats per row)
@@ -553,5 +556,28 @@ def test_ring_pool_over_capacity_rejected_before_any_launch():
         need = moe.moe_workspace_bytes(p, 1024)
         assert L.moe_forward(p, 1024, *([a] * 9), ctypes.c_void_p(0x100000), need - 1,
                              None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    finally:
+        moe.moe_plan_destroy(p)
+
+
+@pytest.mark.parametrize("shape", [(4096, 2048, 256, 6), (7168, 3072, 384, 6)])
+def test_mxfp4_tile_choice_and_workspace_monotone(shape):
+    # MXFP4 takes the 128-row LDS tile only between 64 and 108 routed rows per
+    # expert and the 64-row shared-A tile on both sides, yet a workspace sized
+    # for a token count serves every smaller one
+    H, I, E, K = shape
+    p = moe.moe_plan_create(H, I, E, K, 16384, recipe=moe.MOE_RECIPE_MXFP4)
+    try:
+        last = 0
+        for T in list(range(1, 16385, 61)) + [16384]:
+            info = moe.moe_plan_info(p, T)
+            rows = T * K / E
+            if 64 < rows <= 108:
+                assert (info["tile_m"], info["kernel"]) == (128, 1), T
+            elif rows > 108:
+                assert (info["tile_m"], info["kernel"]) == (64, 2), T
+            b = moe.moe_workspace_bytes(p, T)
+            assert b >= last, T
+            last = b
     finally:
         moe.moe_plan_destroy(p)

@@ -141,9 +141,9 @@ def test_mx_lds_tiles(case, tile):
         assert torch.equal(y, y_direct)
 
 
-def _mx_full_size(cfg, seed, toks, tile=None, kernel=None):
+def _mx_full_size(cfg, seed, toks, tile=None, kernel=None, force_tile=0):
     dev = wl.make_inputs_mx(cfg, seed, "cuda")
-    y, runner = run_gpu_mx(dev, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    y, runner = run_gpu_mx(dev, tile_m=force_tile, weight_layout=moe.MOE_WEIGHTS_PACKED)
     info = moe.moe_plan_info(runner.plan, cfg.T)
     say(f"MX {cfg.name} T={cfg.T}: tile {info}")
     if tile is not None:
@@ -164,15 +164,20 @@ def test_mx_flash_prefill_full_size_sampled():
                   tile=64, kernel=2)
 
 
-@pytest.mark.parametrize("name", ["pro_prefill", "skewed"])
-def test_mx_large_prefill_sampled(name):
+@pytest.mark.parametrize("name,force", [("pro_prefill", 0), ("skewed", 0), ("skewed", 128)])
+def test_mx_large_prefill_sampled(name, force):
     # 128 rows per expert on average (skewed: hot experts with ~4000): the
-    # persistent 128-row LDS tiles
+    # library's choice for MXFP4 there is the 64-row shared-A tile; the
+    # persistent 128-row LDS tile (the choice between 64 and 108 rows) runs
+    # the skewed workload when asked for
     cfg = wl.CONFIGS[name]
     seed = wl.default_seed(cfg)
     rng = np.random.default_rng(seed)
     toks = sorted({0, cfg.T - 1, *rng.choice(cfg.T, 14, replace=False).tolist()})
-    _mx_full_size(cfg, seed, toks, tile=128, kernel=1)
+    if force:
+        _mx_full_size(cfg, seed, toks, tile=128, kernel=1, force_tile=128)
+    else:
+        _mx_full_size(cfg, seed, toks, tile=64, kernel=2)
 
 
 def test_mx_flash_decode_ep8_share_every_token():

@@ -64,6 +64,7 @@ constexpr int META = 512 + 512 + 256;
 constexpr int NMETA = 4;
 constexpr int META_W = 512, META_E = 1024;
 constexpr int kThreads = 512;
+constexpr int kHotBlocks = 4;  // row blocks of an expert that make the walk use panels
 
 // Stage geometry per recipe.  FP8: B = 16 n-subtiles x 2 halves x 1 KiB,
 // copies per wave and block = 2 A + 4 B + 1 scale.  MXFP4: B = 16 subtiles
@@ -142,8 +143,9 @@ __device__ __forceinline__ const uint8_t* weight_src_mx(const FwdArgs& a, int e,
 // multiplied as its two 64-K halves -- bytes 0-15 of every A fragment are K
 // 0-63, bytes 16-31 K 64-127, so a copy with one half zeroed gives that
 // half's sum -- each promoted with its own activation scale.
-template <bool L1, bool PK, bool MX, bool G64>
-__global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
+// HOT: the walk orders the tiles of hot experts in panels (below).
+template <bool L1, bool PK, bool MX, bool G64, bool HOT>
+__device__ __forceinline__ void lds_walk(const FwdArgs& a)
 {
     static_assert(!(MX && G64), "per-64 scales are an FP8-recipe option");
     constexpr bool D64 = G64 && !L1;  // L2 multiplies dual halves
@@ -183,9 +185,38 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     const int W = G / 8;
     const int pos = (G % 8 == 0) ? (b % 8) * W + b / 8 : b;
     auto tile_of = [&](int k) { return pos + k * G; };  // position of tile k
+    // Hot experts (HOT: some expert's segment spans >= kHotBlocks row
+    // blocks).  Such an expert's R row blocks hold R * NT consecutive
+    // positions, so each XCD's W of them would cover a few row blocks x
+    // every column tile and stream the expert's whole weight matrix; its
+    // positions are walked in panels of PC column tiles instead, row block
+    // by row block within a panel (a chunk of 32 positions is 8 row blocks x
+    // 4 columns: a quarter of the weight bytes, 4x the activation bytes).
+    // The map is a bijection on the expert's own positions; only the order
+    // of the tiles changes, never their arithmetic.
+    const int PC = NT % 4 == 0 ? 4 : 2;  // (HOT implies NT even)
+    // wave-uniform reads of the planner's tables through the scalar cache
+    // (they take no part in the vmcnt accounting of the copies)
+    auto sload = [&](const int32_t* q) {
+        return __builtin_amdgcn_readfirstlane(*(const __attribute__((address_space(4))) int32_t*)q);
+    };
     auto tile_at = [&](int p, int& mb, int& nt) {
         mb = p / NT;
         nt = p - mb * NT;
+        if constexpr (HOT) {
+            const int e = sload(a.mblock_expert + mb);
+            if (e < 0 || e >= a.E)
+                return;
+            const int s0 = sload(a.offsets + e) / BM;
+            const int R = sload(a.offsets + e + 1) / BM - s0;
+            if (R < kHotBlocks || mb < s0 || mb >= s0 + R)
+                return;
+            const int q = (mb - s0) * NT + nt;  // the position within the expert's R x NT
+            const int g = q / (R * PC), rem = q - g * (R * PC);
+            const int r = rem / PC;
+            mb = s0 + r;
+            nt = g * PC + (rem - r * PC);
+        }
     };
 
     if (tile_of(0) >= n_pos)
@@ -195,15 +226,12 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     // one dma4 per wave.  Waves 0/1 (and duplicates 5/6) copy row_src of
     // tile k + 1, rows [64 h, 64 h + 64); waves 2/3 gather topk_w of tile k's
     // rows (L1; L2: duplicates of 0/1); waves 4/7 copy tile k + 1's expert.
-    // A tile past the end reads tile k's (valid) rows instead: its slot is
-    // never used.
+    // A tile past the end reads row block 0's (valid) rows instead: its slot
+    // is never used.
     auto issue_meta = [&](int k) {
-        int mbk, ntk, mbn, ntn;
-        tile_at(tile_of(k), mbk, ntk);
+        int mbn = 0, ntn;  // (row block 0 holds routed slots)
         if (tile_of(k + 1) < n_pos)
             tile_at(tile_of(k + 1), mbn, ntn);
-        else
-            mbn = mbk;
         const int rown = mbn * BM;
         const int role = (wave == 5) ? 0 : (wave == 6) ? 1 : (wave == 7) ? 4 : wave;
         if (role <= 1 || (!L1 && role <= 3)) {
@@ -666,6 +694,25 @@ __global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
     }
 }
 
+// Hot experts ("MegaMoE SM90 Implementation Design" §12.2 switches its L2
+// walk to N-major where experts hold many rows; PR #360 "TODO / future
+// work" names the tile order as the lever for large-M cells): the planner's
+// status[3], the largest segment, selects the panel walk for calls with an
+// expert of >= kHotBlocks row blocks.  Each walk is its own kernel (one
+// kernel holding both spilled 21 scalar registers where the plain walk
+// spills 2); both are launched, and the one that does not apply exits at
+// once (~3 us).  (Skewed shape: layer ~2005 -> ~1965 us; remapping 2-block
+// experts too, as on the pro-prefill shape, measured 8 % slower.)
+template <bool L1, bool PK, bool MX, bool G64, bool HOT>
+__global__ __launch_bounds__(kThreads) void gemm_lds(FwdArgs a)
+{
+    const int NT = L1 ? a.I / 128 : a.H / 256;
+    const bool hot = NT % 2 == 0 && a.status[3] / BM >= kHotBlocks;
+    if (hot != HOT)
+        return;
+    lds_walk<L1, PK, MX, G64, HOT>(a);
+}
+
 template <bool L1, bool MX>
 static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
 {
@@ -691,16 +738,26 @@ static hipError_t launch_lds(const FwdArgs& a, hipStream_t s)
         g = a.grid_cap;
     const dim3 grid((unsigned)g);
     const size_t smem = (size_t)LdsCfg<MX>::SMEM;
-    auto kern = a.packed ? gemm_lds<L1, true, MX, false> : gemm_lds<L1, false, MX, false>;
-    if constexpr (!MX) {
-        if (a.sf_gran64)
-            kern = a.packed ? gemm_lds<L1, true, false, true> : gemm_lds<L1, false, false, true>;
+    // the plain walk, then (even column-tile counts) the hot-expert walk:
+    // each kernel runs only if the planner's largest segment selects it
+    const bool can_hot = NT % 2 == 0;
+    for (int hot = 0; hot <= (can_hot ? 1 : 0); ++hot) {
+        auto kern = a.packed ? (hot ? gemm_lds<L1, true, MX, false, true> : gemm_lds<L1, true, MX, false, false>)
+                             : (hot ? gemm_lds<L1, false, MX, false, true> : gemm_lds<L1, false, MX, false, false>);
+        if constexpr (!MX) {
+            if (a.sf_gran64)
+                kern = a.packed ? (hot ? gemm_lds<L1, true, false, true, true> : gemm_lds<L1, true, false, true, false>)
+                                : (hot ? gemm_lds<L1, false, false, true, true> : gemm_lds<L1, false, false, true, false>);
+        }
+        err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (err != hipSuccess)
+            return err;
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, s, a);
+        err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
     }
-    err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (err != hipSuccess)
-        return err;
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, s, a);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s)

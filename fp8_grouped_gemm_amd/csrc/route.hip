@@ -20,6 +20,15 @@
 
 namespace moe {
 
+// Maximum of v over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int wave_max(int v)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        v = max(v, __shfl_xor(v, d));
+    return v;
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_count(RouteArgs a)
 {
     extern __shared__ int32_t hist[];  // [E+1]; hist[E] counts ids >= E
@@ -78,6 +87,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan(RouteArgs a)
     }
     const int start = scan[e] - seg;
     const int used = scan[kRouteThreads - 1];
+    // the largest segment (status[3]: the prefill tiles' walk reads it)
+    __shared__ int32_t seg_max;
+    if (e == 0)
+        seg_max = 0;
+    __syncthreads();
+    const int wmax = wave_max(seg);  // one LDS atomic per wave
+    if ((e & 63) == 0 && wmax > 0)
+        atomicMax(&seg_max, wmax);
+    __syncthreads();
     if (e < a.E) {
         a.offsets[e] = start;
         // Per-chunk base row of this expert's slots (the chunk counts are
@@ -111,7 +129,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan(RouteArgs a)
         a.status[0] = bad_sh > 0 ? 1 : 0;
         a.status[1] = bad_sh;
         a.status[2] = used;
-        a.status[3] = 0;
+        a.status[3] = seg_max;
     }
     for (int r = used + e; r < a.r_cap; r += kRouteThreads)
         a.row_src[r] = -1;
@@ -239,6 +257,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_small(RouteArgs a)
     scan[x] = incl + (wave > 0 ? wave_sum[wave - 1] : 0);
     const int start = scan[x] - seg;
     const int used = wave_sum[kWaves - 1];
+    __shared__ int32_t seg_max;  // the largest segment (status[3])
+    if (x == 0)
+        seg_max = 0;
+    __syncthreads();
+    const int wmax = wave_max(seg);  // one LDS atomic per wave
+    if (lane == 0 && wmax > 0)
+        atomicMax(&seg_max, wmax);
+    __syncthreads();
     if (x < a.E) {
         a.offsets[x] = start;
         for (int r = start + total; r < start + seg; ++r)
@@ -253,7 +279,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_small(RouteArgs a)
         a.status[0] = bad_sh > 0 ? 1 : 0;
         a.status[1] = bad_sh;
         a.status[2] = used;
-        a.status[3] = 0;
+        a.status[3] = seg_max;
     }
     for (int r = used + x; r < a.r_cap; r += kRouteThreads)
         a.row_src[r] = -1;

@@ -173,7 +173,9 @@ typedef struct moe_tile_info {
  *            (ring-pool calls, moe_tile_info.ring_blocks > 0: ring_blocks * tile_m rows
  *            in place of pool_rows, each slot holding the last row block that used it)
  *   partial  uint16 [K, T, H]     bf16 L2 output of slot (t, j) at [j][t]
- *   status   int32 [4]            status[0] = MOE_STATUS_* bits, status[1] = #ids >= E */
+ *   status   int32 [4]            status[0] = MOE_STATUS_* bits, status[1] = #ids >= E,
+ *                                  status[2] = pool rows used, status[3] = rows of the
+ *                                  largest expert segment (both after alignment) */
 typedef struct moe_ws_layout {
     size_t counts, offsets, row_src, src_row, h, h_sf, partial, status;
     size_t total;
@@ -390,7 +392,8 @@ int moe_route_workspace_bytes(moe_plan_t plan, int32_t num_tokens, size_t* bytes
 
 /* Blocking: synchronises `stream`, then copies the 4-int status word of the
  * last call that used `workspace` into host_status[4] (MOE_STATUS_* bits,
- * the number of ids >= E, the pool rows used).  The pages' kernels return
+ * the number of ids >= E, the pool rows used, the rows of the largest
+ * expert segment; rows counted after alignment to the call's tile height).  The pages' kernels return
  * nothing from the device and abort on a timed-out wait (PR #440 "Register
  * inventory": the wait timeout and its handler); this library reports
  * instead: an id the pages leave undefined (>= E) is skipped and counted,

@@ -52,6 +52,9 @@ def assert_route_equal(idx, E, K, ra, what):
     assert np.array_equal(rs, rrs), what
     assert np.array_equal(sr, rsr), what
     assert status[1] == bad and status[0] == (1 if bad else 0), what
+    # pool rows used, and the largest aligned segment (from the oracle's offsets)
+    assert status[2] == ro[E], what
+    assert status[3] == (int(np.diff(ro).max()) if E > 0 else 0), what
 
 
 @pytest.mark.parametrize("name", ["tiny", "flash_decode", "flash_prefill", "pro_prefill", "skewed",
@@ -271,6 +274,39 @@ def test_tile64_shared_a_matches_direct_tiles_and_tile128_bitwise(case):
     y64p, _ = _run_flags(dev, 0, 64, weight_layout=moe.MOE_WEIGHTS_PACKED)
     assert torch.equal(y64, y64p), case
     verify(y64, r64, host, f"tile 64 shared-A {case}")
+
+
+def _hot_mask(T):
+    # every token's first slot on expert 3 (T rows), the second slot of
+    # tokens 0-511 on expert 5 (exactly 4 row blocks of 128), the others on
+    # the remaining experts in turn
+    alt = [0, 1, 2, 4, 6, 7]
+    mask = {(t, 0): 3 for t in range(T)}
+    mask.update({(t, 1): 5 if t < 512 else alt[t % 6] for t in range(T)})
+    return mask
+
+
+def test_lds_hot_expert_panel_walk_bitwise():
+    # Experts spanning >= 4 row blocks of 128 rows are walked in panels of
+    # column tiles (the planner's status[3], the largest segment, switches
+    # it on).  Only the order of the tiles changes, so y is bit-identical to
+    # the 64-row shared-A tiles (which never reorder) and to a 4-workgroup
+    # grid, and it matches the oracle.  Expert 3: 1100 rows (9 row blocks,
+    # not a multiple of the panel), expert 5: 512 rows (the threshold).
+    T = 1100
+    host, dev = small_case(T, 512, 512, 8, 2, 31, mask=_hot_mask(T))
+    y128, r128 = _run_flags(dev, 0, 128)
+    assert moe.moe_plan_info(r128.plan, T)["kernel"] == 1
+    st = moe.moe_read_status(r128.plan, T, r128.workspace)
+    assert st[3] == 9 * 128, st
+    y_small, _ = _run_flags(dev, moe.MOE_FLAG_TEST_SMALL_GRID, 128)
+    assert torch.equal(y128, y_small)
+    y64, r64 = _run_flags(dev, 0, 64)
+    assert moe.moe_plan_info(r64.plan, T)["kernel"] == 2
+    assert torch.equal(y128, y64)
+    y128p, _ = _run_flags(dev, 0, 128, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert torch.equal(y128, y128p)
+    verify(y128, r128, host, "tile 128 hot-expert panel walk")
 
 
 def test_lds_tiles_full_size_packed_small_grid():

@@ -141,6 +141,27 @@ def test_mx_lds_tiles(case, tile):
         assert torch.equal(y, y_direct)
 
 
+def test_mx_lds_hot_expert_panel_walk():
+    # The 128-row LDS tile walks experts of >= 4 row blocks in panels of
+    # column tiles: against the oracle, and bit-identical to a 4-workgroup
+    # grid and to packed weights.  Expert 3 holds every token's first slot
+    # (1100 rows, 9 row blocks), expert 5 exactly 512 rows.
+    T = 1100
+    alt = [0, 1, 2, 4, 6, 7]
+    mask = {(t, 0): 3 for t in range(T)}
+    mask.update({(t, 1): 5 if t < 512 else alt[t % 6] for t in range(T)})
+    host, dev = mx_case(T, 512, 512, 8, 2, 413, mask=mask)
+    y, runner = check_case(host, dev, 128, "LDS tile 128 hot-expert panel walk")
+    assert moe.moe_plan_info(runner.plan, T)["kernel"] == 1
+    assert moe.moe_read_status(runner.plan, T, runner.workspace)[3] == 9 * 128
+    y_pk, _ = run_gpu_mx(dev, tile_m=128, weight_layout=moe.MOE_WEIGHTS_PACKED)
+    assert torch.equal(y, y_pk)
+    small = moe.MoEForward(512, 512, 8, 2, T, tile_m=128, recipe=moe.MOE_RECIPE_MXFP4,
+                           flags=moe.MOE_FLAG_TEST_SMALL_GRID)
+    y_small, _ = run_gpu_mx(dev, runner=small)
+    assert torch.equal(y, y_small)
+
+
 def _mx_full_size(cfg, seed, toks, tile=None, kernel=None, force_tile=0):
     dev = wl.make_inputs_mx(cfg, seed, "cuda")
     y, runner = run_gpu_mx(dev, tile_m=force_tile, weight_layout=moe.MOE_WEIGHTS_PACKED)

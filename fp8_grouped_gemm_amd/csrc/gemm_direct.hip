@@ -198,8 +198,9 @@ __device__ __forceinline__ void splitk_finish(const FwdArgs& a, int tile)
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        lo |= requant_q(hv[q], sf, rsf, a.pow2_scale) << (8 * q);
-        hi |= requant_q(hv[q + 4], sf, rsf, a.pow2_scale) << (8 * q);
+        const uint32_t c2 = requant_q2(hv[q], hv[q + 4], sf, rsf, a.pow2_scale);
+        lo |= (c2 & 0xFFu) << (8 * q);
+        hi |= (c2 >> 8) << (8 * q);
     }
     *reinterpret_cast<uint2*>(a.h + (size_t)r * I + c0) = make_uint2(lo, hi);
     if (a.sf_gran64) {
@@ -387,10 +388,9 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
                                                        fmaxf(red[2][r], red[3][r]));
                 float rsf;
                 const float sf = requant_sf(amax, a.pow2_scale, rsf);
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    qt[r][wave * 32 + s * 16 + lr] =
-                        (uint8_t)requant_q(hv[ms][s][i], sf, rsf, a.pow2_scale);
+                const uint32_t c2 = requant_q2(hv[ms][0][i], hv[ms][1][i], sf, rsf, a.pow2_scale);
+                qt[r][wave * 32 + lr] = (uint8_t)c2;
+                qt[r][wave * 32 + 16 + lr] = (uint8_t)(c2 >> 8);
                 if ((a.sf_gran64 ? (wave & 1) == 0 : wave == 0) && lr == 0) {
                     float* dst = a.sf_gran64 ? a.h_sf + (size_t)(hrow0 + r) * (I / 64) + nt * 2 + (wave >> 1)
                                              : a.h_sf + (size_t)(hrow0 + r) * (I / 128) + nt;

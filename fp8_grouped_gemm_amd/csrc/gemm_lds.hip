@@ -621,10 +621,9 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
                                            : fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
                     float rsf;
                     const float sf = requant_sf(amax, a.pow2_scale, rsf);
-#pragma unroll
-                    for (int s = 0; s < 2; ++s)
-                        qt[r * 128 + wn * 32 + s * 16 + lr] =
-                            (uint8_t)requant_q(acc[ms][s][i], sf, rsf, a.pow2_scale);
+                    const uint32_t c2 = requant_q2(acc[ms][0][i], acc[ms][1][i], sf, rsf, a.pow2_scale);
+                    qt[r * 128 + wn * 32 + lr] = (uint8_t)c2;
+                    qt[r * 128 + wn * 32 + 16 + lr] = (uint8_t)(c2 >> 8);
                     if constexpr (G64) {
                         if ((wn & 1) == 0 && lr == 0)
                             a.h_sf[(size_t)(row0 + r) * (I / 64) + nt * 2 + (wn >> 1)] = sf;

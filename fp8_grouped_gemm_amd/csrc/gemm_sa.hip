@@ -268,10 +268,9 @@ __global__ __launch_bounds__(256, 2) void gemm_sa(FwdArgs a)
                                        : fmaxf(fmaxf(rm.x, rm.y), fmaxf(rm.z, rm.w));
                 float rsf;
                 const float sf = requant_sf(amax, a.pow2_scale, rsf);
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    qt[r][wave * 32 + s * 16 + lr] =
-                        (uint8_t)requant_q(hv[ms][s][i], sf, rsf, a.pow2_scale);
+                const uint32_t c2 = requant_q2(hv[ms][0][i], hv[ms][1][i], sf, rsf, a.pow2_scale);
+                qt[r][wave * 32 + lr] = (uint8_t)c2;
+                qt[r][wave * 32 + 16 + lr] = (uint8_t)(c2 >> 8);
                 if constexpr (G64) {
                     if ((wave & 1) == 0 && lr == 0)
                         a.h_sf[(size_t)(row0 + r) * (I / 64) + nt * 2 + (wave >> 1)] = sf;

@@ -117,13 +117,26 @@ __device__ __forceinline__ uint32_t requant_e4m3(float v, float sf, float rsf)
     return f32_to_e4m3_hw(v / sf);
 }
 
+// x / 448 correctly rounded without the division sequence: q0 = x * c with
+// c = RN(1/448), the residual x - 448 q0 (exact in f32, one fma), and one
+// correction q0 + r c (one fma).  Equal to the IEEE quotient for every
+// f32 significand (checked exhaustively on the CPU; the quotient of a
+// normal x depends on its significand only); x = inf gives q0 = inf.
+__device__ __forceinline__ float div448(float x)
+{
+    constexpr float c = 1.0f / 448.0f;
+    const float q0 = x * c;
+    const float q = __builtin_fmaf(__builtin_fmaf(-q0, 448.0f, x), c, q0);
+    return q == q ? q : q0;
+}
+
 // Requant scale of a block with the given amax: the raw max(amax, 1e-10)/448
 // or, with pow2, the smallest power of two at or above it (PR #383's choice).
 // rsf: the hardware reciprocal of the raw scale (requant_q brackets it) or
 // the exact inverse of the power of two.
 __device__ __forceinline__ float requant_sf(float amax, bool pow2, float& rsf)
 {
-    const float s = fmaxf(amax, 1e-10f) / 448.0f;
+    const float s = div448(fmaxf(amax, 1e-10f));
     if (pow2) {
         const uint32_t c = min(e8m0_ceil_code(s), 253u);
         rsf = e8m0_inverse(c);
@@ -138,6 +151,28 @@ __device__ __forceinline__ float requant_sf(float amax, bool pow2, float& rsf)
 __device__ __forceinline__ uint32_t requant_q(float v, float sf, float rsf, bool pow2)
 {
     return pow2 ? f32_to_e4m3_hw(v * rsf) : requant_e4m3(v, sf, rsf);
+}
+
+// requant_q of two values of one block (v0's code in bits 0-7, v1's in bits
+// 8-15) with one v_cvt_pk_fp8_f32 per bracket end for both.  The pair
+// leaves the fast path (each value then takes requant_q) where either
+// value's bracket ends disagree or its quotient is NaN -- exactly where
+// requant_q would divide or return 0x7F -- so the codes are requant_q's.
+__device__ __forceinline__ uint32_t requant_q2(float v0, float v1, float sf, float rsf, bool pow2)
+{
+    auto sat = [](float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f); };
+    const float y0 = v0 * rsf, y1 = v1 * rsf;
+    if (pow2) {  // y is the exact quotient
+        const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(y0), sat(y1), 0, false);
+        return (y0 != y0 ? 0x7Fu : c & 0xFFu) | ((y1 != y1 ? 0x7Fu : (c >> 8) & 0xFFu) << 8);
+    }
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                            sat(y0 * (1.0f - 0x1p-20f)), sat(y1 * (1.0f - 0x1p-20f)), 0, false) & 0xFFFFu;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                            sat(y0 * (1.0f + 0x1p-20f)), sat(y1 * (1.0f + 0x1p-20f)), 0, false) & 0xFFFFu;
+    if (lo == hi && y0 == y0 && y1 == y1)
+        return lo;
+    return requant_e4m3(v0, sf, rsf) | (requant_e4m3(v1, sf, rsf) << 8);
 }
 
 // Activation clamp of gate / up before the SwiGLU ("MegaMoE SM90

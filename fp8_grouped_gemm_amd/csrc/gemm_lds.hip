@@ -247,7 +247,10 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
     };
 
     // ---- issue side: the next K block of the flattened (tile, kb) stream
-    int i_k = 0, i_kb = 0, i_j = 0;
+    int i_k = 0, i_kb = 0;
+    // LDS offset of the stage the next block is copied into, kept in a
+    // scalar register (each copy's M0 is this plus a constant)
+    uint32_t i_st = smem_base;
     bool i_done = false;
     int i_e = 0, i_nt = 0;
     const uint8_t* a_src[2] = {nullptr, nullptr};
@@ -356,7 +359,7 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
             if (i_done)
                 return 0;
         }
-        const uint32_t st = smem_base + (i_j % NSTAGE) * STAGE;
+        const uint32_t st = __builtin_amdgcn_readfirstlane(i_st);
         const int kb = i_kb;
         static_assert(C::A_COPIES == 2 && C::S_COPIES == 1, "the loops below");
 #pragma unroll
@@ -383,7 +386,7 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
             ++n;
         }
         ++i_kb;
-        ++i_j;
+        i_st = st + STAGE == smem_base + NSTAGE * STAGE ? smem_base : st + STAGE;
         return n;
     };
 
@@ -479,29 +482,34 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
             v8i af[4], bf[4];
             float sa[4][4], sa2[D64 ? 4 : 1][4];
             const float* s_lds = reinterpret_cast<const float*>(st + A_BYTES + B_BYTES);
+            // weight scales: L1 gate / up block; L2 the wave's 128-column block
+            const float sg = L1 ? s_lds[16] : s_lds[16 + (wn >> 1)];
+            const float su = L1 ? s_lds[17] : sg;
+            // one lane address per operand; the subtiles are constant offsets
+            const uint8_t* a_rd = st + wm * 8192 + lane * 16;
+            const uint8_t* b_rd = st + A_BYTES + wn * 8192 + lane * 16;
+            const float* sa_rd = s_lds + wm * 256 + 4 * lg;
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) {
-                af[ms] = lds_frag(st + ((wm * 4 + ms) * 2) * 1024, lane);
-                const float4 s4 = *reinterpret_cast<const float4*>(s_lds + (wm * 4 + ms) * 64 + 4 * lg);
+                af[ms] = pack_frag(*reinterpret_cast<const uint4*>(a_rd + ms * 2048),
+                                   *reinterpret_cast<const uint4*>(a_rd + ms * 2048 + 1024));
+                const float4 s4 = *reinterpret_cast<const float4*>(sa_rd + ms * 64);
                 sa[ms][0] = s4.x;
                 sa[ms][1] = s4.y;
                 sa[ms][2] = s4.z;
                 sa[ms][3] = s4.w;
                 if constexpr (D64) {  // the second half's scales, copied by lanes 32-47
-                    const float4 t4 =
-                        *reinterpret_cast<const float4*>(s_lds + (wm * 4 + ms) * 64 + 32 + 4 * lg);
+                    const float4 t4 = *reinterpret_cast<const float4*>(sa_rd + ms * 64 + 32);
                     sa2[ms][0] = t4.x;
                     sa2[ms][1] = t4.y;
                     sa2[ms][2] = t4.z;
                     sa2[ms][3] = t4.w;
                 }
+                // (read in the order the MFMAs below consume them, so the
+                // first ones start while the rest are in flight)
+                bf[ms] = pack_frag(*reinterpret_cast<const uint4*>(b_rd + ms * 2048),
+                                   *reinterpret_cast<const uint4*>(b_rd + ms * 2048 + 1024));
             }
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                bf[s] = lds_frag(st + A_BYTES + (wn * 4 + s) * 2048, lane);
-            // weight scales: L1 gate / up block; L2 the wave's 128-column block
-            const float sg = L1 ? s_lds[16] : s_lds[16 + (wn >> 1)];
-            const float su = L1 ? s_lds[17] : sg;
 
             issue_shift();
 

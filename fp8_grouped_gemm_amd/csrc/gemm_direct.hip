@@ -472,7 +472,7 @@ __device__ __forceinline__ void l2_splitk_finish(const FwdArgs& a, int tile)
     uint32_t w[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-        w[q] = (uint32_t)f32_to_bf16(p[2 * q]) | ((uint32_t)f32_to_bf16(p[2 * q + 1]) << 16);
+        w[q] = f32x2_to_bf16x2(p[2 * q], p[2 * q + 1]);
     const int t = f / a.K, j = f - t * a.K;
     uint4* dst = reinterpret_cast<uint4*>(a.partial + ((size_t)j * a.T + t) * H + c0);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -773,10 +773,10 @@ __device__ __forceinline__ void combine_chunk(const FwdArgs& a, int blk, int n_l
         }
     }
     uint4 o;
-    o.x = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
-    o.y = (uint32_t)f32_to_bf16(s[2]) | ((uint32_t)f32_to_bf16(s[3]) << 16);
-    o.z = (uint32_t)f32_to_bf16(s[4]) | ((uint32_t)f32_to_bf16(s[5]) << 16);
-    o.w = (uint32_t)f32_to_bf16(s[6]) | ((uint32_t)f32_to_bf16(s[7]) << 16);
+    o.x = f32x2_to_bf16x2(s[0], s[1]);
+    o.y = f32x2_to_bf16x2(s[2], s[3]);
+    o.z = f32x2_to_bf16x2(s[4], s[5]);
+    o.w = f32x2_to_bf16x2(s[6], s[7]);
     *reinterpret_cast<uint4*>(a.y + (size_t)t * a.H + c) = o;
 }
 

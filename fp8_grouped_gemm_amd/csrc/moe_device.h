@@ -203,14 +203,21 @@ __device__ __forceinline__ float silu(float g)
     return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
 }
 
-// f32 -> bf16 bits, round to nearest even (NaN stays NaN).
+// f32 -> bf16 bits, round to nearest even, a NaN quieted with its payload
+// kept: gfx950's v_cvt_pk_bf16_f32 (the compiler's conversion), which
+// equals that rounding done on the integer bits for every one of the 2^32
+// f32 patterns (denormals preserved; moe_probe_conversions checks it).
 __device__ __forceinline__ uint16_t f32_to_bf16(float v)
 {
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Two values in one conversion: a in bits 0-15, b in bits 16-31.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b)

@@ -118,6 +118,29 @@ __global__ void __launch_bounds__(256) mfma_block_probe(const uint8_t* __restric
         out[((size_t)tile * 16 + 4 * g + i) * 16 + r] = d[i];
 }
 
+// Every f32 bit pattern through the two conversions the epilogues rely on:
+// the library's f32 -> bf16 (the hardware conversion) against round to
+// nearest even written out on the integer bits (a NaN quieted, payload
+// kept), and the hardware f32 -> e4m3 (f32_to_e4m3_hw) against the integer
+// encoder f32_to_e4m3.  Lane t of the grid takes patterns t, t + N, ...
+// (N lanes) and writes its two mismatch counts to counts[t], counts[N + t].
+__global__ void __launch_bounds__(256) conversion_probe(uint32_t* __restrict__ counts)
+{
+    const uint32_t n = gridDim.x * 256u;
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    uint32_t c_bf = 0, c_e4 = 0;
+    for (uint64_t i = t; i < (1ull << 32); i += n) {
+        const uint32_t u = (uint32_t)i;
+        const float f = __uint_as_float(u);
+        const uint32_t ref = (u & 0x7FFFFFFFu) > 0x7F800000u ? ((u >> 16) | 0x40u) & 0xFFFFu
+                                                             : (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+        c_bf += moe::f32_to_bf16(f) != (uint16_t)ref ? 1u : 0u;
+        c_e4 += moe::f32_to_e4m3_hw(f) != moe::f32_to_e4m3(f) ? 1u : 0u;
+    }
+    counts[t] = c_bf;
+    counts[n + t] = c_e4;
+}
+
 int device_is_gfx950()
 {
     int dev = 0;
@@ -190,5 +213,17 @@ extern "C" int moe_probe_mfma_block(int32_t mode, int32_t n_tiles, const uint8_t
         hipLaunchKernelGGL(mfma_block_probe<true>, grid, dim3(256), 0, s, a, b, sa, sb, n_tiles, out);
     else
         hipLaunchKernelGGL(mfma_block_probe<false>, grid, dim3(256), 0, s, a, b, sa, sb, n_tiles, out);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" int moe_probe_conversions(int32_t blocks, uint32_t* counts, void* stream)
+{
+    if (!counts || blocks < 1 || blocks > 65536)
+        return MOE_ERR_INVALID_ARG;
+    const int dev = device_is_gfx950();
+    if (dev != MOE_OK)
+        return dev;
+    hipLaunchKernelGGL(conversion_probe, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       counts);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -13,7 +13,8 @@ MOE_PEAK_READ_PLAIN = 0
 MOE_PEAK_READ_NONTEMPORAL = 1
 MOE_PROBE_E4M3 = 0
 MOE_PROBE_E4M3_E2M1 = 1
-EXPORTED_SYMBOLS = ("moe_peak_stream_read", "moe_peak_mfma_fp8", "moe_probe_mfma_block")
+EXPORTED_SYMBOLS = ("moe_peak_stream_read", "moe_peak_mfma_fp8", "moe_probe_mfma_block",
+                    "moe_probe_conversions")
 MFMA_FLOP_PER_WAVE_ROUND = 8 * 2 * 16 * 16 * 128
 
 _lib = None
@@ -30,6 +31,7 @@ def lib():
         L.moe_peak_stream_read.argtypes = [vp, ctypes.c_size_t, i32, i32, i32, vp, vp]
         L.moe_peak_mfma_fp8.argtypes = [i32, i32, vp, vp]
         L.moe_probe_mfma_block.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp]
+        L.moe_probe_conversions.argtypes = [i32, vp, vp]
         for name in EXPORTED_SYMBOLS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -69,3 +71,11 @@ def probe_mfma_block(mode, a, b, out, sa=None, sb=None, stream=None):
                                     _ptr(out), _stream(stream))
     if rc != MOE_OK:
         raise MoEError(rc, "moe_probe_mfma_block")
+
+
+def probe_conversions(blocks, counts, stream=None):
+    """Mismatch counts of the bf16 and e4m3 conversions over every f32
+    pattern; counts: int32/uint32-sized tensor of 2 * 256 * blocks."""
+    rc = lib().moe_probe_conversions(blocks, _ptr(counts), _stream(stream))
+    if rc != MOE_OK:
+        raise MoEError(rc, "moe_probe_conversions")

@@ -76,6 +76,18 @@ int moe_peak_mfma_fp8(int32_t blocks, int32_t iters, float* out, void* stream);
 int moe_probe_mfma_block(int32_t mode, int32_t n_tiles, const uint8_t* a, const uint8_t* b,
                          const uint8_t* sa, const uint8_t* sb, float* out, void* stream);
 
+/* Exhaustive check of the two conversions the epilogues rely on, over all
+ * 2^32 f32 bit patterns: the library's f32 -> bf16 (gfx950's
+ * v_cvt_pk_bf16_f32) against round-to-nearest-even on the integer bits (a
+ * NaN quieted with its payload kept), and the hardware f32 -> e4m3 against
+ * the integer encoder of the requantisation.  `blocks` workgroups of 256
+ * lanes; lane t of the N = 256 * blocks lanes takes patterns t, t + N, ...
+ * and writes its mismatch counts to counts[t] (bf16) and counts[N + t]
+ * (e4m3); all zero means the conversions agree everywhere.
+ *   counts: uint32 [2 * 256 * blocks], written.  1 <= blocks <= 65536.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_NOT_GFX950, MOE_ERR_HIP. */
+int moe_probe_conversions(int32_t blocks, uint32_t* counts, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

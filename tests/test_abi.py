@@ -57,6 +57,8 @@ def test_peaks_reject_invalid_arguments_on_host():
     for blocks, iters, o in [(0, 16, out), (65537, 16, out), (256, 0, out), (256, 2049, out),
                              (256, 16, None)]:
         assert L.moe_peak_mfma_fp8(blocks, iters, o, None) == moe.MOE_ERR_INVALID_ARG
+    for blocks, o in [(0, out), (65537, out), (-1, out), (256, None)]:
+        assert L.moe_probe_conversions(blocks, o, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_strerror_names_every_code():

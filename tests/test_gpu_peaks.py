@@ -3,7 +3,9 @@ the streaming read touches every 32-bit word of the buffer exactly once (the
 XOR of its per-wave results equals the XOR of all words, for every load
 mode, unroll and grid, including sizes with a partial final round), and the
 FP8 MFMA loop runs exactly the instructions its FLOP count assumes (each
-lane's result is exactly 8 * 4 * 64 * iters)."""
+lane's result is exactly 8 * 4 * 64 * iters).  The conversion probe pins the
+two conversions the epilogues use to their integer definitions on every
+f32 bit pattern."""
 import numpy as np
 import pytest
 import torch
@@ -40,3 +42,16 @@ def test_mfma_loop_counts_every_instruction():
         peaks.mfma_fp8(blocks, iters, out)
         torch.cuda.synchronize()
         assert torch.all(out == float(8 * 4 * 64 * iters)), (blocks, iters)
+
+
+def test_conversions_match_their_definitions_on_every_f32():
+    # f32 -> bf16 (hardware) against round to nearest even on the bits, and
+    # the hardware f32 -> e4m3 against the integer encoder: 2^32 patterns
+    blocks = 4096
+    say(f"conversion probe: every f32 pattern over {blocks} workgroups")
+    counts = torch.full((2 * 256 * blocks,), -1, dtype=torch.int32, device="cuda")
+    peaks.probe_conversions(blocks, counts)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy().astype(np.int64).reshape(2, -1)
+    assert c[0].sum() == 0, f"bf16: {c[0].sum()} patterns differ"
+    assert c[1].sum() == 0, f"e4m3: {c[1].sum()} patterns differ"

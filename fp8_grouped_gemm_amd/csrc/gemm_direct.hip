@@ -370,7 +370,7 @@ __device__ __forceinline__ void l1_tile(const FwdArgs& a, int item)
                 hv[ms][s][i] = v;
                 m = fmaxf(m, fabsf(v));
             }
-            m = max16(m);
+            m = max16_nonneg(m);
             if (epi && lr == 0)
                 red[wave][16 * ms + 4 * lg + i] = m;
         }

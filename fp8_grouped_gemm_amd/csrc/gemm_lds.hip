@@ -603,7 +603,8 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = wm * 64 + ms * 16 + 4 * lg + i;
-                    const float w = slot_f(m_rs[r]) >= 0 ? m_w[r] : 0.f;
+                    const float wr = m_w[r];  // (always a finite weight: padding rows copy slot 0's)
+                    const float w = slot_f(m_rs[r]) >= 0 ? wr : 0.f;
                     float m = 0.f;
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
@@ -613,7 +614,7 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
                         acc[ms][s][i] = v;
                         m = fmaxf(m, fabsf(v));
                     }
-                    m = max16(m);
+                    m = max16_nonneg(m);
                     if (lr == 0)
                         red[r * 4 + wn] = m;
                 }

@@ -245,6 +245,27 @@ __device__ __forceinline__ float max16(float v)
     return v;
 }
 
+// max16 for values that are >= 0 and never NaN (a running fmaxf(m, |v|)
+// from m = 0 ignores NaN): on such floats the order of the bit patterns is
+// the order of the values, so the max runs on the integer bits and needs
+// no NaN handling (each step one DPP max instead of a move, a canonicalise
+// and a max).
+template <int CTRL>
+__device__ __forceinline__ uint32_t row_perm_u(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float max16_nonneg(float x)
+{
+    uint32_t v = __float_as_uint(x);
+    v = max(v, row_perm_u<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = max(v, row_perm_u<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = max(v, row_perm_u<0x141>(v));  // row_half_mirror
+    v = max(v, row_perm_u<0x140>(v));  // row_mirror
+    return __uint_as_float(v);
+}
+
 __device__ __forceinline__ v8i pack_frag(const uint4& lo, const uint4& hi)
 {
     v8i r;

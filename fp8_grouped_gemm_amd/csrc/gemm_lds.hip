@@ -420,6 +420,7 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
 
     // ---- multiply side
     int m_k = 0, m_kb = 0, j = 0;
+    int ms_live = 4;     // this wave's m-subtiles holding routed rows in tile m_k
     bool drain = false;  // global stores since the last wait: wait for everything
     for (;;) {
         if (i_done && m_k >= i_k)
@@ -443,6 +444,19 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
         }
         drain = false;
         __syncthreads();
+        // Routed rows form a prefix of each tile (an expert's segment is its
+        // rows, then padding up to the tile height): a wave whose 64 rows
+        // are all past it (wm = 1 in a tile of <= 64 routed rows, an
+        // expert's last tile mostly) skips its MFMAs and promotions --
+        // nothing reads padding rows.  (Skipping single m-subtiles too needs
+        // a branch per MFMA or one straight-line step per count, which
+        // serialises the MFMAs or spills.)
+        if (m_kb == 0) {
+            const int32_t* rs = reinterpret_cast<const int32_t*>(slot(m_k));
+            const int nv = __builtin_popcountll(__ballot(slot_f(rs[lane]) >= 0)) +
+                           __builtin_popcountll(__ballot(slot_f(rs[64 + lane]) >= 0));
+            ms_live = __builtin_amdgcn_readfirstlane(min(4, max(0, (nv - 64 * wm + 15) >> 4)));
+        }
 
         const uint8_t* st = smem + (j % NSTAGE) * STAGE;
         // the copy of the block NSTAGE - 1 ahead, into the stage read last step
@@ -472,6 +486,7 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
                            : s_lds[512 + ((wn * 4 + s) * 16 + lr) * 4 + lg];
             }
             issue_shift();
+            if (ms_live > 0)  // (a wave whose rows are all padding has nothing to multiply)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -513,6 +528,7 @@ __device__ __forceinline__ void lds_walk(const FwdArgs& a)
 
             issue_shift();
 
+            if (ms_live > 0)  // (a wave whose rows are all padding has nothing to multiply)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const float sb = (L1 && s >= 2) ? su : sg;

@@ -2,13 +2,15 @@
  * moe_peaks.h — C ABI of libmoe_peaks.so: the two kernels that measure what
  * an MI355X actually sustains, so the MoE kernels' rates can be stated
  * against the measured ceilings as well as the published ones (8 TB/s HBM,
- * 5.0 PFLOP/s dense FP8).  Not part of the MoE forward; the benchmark calls
- * them beside it.
+ * 5.0 PFLOP/s dense FP8), and two probes of the hardware operations the
+ * MoE kernels rely on (the MFMA's accumulation inside one instruction; the
+ * f32 -> bf16 and f32 -> e4m3 conversions).  Not part of the MoE forward;
+ * the benchmark and the tests call them beside it.
  *
  * Conventions as in moe_fp8.h: device pointers owned by the caller, work
  * enqueued asynchronously on `stream` (NULL = default stream), arguments
  * checked on the host before any HIP call, MOE_OK or a negative MOE_ERR_*
- * code returned.  Neither entry point allocates.
+ * code returned.  No entry point allocates.
  */
 #ifndef MOE_PEAKS_H
 #define MOE_PEAKS_H

@@ -1,6 +1,7 @@
 """Build the HIP libraries in-tree for gfx950 with hipcc: libmoe_fp8.so (the
 MoE forward) and libmoe_peaks.so (the ceiling-measurement kernels)."""
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -21,11 +22,30 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I" + os.path.join(HERE, "..", "include"), "-Wall"]
 
 
+# Kernels whose copy waits are counted by hand (vmcnt) must hold no other
+# vector memory access in their loop; a register spill to scratch would be
+# one, so these sources are compiled with the resource-usage report and the
+# build fails if any of their kernels uses scratch.
+NO_SCRATCH = ("gemm_lds.hip",)
+
+
+def _scratch_users(report):
+    """(kernel, bytes) of every kernel in a resource-usage report with scratch."""
+    out = []
+    for block in report.split("remark: Function Name: ")[1:]:
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", block)
+        if m and int(m.group(1)) > 0:
+            out.append((block.split()[0], int(m.group(1))))
+    return out
+
+
 def _compile(sources, verbose):
     objs, procs = [], []
     for src in sources:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        if src in NO_SCRATCH:
+            cmd.append("-Rpass-analysis=kernel-resource-usage")
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
@@ -51,6 +71,12 @@ def build(verbose: bool = False) -> str:
     failed = False
     for src, p in procs + peak_procs:
         out, _ = p.communicate()
+        if src in NO_SCRATCH:
+            users = _scratch_users(out)
+            out = "\n".join(l for l in out.splitlines() if "kernel-resource-usage" not in l)
+            if users:
+                failed = True
+                sys.stdout.write(f"{src}: kernels spill to scratch: {users}\n")
         if out.strip() and (verbose or p.returncode):
             sys.stdout.write(out)
         if p.returncode:

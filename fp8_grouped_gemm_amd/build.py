@@ -22,10 +22,11 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I" + os.path.join(HERE, "..", "include"), "-Wall"]
 
 
-# Kernels whose copy waits are counted by hand (vmcnt) must hold no other
-# vector memory access in their loop; a register spill to scratch would be
-# one, so these sources are compiled with the resource-usage report and the
-# build fails if any of their kernels uses scratch.
+# The 128-row kernels count their copy waits by hand (vmcnt) on the premise
+# that their loop holds no other vector memory access; a register spill to
+# scratch would add such accesses (each wait then over-waits), so this
+# source is compiled with the resource-usage report and the build fails if
+# any of its kernels uses scratch.
 NO_SCRATCH = ("gemm_lds.hip",)
 
 

@@ -309,6 +309,26 @@ def test_lds_hot_expert_panel_walk_bitwise():
     verify(y128, r128, host, "tile 128 hot-expert panel walk")
 
 
+def test_lds_tile_padding_row_halves_bitwise():
+    # Experts of 1, 63, 64, 65, 127, 128 and 129 routed rows: in the 128-row
+    # tile the waves of a row half that holds only padding skip their MFMAs
+    # (first tiles of <= 64 rows, the 129-row expert's second tile), while a
+    # half with one routed row (65) multiplies.  y is bitwise that of the
+    # 64-row shared-A tile, and matches the oracle.
+    sizes = [1, 63, 64, 65, 127, 128, 129, 0]
+    T = sum(sizes)
+    owner = [e for e, n in enumerate(sizes) for _ in range(n)]
+    host, dev = small_case(T, 256, 256, len(sizes), 1, 41, mask={(t, 0): owner[t] for t in range(T)})
+    y128, r128 = _run_flags(dev, 0, 128)
+    assert moe.moe_plan_info(r128.plan, T)["kernel"] == 1
+    counts = r128.view("counts", T).cpu().numpy()
+    assert counts.tolist() == sizes
+    y64, r64 = _run_flags(dev, 0, 64)
+    assert moe.moe_plan_info(r64.plan, T)["kernel"] == 2
+    assert torch.equal(y128, y64)
+    verify(y128, r128, host, "tile 128 padding row halves")
+
+
 def test_lds_tiles_full_size_packed_small_grid():
     # The flash-prefill workload on 128-row tiles on 4 workgroups (every
     # workgroup walks ~700 L1 tiles) against the full grid, packed weights,

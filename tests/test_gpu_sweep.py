@@ -16,7 +16,7 @@ import torch
 import fp8_grouped_gemm_amd as moe
 import oracle
 import workload as wl
-from parity_util import host_dict, say, verify
+from parity_util import host_copy_for_oracle, host_dict, say, verify
 
 pytestmark = pytest.mark.gpu
 
@@ -121,3 +121,74 @@ def test_random_case_against_oracle(c):
     oflags = ((oracle.ORC_POW2_SCALE if c["pow2"] else 0) |
               (oracle.ORC_SF_GRAN64 if c["gran"] == 64 else 0))
     verify(y, r, host, _name(c), oflags=oflags, clamp=c["clamp"])
+
+
+def _large_cases(n=12, seed=20261203):
+    """Larger calls (many tiles per workgroup, several K blocks per tile),
+    checked on sampled tokens."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        K = int(rng.integers(1, 9))
+        c = dict(
+            mx=bool(rng.random() < 0.3),
+            K=K,
+            E=int(rng.integers(max(K, 8), 65)),
+            T=int(rng.integers(300, 2049)),
+            H=int(rng.choice([1024, 1536, 2048])),
+            I=int(rng.choice([512, 768, 1024])),
+            tile=int(rng.choice([0, 16, 32, 64, 128])),
+            packed=bool(rng.random() < 0.5),
+            flag=str(rng.choice(list(FLAGS))),
+            gran=int(rng.choice([0, 0, 64])),
+            pow2=bool(rng.random() < 0.2),
+            clamp=float(rng.choice([0.0, 0.0, 0.5])),
+            skew=bool(rng.random() < 0.5),
+            n_mask=int(rng.integers(0, 4)),
+            seed=int(rng.integers(0, 1 << 30)),
+        )
+        if _accepted(c):
+            out.append(c)
+    return out
+
+
+LARGE = _large_cases()
+
+
+@pytest.mark.parametrize("c", LARGE, ids=[_name(c) for c in LARGE])
+def test_random_large_case_sampled(c):
+    say(f"sweep large {_name(c)} seed={c['seed']}")
+    cfg = wl.custom_config(c["T"], c["H"], c["I"], c["E"], c["K"], c["skew"])
+    inp = (wl.make_inputs_mx if c["mx"] else wl.make_inputs)(cfg, c["seed"], "cuda")
+    rng = np.random.default_rng(c["seed"])
+    idx = inp["topk_idx"].clone()
+    for _ in range(c["n_mask"]):
+        t, j = int(rng.integers(0, c["T"])), int(rng.integers(0, c["K"]))
+        idx[t, j] = int(rng.choice([-1, c["E"], c["E"] + 77]))
+    inp["topk_idx"] = idx
+    T, E, K = c["T"], c["E"], c["K"]
+    flags = FLAGS[c["flag"]] | (moe.MOE_FLAG_POW2_SCALE if c["pow2"] else 0)
+    r = moe.MoEForward(c["H"], c["I"], E, K, T, tile_m=c["tile"],
+                       weight_layout=moe.MOE_WEIGHTS_PACKED if c["packed"] else
+                       moe.MOE_WEIGHTS_ROW_MAJOR,
+                       flags=flags, act_sf_gran=c["gran"], activation_clamp=c["clamp"],
+                       recipe=moe.MOE_RECIPE_MXFP4 if c["mx"] else moe.MOE_RECIPE_FP8_BLOCK128)
+    if c["mx"]:
+        w1, w1_sf, w2, w2_sf = r.prepare_mx(inp["w1"], inp["w1_sf"], inp["w2"], inp["w2_sf"])
+    else:
+        (w1, w2), w1_sf, w2_sf = r.prepare(inp["w1"], inp["w2"]), inp["w1_sf"], inp["w2_sf"]
+    y = r.forward(inp["x"], inp["x_sf"], inp["topk_idx"], inp["topk_w"], w1, w1_sf, w2, w2_sf)
+    torch.cuda.synchronize()
+    host_idx = inp["topk_idx"].cpu().numpy()
+    info = moe.moe_plan_info(r.plan, T)
+    rc, ro, rrs, rsr, bad = oracle.route(host_idx, E, info["tile_m"], info["pool_rows"])
+    assert np.array_equal(r.view("counts", T).cpu().numpy(), rc)
+    assert np.array_equal(r.view("offsets", T).cpu().numpy(), ro)
+    assert np.array_equal(r.view("row_src", T).cpu().numpy(), rrs)
+    assert np.array_equal(r.view("src_row", T).cpu().numpy(), rsr)
+    assert moe.moe_read_status(r.plan, T, r.workspace)[1] == bad
+    toks = sorted({0, T - 1, *rng.choice(T, 14, replace=False).tolist()})
+    oflags = ((oracle.ORC_POW2_SCALE if c["pow2"] else 0) |
+              (oracle.ORC_SF_GRAN64 if c["gran"] == 64 else 0))
+    verify(y, r, host_copy_for_oracle(inp, toks), _name(c), tokens=toks, oflags=oflags,
+           clamp=c["clamp"])

@@ -8,7 +8,9 @@ activation clamp, skewed routing and a few masked or out-of-range slots, all
 from one fixed seed, keeping only combinations the plan accepts.  The HIP
 path runs through the C ABI and the result goes through parity_util.verify
 against the oracle with the matching options, over every token; the call's
-routing tables are compared bit for bit with the oracle's."""
+routing tables are compared bit for bit with the oracle's, and FP8 calls
+that fit the no-alloc entry point's scratch are repeated through it and
+compared bit for bit with the workspace forward."""
 import numpy as np
 import pytest
 import torch
@@ -19,6 +21,8 @@ import workload as wl
 from parity_util import host_copy_for_oracle, host_dict, say, verify
 
 pytestmark = pytest.mark.gpu
+
+NOALLOC_BYTES = 32 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 FLAGS = {
     "none": 0,
@@ -121,6 +125,14 @@ def test_random_case_against_oracle(c):
     oflags = ((oracle.ORC_POW2_SCALE if c["pow2"] else 0) |
               (oracle.ORC_SF_GRAN64 if c["gran"] == 64 else 0))
     verify(y, r, host, _name(c), oflags=oflags, clamp=c["clamp"])
+    # the entry point that allocates nothing (FP8 plans whose workspace fits
+    # its scratch): the same kernels, so the same bits
+    if not c["mx"] and moe.moe_workspace_bytes(r.plan, T) <= NOALLOC_BYTES:
+        y_na = torch.full_like(y, 0x7FC0)
+        moe.moe_forward_noalloc(r.plan, T, dev["x"], dev["x_sf"], dev["topk_idx"], dev["topk_w"],
+                                w1, w1_sf, w2, w2_sf, y_na)
+        torch.cuda.synchronize()
+        assert torch.equal(y_na, y), "no-alloc entry point differs"
 
 
 def _large_cases(n=12, seed=20261203):

@@ -308,7 +308,7 @@ def main():
                     help="single: L1, L2 and combine in one cooperative launch (direct "
                          "tiles); ring: the same over the lag-ordered ring pool; split: "
                          "one launch per step; auto: the library's choice")
-    ap.add_argument("--tile-m", type=int, default=0, choices=(0, 16, 32, 64, 128),
+    ap.add_argument("--tile-m", type=int, default=0, choices=(0, 16, 32, 64, 128, 160),
                     help="rows per GEMM tile (0 = the library's choice per call)")
     ap.add_argument("--recipe", choices=("fp8", "mxfp4"), default="fp8",
                     help="fp8: e4m3 x e4m3 with f32 block scales (1x128, 128x128); mxfp4: "
@@ -494,7 +494,7 @@ def run_workload(args, cfg, seed, steps, warmup, flush, cpu_1t):
         dom = max(("l1", "l2"), key=lambda n: avg[n])
         dom_bytes = alg[dom]
         kernel_name = (("MXFP4 " if mx else "") + ("L1 step: GEMM gate+up, SwiGLU x topk_w, e4m3 requant "
-                        f"({('direct-load', 'LDS-staged', 'shared-A')[info['kernel']]} tiles, "
+                        f"({('direct-load', 'LDS-staged', 'shared-A', 'LDS-staged')[info['kernel']]} tiles, "
                         f"tile_m {info['tile_m']})") if dom == "l1" else
                        ("MXFP4 " if mx else "") + f"L2 step: GEMM down (tile_m {info['tile_m']})")
     achieved = dom_bytes / (avg[dom] * 1e-6) / 1e9

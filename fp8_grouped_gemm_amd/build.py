@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_fp8.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["moe_api.cpp", "route.hip", "gemm_direct.hip", "gemm_lds.hip", "gemm_sa.hip",
+SOURCES = ["moe_api.cpp", "route.hip", "gemm_direct.hip", "gemm_lds.hip", "gemm_lds160.hip", "gemm_sa.hip",
            "gemm_mx.hip", "pack.hip", "quant.hip"]
 PEAKS_LIB = os.path.join(HERE, "libmoe_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]
@@ -27,7 +27,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # scratch would add such accesses (each wait then over-waits), so this
 # source is compiled with the resource-usage report and the build fails if
 # any of its kernels uses scratch.
-NO_SCRATCH = ("gemm_lds.hip",)
+NO_SCRATCH = ("gemm_lds.hip", "gemm_lds160.hip")
 
 
 def _scratch_users(report):

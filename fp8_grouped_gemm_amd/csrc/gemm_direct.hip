@@ -1069,6 +1069,8 @@ hipError_t launch_l1(const FwdArgs& a, int kernel, hipStream_t s)
         return launch_l1_lds(a, s);
     if (kernel == 2)
         return launch_l1_sa(a, s);
+    if (kernel == 3)
+        return launch_l1_lds160(a, s);
     return a.packed ? launch_l1_t<true>(a, s) : launch_l1_t<false>(a, s);
 }
 
@@ -1078,6 +1080,8 @@ hipError_t launch_l2(const FwdArgs& a, int kernel, hipStream_t s)
         return launch_l2_lds(a, s);
     if (kernel == 2)
         return launch_l2_sa(a, s);
+    if (kernel == 3)
+        return launch_l2_lds160(a, s);
     return a.packed ? launch_l2_t<true>(a, s) : launch_l2_t<false>(a, s);
 }
 

@@ -86,30 +86,6 @@ static_assert(LdsCfg<false>::COPIES == 2 + 4 + 1 && LdsCfg<true>::COPIES == 2 + 
               "copy counts per wave and K block");
 static_assert(LdsCfg<false>::SMEM <= 160 * 1024 && LdsCfg<true>::SMEM <= 160 * 1024, "LDS");
 
-// Address of the 16 bytes lane `lane` copies for weight subtile `sub`
-// (packed order w4 * 4 + s, see pack.hip), half `half`, K block kb.
-template <bool L1, bool PK>
-__device__ __forceinline__ const uint8_t* weight_src(const FwdArgs& a, int e, int nt, int kb,
-                                                     int sub, int half, int lane)
-{
-    const int H = a.H, I = a.I;
-    if constexpr (PK) {
-        const size_t nkb = L1 ? H / 128 : I / 128;
-        const uint8_t* base = L1 ? a.w1 + (size_t)e * 2 * I * H : a.w2 + (size_t)e * H * I;
-        return base + ((size_t)nt * nkb + kb) * 32768 + (sub * 2 + half) * 1024 + lane * 16;
-    } else {
-        const int w4 = sub >> 2, s = sub & 3, lr = lane & 15, lg = lane >> 4;
-        const int col = kb * 128 + half * 64 + 16 * lg;
-        if constexpr (L1) {
-            const int row = (s >= 2 ? I : 0) + nt * 128 + w4 * 32 + (s & 1) * 16 + lr;
-            return a.w1 + ((size_t)e * 2 * I + row) * H + col;
-        } else {
-            const int row = nt * 256 + w4 * 64 + s * 16 + lr;
-            return a.w2 + ((size_t)e * H + row) * I + col;
-        }
-    }
-}
-
 // MXFP4: address of the 16 bytes lane `lane` copies for weight subtile
 // q = 4 w + s of K block kb (packed: moe_prepare_weights_mx order).
 template <bool L1, bool PK>

@@ -60,6 +60,42 @@ bool lds_tile_fits(const moe_shape_t& s)
     return s.hidden % 256 == 0 && s.hidden / 128 >= min_kb && s.intermediate / 128 >= min_kb;
 }
 
+// The 160-row LDS tile (gemm_lds160.hip): FP8 recipe with per-128 scales
+// and packed weights, and copy offsets that fit 31 bits (x rows, pool rows of
+// h; the kernel addresses them as 32-bit offsets from one base).
+bool lds160_fits(const moe_shape_t& s)
+{
+    if (!lds_tile_fits(s) || s.recipe != MOE_RECIPE_FP8_BLOCK128 || sf_gran(s) != 128 ||
+        s.weight_layout != MOE_WEIGHTS_PACKED || (s.flags & MOE_FLAG_RING_POOL))
+        return false;
+    const long long rows = (long long)s.max_tokens * s.top_k + (long long)s.num_experts * 160;
+    return (long long)s.max_tokens * s.hidden < (1LL << 31) && rows * s.intermediate < (1LL << 31);
+}
+
+// 160- or 128-row LDS tiles at a mean of m routed rows per expert: the
+// expected number of row tiles per expert, E[ceil(n / B)] = sum over k >= 0
+// of P(n > k B), with n ~ Normal(m, sqrt(m)) (uniform routing: a Poisson
+// count), each 160-row tile priced at 1.1 times a 128-row one (its stage
+// copies 52 KiB where the 128-row tile copies 48).  Measured on the pro and
+// flash prefill shapes from 72 to 256 rows per expert, this picks the faster
+// tile at every point (160 wins from ~120 to ~170 rows and again at 256;
+// pro prefill at 128 rows: 6680 against 7920 us per layer).  Skewed routing
+// at the same mean (the skewed workload) runs ~3 % slower on 160-row tiles;
+// the plan sees only the mean.
+double expected_tiles(double m, int B)
+{
+    const double sd = std::sqrt(std::max(m, 1.0));
+    double e = 1.0;
+    for (int k = 1; k < 64; ++k) {
+        const double p = 0.5 * std::erfc((k * B + 0.5 - m) / (sd * std::sqrt(2.0)));
+        e += p;
+        if (p < 1e-12)
+            break;
+    }
+    return e;
+}
+bool prefers160(double m) { return 1.1 * expected_tiles(m, 160) < expected_tiles(m, 128); }
+
 constexpr double kRows16 = 10.0;     // FP8: 16-row tiles up to here (12 rows: 32-row 6 % faster)
 constexpr double kRows16Mx = 12.0;   // MXFP4: 16-row tiles up to here, then shared-A
 constexpr double kRows32 = 21.0;
@@ -80,7 +116,7 @@ Config choose_config(const moe_shape_t& s, int T)
     // 64-row tiles where the LDS tiles fit: the shared-A tile (kernel 2)
     const int k64 = lds64 ? 2 : 0;
     if (s.tile_m > 0)
-        return Config{s.tile_m, s.tile_m == 128 ? 1 : s.tile_m == 64 ? k64 : 0};
+        return Config{s.tile_m, s.tile_m == 160 ? 3 : s.tile_m == 128 ? 1 : s.tile_m == 64 ? k64 : 0};
     const double rows = (double)T * s.top_k / s.num_experts;
     const bool mx = s.recipe == MOE_RECIPE_MXFP4;
     if (rows <= (mx ? kRows16Mx : kRows16))
@@ -93,6 +129,8 @@ Config choose_config(const moe_shape_t& s, int T)
         return Config{64, 0};
     if (rows <= kRowsLds64 || (mx && lds64 && rows > kRowsLds128Mx))
         return Config{64, k64};
+    if (lds160_fits(s) && prefers160(rows))
+        return Config{160, 3};
     return Config{128, 1};
 }
 
@@ -250,6 +288,16 @@ size_t splitk_floats(const moe_shape_t& s, int T)
 int max_tile_upto(const moe_shape_t& s, int T)
 {
     int m = choose_config(s, T).tile_m;
+    // 160-row tiles: taken at some token count <= T once the mean reaches the
+    // first mean the rule above prefers them at (scanned in quarter rows)
+    if (lds160_fits(s) && s.tile_m == 0) {
+        const double rows = (double)T * s.top_k / s.num_experts;
+        for (double x = kRowsLds64; x <= rows; x += 0.25)
+            if (prefers160(x)) {
+                m = std::max(m, 160);
+                break;
+            }
+    }
     for (double x : {kRows16, kRows16Mx, kRows32, kRowsLds64, kRowsLds128Mx}) {
         // last token count with at most x rows per expert, and the next
         const long long t = (long long)std::floor(x * s.num_experts / s.top_k);
@@ -360,7 +408,9 @@ int validate_shape(const moe_shape_t* s)
     if (s->hidden > (1 << 16) || s->intermediate > (1 << 16))
         return MOE_ERR_UNSUPPORTED_SHAPE;
     if (s->tile_m != 0 && s->tile_m != 16 && s->tile_m != 32 && s->tile_m != 64 &&
-        s->tile_m != 128)
+        s->tile_m != 128 && s->tile_m != 160)
+        return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (s->tile_m == 160 && !lds160_fits(*s))
         return MOE_ERR_UNSUPPORTED_SHAPE;
     if (s->recipe != MOE_RECIPE_FP8_BLOCK128 && s->recipe != MOE_RECIPE_MXFP4)
         return MOE_ERR_INVALID_ARG;

@@ -131,6 +131,8 @@ hipError_t launch_l1_mx(const FwdArgs& a, hipStream_t s);  // direct tiles, tile
 hipError_t launch_l2_mx(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l1_lds(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l2_lds(const FwdArgs& a, hipStream_t s);
+hipError_t launch_l1_lds160(const FwdArgs& a, hipStream_t s);  // 160-row tiles
+hipError_t launch_l2_lds160(const FwdArgs& a, hipStream_t s);
 hipError_t launch_l1_sa(const FwdArgs& a, hipStream_t s);  // 64-row shared-A tiles
 hipError_t launch_l2_sa(const FwdArgs& a, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* x, int T, int H, uint8_t* q, void* sf, bool mx,

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "moe_device.h"
+#include "moe_internal.h"
 
 namespace moe {
 
@@ -54,6 +55,16 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base)
                  : "memory", "m0");
 }
 
+// The same copy with a wave-uniform 64-bit base in scalar registers and a
+// 32-bit unsigned per-lane byte offset (the global SADDR form): one vector
+// register per lane address instead of two.
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t off, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
+
 // 32-bit LDS offset of a __shared__ object (what M0 expects).
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p)
 {
@@ -67,6 +78,31 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* sub_base, int lane)
     const uint4 lo = *reinterpret_cast<const uint4*>(sub_base + lane * 16);
     const uint4 hi = *reinterpret_cast<const uint4*>(sub_base + 1024 + lane * 16);
     return pack_frag(lo, hi);
+}
+
+// FP8 weights of the LDS-staged tiles (256 columns per tile): address of
+// the 16 bytes lane `lane` copies for weight subtile `sub` (packed order
+// w4 * 4 + s, see pack.hip), half `half`, K block kb of column tile nt.
+template <bool L1, bool PK>
+__device__ __forceinline__ const uint8_t* weight_src(const FwdArgs& a, int e, int nt, int kb,
+                                                     int sub, int half, int lane)
+{
+    const int H = a.H, I = a.I;
+    if constexpr (PK) {
+        const size_t nkb = L1 ? H / 128 : I / 128;
+        const uint8_t* base = L1 ? a.w1 + (size_t)e * 2 * I * H : a.w2 + (size_t)e * H * I;
+        return base + ((size_t)nt * nkb + kb) * 32768 + (sub * 2 + half) * 1024 + lane * 16;
+    } else {
+        const int w4 = sub >> 2, s = sub & 3, lr = lane & 15, lg = lane >> 4;
+        const int col = kb * 128 + half * 64 + 16 * lg;
+        if constexpr (L1) {
+            const int row = (s >= 2 ? I : 0) + nt * 128 + w4 * 32 + (s & 1) * 16 + lr;
+            return a.w1 + ((size_t)e * 2 * I + row) * H + col;
+        } else {
+            const int row = nt * 256 + w4 * 64 + s * 16 + lr;
+            return a.w2 + ((size_t)e * H + row) * I + col;
+        }
+    }
 }
 
 }  // namespace moe

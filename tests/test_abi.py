@@ -150,6 +150,30 @@ def test_tile128_needs_two_k_blocks_per_layer():
     moe.moe_plan_destroy(moe.moe_plan_create(256, 256, 8, 2, 64, tile_m=128))
 
 
+def test_tile160_validation_and_info():
+    # the 160-row LDS tile: FP8 recipe, per-128 intermediate scales, packed
+    # weights, two K blocks per layer, 31-bit copy offsets; no ring pool
+    P = moe.MOE_WEIGHTS_PACKED
+    bad = [((512, 384, 16, 4, 256), dict()),                                  # row-major
+           ((512, 384, 16, 4, 256), dict(weight_layout=P, recipe=moe.MOE_RECIPE_MXFP4)),
+           ((512, 384, 16, 4, 256), dict(weight_layout=P, act_sf_gran=64)),
+           ((512, 384, 16, 4, 256), dict(weight_layout=P, flags=moe.MOE_FLAG_RING_POOL)),
+           ((256, 128, 8, 2, 64), dict(weight_layout=P)),                      # one K block of I
+           ((7168, 3072, 384, 6, 1 << 19), dict(weight_layout=P))]             # T*H >= 2^31
+    for shape, kw in bad:
+        with pytest.raises(moe.MoEError) as e:
+            moe.moe_plan_create(*shape, tile_m=160, **kw)
+        assert e.value.code == moe.MOE_ERR_UNSUPPORTED_SHAPE, (shape, kw)
+    p = moe.moe_plan_create(512, 384, 16, 4, 256, tile_m=160, weight_layout=P)
+    try:
+        info = moe.moe_plan_info(p, 256)
+        assert (info["tile_m"], info["row_align"], info["kernel"]) == (160, 160, 3)
+        # pool capacity: T*K + E*(160 - 1) rounded up to 160 rows
+        assert info["pool_rows"] == -(-(256 * 4 + 16 * 159) // 160) * 160
+    finally:
+        moe.moe_plan_destroy(p)
+
+
 def test_tile64_kernel_choice():
     # 64-row tiles run on the shared-A kernel where the LDS tiles fit (per-64
     # scales included), on the direct-load kernel where they do not (H % 256

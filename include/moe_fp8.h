@@ -109,12 +109,16 @@ typedef struct moe_shape {
     int32_t num_experts;   /* E */
     int32_t top_k;         /* K */
     int32_t max_tokens;    /* largest T any call on this plan may pass */
-    int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64 or 128.
-                              Where the LDS tiles fit (H % 256 == 0, H and I >= 256
-                              (MXFP4: 384), per-128 scales) 128 runs the LDS-staged
-                              kernel and 64 the shared-A kernel;
+    int32_t tile_m;        /* 0 = choose per call from T*K/E; else 16, 32, 64, 128
+                              or 160.  Where the LDS tiles fit (H % 256 == 0, H and
+                              I >= 256 (MXFP4: 384), per-128 scales) 128 runs the
+                              LDS-staged kernel and 64 the shared-A kernel;
                               128 requires it, 64 otherwise (or with
-                              MOE_FLAG_DIRECT_TILES) runs the direct-load kernel */
+                              MOE_FLAG_DIRECT_TILES) runs the direct-load kernel.
+                              160 (the 160-row LDS-staged kernel) requires the FP8
+                              recipe with per-128 scales, packed weights, no ring
+                              pool, max_tokens * H < 2^31 and
+                              (max_tokens * K + 160 E) * I < 2^31 */
     int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR or MOE_WEIGHTS_PACKED */
     int32_t flags;         /* MOE_FLAG_* bits, 0 = defaults */
     int32_t recipe;        /* MOE_RECIPE_*; MXFP4 plans: no single launch,
@@ -140,7 +144,8 @@ typedef struct moe_tile_info {
     int32_t l1_tile_n;   /* L1 output columns per tile (gate + up) */
     int32_t l2_tile_n;   /* L2 output columns per tile */
     int32_t kernel;      /* 0 = direct-load tile kernel, 1 = LDS-staged tile kernel,
-                            2 = shared-A tile kernel (64 rows) */
+                            2 = shared-A tile kernel (64 rows), 3 = 160-row
+                            LDS-staged tile kernel */
     int32_t l1_split;    /* workgroups sharing one L1 tile's K range (1 = no split;
                             16-row tiles with fewer tiles than compute units) */
     int32_t single_launch; /* 1: L1, L2 and combine run as one launch */

@@ -60,7 +60,13 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base)
 // register per lane address instead of two.
 __device__ __forceinline__ void dma16_off(const void* base, uint32_t off, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+    // (the base is wave-uniform; reading it from the first lane keeps it in
+    // scalar registers whatever the compiler concluded about it)
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+                 "s"(reinterpret_cast<const void*>(ub)),
                  "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory", "m0");
 }

@@ -74,6 +74,7 @@ constexpr int B_COPIES = B_BYTES / 1024 / 8;
 __device__ __forceinline__ int s_copies(int w) { return w < 3 ? 1 : 0; }
 __device__ __forceinline__ int m_copies(int w) { return w >= 5 ? 1 : 0; }
 static_assert(4 * 3 + 4 * 2 == A_BYTES / 1024, "A copies: 20 of 1 KiB");
+constexpr int kMinBatch = 2 + B_COPIES;  // the smallest batch any wave issues
 static_assert(2 * 64 + 32 == BM, "scale and row-source copies: 64 + 64 + 32 rows");
 
 }  // namespace
@@ -302,7 +303,14 @@ __device__ __forceinline__ void lds160_walk(const FwdArgs& a)
         // Block j has landed (only the one newer batch may be outstanding)
         // and is visible to all waves; the previous step's fragment reads
         // are done, so the stage issued below is free.
-        wait_vmcnt(drain ? 0 : pend);
+        // Every wave's batches hold at least kMinBatch copies (2 A + 4 B), so
+        // vmcnt <= kMinBatch also leaves block j landed; a wave whose newer
+        // batch is larger waits for its first copies too (issued a step
+        // ago), for one wait instead of a branch per batch size.
+        if (drain || pend == 0)
+            MOE_WAIT_VMCNT(0);
+        else
+            MOE_WAIT_VMCNT(kMinBatch);
         drain = false;
         __syncthreads();
         // Routed rows form a prefix of each tile: a wave whose 80 rows are

@@ -185,9 +185,7 @@ __device__ __forceinline__ void lds160_walk(const FwdArgs& a)
         if constexpr (PK) {
             i_wbase = (L1 ? a.w1 + (size_t)e * 2 * I * H : a.w2 + (size_t)e * H * I) +
                       (size_t)nt * nkb * 32768;
-#pragma unroll
-            for (int j = 0; j < B_COPIES; ++j)
-                b_off[j] = (uint32_t)((wave * B_COPIES + j) * 1024 + lane * 16);
+            b_off[0] = (uint32_t)(lane * 16);  // (copy j adds j KiB as an immediate)
         } else {
             i_wbase = L1 ? a.w1 + (size_t)e * 2 * I * H : a.w2 + (size_t)e * H * I;
 #pragma unroll
@@ -259,9 +257,21 @@ __device__ __forceinline__ void lds160_walk(const FwdArgs& a)
         if (nA == 3)
             dma16_off(abase, a_off[2], st + (wave + 16) * 1024);
         const uint8_t* wbase = i_wbase + (size_t)kb * (PK ? 32768 : 128);
+        if constexpr (PK) {  // this wave's 4 KiB of the block: one offset register
+            // (the instruction's constant offset moves the global and the
+            // LDS address alike, so all four copies take the same M0)
+            static_assert(B_COPIES == 4, "the copies below");
+            const uint8_t* wb = wbase + wave * B_COPIES * 1024;
+            const uint32_t sb = st + A_BYTES + wave * B_COPIES * 1024;
+            dma16_off_imm<0>(wb, b_off[0], sb);
+            dma16_off_imm<1024>(wb, b_off[0], sb);
+            dma16_off_imm<2048>(wb, b_off[0], sb);
+            dma16_off_imm<3072>(wb, b_off[0], sb);
+        } else {
 #pragma unroll
-        for (int j = 0; j < B_COPIES; ++j)
-            dma16_off(wbase, b_off[j], st + A_BYTES + (wave * B_COPIES + j) * 1024);
+            for (int j = 0; j < B_COPIES; ++j)
+                dma16_off(wbase, b_off[j], st + A_BYTES + (wave * B_COPIES + j) * 1024);
+        }
         if (nS && (wave < 2 || lane < 34))
             dma4(s_src + kb, st + A_BYTES + B_BYTES + wave * 256);
         int n = nA + B_COPIES + nS;

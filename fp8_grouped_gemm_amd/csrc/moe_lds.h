@@ -71,6 +71,34 @@ __device__ __forceinline__ void dma16_off(const void* base, uint32_t off, uint32
                  : "memory", "m0");
 }
 
+// dma16_off with a constant byte offset IMM (0 <= IMM < 4096) that the
+// instruction adds to both the global and the LDS address (the LDS copy
+// lands at lds_base + IMM + 16 * lane), so copies that differ by a constant
+// share one offset register and one M0.
+template <int IMM>
+__device__ __forceinline__ void dma16_off_imm(const void* base, uint32_t off, uint32_t lds_base)
+{
+    static_assert(IMM >= 0 && IMM < 4096, "the instruction's offset field");
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(off),
+                 "s"(reinterpret_cast<const void*>(ub)),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base)), "n"(IMM)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4_off(const void* base, uint32_t off, uint32_t lds_base)
+{
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off),
+                 "s"(reinterpret_cast<const void*>(ub)),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory", "m0");
+}
+
 // 32-bit LDS offset of a __shared__ object (what M0 expects).
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p)
 {

@@ -274,6 +274,10 @@ def main():
     ap.add_argument("--tokens", type=int, default=None,
                     help="override the workload's token count (same shapes and routing recipe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one forward in a HIP graph after the warm-up and replay it on "
+                         "the timed steps that carry no stage events (the launches a serving "
+                         "loop would replay; the same kernels and work)")
     ap.add_argument("--event-every", type=int, default=4, metavar="N",
                     help="record the per-stage HIP events on every N-th timed step (1: all)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
@@ -454,6 +458,20 @@ def run_workload(args, cfg, seed, steps, warmup, flush, cpu_1t):
     for step_evs in evs.values():
         for e in step_evs:
             e.record(stream)
+    graph = None
+    if getattr(args, "graph", False):
+        # one forward captured on the bench stream (the library allocates and
+        # copies nothing inside a forward, so it records kernel launches only)
+        # (captured on a side stream of default priority: torch does not
+        # capture on the default stream)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            forward(runner.plan, cfg.T, *fwd_args, stream=cap)
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -462,6 +480,9 @@ def run_workload(args, cfg, seed, steps, warmup, flush, cpu_1t):
     for k in range(steps):
         if k in evs:
             forward_timed(runner.plan, cfg.T, *fwd_args, stream, evs[k])
+        elif graph is not None:
+            with torch.cuda.stream(stream):
+                graph.replay()
         else:
             forward(runner.plan, cfg.T, *fwd_args, stream=stream)
     t_end.record(stream)
@@ -535,6 +556,7 @@ def run_workload(args, cfg, seed, steps, warmup, flush, cpu_1t):
         "active_experts": alg["active_experts"],
         "routed_rows": alg["rows"],
         "wall_s_timed": round(wall, 3),
+        "graph_replay": graph is not None,
         "roofline": {
             "kernel": kernel_name,
             "bound": "hbm",

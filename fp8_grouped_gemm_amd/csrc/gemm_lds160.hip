@@ -39,8 +39,10 @@
 // these): A: 20 copies of 1 KiB, wave w takes w, w + 8 and (w < 4) w + 16;
 // B: 4 each; scales: waves 0-2 one 4-byte copy each (wave 2: rows 128-159
 // in lanes 0-31, the weight scales in lanes 32-33); on a tile's first block
-// waves 5-7 also copy the next tile's row sources.  "Block j landed" is
-// vmcnt <= the size of the one batch this wave issued after it.
+// waves 5-7 also copy the next tile's row sources.  Only the batch of the
+// block after j may be outstanding when block j is multiplied, and every
+// batch holds at least kMinBatch copies, so "block j landed" is
+// vmcnt <= kMinBatch in every wave.
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "moe_lds.h"

@@ -174,6 +174,34 @@ def test_tile160_validation_and_info():
         moe.moe_plan_destroy(p)
 
 
+def test_tile160_auto_choice_follows_the_measured_sweep():
+    # the expected-row-tiles rule against the measured faster tile (pro and
+    # flash prefill shapes, packed FP8 weights): 160 rows from ~120 to ~170
+    # rows per expert and at 256, 128 rows at 96, 112 and 192; row-major
+    # weights and per-64 scales keep the 128-row tile
+    P = moe.MOE_WEIGHTS_PACKED
+    cases = [((7168, 3072, 384, 6), 6144, 128), ((7168, 3072, 384, 6), 7168, 128),
+             ((7168, 3072, 384, 6), 8192, 160), ((7168, 3072, 384, 6), 9216, 160),
+             ((7168, 3072, 384, 6), 10240, 160), ((7168, 3072, 384, 6), 12288, 128),
+             ((7168, 3072, 384, 6), 16384, 160), ((4096, 2048, 256, 6), 4096, 128),
+             ((4096, 2048, 256, 6), 5461, 160), ((4096, 2048, 256, 6), 6827, 160),
+             ((4096, 2048, 256, 6), 8192, 128)]
+    for shape, T, tile in cases:
+        p = moe.moe_plan_create(*shape, T, weight_layout=P)
+        try:
+            info = moe.moe_plan_info(p, T)
+            assert info["tile_m"] == tile, (shape, T, info["tile_m"])
+            assert info["kernel"] == (3 if tile == 160 else 1)
+        finally:
+            moe.moe_plan_destroy(p)
+    for kw in (dict(), dict(weight_layout=P, act_sf_gran=64)):
+        p = moe.moe_plan_create(7168, 3072, 384, 6, 8192, **kw)
+        try:
+            assert moe.moe_plan_info(p, 8192)["tile_m"] == 128, kw
+        finally:
+            moe.moe_plan_destroy(p)
+
+
 def test_tile64_kernel_choice():
     # 64-row tiles run on the shared-A kernel where the LDS tiles fit (per-64
     # scales included), on the direct-load kernel where they do not (H % 256
